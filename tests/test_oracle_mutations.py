@@ -1,0 +1,152 @@
+"""Plants plausible mistakes in the CPU oracle (on the CPU, in this process
+only) and checks that at least one pin of test_oracle_pins fails for each.
+This shows the pins constrain every step of the oracle."""
+import numpy as np
+import pytest
+
+import oracle.nanospec_oracle as O
+from tests.test_oracle_pins import PINS
+
+
+def _topk_tie_desc(z, K):
+    z = np.asarray(z, np.float64)
+    K = min(int(K), len(z))
+    order = np.lexsort((-np.arange(len(z)), -z))
+    return order[:K]
+
+
+def _topk_ascending(z, K):
+    z = np.asarray(z, np.float64)
+    K = min(int(K), len(z))
+    return np.lexsort((np.arange(len(z)), z))[:K]
+
+
+def _first_occ_keep_last(ids):
+    ids = [int(x) for x in ids]
+    out = []
+    for i, x in enumerate(ids):
+        if x not in ids[i + 1:]:
+            out.append(x)
+    return out
+
+
+def _stream_update_dedup_against_S(S, tree, ver):
+    out = list(S)
+    for x in list(tree) + list(ver):
+        if int(x) not in out:
+            out.append(int(x))
+    return out
+
+
+def _stream_update_draft_raw(S, tree, ver):
+    return list(S) + [int(x) for x in tree] + [int(x) for x in ver]
+
+
+def _suffix_prefix(S, w):
+    return list(S[:w])
+
+
+def _suffix_off_by_one(S, w):
+    return list(S[-(w - 1):]) if w > 1 and len(S) >= w else list(S)
+
+
+def _active_recent_distinct(S, w):
+    out = []
+    for v in reversed(list(S)):
+        if v not in out:
+            out.append(v)
+        if len(out) == w:
+            break
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def _bitmap_msb_first(I, V):
+    words = np.zeros((V + 31) // 32, dtype=np.uint32)
+    for v in I:
+        words[int(v) >> 5] |= np.uint32(1) << np.uint32(31 - (int(v) & 31))
+    return words
+
+
+def _project_drop_last_col(h, R, dtype):
+    return O.widen(h, dtype)[:, :-1] @ O.widen(R, dtype)[:, :-1].T
+
+
+def _project_sign(h, R, dtype):
+    return -(O.widen(h, dtype) @ O.widen(R, dtype).T)
+
+
+def _widen_shift15(x, dtype):
+    if dtype == "bf16":
+        b = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+        return b.view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _draft_topk_by_column(logits, I, k):
+    logits = np.atleast_2d(np.asarray(logits, np.float64))
+    I = np.asarray(I, np.int64)
+    M = logits.shape[0]
+    ids = np.full((M, k), -1, np.int64)
+    vals = np.full((M, k), -np.inf)
+    for m in range(M):
+        order = np.lexsort((np.arange(len(I)), -logits[m]))[:k]
+        ids[m, :len(order)] = I[order]
+        vals[m, :len(order)] = logits[m, order]
+    return ids, vals
+
+
+def _draft_topk_no_map(logits, I, k):
+    logits = np.atleast_2d(np.asarray(logits, np.float64))
+    M = logits.shape[0]
+    ids = np.full((M, k), -1, np.int64)
+    vals = np.full((M, k), -np.inf)
+    for m in range(M):
+        order = np.lexsort((np.asarray(I), -logits[m]))[:k]
+        ids[m, :len(order)] = order           # column index instead of global id
+        vals[m, :len(order)] = logits[m, order]
+    return ids, vals
+
+
+def _init_stream_sorted_union(prompt, P):
+    return [int(x) for x in prompt] + sorted(set(int(x) for x in np.asarray(P).reshape(-1)))
+
+
+def _init_stream_rank_major(prompt, P):
+    return [int(x) for x in prompt] + O.first_occurrence(np.asarray(P).T.reshape(-1))
+
+
+def _gather_transposed_index(W, I):
+    return np.asarray(W)[np.asarray(I)[::-1]]
+
+
+MUTATIONS = [
+    ("top_k", _topk_tie_desc),
+    ("top_k", _topk_ascending),
+    ("first_occurrence", _first_occ_keep_last),
+    ("stream_update", _stream_update_dedup_against_S),
+    ("stream_update", _stream_update_draft_raw),
+    ("suffix", _suffix_prefix),
+    ("suffix", _suffix_off_by_one),
+    ("active_set", _active_recent_distinct),
+    ("bitmap", _bitmap_msb_first),
+    ("project", _project_drop_last_col),
+    ("project", _project_sign),
+    ("widen", _widen_shift15),
+    ("draft_topk", _draft_topk_by_column),
+    ("draft_topk", _draft_topk_no_map),
+    ("init_stream", _init_stream_sorted_union),
+    ("init_stream", _init_stream_rank_major),
+    ("gather_rows", _gather_transposed_index),
+]
+
+
+@pytest.mark.parametrize("attr,bad", MUTATIONS, ids=[f"{a}:{f.__name__}" for a, f in MUTATIONS])
+def test_pins_catch_planted_mistake(monkeypatch, attr, bad):
+    monkeypatch.setattr(O, attr, bad)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(O)
+        except Exception:   # an assertion or a shape error both count as caught
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {bad.__name__} in {attr}"
