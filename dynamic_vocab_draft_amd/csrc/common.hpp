@@ -1,0 +1,149 @@
+// Device helpers shared by the nanospec kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nanospec.h"
+
+#define NS_WAVE 64
+
+namespace ns {
+
+// ---------------------------------------------------------------------------
+// Ordered 64-bit keys: (orderable float32 bits) << 32 | (0xFFFFFFFF - id).
+// Larger key = larger value, and for equal values the smaller id.  +0.0 and
+// -0.0 map to the same orderable bits.  Key 0 is "empty": it is below every
+// key made from a non-NaN value (those have a high word >= 0x007FFFFF).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ord_f32(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float v, int32_t id) {
+  return ((uint64_t)ord_f32(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+__device__ __forceinline__ int32_t key_id(uint64_t k) {
+  return (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+__device__ __forceinline__ float key_val(uint64_t k) { return unord_f32((uint32_t)(k >> 32)); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// Wave-level helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = __shfl_xor((unsigned int)(v & 0xFFFFFFFFull), mask, NS_WAVE);
+  uint32_t hi = __shfl_xor((unsigned int)(v >> 32), mask, NS_WAVE);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, NS_WAVE);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < NS_WAVE; d <<= 1) {
+    int o = __shfl_up(v, d, NS_WAVE);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64,
+// NT <= 64*64).  `sh` is LDS scratch of at least NT/64 + 1 ints.  Returns the
+// thread's exclusive prefix; *total receives the block sum.  Contains two
+// __syncthreads and must be reached by every thread of the block.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  constexpr int NW = NT / NS_WAVE;
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), w = tid / NS_WAVE;
+  int inc = wave_incl_scan(v, lane);
+  if (lane == NS_WAVE - 1) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    int t = lane < NW ? sh[lane] : 0;
+    int ti = wave_incl_scan(t, lane);
+    if (lane < NW) sh[lane] = ti - t;          // exclusive wave offsets
+    if (lane == NW - 1) sh[NW] = ti;           // block total
+  }
+  __syncthreads();
+  int r = sh[w] + inc - v;
+  *total = sh[NW];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Per-thread sorted (descending) candidate lists of CAP keys, and a block
+// merge that pops the k largest keys across all threads' lists.
+// ---------------------------------------------------------------------------
+template <int CAP>
+__device__ __forceinline__ void list_insert(uint64_t (&lst)[CAP], uint64_t key) {
+  // Precondition: key > lst[CAP-1].  Shifts smaller entries down by one.
+#pragma unroll
+  for (int i = CAP - 1; i > 0; --i) {
+    uint64_t prev = lst[i - 1];
+    uint64_t cur = lst[i];
+    lst[i] = key > prev ? prev : (key > cur ? key : cur);
+  }
+  lst[0] = key > lst[0] ? key : lst[0];
+}
+
+template <int CAP>
+__device__ __forceinline__ void list_pop(uint64_t (&lst)[CAP]) {
+#pragma unroll
+  for (int i = 0; i < CAP - 1; ++i) lst[i] = lst[i + 1];
+  lst[CAP - 1] = 0;
+}
+
+// Pops the k largest keys over all threads of a block of NT threads, in
+// descending order, handing each to emit(r, key) on thread 0.  Keys must be
+// unique among non-empty entries (ids are distinct).  `sh` is LDS scratch of
+// NT/64 uint64.  Every thread of the block must call it.
+template <int NT, int CAP, typename Emit>
+__device__ __forceinline__ void block_pop_topk(uint64_t (&lst)[CAP], int k, uint64_t* sh, Emit emit) {
+  constexpr int NW = NT / NS_WAVE;
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), w = tid / NS_WAVE;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = wave_max_u64(lst[0]);
+    if (lane == 0) sh[w] = best;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { uint64_t o = sh[i]; best = o > best ? o : best; }
+    __syncthreads();
+    if (best != 0 && lst[0] == best) list_pop(lst);
+    if (tid == 0) emit(r, best);
+  }
+}
+
+}  // namespace ns
+
+// Launch-error helper for host code.
+static inline int ns_launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NS_OK : NS_EHIP;
+}

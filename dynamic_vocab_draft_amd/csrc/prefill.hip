@@ -1,0 +1,135 @@
+// Prefill candidates: P[i] = T_Kpre(z_i) for every prompt position i.
+//
+// MicroSpec/NanoSpec (arXiv 2605.26444) Sec. 3.2 "Candidate Stream
+// Initialization": the stream starts as the prompt followed by the union of
+// each position's top-K_pre logits.  The pass reads L x V logits once, so it
+// is HBM-bound; one 256-thread block owns one row and streams it with
+// 16-byte loads (four in flight per lane).  Each thread scans its elements in
+// ascending id order and keeps a sorted list of its CAP best (value, id) keys;
+// because later elements have larger ids, an element that only ties the
+// list's last value can be dropped, so most elements cost a conversion and a
+// compare against an 8-element maximum.  A block-wide pop then emits the k
+// winners ordered by (value desc, id asc).  Values are the stored logits
+// widened to float32, so the result is exact.
+#include "common.hpp"
+
+namespace {
+
+constexpr int kPrefillThreads = 256;
+constexpr int kPrefillUnroll = 4;
+
+template <int CAP>
+struct Cands {
+  uint64_t lst[CAP];
+  float thr;     // value of lst[CAP-1] once the list is full
+  int filled;
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < CAP; ++i) lst[i] = 0;
+    thr = -INFINITY;
+    filled = 0;
+  }
+  __device__ __forceinline__ bool wants(float v) const { return filled < CAP || v > thr; }
+  __device__ __forceinline__ void add(float v, int id) {
+    if (!wants(v)) return;
+    ns::list_insert(lst, ns::make_key(v, id));
+    ++filled;
+    if (filled >= CAP) thr = ns::key_val(lst[CAP - 1]);
+  }
+};
+
+template <bool BF16, bool VEC, int CAP>
+__global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restrict__ Z, int V, int k,
+                                                             int32_t* __restrict__ out_ids,
+                                                             float* __restrict__ out_vals) {
+  __shared__ uint64_t sh[kPrefillThreads / NS_WAVE];
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  Cands<CAP> c;
+  c.init();
+  if (VEC) {
+    constexpr int EPV = BF16 ? 8 : 4;     // elements per 16-byte vector
+    const int nvec = V / EPV;
+    const uint4* __restrict__ p = (const uint4*)((const char*)Z + row * (size_t)V * (BF16 ? 2 : 4));
+    for (int q0 = tid; q0 < nvec; q0 += kPrefillThreads * kPrefillUnroll) {
+      uint4 x[kPrefillUnroll];
+#pragma unroll
+      for (int u = 0; u < kPrefillUnroll; ++u) {
+        const int q = q0 + u * kPrefillThreads;
+        x[u] = q < nvec ? p[q] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+      }
+#pragma unroll
+      for (int u = 0; u < kPrefillUnroll; ++u) {
+        const int q = q0 + u * kPrefillThreads;
+        if (q >= nvec) continue;
+        const uint32_t wv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        float v[EPV];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (BF16) {
+            v[2 * e] = ns::bf16_lo(wv[e]);
+            v[2 * e + 1] = ns::bf16_hi(wv[e]);
+          } else {
+            v[e] = __uint_as_float(wv[e]);
+          }
+        }
+        float mx = v[0];
+#pragma unroll
+        for (int e = 1; e < EPV; ++e) mx = fmaxf(mx, v[e]);
+        if (c.wants(mx)) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) c.add(v[e], q * EPV + e);
+        }
+      }
+    }
+  } else {
+    if (BF16) {
+      const uint16_t* __restrict__ p = (const uint16_t*)Z + row * (size_t)V;
+      for (int e = tid; e < V; e += kPrefillThreads) c.add(__uint_as_float((uint32_t)p[e] << 16), e);
+    } else {
+      const float* __restrict__ p = (const float*)Z + row * (size_t)V;
+      for (int e = tid; e < V; e += kPrefillThreads) c.add(p[e], e);
+    }
+  }
+  ns::block_pop_topk<kPrefillThreads, CAP>(c.lst, k, sh, [&](int r, uint64_t key) {
+    out_ids[row * k + r] = key ? ns::key_id(key) : -1;
+    out_vals[row * k + r] = key ? ns::key_val(key) : -INFINITY;
+  });
+}
+
+template <bool BF16, bool VEC>
+void launch_cap(int cap, const void* Z, int L, int V, int k, int32_t* ids, float* vals, hipStream_t s) {
+#define NS_LAUNCH_PREFILL(C) \
+  hipLaunchKernelGGL((k_prefill<BF16, VEC, C>), dim3(L), dim3(kPrefillThreads), 0, s, Z, V, k, ids, vals)
+  switch (cap) {
+    case 4: NS_LAUNCH_PREFILL(4); break;
+    case 8: NS_LAUNCH_PREFILL(8); break;
+    case 16: NS_LAUNCH_PREFILL(16); break;
+    case 32: NS_LAUNCH_PREFILL(32); break;
+    default: NS_LAUNCH_PREFILL(64); break;
+  }
+#undef NS_LAUNCH_PREFILL
+}
+
+}  // namespace
+
+extern "C" int nanospec_prefill_topk(const void* logits, int32_t L, int32_t V, int32_t dtype, int32_t k,
+                                     int32_t* out_ids, float* out_vals, hipStream_t stream) {
+  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (L < 0 || V < 1 || k < 1 || k > NS_MAX_K || k > V) return NS_EINVAL;
+  if (L == 0) return NS_OK;
+  if (!logits || !out_ids || !out_vals) return NS_EINVAL;
+  const int esz = dtype == NS_BF16 ? 2 : 4;
+  const bool vec = (((uintptr_t)logits) & 15u) == 0 && (((size_t)V * esz) % 16) == 0;
+  const int cap = k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
+  (void)hipGetLastError();
+  if (dtype == NS_BF16) {
+    if (vec) launch_cap<true, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    else launch_cap<true, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
+  } else {
+    if (vec) launch_cap<false, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    else launch_cap<false, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
+  }
+  return ns_launch_status();
+}

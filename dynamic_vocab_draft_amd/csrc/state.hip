@@ -1,0 +1,378 @@
+// Window state of the candidate stream: append (with in-tuple first-occurrence
+// dedup), the sliding-window active set as an LDS-built bitmap with ascending
+// compaction, and the fused per-step update.
+//
+// MicroSpec/NanoSpec (arXiv 2605.26444) Sec. 3.2: S_init and S_new are
+// concatenations of tuples, and I_{t+1} = Unique(Suffix(S_new, W_max)).
+// NanoSpec "Eliminating Overhead via GPU-Resident State Management": the state
+// stays on the GPU as a bitmap and is updated by device kernels only.
+//
+// Device layout of a state (caller-owned, 256-byte aligned):
+//   [0, 256)            control: int64 len (|S|), uint32 status
+//   ring   int32[w_max] S entry p lives at ring[p % w_max] while p >= |S|-w_max
+//   first  int32[V]     per-id first position inside the current append
+//                       (INT32_MAX between calls)
+//   bitmap uint32[ceil(V/32)]  the active set of the latest rebuild
+//
+// All state kernels run as ONE workgroup of 1024 threads: the per-step work
+// is a few thousand ids and words, so a single CU finishes it in a few
+// microseconds, and a single workgroup needs no grid-wide synchronisation
+// between the dedup, scan, write and rebuild phases.  Only integer atomics
+// (atomicMin, atomicOr) are used, so results do not depend on scheduling.
+#include <new>
+
+#include "common.hpp"
+#include "state_internal.hpp"
+
+namespace {
+
+constexpr int kStateThreads = 1024;
+constexpr int kNW = kStateThreads / NS_WAVE;
+
+struct StateDev {
+  int64_t* len;
+  uint32_t* status;
+  int32_t* ring;
+  int32_t* first;
+  uint32_t* bitmap;
+  int V;
+  int w_max;
+};
+
+__device__ __forceinline__ int load_first(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Appends ids[0..n) to the stream (Sec. 3.2 tuple concatenation).  `len` is
+// the block-uniform stream length, updated in place.  Returns through *bad
+// whether any id was outside [0, V).  Must be called by all threads.
+__device__ void block_append(const StateDev& s, const int32_t* __restrict__ ids, int n,
+                             bool dedup, int64_t& len, int* sh_scan, int* sh_flag) {
+  const int tid = threadIdx.x;
+  if (n <= 0) return;
+  // Phase 1: first position of each id inside this tuple.
+  if (dedup) {
+    for (int i = tid; i < n; i += kStateThreads) {
+      int id = ids[i];
+      if (id >= 0 && id < s.V) atomicMin(&s.first[id], i);
+    }
+  }
+  __syncthreads();
+  // Phase 2: number of entries this tuple contributes.
+  int c = 0;
+  bool bad = false;
+  for (int i = tid; i < n; i += kStateThreads) {
+    int id = ids[i];
+    bool valid = id >= 0 && id < s.V;
+    bad |= !valid;
+    c += valid && (!dedup || load_first(&s.first[id]) == i);
+  }
+  if (bad) *sh_flag = 1;
+  int total = 0;
+  (void)ns::block_excl_scan<kStateThreads>(c, sh_scan, &total);
+  const int C = total;
+  // Phase 3: ordered positions; only the last w_max kept entries can still
+  // be inside the window, so only those are written (no slot collisions).
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += kStateThreads) {
+    int i = c0 + tid;
+    int id = i < n ? ids[i] : -1;
+    bool keep = i < n && id >= 0 && id < s.V && (!dedup || load_first(&s.first[id]) == i);
+    int chunk_total = 0;
+    int pos = ns::block_excl_scan<kStateThreads>(keep ? 1 : 0, sh_scan, &chunk_total);
+    if (keep) {
+      int p = base + pos;
+      if (p >= C - s.w_max) {
+        int64_t q = len + (int64_t)p;
+        s.ring[(int)(q % (int64_t)s.w_max)] = id;
+      }
+    }
+    base += chunk_total;
+  }
+  __syncthreads();
+  // Phase 4: restore the first-position table for the next call.
+  if (dedup) {
+    for (int i = tid; i < n; i += kStateThreads) {
+      int id = ids[i];
+      if (id >= 0 && id < s.V)
+        __hip_atomic_store(&s.first[id], INT32_MAX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  len += (int64_t)C;
+  __syncthreads();
+}
+
+// Rebuilds I = Unique(Suffix(S, W_max)) from the ring: bits set in an LDS
+// bitmap, then a popcount prefix scan over the words emits ids in ascending
+// order.  Must be called by all threads.
+__device__ void block_active(const StateDev& s, int64_t len, uint32_t* lds_bm, int32_t* __restrict__ active_ids,
+                             int32_t* __restrict__ n_active, uint32_t* __restrict__ bitmap_out, int* sh_scan) {
+  const int tid = threadIdx.x;
+  const int words = (s.V + 31) >> 5;
+  for (int w = tid; w < words; w += kStateThreads) lds_bm[w] = 0u;
+  __syncthreads();
+  const int cnt = (int)(len < (int64_t)s.w_max ? len : (int64_t)s.w_max);
+  // While |S| < w_max the entries sit in ring[0..|S|); afterwards every slot
+  // holds one of the last w_max entries.
+  for (int e = tid; e < cnt; e += kStateThreads) {
+    int id = s.ring[e];
+    if (id >= 0 && id < s.V) atomicOr(&lds_bm[id >> 5], 1u << (id & 31));
+  }
+  __syncthreads();
+  const int per = (words + kStateThreads - 1) / kStateThreads;
+  const int w0 = tid * per;
+  const int w1 = min(words, w0 + per);
+  int pc = 0;
+  for (int w = w0; w < w1; ++w) pc += __popc(lds_bm[w]);
+  int total = 0;
+  int off = ns::block_excl_scan<kStateThreads>(pc, sh_scan, &total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b = lds_bm[w];
+    s.bitmap[w] = b;
+    if (bitmap_out) bitmap_out[w] = b;
+    while (b) {
+      int bit = __ffs(b) - 1;
+      active_ids[off++] = (w << 5) + bit;
+      b &= b - 1u;
+    }
+  }
+  if (tid == 0) *n_active = total;
+}
+
+__device__ __forceinline__ StateDev state_dev(const ns_state_view& v) {
+  StateDev s;
+  s.len = v.len;
+  s.status = v.status;
+  s.ring = v.ring;
+  s.first = v.first;
+  s.bitmap = v.bitmap;
+  s.V = v.V;
+  s.w_max = v.w_max;
+  return s;
+}
+
+__device__ __forceinline__ void finish(const StateDev& s, int64_t len, int flag) {
+  if (threadIdx.x == 0) {
+    *s.len = len;
+    if (flag) atomicOr(s.status, NS_STATUS_BAD_ID);
+  }
+}
+
+__global__ __launch_bounds__(kStateThreads) void k_append(ns_state_view v, const int32_t* __restrict__ ids,
+                                                          int n, int dedup) {
+  __shared__ int sh_scan[kNW + 1];
+  __shared__ int sh_flag;
+  __shared__ int64_t sh_len;
+  StateDev s = state_dev(v);
+  if (threadIdx.x == 0) { sh_flag = 0; sh_len = *s.len; }
+  __syncthreads();
+  int64_t len = sh_len;
+  block_append(s, ids, n, dedup != 0, len, sh_scan, &sh_flag);
+  finish(s, len, sh_flag);
+}
+
+__global__ __launch_bounds__(kStateThreads) void k_active(ns_state_view v, int32_t* __restrict__ active_ids,
+                                                          int32_t* __restrict__ n_active,
+                                                          uint32_t* __restrict__ bitmap_out) {
+  extern __shared__ uint32_t lds_bm[];
+  __shared__ int sh_scan[kNW + 1];
+  StateDev s = state_dev(v);
+  int64_t len = *s.len;
+  block_active(s, len, lds_bm, active_ids, n_active, bitmap_out, sh_scan);
+}
+
+__global__ __launch_bounds__(kStateThreads) void k_step(ns_state_view v, const int32_t* __restrict__ draft_ids,
+                                                        int n_draft, const int32_t* __restrict__ ver_ids, int n_ver,
+                                                        int32_t* __restrict__ active_ids, int32_t* __restrict__ n_active,
+                                                        uint32_t* __restrict__ bitmap_out) {
+  extern __shared__ uint32_t lds_bm[];
+  __shared__ int sh_scan[kNW + 1];
+  __shared__ int sh_flag;
+  __shared__ int64_t sh_len;
+  StateDev s = state_dev(v);
+  if (threadIdx.x == 0) { sh_flag = 0; sh_len = *s.len; }
+  __syncthreads();
+  int64_t len = sh_len;
+  block_append(s, draft_ids, n_draft, true, len, sh_scan, &sh_flag);
+  block_append(s, ver_ids, n_ver, false, len, sh_scan, &sh_flag);
+  block_active(s, len, lds_bm, active_ids, n_active, bitmap_out, sh_scan);
+  finish(s, len, sh_flag);
+}
+
+// Initialisation / reset: empty stream, cleared status, first[] = INT32_MAX,
+// empty bitmap.  A grid-stride fill kernel (no memset nodes, so the call can
+// be captured in a graph).
+__global__ void k_init(ns_state_view v) {
+  const int gt = blockIdx.x * blockDim.x + threadIdx.x;
+  const int gs = gridDim.x * blockDim.x;
+  if (gt == 0) { *v.len = 0; *v.status = 0u; }
+  for (int i = gt; i < v.w_max; i += gs) v.ring[i] = -1;
+  for (int i = gt; i < v.V; i += gs) v.first[i] = INT32_MAX;
+  const int words = (v.V + 31) >> 5;
+  for (int i = gt; i < words; i += gs) v.bitmap[i] = 0u;
+}
+
+__global__ void k_window(ns_state_view v, int32_t* __restrict__ window, int64_t* __restrict__ len_out) {
+  const int64_t len = *v.len;
+  const int cnt = (int)(len < (int64_t)v.w_max ? len : (int64_t)v.w_max);
+  const int gt = blockIdx.x * blockDim.x + threadIdx.x;
+  const int gs = gridDim.x * blockDim.x;
+  if (window) {
+    for (int e = gt; e < v.w_max; e += gs) {
+      int val = -1;
+      if (e < cnt) {
+        int64_t p = len - cnt + e;
+        val = v.ring[(int)(p % (int64_t)v.w_max)];
+      }
+      window[e] = val;
+    }
+  }
+  if (len_out && gt == 0) *len_out = len;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool state_dims_ok(int32_t V, int32_t w_max) {
+  return V >= 1 && V <= NS_MAX_V && w_max >= 1 && w_max <= NS_MAX_WMAX;
+}
+
+size_t lds_bitmap_bytes(int V) { return (size_t)((V + 31) >> 5) * sizeof(uint32_t); }
+
+int set_lds_limit(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return NS_OK;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess
+             ? NS_OK : NS_EHIP;
+}
+
+int fill_grid(const ns_state_view& v) {
+  int n = v.V > v.w_max ? v.V : v.w_max;
+  int g = (n + 255) / 256;
+  return g < 1 ? 1 : (g > 1024 ? 1024 : g);
+}
+
+}  // namespace
+
+struct nanospec_state {
+  ns_state_view view;
+};
+
+extern "C" {
+
+const char* nanospec_strerror(int code) {
+  switch (code) {
+    case NS_OK: return "ok";
+    case NS_EINVAL: return "invalid argument (null pointer, bad size or limit exceeded)";
+    case NS_EDTYPE: return "unknown dtype or mode";
+    case NS_ECAPACITY: return "buffer too small";
+    case NS_EHIP: return "HIP launch or runtime error";
+    default: return "unknown error code";
+  }
+}
+
+int nanospec_version(void) { return 100; }
+
+size_t nanospec_state_bytes(int32_t V, int32_t w_max) {
+  if (!state_dims_ok(V, w_max)) return 0;
+  size_t b = 256;
+  b += align256((size_t)w_max * 4);
+  b += align256((size_t)V * 4);
+  b += align256((size_t)((V + 31) >> 5) * 4);
+  return b;
+}
+
+int nanospec_state_create(nanospec_state** out, int32_t V, int32_t w_max, void* dev_mem, size_t dev_bytes,
+                          hipStream_t stream) {
+  if (!out || !dev_mem || !state_dims_ok(V, w_max)) return NS_EINVAL;
+  if (((uintptr_t)dev_mem & 255u) != 0) return NS_EINVAL;
+  size_t need = nanospec_state_bytes(V, w_max);
+  if (dev_bytes < need) return NS_ECAPACITY;
+  nanospec_state* st = new (std::nothrow) nanospec_state;
+  if (!st) return NS_EINVAL;
+  char* p = (char*)dev_mem;
+  ns_state_view& v = st->view;
+  v.len = (int64_t*)p;
+  v.status = (uint32_t*)(p + 8);
+  size_t off = 256;
+  v.ring = (int32_t*)(p + off);
+  off += align256((size_t)w_max * 4);
+  v.first = (int32_t*)(p + off);
+  off += align256((size_t)V * 4);
+  v.bitmap = (uint32_t*)(p + off);
+  v.V = V;
+  v.w_max = w_max;
+  int rc = set_lds_limit((const void*)k_active, lds_bitmap_bytes(V));
+  if (rc == NS_OK) rc = set_lds_limit((const void*)k_step, lds_bitmap_bytes(V));
+  if (rc != NS_OK) { delete st; return rc; }
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_init, dim3(fill_grid(v)), dim3(256), 0, stream, v);
+  rc = ns_launch_status();
+  if (rc != NS_OK) { delete st; return rc; }
+  *out = st;
+  return NS_OK;
+}
+
+int nanospec_state_reset(nanospec_state* st, hipStream_t stream) {
+  if (!st) return NS_EINVAL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_init, dim3(fill_grid(st->view)), dim3(256), 0, stream, st->view);
+  return ns_launch_status();
+}
+
+int nanospec_state_destroy(nanospec_state* st) {
+  if (!st) return NS_EINVAL;
+  delete st;
+  return NS_OK;
+}
+
+int nanospec_state_status(nanospec_state* st, uint32_t* flags, hipStream_t stream) {
+  if (!st || !flags) return NS_EINVAL;
+  uint32_t h = 0;
+  const uint32_t zero = 0;
+  if (hipMemcpyAsync(&h, st->view.status, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return NS_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return NS_EHIP;
+  if (hipMemcpyAsync(st->view.status, &zero, 4, hipMemcpyHostToDevice, stream) != hipSuccess) return NS_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return NS_EHIP;
+  *flags = h;
+  return NS_OK;
+}
+
+int nanospec_state_window(nanospec_state* st, int32_t* window, int64_t* len, hipStream_t stream) {
+  if (!st) return NS_EINVAL;
+  if (!window && !len) return NS_OK;
+  (void)hipGetLastError();
+  int g = (st->view.w_max + 255) / 256;
+  hipLaunchKernelGGL(k_window, dim3(g > 1024 ? 1024 : g), dim3(256), 0, stream, st->view, window, len);
+  return ns_launch_status();
+}
+
+int nanospec_stream_append(nanospec_state* st, const int32_t* ids, int32_t n, int32_t dedup_first,
+                           hipStream_t stream) {
+  if (!st || n < 0 || (n > 0 && !ids)) return NS_EINVAL;
+  if (dedup_first != 0 && dedup_first != 1) return NS_EINVAL;
+  if (n == 0) return NS_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_append, dim3(1), dim3(kStateThreads), 0, stream, st->view, ids, n, dedup_first);
+  return ns_launch_status();
+}
+
+int nanospec_active_vocab(nanospec_state* st, int32_t* active_ids, int32_t* n_active, uint32_t* bitmap,
+                          hipStream_t stream) {
+  if (!st || !active_ids || !n_active) return NS_EINVAL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_active, dim3(1), dim3(kStateThreads), lds_bitmap_bytes(st->view.V), stream, st->view,
+                     active_ids, n_active, bitmap);
+  return ns_launch_status();
+}
+
+int nanospec_step_update(nanospec_state* st, const int32_t* draft_ids, int32_t n_draft, const int32_t* ver_ids,
+                         int32_t n_ver, int32_t* active_ids, int32_t* n_active, uint32_t* bitmap,
+                         hipStream_t stream) {
+  if (!st || !active_ids || !n_active || n_draft < 0 || n_ver < 0) return NS_EINVAL;
+  if ((n_draft > 0 && !draft_ids) || (n_ver > 0 && !ver_ids)) return NS_EINVAL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_step, dim3(1), dim3(kStateThreads), lds_bitmap_bytes(st->view.V), stream, st->view,
+                     draft_ids, n_draft, ver_ids, n_ver, active_ids, n_active, bitmap);
+  return ns_launch_status();
+}
+
+}  // extern "C"

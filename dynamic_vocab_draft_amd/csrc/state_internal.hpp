@@ -1,0 +1,13 @@
+// Device pointers and sizes of one window state (passed to kernels by value).
+#pragma once
+#include <stdint.h>
+
+struct ns_state_view {
+  int64_t* len;       // |S|, the total number of stream entries appended
+  uint32_t* status;   // sticky NS_STATUS_* bits
+  int32_t* ring;      // [w_max] tail of S
+  int32_t* first;     // [V] first-position table (INT32_MAX between calls)
+  uint32_t* bitmap;   // [ceil(V/32)] active set of the latest rebuild
+  int V;
+  int w_max;
+};

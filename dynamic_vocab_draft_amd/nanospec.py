@@ -1,0 +1,231 @@
+"""Thin ctypes binding of libnanospec.so (include/nanospec.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Functions keep the C names and take torch tensors (device memory)
+plus an optional ``torch.cuda.Stream``; they raise ``NanoSpecError`` on a
+non-zero return code.  The library must have been built
+(``python -m dynamic_vocab_draft_amd.build``); importing this module without
+it raises, and there is no fallback.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (same SONAME), and the two share
+streams and device memory.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnanospec.so")
+
+NS_OK, NS_EINVAL, NS_EDTYPE, NS_ECAPACITY, NS_EHIP = 0, 1, 2, 3, 4
+NS_BF16, NS_FP32 = 0, 1
+NS_PACKED, NS_INDEXED = 0, 1
+NS_STATUS_BAD_ID = 0x1
+NS_MAX_M = NS_MAX_K = 64
+NS_MAX_V = NS_MAX_WMAX = 1 << 20
+NS_MAX_D = 16384
+
+
+class NanoSpecError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {code} ({_strerror(code)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing; build it with `python -m dynamic_vocab_draft_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_LOCAL)
+    _check_single_runtime()
+    return lib
+
+
+def _check_single_runtime() -> None:
+    """Fails if two different HIP runtimes ended up in this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {l.split()[-1] for l in f if "libamdhip64" in l}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths}
+    if len(real) > 1:
+        raise ImportError(f"more than one HIP runtime loaded: {sorted(real)}")
+
+
+_lib = _load()
+
+c_int32, c_size, c_vp, c_u32p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32)
+
+_SIGS = {
+    "nanospec_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "nanospec_version": (ctypes.c_int, []),
+    "nanospec_state_bytes": (c_size, [c_int32, c_int32]),
+    "nanospec_state_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_vp, c_size, c_vp]),
+    "nanospec_state_reset": (ctypes.c_int, [c_vp, c_vp]),
+    "nanospec_state_destroy": (ctypes.c_int, [c_vp]),
+    "nanospec_state_status": (ctypes.c_int, [c_vp, c_u32p, c_vp]),
+    "nanospec_state_window": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp]),
+    "nanospec_stream_append": (ctypes.c_int, [c_vp, c_vp, c_int32, c_int32, c_vp]),
+    "nanospec_active_vocab": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "nanospec_step_update": (ctypes.c_int, [c_vp, c_vp, c_int32, c_vp, c_int32, c_vp, c_vp, c_vp, c_vp]),
+    "nanospec_gather_rows": (ctypes.c_int, [c_vp, c_int32, c_int32, c_int32, c_vp, c_vp, c_int32, c_vp, c_vp]),
+    "nanospec_draft_workspace_bytes": (c_size, [c_int32, c_int32, c_int32]),
+    "nanospec_draft_logits_topk": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
+                                                  c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "nanospec_prefill_topk": (ctypes.c_int, [c_vp, c_int32, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def _strerror(code: int) -> str:
+    return _lib.nanospec_strerror(code).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != NS_OK:
+        raise NanoSpecError(rc, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NS_BF16
+    if t.dtype == torch.float32:
+        return NS_FP32
+    raise NanoSpecError(NS_EDTYPE, f"dtype {t.dtype}")
+
+
+def nanospec_version() -> int:
+    return _lib.nanospec_version()
+
+
+def nanospec_strerror(code: int) -> str:
+    return _strerror(code)
+
+
+# ---------------------------------------------------------------------------
+# Window state
+# ---------------------------------------------------------------------------
+
+
+def nanospec_state_bytes(V: int, w_max: int) -> int:
+    return _lib.nanospec_state_bytes(V, w_max)
+
+
+class NanoSpecState:
+    """Host handle plus the caller-owned device buffer of one window state."""
+
+    def __init__(self, V: int, w_max: int, device="cuda", stream=None):
+        nbytes = nanospec_state_bytes(V, w_max)
+        if nbytes == 0:
+            raise NanoSpecError(NS_EINVAL, f"nanospec_state_bytes(V={V}, w_max={w_max})")
+        self.V, self.w_max = V, w_max
+        self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.mem.data_ptr()) % 256
+        self.buf = self.mem[off:off + nbytes]
+        h = ctypes.c_void_p()
+        _check(_lib.nanospec_state_create(ctypes.byref(h), V, w_max, _ptr(self.buf), nbytes, _stream(stream)),
+               "nanospec_state_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _lib.nanospec_state_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def nanospec_state_reset(st: NanoSpecState, stream=None) -> None:
+    _check(_lib.nanospec_state_reset(st.handle, _stream(stream)), "nanospec_state_reset")
+
+
+def nanospec_state_status(st: NanoSpecState, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(_lib.nanospec_state_status(st.handle, ctypes.byref(flags), _stream(stream)), "nanospec_state_status")
+    return flags.value
+
+
+def nanospec_state_window(st: NanoSpecState, window: Optional[torch.Tensor], length: Optional[torch.Tensor],
+                          stream=None) -> None:
+    _check(_lib.nanospec_state_window(st.handle, _ptr(window), _ptr(length), _stream(stream)),
+           "nanospec_state_window")
+
+
+def nanospec_stream_append(st: NanoSpecState, ids: Optional[torch.Tensor], n: int, dedup_first: int,
+                           stream=None) -> None:
+    _check(_lib.nanospec_stream_append(st.handle, _ptr(ids), n, dedup_first, _stream(stream)),
+           "nanospec_stream_append")
+
+
+def nanospec_active_vocab(st: NanoSpecState, active_ids: torch.Tensor, n_active: torch.Tensor,
+                          bitmap: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(_lib.nanospec_active_vocab(st.handle, _ptr(active_ids), _ptr(n_active), _ptr(bitmap),
+                                      _stream(stream)), "nanospec_active_vocab")
+
+
+def nanospec_step_update(st: NanoSpecState, draft_ids: Optional[torch.Tensor], n_draft: int,
+                         ver_ids: Optional[torch.Tensor], n_ver: int, active_ids: torch.Tensor,
+                         n_active: torch.Tensor, bitmap: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(_lib.nanospec_step_update(st.handle, _ptr(draft_ids), n_draft, _ptr(ver_ids), n_ver,
+                                     _ptr(active_ids), _ptr(n_active), _ptr(bitmap), _stream(stream)),
+           "nanospec_step_update")
+
+
+# ---------------------------------------------------------------------------
+# Gather, draft head, prefill
+# ---------------------------------------------------------------------------
+
+
+def nanospec_gather_rows(w: torch.Tensor, V: int, d: int, dtype: int, ids: torch.Tensor,
+                         n_dev: Optional[torch.Tensor], n_max: int, out: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_gather_rows(_ptr(w), V, d, dtype, _ptr(ids), _ptr(n_dev), n_max, _ptr(out),
+                                     _stream(stream)), "nanospec_gather_rows")
+
+
+def nanospec_draft_workspace_bytes(n_max: int, M: int, k: int) -> int:
+    return _lib.nanospec_draft_workspace_bytes(n_max, M, k)
+
+
+def nanospec_draft_logits_topk(rows: torch.Tensor, mode: int, row_ids: Optional[torch.Tensor],
+                               n_dev: Optional[torch.Tensor], n_max: int, V: int, d: int, dtype: int,
+                               h: torch.Tensor, M: int, k: int, logits: Optional[torch.Tensor],
+                               topk_ids: torch.Tensor, topk_vals: torch.Tensor, ws: torch.Tensor,
+                               stream=None) -> None:
+    _check(_lib.nanospec_draft_logits_topk(_ptr(rows), mode, _ptr(row_ids), _ptr(n_dev), n_max, V, d, dtype,
+                                           _ptr(h), M, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_vals),
+                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nanospec_draft_logits_topk")
+
+
+def nanospec_prefill_topk(logits: torch.Tensor, L: int, V: int, dtype: int, k: int, out_ids: torch.Tensor,
+                          out_vals: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_prefill_topk(_ptr(logits), L, V, dtype, k, _ptr(out_ids), _ptr(out_vals),
+                                      _stream(stream)), "nanospec_prefill_topk")
+
+
+def alloc_workspace(n_max: int, M: int, k: int, device="cuda") -> torch.Tensor:
+    """A 256-byte-aligned uint8 workspace of nanospec_draft_workspace_bytes."""
+    nbytes = nanospec_draft_workspace_bytes(n_max, M, k)
+    if nbytes == 0:
+        raise NanoSpecError(NS_EINVAL, "nanospec_draft_workspace_bytes")
+    mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-mem.data_ptr()) % 256
+    return mem[off:off + nbytes]

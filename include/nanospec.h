@@ -1,0 +1,219 @@
+/*
+ * nanospec.h -- C ABI of the dynamic-vocabulary draft LM head for AMD MI355X
+ * (gfx950).
+ *
+ * The method (MicroSpec / NanoSpec, arXiv 2605.26444):
+ *   Sec. 3.1, Eq. 1         : the LM head z = W_head h, W_head in R^{V x d};
+ *                             the draft computes it only on W_head[I_t, :].
+ *   Sec. 3.2 (prefill)      : T_K(z) = indices of the K largest logits;
+ *                             S_init = prompt (+) tuple(U_i T_Kpre(z_i)).
+ *   Sec. 3.2 (decoding)     : S_new = S_old (+) tuple(C_draft) (+) tuple(C_ver).
+ *   Sec. 3.2 (sliding window): I_{t+1} = Unique(Suffix(S_new, W_max)).
+ *   Sec. 3.3 / NanoSpec "Eliminating Overhead via GPU-Resident State
+ *   Management": the window state lives on the GPU as a bitmap and is updated
+ *   without host round trips; "Avoiding Sparse Computation via Asynchronous
+ *   Gathering": the rows W_head[I_t, :] are packed into a preallocated buffer
+ *   on a second stream.
+ *
+ * Conventions (every entry point):
+ *   - Pointers are DEVICE pointers unless the comment says "host".
+ *   - Every call enqueues its work on `stream` and returns without waiting
+ *     for it; only nanospec_state_status synchronises (the given stream).
+ *   - The library never allocates device memory: the caller owns the state
+ *     buffer, workspaces and outputs, and must keep them alive until the
+ *     enqueued work has finished.  The library owns only the small host
+ *     handle made by nanospec_state_create.
+ *   - Return value: NS_OK, or an error code.  Argument errors (NS_EINVAL,
+ *     NS_EDTYPE, NS_ECAPACITY) are detected on the host before anything is
+ *     enqueued.  NS_EHIP reports a failed kernel launch; for calls that
+ *     launch more than one kernel, kernels launched before the failure stay
+ *     enqueued.
+ *   - Errors only the device can see (an id outside [0, V)) set sticky bits
+ *     in the state's status word (NS_STATUS_*); the offending entries are
+ *     skipped, so results equal the definition applied to the valid entries.
+ *   - Tie rule for every top-k: value descending, then id ascending; +0.0 and
+ *     -0.0 are equal.  If k exceeds the candidate count, trailing entries are
+ *     (id -1, value -INFINITY).
+ *   - Calls on one state must be ordered (same stream, or events); calls on
+ *     distinct states and buffers may run concurrently.
+ */
+#ifndef NANOSPEC_H
+#define NANOSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------- */
+#define NS_OK        0
+#define NS_EINVAL    1   /* null pointer, bad size, limit exceeded */
+#define NS_EDTYPE    2   /* unknown dtype or mode */
+#define NS_ECAPACITY 3   /* state or workspace buffer too small */
+#define NS_EHIP      4   /* a HIP launch or runtime call failed */
+
+/* ---- element types of W_head, h and logits ---------------------------- */
+#define NS_BF16 0        /* bfloat16, stored as 16-bit patterns */
+#define NS_FP32 1        /* IEEE float32 */
+
+/* ---- row modes of nanospec_draft_logits_topk --------------------------- */
+#define NS_PACKED  0     /* rows = packed buffer [n_max x d]; row j is rows[j] */
+#define NS_INDEXED 1     /* rows = W_head [V x d]; row j is W_head[row_ids[j]] */
+
+/* ---- sticky device status bits ---------------------------------------- */
+#define NS_STATUS_BAD_ID 0x1u   /* an appended id was outside [0, V) and was skipped */
+
+/* ---- limits ------------------------------------------------------------ */
+#define NS_MAX_M      64        /* hidden rows per draft-head call */
+#define NS_MAX_K      64        /* draft top-k and prefill K_pre */
+#define NS_MAX_V      1048576   /* vocabulary size (the bitmap is built in LDS) */
+#define NS_MAX_WMAX   1048576   /* sliding-window length */
+#define NS_MAX_D      16384     /* hidden size; d % 8 == 0 */
+
+typedef struct nanospec_state nanospec_state;   /* opaque host handle */
+
+/* Human-readable text for a return code (static storage, never NULL). */
+const char* nanospec_strerror(int code);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int nanospec_version(void);
+
+/* ======================================================================
+ * Window state: the tail of the candidate stream S and the active bitmap.
+ * Sec. 3.2 "Vocabulary Construction via Sliding Window" needs only the last
+ * W_max entries of S, so the state keeps them in a ring of W_max int32 plus
+ * the total stream length (int64); the per-id first-position table (int32[V],
+ * used for in-tuple dedup) and the active bitmap (uint32[ceil(V/32)]) make up
+ * the rest.  Size is O(V + W_max), independent of sequence length.
+ * ====================================================================== */
+
+/* Bytes of device memory a state for (V, w_max) needs; 0 if out of limits. */
+size_t nanospec_state_bytes(int32_t V, int32_t w_max);
+
+/* Binds a state to caller-owned device memory `dev_mem` (>= state_bytes,
+ * 256-byte aligned) and enqueues its initialisation (empty stream, empty
+ * active set) on `stream`.  *out (host) receives the handle.
+ * Errors: NS_EINVAL (null, V or w_max outside [1, limit], misaligned),
+ * NS_ECAPACITY (dev_bytes too small), NS_EHIP. */
+int nanospec_state_create(nanospec_state** out, int32_t V, int32_t w_max,
+                          void* dev_mem, size_t dev_bytes, hipStream_t stream);
+
+/* Enqueues a reset to the empty stream (status bits cleared). */
+int nanospec_state_reset(nanospec_state* st, hipStream_t stream);
+
+/* Frees the host handle (the device memory stays the caller's). */
+int nanospec_state_destroy(nanospec_state* st);
+
+/* Synchronises `stream`, then writes the sticky status bits to *flags (host)
+ * and clears them. */
+int nanospec_state_status(nanospec_state* st, uint32_t* flags, hipStream_t stream);
+
+/* Enqueues a copy of Suffix(S, W_max) in stream order into window[0..w_max)
+ * (entries past min(|S|, W_max) are set to -1) and |S| into *len (int64).
+ * Either output may be NULL. */
+int nanospec_state_window(nanospec_state* st, int32_t* window, int64_t* len,
+                          hipStream_t stream);
+
+/* ======================================================================
+ * Stream append.  Sec. 3.2: S_init = prompt (+) tuple(U_i T_Kpre(z_i)) and
+ * S_new = S_old (+) tuple(C_draft) (+) tuple(C_ver).
+ *   ids[0..n)    : candidate ids (device, int32), read in the given order.
+ *   dedup_first  : 0 -> append every id as given (prompt, C_ver);
+ *                  1 -> append each distinct id once, at its first occurrence
+ *                  (tuple() of the prefill union, C_draft from raw tree ids).
+ * Dedup is within this call only; S keeps repeats across calls.  Ids outside
+ * [0, V) are skipped and set NS_STATUS_BAD_ID.  n may be 0.
+ * Errors: NS_EINVAL (null state, n < 0, ids NULL with n > 0), NS_EHIP. */
+int nanospec_stream_append(nanospec_state* st, const int32_t* ids, int32_t n,
+                           int32_t dedup_first, hipStream_t stream);
+
+/* ======================================================================
+ * Active vocabulary.  Sec. 3.2: I = Unique(Suffix(S, W_max)).
+ *   active_ids[0..w_max) : receives I in ascending id order; entries past
+ *                          |I| are left untouched.
+ *   n_active[1]          : receives |I| (int32, device; no host readback).
+ *   bitmap[ceil(V/32)]   : optional (may be NULL) copy of the state's bitmap:
+ *                          bit b of word w (LSB first) is set iff 32w+b is
+ *                          in I; padding bits are 0.
+ * The state's own bitmap is always updated.
+ * Errors: NS_EINVAL (null state / active_ids / n_active), NS_EHIP. */
+int nanospec_active_vocab(nanospec_state* st, int32_t* active_ids, int32_t* n_active,
+                          uint32_t* bitmap, hipStream_t stream);
+
+/* One decode-step state update in a single launch: the same as
+ *   stream_append(draft_ids, n_draft, 1); stream_append(ver_ids, n_ver, 0);
+ *   active_vocab(active_ids, n_active, bitmap);
+ * (Sec. 3.2 decoding phase followed by the sliding-window rebuild). */
+int nanospec_step_update(nanospec_state* st,
+                         const int32_t* draft_ids, int32_t n_draft,
+                         const int32_t* ver_ids, int32_t n_ver,
+                         int32_t* active_ids, int32_t* n_active, uint32_t* bitmap,
+                         hipStream_t stream);
+
+/* ======================================================================
+ * Row gather ("pack").  NanoSpec "Avoiding Sparse Computation via
+ * Asynchronous Gathering": out[j, :] = w[ids[j], :] for j < n, a bit copy.
+ *   w     : W_head, [V x d] row-major, elements of `dtype`, 16-byte aligned.
+ *   ids   : [n_max] int32 row ids; ids outside [0, V) leave out[j] untouched.
+ *   n_dev : [1] int32 row count on the device (NULL -> n = n_max); n is
+ *           clamped to [0, n_max].
+ *   out   : [n_max x d] packed buffer, 16-byte aligned; rows j >= n untouched.
+ * Meant to run on a copy stream, with an event recorded after it that the
+ * compute stream waits on before the projection.
+ * Errors: NS_EINVAL (nulls, d % 8 != 0, d > NS_MAX_D, V or n_max < 1),
+ * NS_EDTYPE, NS_EHIP. */
+int nanospec_gather_rows(const void* w, int32_t V, int32_t d, int32_t dtype,
+                         const int32_t* ids, const int32_t* n_dev, int32_t n_max,
+                         void* out, hipStream_t stream);
+
+/* ======================================================================
+ * Restricted LM head + top-k + map back to global ids.  Sec. 3.1, Eq. 1 on
+ * the sub-matrix W_head[I, :] for M hidden rows, then T_k per row.
+ *   rows    : NS_PACKED  -> packed rows [n_max x d] (row j = rows[j]);
+ *             NS_INDEXED -> W_head [V x d] (row j = W_head[row_ids[j]]).
+ *   row_ids : [n_max] global id of row j (a hole if outside [0, V): skipped).
+ *             May be NULL in NS_PACKED mode only: then row j has id j (with
+ *             rows = W_head and n_max = V this is the full-vocabulary head).
+ *   n_dev   : [1] int32 active row count (NULL -> n_max), clamped to n_max.
+ *   h       : [M x d] hidden rows, same dtype as rows, 16-byte aligned.
+ *   logits  : optional [M x n_max] float32 output (NULL -> kept in the
+ *             workspace); columns j >= n and holes are left untouched.
+ *   topk_ids/topk_vals : [M x k] int32 / float32 outputs; row m holds the k
+ *             largest logits of hidden row m, ordered by (value desc, global
+ *             id asc), with the global ids.
+ *   ws      : workspace of >= nanospec_draft_workspace_bytes(n_max, M, k)
+ *             bytes, 256-byte aligned; no initialisation needed.
+ * Arithmetic: products in float32 from bf16/fp32 inputs, float32 sums (order
+ * unspecified; no atomics, so results are deterministic).
+ * Errors: NS_EINVAL (nulls, M not in [1,64], k not in [1,64], d % 8 != 0,
+ * n_max < 1), NS_EDTYPE, NS_ECAPACITY (ws too small), NS_EHIP. */
+size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k);
+int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* row_ids,
+                               const int32_t* n_dev, int32_t n_max, int32_t V,
+                               int32_t d, int32_t dtype, const void* h, int32_t M,
+                               int32_t k, float* logits, int32_t* topk_ids,
+                               float* topk_vals, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* ======================================================================
+ * Prefill candidates.  Sec. 3.2 prefill: P[i] = T_Kpre(z_i) for every prompt
+ * position i.
+ *   logits   : [L x V] target logits, NS_BF16 or NS_FP32, row-major.
+ *   out_ids  : [L x k] int32, out_vals : [L x k] float32 (exact: the stored
+ *              logits widened to float32), each row ordered by (value desc,
+ *              id asc).  out_ids may be fed to nanospec_stream_append with
+ *              dedup_first = 1 to append tuple(U_i T_Kpre(z_i)), which orders
+ *              the union position-major, rank-minor.
+ * Errors: NS_EINVAL (nulls, L < 0, V < 1, k not in [1, min(64, V)]),
+ * NS_EDTYPE, NS_EHIP.  L = 0 enqueues nothing. */
+int nanospec_prefill_topk(const void* logits, int32_t L, int32_t V, int32_t dtype,
+                          int32_t k, int32_t* out_ids, float* out_vals,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NANOSPEC_H */

@@ -1,0 +1,102 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/nanospec.h, and rejects bad arguments on the host before
+anything is enqueued (these calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nanospec.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nanospec_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def ns():
+    from dynamic_vocab_draft_amd import nanospec
+    return nanospec
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for f in ["nanospec_stream_append", "nanospec_active_vocab", "nanospec_gather_rows",
+              "nanospec_draft_logits_topk", "nanospec_prefill_topk"]:
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(ns):
+    lib = ctypes.CDLL(ns.LIB_PATH)
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_binding_wraps_every_declared_symbol(ns):
+    for f in declared_functions():
+        assert f in ns._SIGS, f
+
+
+def test_codes_and_sizes(ns):
+    L = ns._lib
+    assert L.nanospec_version() >= 100
+    assert L.nanospec_strerror(0) == b"ok"
+    assert L.nanospec_strerror(99) == b"unknown error code"
+    assert L.nanospec_state_bytes(0, 10) == 0
+    assert L.nanospec_state_bytes(10, 0) == 0
+    assert L.nanospec_state_bytes(ns.NS_MAX_V + 1, 10) == 0
+    b = L.nanospec_state_bytes(128256, 3072)
+    # control + ring + first[V] + bitmap, each 256-byte aligned
+    assert b == 256 + 12288 + 513024 + 16128
+    assert L.nanospec_draft_workspace_bytes(3072, 8, 8) >= 3072 * 8 * 4
+    assert L.nanospec_draft_workspace_bytes(3072, 65, 8) == 0
+    assert L.nanospec_draft_workspace_bytes(3072, 8, 65) == 0
+
+
+def test_host_validation_rejects_before_launch(ns):
+    L = ns._lib
+    fake = ctypes.c_void_p(0x1000)        # never dereferenced: validation fails first
+    h = ctypes.c_void_p()
+    assert L.nanospec_state_create(None, 10, 4, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_state_create(ctypes.byref(h), 10, 4, None, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_state_create(ctypes.byref(h), 10, 4, ctypes.c_void_p(0x1010), 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_state_create(ctypes.byref(h), 10, 4, fake, 16, None) == ns.NS_ECAPACITY
+    assert L.nanospec_stream_append(None, fake, 3, 1, None) == ns.NS_EINVAL
+    assert L.nanospec_active_vocab(None, fake, fake, None, None) == ns.NS_EINVAL
+    assert L.nanospec_state_status(None, None, None) == ns.NS_EINVAL
+    assert L.nanospec_state_destroy(None) == ns.NS_EINVAL
+    # gather: null, bad d, bad dtype, misaligned
+    assert L.nanospec_gather_rows(None, 10, 8, 0, fake, None, 4, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_gather_rows(fake, 10, 12, 0, fake, None, 4, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_gather_rows(fake, 10, 8, 7, fake, None, 4, fake, None) == ns.NS_EDTYPE
+    assert L.nanospec_gather_rows(ctypes.c_void_p(0x1008), 10, 8, 0, fake, None, 4, fake, None) == ns.NS_EINVAL
+    # draft head
+    args = dict(rows=fake, mode=0, row_ids=fake, n_dev=None, n_max=16, V=100, d=64, dtype=0, h=fake, M=8, k=8,
+                logits=None, ids=fake, vals=fake, ws=fake, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.nanospec_draft_logits_topk(a["rows"], a["mode"], a["row_ids"], a["n_dev"], a["n_max"], a["V"],
+                                            a["d"], a["dtype"], a["h"], a["M"], a["k"], a["logits"], a["ids"],
+                                            a["vals"], a["ws"], a["ws_bytes"], None)
+    assert call(mode=5) == ns.NS_EDTYPE
+    assert call(dtype=3) == ns.NS_EDTYPE
+    assert call(M=0) == ns.NS_EINVAL
+    assert call(M=65) == ns.NS_EINVAL
+    assert call(k=0) == ns.NS_EINVAL
+    assert call(k=65) == ns.NS_EINVAL
+    assert call(d=60) == ns.NS_EINVAL
+    assert call(mode=1, row_ids=None) == ns.NS_EINVAL
+    assert call(h=None) == ns.NS_EINVAL
+    assert call(ws_bytes=64) == ns.NS_ECAPACITY
+    assert call(ws=ctypes.c_void_p(0x1010)) == ns.NS_EINVAL
+    # prefill
+    assert L.nanospec_prefill_topk(fake, 4, 10, 0, 0, fake, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_prefill_topk(fake, 4, 10, 0, 11, fake, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_prefill_topk(fake, 4, 10, 9, 2, fake, fake, None) == ns.NS_EDTYPE
+    assert L.nanospec_prefill_topk(None, 4, 10, 0, 2, fake, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_prefill_topk(None, 0, 10, 0, 2, fake, fake, None) == ns.NS_OK   # L = 0: nothing to do
