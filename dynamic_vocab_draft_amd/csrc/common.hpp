@@ -8,6 +8,16 @@
 
 #define NS_WAVE 64
 
+// Ends a batch of independent loads: the compiler may not sink a load of the
+// batch below this point (into the block that uses it) nor let the machine
+// scheduler interleave the batch with later work, so all of the batch's
+// requests are in flight before the first wait.
+#define NS_ISSUE_FENCE()                   \
+  do {                                     \
+    asm volatile("" ::: "memory");         \
+    __builtin_amdgcn_sched_barrier(0);     \
+  } while (0)
+
 namespace ns {
 
 // ---------------------------------------------------------------------------
@@ -64,13 +74,16 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < NS_WAVE; d <<= 1) {
-    int o = __shfl_up(v, d, NS_WAVE);
-    if (lane >= d) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves
+// (row_shr 1/2/4/8 within each row of 16 lanes, then row_bcast 15 and 31
+// carry row totals forward); lanes whose DPP source is out of range add 0.
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -138,6 +151,23 @@ __device__ __forceinline__ void block_pop_topk(uint64_t (&lst)[CAP], int k, uint
     if (best != 0 && lst[0] == best) list_pop(lst);
     if (tid == 0) emit(r, best);
   }
+}
+
+// Pops the k largest keys over the lists of the 64 lanes of one wave (no
+// barriers).  Lane r (r < k) returns the r-th key (0 if there are fewer than
+// r+1 non-empty keys).  If several lanes hold the same key at their heads,
+// only the lowest such lane pops it.
+template <int CAP>
+__device__ __forceinline__ uint64_t wave_pop_topk(uint64_t (&lst)[CAP], int k, int lane) {
+  uint64_t mine = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t best = wave_max_u64(lst[0]);
+    const unsigned long long ball = __ballot(best != 0 && lst[0] == best);
+    const int owner = ball ? (__ffsll((unsigned long long)ball) - 1) : -1;
+    if (lane == owner) list_pop(lst);
+    if (lane == r) mine = best;
+  }
+  return mine;
 }
 
 }  // namespace ns

@@ -10,28 +10,52 @@
 // contiguous 16-byte-aligned run, so an indexed row read is as coalesced as a
 // packed one); which is faster is decided by measurement.
 //
-// Kernels:
-//   k_proj_valu : VALU projection.  A block stages MT hidden rows in LDS and
-//                 its four waves stream rows of W (one row per wave, 16-byte
-//                 vectors, all of a lane's loads in flight together); bf16
-//                 pairs use v_dot2_f32_bf16.  Grid-stride over rows, grid.y
-//                 over chunks of MT hidden rows.
-//   k_proj_mfma : bf16 MFMA projection (v_mfma_f32_16x16x32_bf16), for the
-//                 wider M where fp32 VALU work would exceed the HBM time.
-//   k_topk_merge: one block per hidden row; per-thread sorted candidate lists
-//                 of 64-bit keys (orderable value, inverted global id), then a
-//                 block-wide pop of the k largest.
+// Two kernels per call:
+//   k_proj_mfma  (bf16) / k_proj_valu (fp32): partial products.  For bf16 a
+//       block owns 16*RT active rows (the A operand of
+//       v_mfma_f32_16x16x32_bf16, one row per lane group of 16) and all M
+//       hidden rows (the B operand, padded to 16*NMT), over one of S slices
+//       of d; its 4 waves split the slice further and their tiles are summed
+//       through LDS.  Splitting d across blocks is what puts enough blocks on
+//       the 256 CUs: ~1k active rows x 8 KiB is only ~60 row tiles, and one
+//       CU alone cannot pull a tile's 128 KiB fast enough.  Every load of a
+//       wave's slice is issued before the first MFMA waits on it.  Padded
+//       B-operand lanes (m >= M) read the same address as a real lane, so
+//       they cost no extra traffic, and are zeroed.  Each block writes its
+//       partial sums (deterministic; no atomics) to partial[m][j][s], the S
+//       slices of one column side by side (row stride SP = S rounded up to
+//       4) so the merge reads them with 16-byte loads.
+//   k_merge: one block per hidden row m sums the S partials of each active
+//       column in a fixed order, keeps each thread's CAP best (value, id)
+//       keys, takes the k-th largest of the first 64 thread maxima as a
+//       lower bound T for the k-th largest key overall, and ranks the (few)
+//       keys >= T by counting in LDS.  No k rounds of cross-lane reductions.
 #include "common.hpp"
 
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kProjThreads = 256;
+constexpr int kProjThreads = 256;                 // VALU projection block
 constexpr int kProjWaves = kProjThreads / NS_WAVE;
 constexpr int kProjUnroll = 8;
+constexpr size_t kHLdsBytes = 65536;              // LDS budget for staged hidden rows (VALU)
+
+constexpr int kPW = 4;                            // waves per MFMA projection block
+constexpr int kPThreads = kPW * NS_WAVE;
+constexpr int kTile = 16;                         // rows per MFMA tile
+constexpr int kKC = 4;                            // 32-column steps loaded per batch
+constexpr int kTargetBlocks = 1536;               // MFMA blocks aimed for when choosing S
+constexpr int kMaxSplits = 16;
+
 constexpr int kMergeThreads = 256;
-constexpr size_t kHLdsBytes = 65536;   // LDS budget for staged hidden rows
+
+__device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
+  int n = n_dev ? *n_dev : n_max;
+  return n < 0 ? 0 : (n > n_max ? n_max : n);
+}
 
 __device__ __forceinline__ float dot16(uint4 w, uint4 h, float acc, bool bf16) {
   if (bf16) {
@@ -48,17 +72,17 @@ __device__ __forceinline__ float dot16(uint4 w, uint4 h, float acc, bool bf16) {
   return acc;
 }
 
-__device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
-  int n = n_dev ? *n_dev : n_max;
-  return n < 0 ? 0 : (n > n_max ? n_max : n);
-}
-
+// ---------------------------------------------------------------------------
+// fp32 VALU projection: a block stages MT hidden rows in LDS and its four
+// waves stream rows (one row per wave, 16-byte vectors).  Writes complete dot
+// products into part (a single slice).
+// ---------------------------------------------------------------------------
 template <bool BF16, int MT>
 __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restrict__ rows, int mode,
                                                             const int32_t* __restrict__ row_ids,
                                                             const int32_t* __restrict__ n_dev, int n_max, int V,
                                                             int dvec, const uint4* __restrict__ h, int M,
-                                                            float* __restrict__ logits) {
+                                                            int SP, float* __restrict__ part) {
   extern __shared__ uint4 hs[];   // [mt][dvec]
   const int n = clamp_n(n_dev, n_max);
   if ((int)blockIdx.x * kProjWaves >= n) return;      // block-uniform
@@ -80,8 +104,9 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
 #pragma unroll
       for (int u = 0; u < kProjUnroll; ++u) {
         const int q = q0 + u * NS_WAVE + lane;
-        w[u] = q < dvec ? src[q] : make_uint4(0, 0, 0, 0);
+        w[u] = src[q < dvec ? q : 0];
       }
+      NS_ISSUE_FENCE();
 #pragma unroll
       for (int u = 0; u < kProjUnroll; ++u) {
         const int q = q0 + u * NS_WAVE + lane;
@@ -97,36 +122,210 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
     if (lane == 0) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        if (m < mt) logits[(size_t)(m0 + m) * n_max + j] = acc[m];
+        if (m < mt) part[((size_t)(m0 + m) * n_max + j) * SP] = acc[m];
     }
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA projection over one slice of d.  grid = (row tiles, S slices).
+// ---------------------------------------------------------------------------
+template <int NMT, int RT>
+__global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict__ rows, int mode,
+                                                         const int32_t* __restrict__ row_ids,
+                                                         const int32_t* __restrict__ n_dev, int n_max, int V,
+                                                         int dv, const uint4* __restrict__ h, int M,
+                                                         int ks_per_split, int SP, float* __restrict__ part) {
+  __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
+  __shared__ int sh_ok[RT * kTile];
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), w = tid / NS_WAVE;
+  const int i = lane & 15, g = lane >> 4;
+  const int r0 = blockIdx.x * (kTile * RT);
+  const int split = blockIdx.y;
+  // Independent loads first: the active count and this lane's row ids.
+  const int n = clamp_n(n_dev, n_max);
+  int gid[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int row = r0 + r * kTile + i;
+    gid[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+  }
+  if (r0 >= n) return;                                  // block-uniform: nothing live here
+  bool ok[RT];
+  const uint4* src[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int row = r0 + r * kTile + i;
+    ok[r] = row < n && gid[r] >= 0 && gid[r] < V;
+    src[r] = rows + (size_t)(ok[r] ? (mode == NS_INDEXED ? gid[r] : row) : 0) * dv;
+    if (w == 0 && lane < kTile) sh_ok[r * kTile + lane] = ok[r];
+  }
+  const uint4* hrow[NMT];
+  bool m_ok[NMT];
+#pragma unroll
+  for (int t = 0; t < NMT; ++t) {
+    const int m = t * 16 + i;
+    m_ok[t] = m < M;
+    hrow[t] = h + (size_t)(m_ok[t] ? m : m % M) * dv;   // padded lanes alias a real row
+  }
+  // This wave's 32-column steps: the split's range, divided among the waves.
+  const int ksteps = (dv + 3) >> 2;
+  const int kb = split * ks_per_split;
+  const int ke = min(ksteps, kb + ks_per_split);
+  const int per = (ke - kb + kPW - 1) / kPW;
+  const int s_begin = kb + w * per;
+  const int s_end = min(ke, s_begin + per);
+  f32x4_t acc[RT][NMT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < NMT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int s0 = s_begin; s0 < s_end; s0 += kKC) {
+    uint4 a[kKC][RT];
+    uint4 b[kKC][NMT];
+#pragma unroll
+    for (int kk = 0; kk < kKC; ++kk) {
+      const int c8 = (s0 + kk) * 4 + g;
+      const int cc = ((s0 + kk) < s_end && c8 < dv) ? c8 : 0;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[kk][r] = src[r][cc];
+#pragma unroll
+      for (int t = 0; t < NMT; ++t) b[kk][t] = hrow[t][cc];
+    }
+    NS_ISSUE_FENCE();
+#pragma unroll
+    for (int kk = 0; kk < kKC; ++kk) {
+      const int c8 = (s0 + kk) * 4 + g;
+      const bool kok = (s0 + kk) < s_end && c8 < dv;
+#pragma unroll
+      for (int t = 0; t < NMT; ++t) {
+        const uint4 bv = (kok && m_ok[t]) ? b[kk][t] : z;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const uint4 av = (kok && ok[r]) ? a[kk][r] : z;
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                              __builtin_bit_cast(bf16x8_t, bv), acc[r][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < NMT; ++t) red[w][r][t][lane] = acc[r][t];
+  __syncthreads();
+  // Sum the wave tiles.  In a 16x16 result tile, lane L holds rows
+  // 4*(L/16) .. +3 (one per register) of column L%16.
+  for (int e = tid; e < RT * NMT * NS_WAVE; e += kPThreads) {
+    const int r = e / (NMT * NS_WAVE);
+    const int t = (e / NS_WAVE) % NMT;
+    const int l2 = e % NS_WAVE;
+    f32x4_t sum = red[0][r][t][l2];
+#pragma unroll
+    for (int ww = 1; ww < kPW; ++ww) sum += red[ww][r][t][l2];
+    const int m = t * 16 + (l2 & 15);
+    if (m < M) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ri = r * kTile + (l2 >> 4) * 4 + v;
+        if (sh_ok[ri]) part[((size_t)m * n_max + r0 + ri) * SP + split] = sum[v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: one block per hidden row m.
+// ---------------------------------------------------------------------------
 template <int CAP>
-__global__ __launch_bounds__(kMergeThreads) void k_topk_merge(const float* __restrict__ logits, int n_max,
-                                                              const int32_t* __restrict__ row_ids,
-                                                              const int32_t* __restrict__ n_dev, int V, int k,
-                                                              int32_t* __restrict__ out_ids,
-                                                              float* __restrict__ out_vals) {
-  __shared__ uint64_t sh[kMergeThreads / NS_WAVE];
-  const int m = blockIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict__ part, int S, int SP, int n_max,
+                                                         const int32_t* __restrict__ row_ids,
+                                                         const int32_t* __restrict__ n_dev, int V, int M, int k,
+                                                         float* __restrict__ logits_out,
+                                                         int32_t* __restrict__ out_ids,
+                                                         float* __restrict__ out_vals) {
+  extern __shared__ uint64_t cand[];                 // kMergeThreads * min(CAP, k)
+  __shared__ uint64_t tmax[NS_WAVE];
+  __shared__ uint64_t sh_T;
+  __shared__ int sh_cnt;
+  const int m = blockIdx.x, tid = threadIdx.x;
   const int n = clamp_n(n_dev, n_max);
   uint64_t lst[CAP];
 #pragma unroll
-  for (int i = 0; i < CAP; ++i) lst[i] = 0;
-  const float* __restrict__ lrow = logits + (size_t)m * n_max;
-  for (int j = threadIdx.x; j < n; j += kMergeThreads) {
-    const int gid = row_ids ? row_ids[j] : j;
-    if (gid < 0 || gid >= V) continue;
-    const uint64_t key = ns::make_key(lrow[j], gid);
-    if (key > lst[CAP - 1]) ns::list_insert(lst, key);
+  for (int c = 0; c < CAP; ++c) lst[c] = 0;
+  constexpr int U = 4;                               // columns per thread per batch
+  const int SQ = SP >> 2;                            // 16-byte loads per column (<= 4)
+  const float4* __restrict__ prow = (const float4*)(part + (size_t)m * n_max * SP);
+  for (int j0 = tid; j0 < n; j0 += kMergeThreads * U) {
+    int gv[U];
+    float4 pv[U][kMaxSplits / 4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kMergeThreads;
+      const int jc = j < n ? j : 0;
+      gv[u] = row_ids ? row_ids[jc] : jc;
+#pragma unroll
+      for (int q = 0; q < kMaxSplits / 4; ++q) pv[u][q] = prow[(size_t)jc * SQ + (q < SQ ? q : 0)];
+    }
+    NS_ISSUE_FENCE();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kMergeThreads;
+      float sv = 0.f;                                // slices summed in a fixed order
+#pragma unroll
+      for (int q = 0; q < kMaxSplits / 4; ++q) {
+        if (4 * q + 0 < S) sv += pv[u][q].x;
+        if (4 * q + 1 < S) sv += pv[u][q].y;
+        if (4 * q + 2 < S) sv += pv[u][q].z;
+        if (4 * q + 3 < S) sv += pv[u][q].w;
+      }
+      if (j < n && gv[u] >= 0 && gv[u] < V) {
+        if (logits_out) logits_out[(size_t)m * n_max + j] = sv;
+        const uint64_t key = ns::make_key(sv, gv[u]);
+        if (key > lst[CAP - 1]) ns::list_insert(lst, key);
+      }
+    }
   }
-  ns::block_pop_topk<kMergeThreads, CAP>(lst, k, sh, [&](int r, uint64_t key) {
-    out_ids[(size_t)m * k + r] = key ? ns::key_id(key) : -1;
-    out_vals[(size_t)m * k + r] = key ? ns::key_val(key) : -INFINITY;
-  });
+  // T = k-th largest of wave 0's thread maxima.  These are k real keys, so
+  // the k-th largest key overall is >= T and every key of the top k is >= T.
+  const uint64_t mk = lst[0];
+  if (tid < NS_WAVE) tmax[tid] = mk;
+  if (tid == 0) { sh_T = 0; sh_cnt = 0; }
+  __syncthreads();
+  if (tid < NS_WAVE && mk != 0) {
+    int rank = 0;
+#pragma unroll 16
+    for (int q = 0; q < NS_WAVE; ++q) rank += tmax[q] > mk;
+    if (rank == k - 1) sh_T = mk;
+  }
+  __syncthreads();
+  const uint64_t T = sh_T;
+  // Keys >= T; a thread's keys past its own k best cannot be in the top k.
+#pragma unroll
+  for (int c = 0; c < CAP; ++c) {
+    if (c < k && lst[c] != 0 && lst[c] >= T) cand[atomicAdd(&sh_cnt, 1)] = lst[c];
+  }
+  __syncthreads();
+  const int C = sh_cnt;
+  for (int q = tid; q < C; q += kMergeThreads) {
+    const uint64_t x = cand[q];
+    int r = 0;
+    for (int p = 0; p < C; ++p) r += cand[p] > x;
+    if (r < k) {
+      out_ids[(size_t)m * k + r] = ns::key_id(x);
+      out_vals[(size_t)m * k + r] = ns::key_val(x);
+    }
+  }
+  for (int r = C + tid; r < k; r += kMergeThreads) {
+    out_ids[(size_t)m * k + r] = -1;
+    out_vals[(size_t)m * k + r] = -INFINITY;
+  }
 }
 
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int pick_mt(int M, int d, int esz) {
@@ -135,9 +334,29 @@ int pick_mt(int M, int d, int esz) {
   return ((size_t)mt * d * esz > kHLdsBytes) ? 0 : mt;
 }
 
+int pick_rt(int M) { return M <= 16 ? 1 : 2; }
+
+// Number of d-slices for the MFMA path: enough blocks to spread a call over
+// the chip, each wave keeping at least one batch of kKC steps.
+int pick_splits(int n_max, int M, int d, int dtype) {
+  if (dtype != NS_BF16) return 1;
+  const int ksteps = (d / 8 + 3) / 4;
+  const int tiles = (n_max + kTile * pick_rt(M) - 1) / (kTile * pick_rt(M));
+  int s = (kTargetBlocks + tiles - 1) / tiles;
+  const int smax = ksteps / (kPW * kKC) > 0 ? ksteps / (kPW * kKC) : 1;
+  if (s > smax) s = smax;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : s;
+}
+
+size_t merge_lds_bytes(int k) {
+  const int cap = k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
+  return (size_t)kMergeThreads * (k < cap ? k : cap) * sizeof(uint64_t);
+}
+
 template <bool BF16>
 int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V,
-                int d, const void* h, int M, float* logits, hipStream_t stream) {
+                int d, const void* h, int M, int SP, float* part, hipStream_t stream) {
   const int esz = BF16 ? 2 : 4;
   const int dvec = d * esz / 16;
   const int quads = (n_max + kProjWaves - 1) / kProjWaves;
@@ -146,7 +365,7 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   const size_t lds = (size_t)mt * dvec * 16;
 #define NS_LAUNCH_VALU(MTV)                                                                                     \
   hipLaunchKernelGGL((k_proj_valu<BF16, MTV>), grid, dim3(kProjThreads), lds, stream, (const uint4*)rows, mode, \
-                     row_ids, n_dev, n_max, V, dvec, (const uint4*)h, M, logits)
+                     row_ids, n_dev, n_max, V, dvec, (const uint4*)h, M, SP, part)
   switch (mt) {
     case 1: NS_LAUNCH_VALU(1); break;
     case 2: NS_LAUNCH_VALU(2); break;
@@ -157,26 +376,70 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   return ns_launch_status();
 }
 
-int launch_merge(const float* logits, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V, int M, int k,
-                 int32_t* ids, float* vals, hipStream_t stream) {
-#define NS_LAUNCH_MERGE(CAPV)                                                                                 \
-  hipLaunchKernelGGL((k_topk_merge<CAPV>), dim3(M), dim3(kMergeThreads), 0, stream, logits, n_max, row_ids, \
-                     n_dev, V, k, ids, vals)
-  if (k <= 8) NS_LAUNCH_MERGE(8);
-  else if (k <= 16) NS_LAUNCH_MERGE(16);
-  else if (k <= 32) NS_LAUNCH_MERGE(32);
-  else NS_LAUNCH_MERGE(64);
-#undef NS_LAUNCH_MERGE
+template <int NMT, int RT>
+void launch_mfma_t(dim3 grid, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
+                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int ks, int SP, float* part) {
+  hipLaunchKernelGGL((k_proj_mfma<NMT, RT>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
+                     n_dev, n_max, V, dv, (const uint4*)h, M, ks, SP, part);
+}
+
+int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
+                const void* h, int M, int S, int SP, float* part, hipStream_t stream) {
+  const int dv = d / 8;
+  const int ksteps = (dv + 3) / 4;
+  const int ks = (ksteps + S - 1) / S;
+  const int rt = pick_rt(M);
+  const dim3 grid((n_max + kTile * rt - 1) / (kTile * rt), S);
+  switch ((M + 15) / 16) {
+    case 1: launch_mfma_t<1, 1>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
+    case 2: launch_mfma_t<2, 2>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
+    case 3: launch_mfma_t<3, 2>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
+    default: launch_mfma_t<4, 2>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
+  }
   return ns_launch_status();
+}
+
+template <int CAP>
+int launch_merge_t(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V, int M,
+                   int k, float* logits, int32_t* ids, float* vals, hipStream_t stream) {
+  const size_t lds = merge_lds_bytes(k);
+  if (lds > 65536) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      if (hipFuncSetAttribute((const void*)k_merge<CAP>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+          hipSuccess)
+        return NS_EHIP;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL((k_merge<CAP>), dim3(M), dim3(kMergeThreads), lds, stream, part, S, SP, n_max, row_ids, n_dev,
+                     V, M, k, logits, ids, vals);
+  return ns_launch_status();
+}
+
+int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
+                 int M, int k, float* logits, int32_t* ids, float* vals, hipStream_t stream) {
+  if (k <= 8) return launch_merge_t<8>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
+  if (k <= 16) return launch_merge_t<16>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
+  if (k <= 32) return launch_merge_t<32>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
+  return launch_merge_t<64>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
+}
+
+bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
+  return n_max >= 1 && M >= 1 && M <= NS_MAX_M && k >= 1 && k <= NS_MAX_K && d >= 8 && d <= NS_MAX_D &&
+         (d % 8) == 0;
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k) {
-  if (n_max < 1 || M < 1 || M > NS_MAX_M || k < 1 || k > NS_MAX_K) return 0;
-  return 256 + align256((size_t)M * n_max * sizeof(float));
+// Workspace: partial sums [M x n_max x SP] float32 (SP = S rounded up to 4)
+// at offset 256.
+size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d) {
+  if (!draft_dims_ok(n_max, M, k, d)) return 0;
+  const int SP = (pick_splits(n_max, M, d, NS_BF16) + 3) & ~3;
+  return 256 + align256((size_t)SP * M * n_max * sizeof(float));
 }
 
 int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
@@ -187,19 +450,23 @@ int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* ro
   if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
   if (!rows || !h || !topk_ids || !topk_vals || !ws) return NS_EINVAL;
   if (mode == NS_INDEXED && !row_ids) return NS_EINVAL;
-  if (n_max < 1 || V < 1 || M < 1 || M > NS_MAX_M || k < 1 || k > NS_MAX_K) return NS_EINVAL;
-  if (d < 8 || d > NS_MAX_D || (d % 8) != 0) return NS_EINVAL;
+  if (V < 1 || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
   if ((((uintptr_t)rows) & 15u) || (((uintptr_t)h) & 15u) || (((uintptr_t)ws) & 255u)) return NS_EINVAL;
-  if (ws_bytes < nanospec_draft_workspace_bytes(n_max, M, k)) return NS_ECAPACITY;
-  const int esz = dtype == NS_BF16 ? 2 : 4;
-  const int mt = pick_mt(M, d, esz);
-  if (mt == 0) return NS_EINVAL;
-  float* lg = logits ? logits : (float*)((char*)ws + 256);
+  if (ws_bytes < nanospec_draft_workspace_bytes(n_max, M, k, d)) return NS_ECAPACITY;
+  float* part = (float*)((char*)ws + 256);
   (void)hipGetLastError();
-  int rc = dtype == NS_BF16 ? launch_valu<true>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, lg, stream)
-                            : launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, lg, stream);
+  const int S = pick_splits(n_max, M, d, dtype);
+  const int SP = (S + 3) & ~3;
+  int rc;
+  if (dtype == NS_BF16) {
+    rc = launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, S, SP, part, stream);
+  } else {
+    const int mt = pick_mt(M, d, 4);
+    if (mt == 0) return NS_EINVAL;
+    rc = launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, SP, part, stream);
+  }
   if (rc != NS_OK) return rc;
-  return launch_merge(lg, n_max, row_ids, n_dev, V, M, k, topk_ids, topk_vals, stream);
+  return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, stream);
 }
 
 }  // extern "C"

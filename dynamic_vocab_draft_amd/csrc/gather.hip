@@ -27,19 +27,16 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(const uint4* __restri
   if (id < 0 || id >= V) return;
   const uint4* __restrict__ src = w + (size_t)id * dvec;
   uint4* __restrict__ dst = out + (size_t)j * dvec;
-  for (int q0 = 0; q0 < dvec; q0 += NS_WAVE * kUnroll) {
+  // Full batches: kUnroll unguarded 16-byte loads per lane, then the stores.
+  int q0 = 0;
+  for (; q0 + NS_WAVE * kUnroll <= dvec; q0 += NS_WAVE * kUnroll) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int q = q0 + u * NS_WAVE + lane;
-      if (q < dvec) v[u] = src[q];
-    }
+    for (int u = 0; u < kUnroll; ++u) v[u] = src[q0 + u * NS_WAVE + lane];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int q = q0 + u * NS_WAVE + lane;
-      if (q < dvec) dst[q] = v[u];
-    }
+    for (int u = 0; u < kUnroll; ++u) dst[q0 + u * NS_WAVE + lane] = v[u];
   }
+  for (int q = q0 + lane; q < dvec; q += NS_WAVE) dst[q] = src[q];
 }
 
 }  // namespace

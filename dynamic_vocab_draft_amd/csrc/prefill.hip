@@ -57,8 +57,9 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
 #pragma unroll
       for (int u = 0; u < kPrefillUnroll; ++u) {
         const int q = q0 + u * kPrefillThreads;
-        x[u] = q < nvec ? p[q] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+        x[u] = p[q < nvec ? q : 0];          // unconditional: all loads in flight at once
       }
+      NS_ISSUE_FENCE();
 #pragma unroll
       for (int u = 0; u < kPrefillUnroll; ++u) {
         const int q = q0 + u * kPrefillThreads;

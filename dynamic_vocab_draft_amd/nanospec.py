@@ -74,7 +74,7 @@ _SIGS = {
     "nanospec_active_vocab": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp]),
     "nanospec_step_update": (ctypes.c_int, [c_vp, c_vp, c_int32, c_vp, c_int32, c_vp, c_vp, c_vp, c_vp]),
     "nanospec_gather_rows": (ctypes.c_int, [c_vp, c_int32, c_int32, c_int32, c_vp, c_vp, c_int32, c_vp, c_vp]),
-    "nanospec_draft_workspace_bytes": (c_size, [c_int32, c_int32, c_int32]),
+    "nanospec_draft_workspace_bytes": (c_size, [c_int32, c_int32, c_int32, c_int32]),
     "nanospec_draft_logits_topk": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
                                                   c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "nanospec_prefill_topk": (ctypes.c_int, [c_vp, c_int32, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp]),
@@ -200,8 +200,8 @@ def nanospec_gather_rows(w: torch.Tensor, V: int, d: int, dtype: int, ids: torch
                                      _stream(stream)), "nanospec_gather_rows")
 
 
-def nanospec_draft_workspace_bytes(n_max: int, M: int, k: int) -> int:
-    return _lib.nanospec_draft_workspace_bytes(n_max, M, k)
+def nanospec_draft_workspace_bytes(n_max: int, M: int, k: int, d: int) -> int:
+    return _lib.nanospec_draft_workspace_bytes(n_max, M, k, d)
 
 
 def nanospec_draft_logits_topk(rows: torch.Tensor, mode: int, row_ids: Optional[torch.Tensor],
@@ -221,11 +221,11 @@ def nanospec_prefill_topk(logits: torch.Tensor, L: int, V: int, dtype: int, k: i
                                       _stream(stream)), "nanospec_prefill_topk")
 
 
-def alloc_workspace(n_max: int, M: int, k: int, device="cuda") -> torch.Tensor:
+def alloc_workspace(n_max: int, M: int, k: int, d: int, device="cuda") -> torch.Tensor:
     """A 256-byte-aligned uint8 workspace of nanospec_draft_workspace_bytes."""
-    nbytes = nanospec_draft_workspace_bytes(n_max, M, k)
+    nbytes = nanospec_draft_workspace_bytes(n_max, M, k, d)
     if nbytes == 0:
         raise NanoSpecError(NS_EINVAL, "nanospec_draft_workspace_bytes")
-    mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    mem = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-mem.data_ptr()) % 256
     return mem[off:off + nbytes]

@@ -184,13 +184,17 @@ int nanospec_gather_rows(const void* w, int32_t V, int32_t d, int32_t dtype,
  *   topk_ids/topk_vals : [M x k] int32 / float32 outputs; row m holds the k
  *             largest logits of hidden row m, ordered by (value desc, global
  *             id asc), with the global ids.
- *   ws      : workspace of >= nanospec_draft_workspace_bytes(n_max, M, k)
- *             bytes, 256-byte aligned; no initialisation needed.
- * Arithmetic: products in float32 from bf16/fp32 inputs, float32 sums (order
- * unspecified; no atomics, so results are deterministic).
+ *   ws      : workspace of >= nanospec_draft_workspace_bytes(n_max, M, k, d)
+ *             bytes, 256-byte aligned (partial sums; no initialisation
+ *             needed).  Calls sharing a workspace must be ordered.
+ * Arithmetic: bf16 products are exact in float32 and summed in float32 on the
+ * matrix cores (v_mfma_f32_16x16x32_bf16), in slices of d whose partial sums
+ * are added in a fixed order; fp32 inputs use float32 FMAs.  No float
+ * atomics: results are deterministic for a given (n_max, M, d).
+ * row_ids must be distinct apart from holes.
  * Errors: NS_EINVAL (nulls, M not in [1,64], k not in [1,64], d % 8 != 0,
  * n_max < 1), NS_EDTYPE, NS_ECAPACITY (ws too small), NS_EHIP. */
-size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k);
+size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d);
 int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* row_ids,
                                const int32_t* n_dev, int32_t n_max, int32_t V,
                                int32_t d, int32_t dtype, const void* h, int32_t M,

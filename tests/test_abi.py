@@ -52,9 +52,10 @@ def test_codes_and_sizes(ns):
     b = L.nanospec_state_bytes(128256, 3072)
     # control + ring + first[V] + bitmap, each 256-byte aligned
     assert b == 256 + 12288 + 513024 + 16128
-    assert L.nanospec_draft_workspace_bytes(3072, 8, 8) >= 3072 * 8 * 4
-    assert L.nanospec_draft_workspace_bytes(3072, 65, 8) == 0
-    assert L.nanospec_draft_workspace_bytes(3072, 8, 65) == 0
+    assert L.nanospec_draft_workspace_bytes(3072, 8, 8, 4096) >= 3072 * 8 * 4
+    assert L.nanospec_draft_workspace_bytes(3072, 65, 8, 4096) == 0
+    assert L.nanospec_draft_workspace_bytes(3072, 8, 65, 4096) == 0
+    assert L.nanospec_draft_workspace_bytes(3072, 8, 8, 4100) == 0      # d % 8 != 0
 
 
 def test_host_validation_rejects_before_launch(ns):

@@ -76,7 +76,7 @@ def run_draft(ns, W_dev, h_dev, I, n_max, V, d, dtype, M, k, mode, packed=None, 
     logits = torch.full((M, n_max), float("nan"), device="cuda") if with_logits else None
     tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((M, k), dtype=torch.float32, device="cuda")
-    ws = ns.alloc_workspace(n_max, M, k)
+    ws = ns.alloc_workspace(n_max, M, k, d)
     if mode == ns.NS_PACKED:
         if packed is None:
             packed = torch.zeros((n_max, d), dtype=W_dev.dtype, device="cuda")
@@ -237,6 +237,34 @@ def test_state_edges(ns):
         check_state(g1, s1, V, "w_max=1")
 
 
+def test_step_update_paths(ns):
+    """nanospec_step_update on both kernels: tuples of up to 512 ids take the
+    one-round-trip LDS path, longer ones the general path; w_max not a
+    multiple of 4 takes the scalar ring copy."""
+    say("step update: fast and general paths")
+    rng = np.random.default_rng(8)
+    V = 1000
+    for w_max, n_tree, n_ver in ((37, 60, 8), (64, 512, 512), (250, 700, 10), (301, 5, 600), (1, 3, 1)):
+        g = GpuSeq(ns, V, w_max)
+        s = O.Sequence_(w_max)
+        for step in range(6):
+            tree = rng.integers(0, 150, size=n_tree).astype(np.int32)
+            ver = rng.choice(V, size=n_ver, replace=False).astype(np.int32)
+            g.step(tree, ver)
+            s.step(tree, ver)
+            check_state(g, s, V, f"w_max={w_max} tree={n_tree} ver={n_ver} step {step}")
+        assert ns.nanospec_state_status(g.st) == 0
+    # invalid ids in a step: skipped, status bit set, both paths
+    for n_tree in (10, 600):
+        g = GpuSeq(ns, V, 50)
+        s = O.Sequence_(50)
+        tree = np.array([3, -1, 3, 1000, 7] + [8] * (n_tree - 5), np.int32)
+        g.step(tree, np.array([9, 5000, 2], np.int32))
+        s.step([3, 7, 8][: 2 + (n_tree > 5)], [9, 2])
+        check_state(g, s, V, f"invalid ids, tree={n_tree}")
+        assert ns.nanospec_state_status(g.st) == ns.NS_STATUS_BAD_ID
+
+
 def test_dedup_many_chunks(ns):
     """An append of many ids (several 1024-thread chunks) with heavy repeats."""
     say("dedup over several chunks")
@@ -283,7 +311,7 @@ def test_draft_edges(ns):
         dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
         tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
         tvals = torch.empty((M, k), dtype=torch.float32, device="cuda")
-        ws = ns.alloc_workspace(64, M, k)
+        ws = ns.alloc_workspace(64, M, k, d)
         ns.nanospec_draft_logits_topk(Wsub_dev, ns.NS_PACKED, None, None, 64, 64, d, dcode, dev_elems(h, dtype), M, k,
                                       None, tids, tvals, ws)
         torch.cuda.synchronize()
@@ -370,7 +398,7 @@ def test_llama3_8b_config(ns):
     tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((cfg.M, cfg.k), dtype=torch.float32, device="cuda")
     logits = torch.empty((cfg.M, cfg.V), dtype=torch.float32, device="cuda")
-    ws = ns.alloc_workspace(cfg.V, cfg.M, cfg.k)
+    ws = ns.alloc_workspace(cfg.V, cfg.M, cfg.k, cfg.d)
     ns.nanospec_draft_logits_topk(W_dev, ns.NS_PACKED, None, None, cfg.V, cfg.V, cfg.d, dcode, dev_elems(h, "bf16"),
                                   cfg.M, cfg.k, logits, tids, tvals, ws)
     torch.cuda.synchronize()
