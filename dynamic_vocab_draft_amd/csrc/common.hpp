@@ -68,6 +68,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Running maximum over the 16 lanes of each DPP row (row_shr 1, 2, 4, 8 with
+// 0 shifted in, 0 being the empty key): lane 15 of a row ends with the
+// row's maximum.
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+#define NS_ROW_MAX_STEP(CTRL)                                                                              \
+  {                                                                                                       \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);  \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, \
+                                                              false);                                     \
+    const uint64_t o = ((uint64_t)hi << 32) | lo;                                                         \
+    v = o > v ? o : v;                                                                                    \
+  }
+  NS_ROW_MAX_STEP(0x111)
+  NS_ROW_MAX_STEP(0x112)
+  NS_ROW_MAX_STEP(0x114)
+  NS_ROW_MAX_STEP(0x118)
+#undef NS_ROW_MAX_STEP
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, NS_WAVE);

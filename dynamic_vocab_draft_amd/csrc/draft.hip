@@ -324,6 +324,139 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Merge for n_max <= 4096: one 1024-thread block per hidden row m, at most
+// four columns per thread.  The first column of every thread is requested in
+// the same round as |I|, so the partial sums are in flight before |I| is
+// known.  Selection: T = the k-th largest of the 64 maxima of 16-lane rows.
+// Each of those is a real key, so the k-th largest key overall is >= T and
+// the top k are among the keys >= T; those are collected in LDS and ranked by
+// counting.  If more than kCandCap keys reach T, the block falls back to k
+// rounds of block-wide maxima.
+// ---------------------------------------------------------------------------
+constexpr int kMergeSmallThreads = 1024;
+constexpr int kMergeSmallCols = 4;
+constexpr int kCandCap = 1024;
+
+template <int SQ>
+__device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
+  float sv = 0.f;                                    // slices summed in a fixed order
+#pragma unroll
+  for (int q = 0; q < SQ; ++q) {
+    if (4 * q + 0 < S) sv += p[q].x;
+    if (4 * q + 1 < S) sv += p[q].y;
+    if (4 * q + 2 < S) sv += p[q].z;
+    if (4 * q + 3 < S) sv += p[q].w;
+  }
+  return sv;
+}
+
+template <int SQ>
+__global__ __launch_bounds__(kMergeSmallThreads) void k_merge_small(const float* __restrict__ part, int S, int n_max,
+                                                                    const int32_t* __restrict__ row_ids,
+                                                                    const int32_t* __restrict__ n_dev, int V, int k,
+                                                                    float* __restrict__ logits_out,
+                                                                    int32_t* __restrict__ out_ids,
+                                                                    float* __restrict__ out_vals) {
+  constexpr int NT = kMergeSmallThreads, U = kMergeSmallCols;
+  __shared__ uint64_t rmax[NS_WAVE];                 // (NT / 64 waves) x (4 rows of 16 lanes)
+  __shared__ uint64_t cand[kCandCap];
+  __shared__ uint64_t sh_red[NT / NS_WAVE];
+  __shared__ int sh_cnt;
+  static_assert(NT / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
+  const float4* prow = (const float4*)(part + (size_t)m * n_max * (SQ * 4));
+  const int n_raw = n_dev ? *n_dev : n_max;
+  int gv[U];
+  float4 pv[U][SQ];
+  {
+    const int jc = tid < n_max ? tid : n_max - 1;
+    gv[0] = row_ids ? row_ids[jc] : jc;
+#pragma unroll
+    for (int q = 0; q < SQ; ++q) pv[0][q] = prow[(size_t)jc * SQ + q];
+  }
+  NS_ISSUE_FENCE();
+  const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
+  if (n > NT) {                                      // block-uniform
+#pragma unroll
+    for (int u = 1; u < U; ++u) {
+      const int j = tid + u * NT;
+      const int jc = j < n ? j : n - 1;
+      gv[u] = row_ids ? row_ids[jc] : jc;
+#pragma unroll
+      for (int q = 0; q < SQ; ++q) pv[u][q] = prow[(size_t)jc * SQ + q];
+    }
+    NS_ISSUE_FENCE();
+  }
+  uint64_t key[U];
+  uint64_t best = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = tid + u * NT;
+    key[u] = 0;
+    if (u == 0 || n > NT) {
+      const float sv = sum_slices<SQ>(pv[u], S);
+      if (j < n && gv[u] >= 0 && gv[u] < V) {
+        if (logits_out) logits_out[(size_t)m * n_max + j] = sv;
+        key[u] = ns::make_key(sv, gv[u]);
+      }
+    }
+    best = key[u] > best ? key[u] : best;
+  }
+  const uint64_t rm = ns::row16_max_u64(best);
+  if ((lane & 15) == 15) rmax[(tid / NS_WAVE) * 4 + (lane >> 4)] = rm;
+  if (tid == 0) sh_cnt = 0;
+  __syncthreads();
+  // Every wave finds T itself: lane l ranks row maximum l among the 64.
+  const uint64_t mine = rmax[lane];
+  int rank = 0;
+#pragma unroll 16
+  for (int q = 0; q < NS_WAVE; ++q) rank += rmax[q] > mine;
+  const unsigned long long ball = __ballot(mine != 0 && rank == k - 1);
+  uint64_t T = 0;
+  if (ball) {
+    const int src = __ffsll(ball) - 1;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), src);
+    T = ((uint64_t)hi << 32) | lo;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (key[u] != 0 && key[u] >= T) {
+      const int slot = atomicAdd(&sh_cnt, 1);
+      if (slot < kCandCap) cand[slot] = key[u];
+    }
+  }
+  __syncthreads();
+  const int C = sh_cnt;
+  if (C <= kCandCap) {
+    for (int q = tid; q < C; q += NT) {
+      const uint64_t x = cand[q];
+      int r = 0;
+#pragma unroll 8
+      for (int p = 0; p < C; ++p) r += cand[p] > x;
+      if (r < k) {
+        out_ids[(size_t)m * k + r] = ns::key_id(x);
+        out_vals[(size_t)m * k + r] = ns::key_val(x);
+      }
+    }
+    for (int r = C + tid; r < k; r += NT) {
+      out_ids[(size_t)m * k + r] = -1;
+      out_vals[(size_t)m * k + r] = -INFINITY;
+    }
+  } else {                                           // block-uniform: too many keys at T
+    uint64_t lst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) lst[u] = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) ns::list_insert(lst, key[u]);
+    ns::block_pop_topk<NT, U>(lst, k, sh_red, [&](int r, uint64_t x) {
+      out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
+      out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -419,6 +552,19 @@ int launch_merge_t(const float* part, int S, int SP, int n_max, const int32_t* r
 
 int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
                  int M, int k, float* logits, int32_t* ids, float* vals, hipStream_t stream) {
+  if (n_max <= kMergeSmallThreads * kMergeSmallCols) {
+#define NS_LAUNCH_MERGE_SMALL(SQV)                                                                                   \
+  hipLaunchKernelGGL((k_merge_small<SQV>), dim3(M), dim3(kMergeSmallThreads), 0, stream, part, S, n_max, row_ids, \
+                     n_dev, V, k, logits, ids, vals)
+    switch (SP / 4) {
+      case 1: NS_LAUNCH_MERGE_SMALL(1); break;
+      case 2: NS_LAUNCH_MERGE_SMALL(2); break;
+      case 3: NS_LAUNCH_MERGE_SMALL(3); break;
+      default: NS_LAUNCH_MERGE_SMALL(4); break;
+    }
+#undef NS_LAUNCH_MERGE_SMALL
+    return ns_launch_status();
+  }
   if (k <= 8) return launch_merge_t<8>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
   if (k <= 16) return launch_merge_t<16>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
   if (k <= 32) return launch_merge_t<32>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);

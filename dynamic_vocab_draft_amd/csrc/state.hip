@@ -199,104 +199,96 @@ __global__ __launch_bounds__(kStateThreads) void k_step(ns_state_view v, const i
   finish(s, len, sh_flag);
 }
 
-// Per-step update with one round of global loads.  Every global read the
-// step needs (|S|, the whole ring, both tuples) is issued at once into LDS;
-// C_draft is deduplicated in LDS (each id compared with the ones before it,
-// fine for a draft tree of up to kFastMaxIds ids); the new entries are
-// written to the ring in global memory and to its LDS copy; the active set is
-// then rebuilt from the LDS ring.  Ring slots outside the window hold -1
-// (they were never written), so reading all w_max slots needs no |S|.
+// Per-step update with one round of global loads and no LDS copy of the
+// ring.  Every global read the step needs (|S|, the whole ring, both tuples)
+// is issued at once; each thread keeps its ring slots in registers.  C_draft
+// is deduplicated against an LDS copy of the tuple (fine for a draft tree of
+// up to kFastMaxIds ids).  After the tuple positions are scanned, the active
+// bitmap is built in LDS from (a) the new entries that land in the window and
+// (b) the old slots that they do not overwrite: with |S| = len and
+// C = |C_draft| + |C_ver|, the new entries take slots (len + p) mod w_max, so
+// an old slot s survives iff C < w_max and (s - len) mod w_max >= C.  Slots
+// never written hold -1.  The ascending compaction gives each thread a
+// contiguous run of WPT words (a multiple of 8, read as 16-byte LDS vectors).
 constexpr int kFastThreads = 512;
 constexpr int kFastMaxIds = kFastThreads;      // one tuple entry per thread
+constexpr int kFastMaxRing = 32 * kFastThreads; // ring entries held in registers
 constexpr size_t kFastLdsMax = 144 * 1024;
 
-// Copies src[0..count) to LDS (count >= 1) in batches of U unconditional
-// (index-clamped) loads per thread; the memory fence keeps a batch's loads
-// ahead of its guarded stores.  `first` runs between the first batch's loads
-// and its stores, so loads it issues join that batch's round trip.  Neither
-// pointer is restrict-qualified: the fence must order them.
-template <typename T, int U, typename First>
-__device__ __forceinline__ void copy_to_lds(T* dst, const T* src, int count, First first) {
-  for (int base = threadIdx.x, it = 0; it == 0 || base < count; base += kFastThreads * U, ++it) {
-    T tmp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * kFastThreads;
-      tmp[u] = src[idx < count ? idx : 0];
-    }
-    if (it == 0) first();
-    NS_ISSUE_FENCE();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * kFastThreads;
-      if (idx < count) dst[idx] = tmp[u];
-    }
-  }
+__host__ __device__ __forceinline__ int fast_wpt(int V) {
+  const int words = (V + 31) >> 5;
+  return ((words + kFastThreads * 8 - 1) / (kFastThreads * 8)) * 8;
 }
 
+__device__ __forceinline__ void bm_set(uint32_t* bm, int id) { atomicOr(&bm[id >> 5], 1u << (id & 31)); }
+
+template <typename T, int RU>
 __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, const int32_t* draft_ids,
-                                                            int n_draft, const int32_t* ver_ids, int n_ver, int32_t* __restrict__ active_ids,
+                                                            int n_draft, const int32_t* ver_ids, int n_ver,
+                                                            int32_t* __restrict__ active_ids,
                                                             int32_t* __restrict__ n_active,
                                                             uint32_t* __restrict__ bitmap_out) {
-  extern __shared__ int4 lds4[];
+  constexpr int EPT = (int)(sizeof(T) / 4);     // ring entries per load
   constexpr int NW = kFastThreads / NS_WAVE;
+  extern __shared__ int4 lds4[];
   __shared__ int sh_scan[NW + 1];
   __shared__ int sh_flag;
   const int tid = threadIdx.x;
   const int w_max = v.w_max, V = v.V;
   const int words = (V + 31) >> 5;
-  const int ring_pad = (w_max + 3) & ~3;
-  int32_t* ring = (int32_t*)lds4;
-  uint32_t* bm = (uint32_t*)(ring + ring_pad);
-  int32_t* dids = (int32_t*)(bm + ((words + 3) & ~3));
-  int32_t* vids = dids + ((n_draft + 3) & ~3);
-  // ---- one round of global loads -------------------------------------
-  // |S| and the tuple ids are requested unconditionally (the host never
-  // passes a null tuple pointer; clamped indices stay in range) and consumed
-  // after the ring copy, so all of the kernel's global reads overlap.
-  int64_t len_in = 0;
-  int d_in = -1, v_in = -1;
-  auto tuple_loads = [&]() {
-    len_in = *v.len;
-    d_in = draft_ids[tid < n_draft ? tid : 0];
-    v_in = ver_ids[tid < n_ver ? tid : 0];
-  };
-  if ((w_max & 3) == 0) copy_to_lds<int4, 2>((int4*)ring, (const int4*)v.ring, w_max >> 2, tuple_loads);
-  else copy_to_lds<int32_t, 8>(ring, v.ring, w_max, tuple_loads);
-  for (int w = tid; w < words; w += kFastThreads) bm[w] = 0u;
-  if (tid < n_draft) dids[tid] = d_in;
-  if (tid < n_ver) vids[tid] = v_in;
+  const int wpt = fast_wpt(V);
+  uint32_t* bm = (uint32_t*)lds4;                                 // kFastThreads * wpt words
+  int32_t* dids = (int32_t*)(bm + (size_t)kFastThreads * wpt);    // n_draft rounded up to 64
+  // ---- one round of global loads --------------------------------------
+  // An index the compiler cannot prove uniform keeps |S| in a vector
+  // register, so no early wait is placed on it ahead of the other loads.
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  const int nl = w_max / EPT;                                     // loads covering the ring
+  const T* src = (const T*)v.ring;
+  T r[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int q = tid + u * kFastThreads;
+    r[u] = src[q < nl ? q : 0];
+  }
+  const int64_t len_in = v.len[zero];
+  const int d_in = draft_ids[tid < n_draft ? tid : 0];
+  const int v_in = ver_ids[tid < n_ver ? tid : 0];
+  NS_ISSUE_FENCE();
+  for (int w = tid; w < kFastThreads * wpt; w += kFastThreads) bm[w] = 0u;
+  const int nd64 = (n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1);
+  for (int q = tid; q < nd64; q += kFastThreads) dids[q] = q < n_draft ? d_in : -1;
   if (tid == 0) sh_flag = 0;
   __syncthreads();
   // ---- tuple positions (C_draft deduplicated, then C_ver as given) ----
-  int id_d = -1, id_v = -1;
   bool keep_d = false, keep_v = false, bad = false;
   if (tid < n_draft) {
-    id_d = d_in;
-    keep_d = id_d >= 0 && id_d < V;
+    keep_d = d_in >= 0 && d_in < V;
     bad |= !keep_d;
   }
-  // First occurrence: keep iff the smallest position holding this id is the
-  // thread's own.  Scanning positions downward with a compare and a select
-  // per id leaves that smallest position; every lane reads the same LDS words
-  // (broadcast), four ids per read.  Padding past n_draft cannot win: the
-  // thread's own position is smaller.  Only waves that hold tree ids scan.
+  // First occurrence: keep iff no earlier position holds the same id.  All
+  // lanes read the same LDS words (broadcast), sixteen 4-id reads per batch.
   if ((tid & ~(NS_WAVE - 1)) < n_draft) {
     const int4* d4 = (const int4*)dids;
-    int fp = INT32_MAX;
-    for (int j4 = ((n_draft + 3) >> 2) - 1; j4 >= 0; --j4) {
-      const int4 q = d4[j4];
-      const int j = j4 * 4;
-      fp = q.w == id_d ? j + 3 : fp;
-      fp = q.z == id_d ? j + 2 : fp;
-      fp = q.y == id_d ? j + 1 : fp;
-      fp = q.x == id_d ? j : fp;
+    int fp = tid;
+    for (int c = 0; c < nd64; c += NS_WAVE) {
+      int4 q[NS_WAVE / 4];
+#pragma unroll
+      for (int i = 0; i < NS_WAVE / 4; ++i) q[i] = d4[(c >> 2) + i];
+#pragma unroll
+      for (int i = 0; i < NS_WAVE / 4; ++i) {
+        const int j = c + 4 * i;
+        fp = min(fp, q[i].x == d_in ? j : INT32_MAX);
+        fp = min(fp, q[i].y == d_in ? j + 1 : INT32_MAX);
+        fp = min(fp, q[i].z == d_in ? j + 2 : INT32_MAX);
+        fp = min(fp, q[i].w == d_in ? j + 3 : INT32_MAX);
+      }
     }
     keep_d &= fp == tid;
   }
   if (tid < n_ver) {
-    id_v = v_in;
-    keep_v = id_v >= 0 && id_v < V;
+    keep_v = v_in >= 0 && v_in < V;
     bad |= !keep_v;
   }
   if (bad) sh_flag = 1;
@@ -305,53 +297,79 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
   const int Cd = total & 0xFFFF, Cv = total >> 16, C = Cd + Cv;
   const int64_t len = len_in;
   const int lm = (int)(len % (int64_t)w_max);         // slot of position |S|
-  // Only the last w_max entries of this step can be inside the window.
+  // New entries: only the last w_max of this step can be inside the window.
   if (keep_d) {
     const int p = pre & 0xFFFF;
     if (p >= C - w_max) {
-      const int slot = (lm + p) % w_max;
-      ring[slot] = id_d;
-      v.ring[slot] = id_d;
+      v.ring[(lm + p) % w_max] = d_in;
+      bm_set(bm, d_in);
     }
   }
   if (keep_v) {
     const int p = Cd + (pre >> 16);
     if (p >= C - w_max) {
-      const int slot = (lm + p) % w_max;
-      ring[slot] = id_v;
-      v.ring[slot] = id_v;
+      v.ring[(lm + p) % w_max] = v_in;
+      bm_set(bm, v_in);
+    }
+  }
+  // Old entries that stay in the window.
+  if (C < w_max) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int q = tid + u * kFastThreads;
+      if (q < nl) {
+        const int32_t* e = (const int32_t*)&r[u];
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) {
+          const int slot = q * EPT + x;
+          const int id = e[x];
+          int rel = slot - lm;
+          rel += rel < 0 ? w_max : 0;
+          if (rel >= C && id >= 0 && id < V) bm_set(bm, id);
+        }
+      }
     }
   }
   __syncthreads();
-  // ---- I = Unique(window): bitmap from the LDS ring, ascending compaction
-  for (int e = tid; e < w_max; e += kFastThreads) {
-    const int id = ring[e];
-    if (id >= 0 && id < V) atomicOr(&bm[id >> 5], 1u << (id & 31));
-  }
-  __syncthreads();
-  const int per = (words + kFastThreads - 1) / kFastThreads;
-  const int w0 = tid * per;
-  const int w1 = min(words, w0 + per);
+  // ---- ascending compaction ------------------------------------------
+  const uint4* bm4 = (const uint4*)(bm + (size_t)tid * wpt);
   int pc = 0;
-  for (int w = w0; w < w1; ++w) pc += __popc(bm[w]);
+  uint4 c0a = bm4[0], c0b = bm4[1];                   // first 8 words stay in registers
+  pc += __popc(c0a.x) + __popc(c0a.y) + __popc(c0a.z) + __popc(c0a.w);
+  pc += __popc(c0b.x) + __popc(c0b.y) + __popc(c0b.z) + __popc(c0b.w);
+  for (int c = 2; c < wpt / 4; ++c) {
+    const uint4 x = bm4[c];
+    pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+  }
   int n_tot = 0;
   int off = ns::block_excl_scan<kFastThreads>(pc, sh_scan, &n_tot);
-  // The ascending ids are staged in LDS (the ring copy is no longer needed,
-  // and n <= w_max) so the global writes below are coalesced.
-  int32_t* sids = ring;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t b = bm[w];
+  const int wbase = tid * wpt;
+  auto emit = [&](uint32_t b, int w) {
     while (b) {
-      sids[off++] = (w << 5) + (__ffs(b) - 1);
+      active_ids[off++] = (w << 5) + (__ffs(b) - 1);
       b &= b - 1u;
     }
+  };
+  emit(c0a.x, wbase); emit(c0a.y, wbase + 1); emit(c0a.z, wbase + 2); emit(c0a.w, wbase + 3);
+  emit(c0b.x, wbase + 4); emit(c0b.y, wbase + 5); emit(c0b.z, wbase + 6); emit(c0b.w, wbase + 7);
+  for (int c = 2; c < wpt / 4; ++c) {
+    const uint4 x = bm4[c];
+    const int w = wbase + 4 * c;
+    emit(x.x, w); emit(x.y, w + 1); emit(x.z, w + 2); emit(x.w, w + 3);
   }
-  __syncthreads();
-  for (int q = tid; q < n_tot; q += kFastThreads) active_ids[q] = sids[q];
-  for (int w = tid; w < words; w += kFastThreads) {
-    const uint32_t b = bm[w];
-    v.bitmap[w] = b;
-    if (bitmap_out) bitmap_out[w] = b;
+  // Bitmap copies: coalesced, eight LDS reads in flight per thread.
+  for (int w0 = tid; w0 < words; w0 += kFastThreads * 8) {
+    uint32_t b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = bm[w0 + u * kFastThreads];   // < kFastThreads * wpt
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int w = w0 + u * kFastThreads;
+      if (w < words) {
+        v.bitmap[w] = b[u];
+        if (bitmap_out) bitmap_out[w] = b[u];
+      }
+    }
   }
   if (tid == 0) {
     *n_active = n_tot;
@@ -360,10 +378,29 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
   }
 }
 
-size_t fast_lds_bytes(int V, int w_max, int n_draft, int n_ver) {
-  const size_t words = (size_t)((V + 31) >> 5);
-  return ((size_t)((w_max + 3) & ~3) + ((words + 3) & ~(size_t)3) + (size_t)((n_draft + 3) & ~3) +
-          (size_t)n_ver) * 4;
+size_t fast_lds_bytes(int V, int n_draft) {
+  return ((size_t)kFastThreads * fast_wpt(V) + (size_t)((n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1))) * 4;
+}
+
+typedef void (*step_fast_fn)(ns_state_view, const int32_t*, int, const int32_t*, int, int32_t*, int32_t*, uint32_t*);
+
+// Kernel instance holding ring entries of a w_max-slot ring in registers.
+step_fast_fn pick_step_fast(int w_max) {
+  if (w_max > kFastMaxRing) return nullptr;
+  if ((w_max & 3) == 0) {
+    const int per = (w_max / 4 + kFastThreads - 1) / kFastThreads;
+    if (per <= 1) return k_step_fast<int4, 1>;
+    if (per <= 2) return k_step_fast<int4, 2>;
+    if (per <= 4) return k_step_fast<int4, 4>;
+    return k_step_fast<int4, 8>;
+  }
+  const int per = (w_max + kFastThreads - 1) / kFastThreads;
+  if (per <= 1) return k_step_fast<int, 1>;
+  if (per <= 2) return k_step_fast<int, 2>;
+  if (per <= 4) return k_step_fast<int, 4>;
+  if (per <= 8) return k_step_fast<int, 8>;
+  if (per <= 16) return k_step_fast<int, 16>;
+  return k_step_fast<int, 32>;
 }
 
 // Initialisation / reset: empty stream, cleared status, first[] = INT32_MAX,
@@ -469,9 +506,10 @@ int nanospec_state_create(nanospec_state** out, int32_t V, int32_t w_max, void* 
   v.w_max = w_max;
   int rc = set_lds_limit((const void*)k_active, lds_bitmap_bytes(V));
   if (rc == NS_OK) rc = set_lds_limit((const void*)k_step, lds_bitmap_bytes(V));
-  const size_t fast_max = fast_lds_bytes(V, w_max, kFastMaxIds, kFastMaxIds);
-  if (rc == NS_OK)
-    rc = set_lds_limit((const void*)k_step_fast, fast_max < kFastLdsMax ? fast_max : kFastLdsMax);
+  const size_t fast_max = fast_lds_bytes(V, kFastMaxIds);
+  step_fast_fn fast_fn = pick_step_fast(w_max);
+  if (rc == NS_OK && fast_fn)
+    rc = set_lds_limit((const void*)fast_fn, fast_max < kFastLdsMax ? fast_max : kFastLdsMax);
   if (rc != NS_OK) { delete st; return rc; }
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_init, dim3(fill_grid(v)), dim3(256), 0, stream, v);
@@ -540,12 +578,13 @@ int nanospec_step_update(nanospec_state* st, const int32_t* draft_ids, int32_t n
   if (!st || !active_ids || !n_active || n_draft < 0 || n_ver < 0) return NS_EINVAL;
   if ((n_draft > 0 && !draft_ids) || (n_ver > 0 && !ver_ids)) return NS_EINVAL;
   (void)hipGetLastError();
-  const size_t fast = fast_lds_bytes(st->view.V, st->view.w_max, n_draft, n_ver);
-  if (n_draft <= kFastMaxIds && n_ver <= kFastMaxIds && fast <= kFastLdsMax) {
+  const size_t fast = fast_lds_bytes(st->view.V, n_draft);
+  step_fast_fn fast_fn = pick_step_fast(st->view.w_max);
+  if (fast_fn && n_draft <= kFastMaxIds && n_ver <= kFastMaxIds && fast <= kFastLdsMax) {
     // The kernel reads element 0 of an empty tuple unconditionally.
     const int32_t* dptr = n_draft > 0 ? draft_ids : st->view.ring;
     const int32_t* vptr = n_ver > 0 ? ver_ids : st->view.ring;
-    hipLaunchKernelGGL(k_step_fast, dim3(1), dim3(kFastThreads), fast, stream, st->view, dptr, n_draft, vptr, n_ver,
+    hipLaunchKernelGGL(fast_fn, dim3(1), dim3(kFastThreads), fast, stream, st->view, dptr, n_draft, vptr, n_ver,
                        active_ids, n_active, bitmap);
   } else {
     hipLaunchKernelGGL(k_step, dim3(1), dim3(kStateThreads), lds_bitmap_bytes(st->view.V), stream, st->view,

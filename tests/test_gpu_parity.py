@@ -320,6 +320,41 @@ def test_draft_edges(ns):
         check_topk(tids.cpu().numpy(), tvals.cpu().numpy(), ref_logits, I, o_ids, o_vals, k, "identity rows")
 
 
+def test_merge_paths(ns):
+    """Column counts around the merge kernel's limits (one column per thread,
+    up to four per thread, the general kernel past 4096) and a logit pattern
+    that pushes more than 1024 keys over the selection threshold."""
+    say("merge paths")
+    rng = np.random.default_rng(11)
+    V, d = 5000, 64
+    for dtype in ("bf16", "fp32"):
+        Wf = (rng.standard_normal((V, d)) * 0.1).astype(np.float32)
+        W = WL.f32_to_bf16_bits(Wf) if dtype == "bf16" else Wf
+        W_dev = dev_elems(W, dtype)
+        for M, k, n, n_max in ((2, 8, 1024, 1024), (3, 8, 1025, 1100), (4, 16, 2900, 4096), (2, 64, 4096, 4096),
+                               (2, 8, 4097, 4097), (5, 10, 3000, 4500)):
+            hf = rng.standard_normal((M, d)).astype(np.float32)
+            h = WL.f32_to_bf16_bits(hf) if dtype == "bf16" else hf
+            I = np.sort(rng.choice(V, size=n, replace=False))
+            for mode in (ns.NS_PACKED, ns.NS_INDEXED):
+                out = run_draft(ns, W_dev, dev_elems(h, dtype), I, n_max, V, d, dtype, M, k, mode)
+                check_draft(out, h, W, I, k, dtype, f"{dtype} M={M} k={k} n={n} n_max={n_max} mode={mode}")
+        # Columns j with j % 1024 < 16 (the first 16 lanes of the first wave)
+        # get very low logits, so the threshold is that row's maximum and
+        # every key passes it: the block takes its fallback path.
+        n = 4000
+        Wa = (rng.standard_normal((n, d)) * 0.1).astype(np.float32)
+        Wa[(np.arange(n) % 1024) < 16, 0] = -100.0
+        Wa = WL.f32_to_bf16_bits(Wa) if dtype == "bf16" else Wa
+        hf = np.zeros((1, d), np.float32)
+        hf[0, 0] = 1.0
+        hf[0, 1:] = rng.standard_normal(d - 1) * 0.01
+        h = WL.f32_to_bf16_bits(hf) if dtype == "bf16" else hf
+        I = np.arange(n)
+        out = run_draft(ns, dev_elems(Wa, dtype), dev_elems(h, dtype), I, n, n, d, dtype, 1, 64, ns.NS_INDEXED)
+        check_draft(out, h, Wa, I, 64, dtype, f"{dtype} fallback")
+
+
 def test_draft_deterministic(ns):
     say("determinism")
     cfg = WL.get_config("tiny")
