@@ -361,6 +361,7 @@ __global__ __launch_bounds__(kMergeSmallThreads) void k_merge_small(const float*
   __shared__ uint64_t rmax[NS_WAVE];                 // (NT / 64 waves) x (4 rows of 16 lanes)
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint64_t sh_red[NT / NS_WAVE];
+  __shared__ uint64_t sh_T;
   __shared__ int sh_cnt;
   static_assert(NT / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
@@ -406,19 +407,17 @@ __global__ __launch_bounds__(kMergeSmallThreads) void k_merge_small(const float*
   if ((lane & 15) == 15) rmax[(tid / NS_WAVE) * 4 + (lane >> 4)] = rm;
   if (tid == 0) sh_cnt = 0;
   __syncthreads();
-  // Every wave finds T itself: lane l ranks row maximum l among the 64.
-  const uint64_t mine = rmax[lane];
-  int rank = 0;
+  // Wave 0 finds T: lane l ranks row maximum l among the 64.
+  if (tid < NS_WAVE) {
+    const uint64_t mine = rmax[lane];
+    int rank = 0;
 #pragma unroll 16
-  for (int q = 0; q < NS_WAVE; ++q) rank += rmax[q] > mine;
-  const unsigned long long ball = __ballot(mine != 0 && rank == k - 1);
-  uint64_t T = 0;
-  if (ball) {
-    const int src = __ffsll(ball) - 1;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), src);
-    T = ((uint64_t)hi << 32) | lo;
+    for (int q = 0; q < NS_WAVE; ++q) rank += rmax[q] > mine;
+    const unsigned long long ball = __ballot(mine != 0 && rank == k - 1);
+    if (lane == 0) sh_T = ball ? rmax[__ffsll(ball) - 1] : 0;
   }
+  __syncthreads();
+  const uint64_t T = sh_T;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (key[u] != 0 && key[u] >= T) {
