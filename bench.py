@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-extras", action="store_true", help="skip the prefill and overlap legs")
+    p.add_argument("--sweep", action="store_true",
+                   help="only sweep the draft head over |I| x M (cold) and print one JSON line per point")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES (calibrates HBM byte counters) and exit")
     return p.parse_args()
@@ -71,6 +74,9 @@ def main():
     from dynamic_vocab_draft_amd import workloads as WL
 
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(torch, ns, WL, args)
+        return
     cfg = WL.get_config(args.config)
     K, Wm = args.steps, args.warmup
     T = Wm + K
@@ -242,6 +248,13 @@ def main():
                  "flush_ms": t_flush / K},
         "cpu_baseline": None,
     }
+    if not args.no_extras:
+        flush_fn = lambda i: sink.copy_(flush_lines[:, i % 128])
+        progress("prefill top-K leg")
+        out["prefill"] = prefill_leg(torch, ns, WL, flush_fn)
+        progress("gather / backbone overlap leg")
+        out["overlap"] = overlap_leg(torch, ns, cfg, W, ids, n_act, packed, hs[Wm], ws, dcode, copy_stream,
+                                     flush_fn)
     if not args.no_dense:
         out["dense"] = dense_compare(torch, ns, cfg, W, hs[Wm], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
     if not args.no_cpu_baseline:
@@ -293,6 +306,198 @@ def measured_traffic(workload, mode):
         return float(kv["traffic_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
+def _event_time(torch, fn, flush, reps, stream=None):
+    """Median of `reps` event-bracketed calls of fn(), each after a cold flush."""
+    ts = []
+    for i in range(reps + 2):
+        flush(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def prefill_leg(torch, ns, WL, flush):
+    """a1: per-position top-K_pre over the prefill workload's logits
+    (L=4096 x V=128256 bf16, N(0, 3^2) plus 32 peaks of +8 per row), cold.
+    The logits are drawn on the GPU from a seeded torch generator (same shape
+    and distribution as the test inputs; peak ids uniform here)."""
+    cfg = WL.get_config("prefill")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    Z = torch.randn((cfg.L, cfg.V), generator=g, device="cuda", dtype=torch.float32).mul_(cfg.sigma)
+    peaks = torch.randint(0, cfg.V, (cfg.L, cfg.n_peaks), generator=g, device="cuda")
+    Z.scatter_(1, peaks, Z.gather(1, peaks) + cfg.peak)
+    Zb = Z.to(torch.bfloat16)
+    del Z
+    pid = torch.empty((cfg.L, cfg.k_pre), dtype=torch.int32, device="cuda")
+    pval = torch.empty((cfg.L, cfg.k_pre), dtype=torch.float32, device="cuda")
+    call = lambda: ns.nanospec_prefill_topk(Zb, cfg.L, cfg.V, ns.NS_BF16, cfg.k_pre, pid, pval)
+    ms = _event_time(torch, call, flush, 10)
+    nbytes = cfg.L * cfg.V * 2 + cfg.L * cfg.k_pre * 8
+    # sanity: the planted ids dominate most rows' top-K
+    ref = torch.topk(Zb[:64].float(), cfg.k_pre, dim=1).values
+    ok = bool(torch.equal(ref, pval[:64]))
+    del Zb
+    return {"workload": f"prefill: L={cfg.L} V={cfg.V} bf16, K_pre={cfg.k_pre}", "ms": ms,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes": nbytes, "values_match_torch_topk_first_64_rows": ok, "cache": "cold"}
+
+
+def overlap_leg(torch, ns, cfg, W, ids, n_act, packed, h, ws, dcode, copy_stream, flush):
+    """a7: the gather on a second stream while a backbone stand-in runs on the
+    compute stream (a chain of bf16 GEMMs with one Llama-3-8B decoder layer's
+    weight shapes, M rows), then the PACKED draft head after the join.
+    Each variant is captured R times (with the cache-streaming read before
+    each repetition) into a HIP graph; the read alone is subtracted.
+    hidden = (T_serial - T_overlap) / T_gather."""
+    M, d = cfg.M, cfg.d
+    R = 20
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed + 7)
+    shapes = [(4096, 4096), (4096, 4096), (4096, 1024), (4096, 1024), (4096, 14336), (4096, 14336), (14336, 4096)]
+    Ws = [(torch.randn((i, o), generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for i, o in shapes]
+    xs = {n: torch.randn((M, n), generator=gen, device="cuda").to(torch.bfloat16) for n in (4096, 14336)}
+    outs = [torch.empty((M, o), dtype=torch.bfloat16, device="cuda") for _, o in shapes]
+    tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((cfg.M, cfg.k), dtype=torch.float32, device="cuda")
+
+    def backbone():
+        for (i, _), w, o in zip(shapes, Ws, outs):
+            torch.matmul(xs[i], w, out=o)
+
+    def gather(stream):
+        ns.nanospec_gather_rows(W, cfg.V, d, dcode, ids, n_act, cfg.w_max, packed, stream=stream)
+
+    def head():
+        ns.nanospec_draft_logits_topk(packed, ns.NS_PACKED, ids, n_act, cfg.w_max, cfg.V, d, dcode, h, M, cfg.k,
+                                      None, tids, tvals, ws)
+
+    def variant(kind):
+        def run():
+            comp = torch.cuda.current_stream()
+            for i in range(R):
+                flush(i)
+                if kind == "backbone":
+                    backbone()
+                elif kind == "gather":
+                    gather(comp)
+                elif kind == "head":
+                    head()
+                elif kind == "serial":
+                    backbone()
+                    gather(comp)
+                    head()
+                elif kind == "overlap":
+                    copy_stream.wait_stream(comp)
+                    gather(copy_stream)
+                    backbone()
+                    comp.wait_stream(copy_stream)
+                    head()
+                elif kind == "forkjoin":                # the same stream dependencies, no gather
+                    copy_stream.wait_stream(comp)
+                    backbone()
+                    comp.wait_stream(copy_stream)
+                    head()
+        return run
+
+    kinds = ("flush", "backbone", "gather", "head", "serial", "overlap", "forkjoin")
+    for kd in kinds:                                   # warm up every path eagerly first
+        variant(kd)()
+    torch.cuda.synchronize()
+    graphs = {}
+    for kd in kinds:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            variant(kd)()
+        graphs[kd] = g
+    torch.cuda.synchronize()
+
+    def t(kd):
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            graphs[kd].replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    base = t("flush")
+    r = {kd: (t(kd) - base) / R for kd in kinds[1:]}
+    del graphs
+    return {"backbone": "bf16 GEMM chain, Llama-3-8B decoder-layer weight shapes, M rows",
+            "T_backbone_ms": r["backbone"], "T_gather_ms": r["gather"], "T_head_ms": r["head"],
+            "T_serial_ms": r["serial"], "T_overlap_ms": r["overlap"], "T_forkjoin_no_gather_ms": r["forkjoin"],
+            "hidden_fraction": (r["serial"] - r["overlap"]) / r["gather"] if r["gather"] > 0 else None,
+            "note": "cold, hipGraph replay of 20 repetitions per variant, cache-streaming read subtracted"}
+
+
+def sweep(torch, ns, WL, args):
+    """Draft head alone (INDEXED, cold, graph replay) over |I| x M on the
+    Llama-3-8B-shaped head; one JSON line per point."""
+    cfg = WL.get_config("llama3_8b")
+    W_host = WL.make_weights(cfg)
+    W = torch.from_numpy(W_host.view(np.int16)).cuda().view(torch.bfloat16)
+    del W_host
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    lines = flush.view(-1, 128)
+    sink = torch.empty(lines.shape[0], dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(cfg.seed + 11)
+    R = 50
+    for n in (512, 1024, 2048, 3072, 8192, 16384):
+        I = np.sort(rng.choice(cfg.V, size=n, replace=False)).astype(np.int32)
+        ids = torch.as_tensor(I).cuda()
+        n_dev = torch.tensor([n], dtype=torch.int32, device="cuda")
+        for M in (1, 8, 16, 64):
+            k = cfg.k
+            h = (torch.randn((M, cfg.d), device="cuda")).to(torch.bfloat16)
+            ws = ns.alloc_workspace(n, M, k, cfg.d)
+            tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+            tvals = torch.empty((M, k), dtype=torch.float32, device="cuda")
+
+            def body(with_head):
+                def run():
+                    for i in range(R):
+                        sink.copy_(lines[:, (i * 7) % 128])
+                        if with_head:
+                            ns.nanospec_draft_logits_topk(W, ns.NS_INDEXED, ids, n_dev, n, cfg.V, cfg.d, ns.NS_BF16,
+                                                          h, M, k, None, tids, tvals, ws)
+                return run
+
+            def capture(fn):
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn()
+                torch.cuda.synchronize()
+                return g
+
+            def timed(g):
+                ts = []
+                for _ in range(3):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    g.replay()
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                return float(np.median(ts))
+
+            g_all, g_fl = capture(body(True)), capture(body(False))
+            us = (timed(g_all) - timed(g_fl)) / R * 1e3
+            nbytes = n * cfg.d * 2 + M * cfg.d * 2 + n * 4 + M * k * 8
+            print(json.dumps({"n": n, "M": M, "k": k, "d": cfg.d, "us": us, "bytes": nbytes,
+                              "GBps": nbytes / (us * 1e-6) / 1e9,
+                              "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}), flush=True)
+            del g_all, g_fl
 
 
 def dense_compare(torch, ns, cfg, W, h, dcode, flush, step_ms):

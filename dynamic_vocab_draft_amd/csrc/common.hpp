@@ -88,6 +88,21 @@ __device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
   return v;
 }
 
+// Maximum over all 64 lanes (every lane must be active): running maxima
+// within each 16-lane DPP row, then the four row results read as scalars.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xf, 0xf, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, NS_WAVE);

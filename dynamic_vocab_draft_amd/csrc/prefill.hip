@@ -3,41 +3,85 @@
 // MicroSpec/NanoSpec (arXiv 2605.26444) Sec. 3.2 "Candidate Stream
 // Initialization": the stream starts as the prompt followed by the union of
 // each position's top-K_pre logits.  The pass reads L x V logits once, so it
-// is HBM-bound; one 256-thread block owns one row and streams it with
-// 16-byte loads (four in flight per lane).  Each thread scans its elements in
-// ascending id order and keeps a sorted list of its CAP best (value, id) keys;
-// because later elements have larger ids, an element that only ties the
-// list's last value can be dropped, so most elements cost a conversion and a
-// compare against an 8-element maximum.  A block-wide pop then emits the k
-// winners ordered by (value desc, id asc).  Values are the stored logits
-// widened to float32, so the result is exact.
+// is HBM-bound.  One wave owns one row and streams it with 16-byte loads, in
+// batches of four per lane that alternate between two register sets.  Each
+// lane scans its elements in ascending id order and keeps a sorted list of its
+// CAP best (value, id) keys; an element that only ties the list's last value
+// has a larger id and is dropped.  After every batch the wave shares the
+// largest k-th best value held by any lane as a floor (the row's k-th largest
+// cannot be below it), so most vectors cost a conversion and one compare of
+// their 8-element maximum.  A pop over the lanes then emits the k winners
+// ordered by (value desc, id asc).  Values are the stored logits widened to
+// float32, so the result is exact.
 #include "common.hpp"
 
 namespace {
 
-constexpr int kPrefillThreads = 256;
+constexpr int kPrefillThreads = 64;       // one wave per row: all rows resident at once
 constexpr int kPrefillUnroll = 4;
 
 template <int CAP>
 struct Cands {
   uint64_t lst[CAP];
   float thr;     // value of lst[CAP-1] once the list is full
+  float floor;   // lower bound on the row's k-th largest value (shared by the wave)
   int filled;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int i = 0; i < CAP; ++i) lst[i] = 0;
     thr = -INFINITY;
+    floor = -INFINITY;
     filled = 0;
   }
-  __device__ __forceinline__ bool wants(float v) const { return filled < CAP || v > thr; }
+  // A value below `floor` has k larger values in the row; a value that only
+  // ties the full list's last one loses to it on id (ids ascend in the scan).
+  __device__ __forceinline__ bool wants(float v) const { return v >= floor && (filled < CAP || v > thr); }
   __device__ __forceinline__ void add(float v, int id) {
     if (!wants(v)) return;
     ns::list_insert(lst, ns::make_key(v, id));
     ++filled;
     if (filled >= CAP) thr = ns::key_val(lst[CAP - 1]);
   }
+  // Value of this thread's k-th best so far (-inf if it holds fewer).
+  __device__ __forceinline__ float kth(int k) const {
+    float r = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CAP; ++i)
+      if (i == k - 1 && lst[i] != 0) r = ns::key_val(lst[i]);
+    return r;
+  }
 };
+
+// Scans one batch of 16-byte vectors (vector q0 + u * threads for u < U);
+// vectors past the row were loaded clamped and are skipped.
+template <bool BF16, int CAP>
+__device__ __forceinline__ void scan_batch(const uint4 (&x)[kPrefillUnroll], int q0, int nvec, Cands<CAP>& c) {
+  constexpr int EPV = BF16 ? 8 : 4;
+#pragma unroll
+  for (int u = 0; u < kPrefillUnroll; ++u) {
+    const int q = q0 + u * kPrefillThreads;
+    if (q >= nvec) continue;
+    const uint32_t wv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    float v[EPV];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (BF16) {
+        v[2 * e] = ns::bf16_lo(wv[e]);
+        v[2 * e + 1] = ns::bf16_hi(wv[e]);
+      } else {
+        v[e] = __uint_as_float(wv[e]);
+      }
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int e = 1; e < EPV; ++e) mx = fmaxf(mx, v[e]);
+    if (c.wants(mx)) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) c.add(v[e], q * EPV + e);
+    }
+  }
+}
 
 template <bool BF16, bool VEC, int CAP>
 __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restrict__ Z, int V, int k,
@@ -50,39 +94,39 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
   c.init();
   if (VEC) {
     constexpr int EPV = BF16 ? 8 : 4;     // elements per 16-byte vector
+    constexpr int STEP = kPrefillThreads * kPrefillUnroll;
     const int nvec = V / EPV;
     const uint4* __restrict__ p = (const uint4*)((const char*)Z + row * (size_t)V * (BF16 ? 2 : 4));
-    for (int q0 = tid; q0 < nvec; q0 += kPrefillThreads * kPrefillUnroll) {
-      uint4 x[kPrefillUnroll];
+    // Two register batches, a and b, alternate so that the loads of one are
+    // in flight while the other is scanned.  Indices are clamped into the row,
+    // so every load is in bounds.  The loop trip count is the same for all
+    // threads: after each batch the wave raises every thread's floor to the
+    // largest k-th best held by any of its lanes, which turns most vectors
+    // into a single compare and keeps the lanes from diverging into inserts.
+    uint4 a[kPrefillUnroll], b[kPrefillUnroll];
+#pragma unroll
+    for (int u = 0; u < kPrefillUnroll; ++u) {
+      const int q = tid + u * kPrefillThreads;
+      a[u] = p[q < nvec ? q : 0];
+    }
+    for (int base = 0; base < nvec; base += 2 * STEP) {
 #pragma unroll
       for (int u = 0; u < kPrefillUnroll; ++u) {
-        const int q = q0 + u * kPrefillThreads;
-        x[u] = p[q < nvec ? q : 0];          // unconditional: all loads in flight at once
+        const int q = base + STEP + tid + u * kPrefillThreads;
+        b[u] = p[q < nvec ? q : 0];
       }
       NS_ISSUE_FENCE();
+      scan_batch<BF16, CAP>(a, base + tid, nvec, c);
+      c.floor = fmaxf(c.floor, ns::wave_max_f32(c.kth(k)));
+      if (base + STEP >= nvec) break;                   // uniform
 #pragma unroll
       for (int u = 0; u < kPrefillUnroll; ++u) {
-        const int q = q0 + u * kPrefillThreads;
-        if (q >= nvec) continue;
-        const uint32_t wv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-        float v[EPV];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (BF16) {
-            v[2 * e] = ns::bf16_lo(wv[e]);
-            v[2 * e + 1] = ns::bf16_hi(wv[e]);
-          } else {
-            v[e] = __uint_as_float(wv[e]);
-          }
-        }
-        float mx = v[0];
-#pragma unroll
-        for (int e = 1; e < EPV; ++e) mx = fmaxf(mx, v[e]);
-        if (c.wants(mx)) {
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) c.add(v[e], q * EPV + e);
-        }
+        const int q = base + 2 * STEP + tid + u * kPrefillThreads;
+        a[u] = p[q < nvec ? q : 0];
       }
+      NS_ISSUE_FENCE();
+      scan_batch<BF16, CAP>(b, base + STEP + tid, nvec, c);
+      c.floor = fmaxf(c.floor, ns::wave_max_f32(c.kth(k)));
     }
   } else {
     if (BF16) {
