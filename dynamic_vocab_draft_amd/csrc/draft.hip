@@ -25,11 +25,12 @@
 //       partial sums (deterministic; no atomics) to partial[m][j][s], the S
 //       slices of one column side by side (row stride SP = S rounded up to
 //       4) so the merge reads them with 16-byte loads.
-//   k_merge: one block per hidden row m sums the S partials of each active
-//       column in a fixed order, keeps each thread's CAP best (value, id)
-//       keys, takes the k-th largest of the first 64 thread maxima as a
-//       lower bound T for the k-th largest key overall, and ranks the (few)
-//       keys >= T by counting in LDS.  No k rounds of cross-lane reductions.
+//   k_merge_cols (+ k_merge_keys when n_max > 4096): per hidden row m and
+//       4096-column chunk, a 1024-thread block sums the S partials of each
+//       active column in a fixed order and selects the chunk's k best
+//       (value, id) keys with a threshold from 64 row maxima and a rank
+//       count in LDS; with several chunks a second kernel selects the final
+//       k from the chunks' keys.  No k rounds of cross-lane reductions.
 #include "common.hpp"
 
 namespace {
@@ -50,7 +51,6 @@ constexpr int kKC = 4;                            // 32-column steps loaded per 
 constexpr int kTargetBlocks = 1536;               // MFMA blocks aimed for when choosing S
 constexpr int kMaxSplits = 16;
 
-constexpr int kMergeThreads = 256;
 
 __device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
   int n = n_dev ? *n_dev : n_max;
@@ -236,110 +236,83 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one block per hidden row m.
+// Merge.  Keys are (ordered f32 bits << 32) | ~id, so one 64-bit compare
+// orders by (value desc, id asc); 0 is the empty key.
+//
+// block_select_topk: the k largest keys held by a 1024-thread block (U keys
+// per thread).  T = the k-th largest of the 64 maxima of 16-lane DPP rows;
+// each of those is a real key, so the k-th largest key overall is >= T and
+// the top k are among the keys >= T.  Those are collected in LDS and ranked
+// by counting; if more than kCandCap reach T, the block falls back to k
+// rounds of block-wide maxima.  emit(r, key) is called once for every rank
+// r < k (key 0 when fewer than r + 1 keys exist).
 // ---------------------------------------------------------------------------
-template <int CAP>
-__global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict__ part, int S, int SP, int n_max,
-                                                         const int32_t* __restrict__ row_ids,
-                                                         const int32_t* __restrict__ n_dev, int V, int M, int k,
-                                                         float* __restrict__ logits_out,
-                                                         int32_t* __restrict__ out_ids,
-                                                         float* __restrict__ out_vals) {
-  extern __shared__ uint64_t cand[];                 // kMergeThreads * min(CAP, k)
-  __shared__ uint64_t tmax[NS_WAVE];
-  __shared__ uint64_t sh_T;
-  __shared__ int sh_cnt;
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const int n = clamp_n(n_dev, n_max);
-  uint64_t lst[CAP];
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeCols = 4;                      // columns per thread
+constexpr int kMergeChunk = kMergeThreads * kMergeCols;
+constexpr int kCandCap = 1024;
+
+struct SelectSmem {
+  uint64_t rmax[NS_WAVE];                          // (1024 / 64 waves) x (4 rows of 16 lanes)
+  uint64_t cand[kCandCap];
+  uint64_t red[kMergeThreads / NS_WAVE];
+  uint64_t T;
+  int cnt;
+};
+
+template <int U, typename Emit>
+__device__ __forceinline__ void block_select_topk(const uint64_t (&key)[U], int k, SelectSmem& sm, Emit emit) {
+  static_assert(kMergeThreads / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
+  uint64_t best = 0;
 #pragma unroll
-  for (int c = 0; c < CAP; ++c) lst[c] = 0;
-  constexpr int U = 4;                               // columns per thread per batch
-  const int SQ = SP >> 2;                            // 16-byte loads per column (<= 4)
-  const float4* __restrict__ prow = (const float4*)(part + (size_t)m * n_max * SP);
-  for (int j0 = tid; j0 < n; j0 += kMergeThreads * U) {
-    int gv[U];
-    float4 pv[U][kMaxSplits / 4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * kMergeThreads;
-      const int jc = j < n ? j : 0;
-      gv[u] = row_ids ? row_ids[jc] : jc;
-#pragma unroll
-      for (int q = 0; q < kMaxSplits / 4; ++q) pv[u][q] = prow[(size_t)jc * SQ + (q < SQ ? q : 0)];
-    }
-    NS_ISSUE_FENCE();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * kMergeThreads;
-      float sv = 0.f;                                // slices summed in a fixed order
-#pragma unroll
-      for (int q = 0; q < kMaxSplits / 4; ++q) {
-        if (4 * q + 0 < S) sv += pv[u][q].x;
-        if (4 * q + 1 < S) sv += pv[u][q].y;
-        if (4 * q + 2 < S) sv += pv[u][q].z;
-        if (4 * q + 3 < S) sv += pv[u][q].w;
-      }
-      if (j < n && gv[u] >= 0 && gv[u] < V) {
-        if (logits_out) logits_out[(size_t)m * n_max + j] = sv;
-        const uint64_t key = ns::make_key(sv, gv[u]);
-        if (key > lst[CAP - 1]) ns::list_insert(lst, key);
-      }
-    }
-  }
-  // T = k-th largest of wave 0's thread maxima.  These are k real keys, so
-  // the k-th largest key overall is >= T and every key of the top k is >= T.
-  const uint64_t mk = lst[0];
-  if (tid < NS_WAVE) tmax[tid] = mk;
-  if (tid == 0) { sh_T = 0; sh_cnt = 0; }
+  for (int u = 0; u < U; ++u) best = key[u] > best ? key[u] : best;
+  const uint64_t rm = ns::row16_max_u64(best);
+  if ((lane & 15) == 15) sm.rmax[(tid / NS_WAVE) * 4 + (lane >> 4)] = rm;
+  if (tid == 0) sm.cnt = 0;
   __syncthreads();
-  if (tid < NS_WAVE && mk != 0) {
+  // Wave 0 finds T: lane l ranks row maximum l among the 64.
+  if (tid < NS_WAVE) {
+    const uint64_t mine = sm.rmax[lane];
     int rank = 0;
 #pragma unroll 16
-    for (int q = 0; q < NS_WAVE; ++q) rank += tmax[q] > mk;
-    if (rank == k - 1) sh_T = mk;
+    for (int q = 0; q < NS_WAVE; ++q) rank += sm.rmax[q] > mine;
+    const unsigned long long ball = __ballot(mine != 0 && rank == k - 1);
+    if (lane == 0) sm.T = ball ? sm.rmax[__ffsll(ball) - 1] : 0;
   }
   __syncthreads();
-  const uint64_t T = sh_T;
-  // Keys >= T; a thread's keys past its own k best cannot be in the top k.
+  const uint64_t T = sm.T;
 #pragma unroll
-  for (int c = 0; c < CAP; ++c) {
-    if (c < k && lst[c] != 0 && lst[c] >= T) cand[atomicAdd(&sh_cnt, 1)] = lst[c];
-  }
-  __syncthreads();
-  const int C = sh_cnt;
-  for (int q = tid; q < C; q += kMergeThreads) {
-    const uint64_t x = cand[q];
-    int r = 0;
-    for (int p = 0; p < C; ++p) r += cand[p] > x;
-    if (r < k) {
-      out_ids[(size_t)m * k + r] = ns::key_id(x);
-      out_vals[(size_t)m * k + r] = ns::key_val(x);
+  for (int u = 0; u < U; ++u) {
+    if (key[u] != 0 && key[u] >= T) {
+      const int slot = atomicAdd(&sm.cnt, 1);
+      if (slot < kCandCap) sm.cand[slot] = key[u];
     }
   }
-  for (int r = C + tid; r < k; r += kMergeThreads) {
-    out_ids[(size_t)m * k + r] = -1;
-    out_vals[(size_t)m * k + r] = -INFINITY;
+  __syncthreads();
+  const int C = sm.cnt;
+  if (C <= kCandCap) {
+    for (int q = tid; q < C; q += kMergeThreads) {
+      const uint64_t x = sm.cand[q];
+      int r = 0;
+#pragma unroll 8
+      for (int p = 0; p < C; ++p) r += sm.cand[p] > x;
+      if (r < k) emit(r, x);
+    }
+    for (int r = C + tid; r < k; r += kMergeThreads) emit(r, (uint64_t)0);
+  } else {                                         // block-uniform: too many keys at T
+    uint64_t lst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) lst[u] = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) ns::list_insert(lst, key[u]);
+    ns::block_pop_topk<kMergeThreads, U>(lst, k, sm.red, emit);
   }
 }
 
-// ---------------------------------------------------------------------------
-// Merge for n_max <= 4096: one 1024-thread block per hidden row m, at most
-// four columns per thread.  The first column of every thread is requested in
-// the same round as |I|, so the partial sums are in flight before |I| is
-// known.  Selection: T = the k-th largest of the 64 maxima of 16-lane rows.
-// Each of those is a real key, so the k-th largest key overall is >= T and
-// the top k are among the keys >= T; those are collected in LDS and ranked by
-// counting.  If more than kCandCap keys reach T, the block falls back to k
-// rounds of block-wide maxima.
-// ---------------------------------------------------------------------------
-constexpr int kMergeSmallThreads = 1024;
-constexpr int kMergeSmallCols = 4;
-constexpr int kCandCap = 1024;
-
 template <int SQ>
 __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
-  float sv = 0.f;                                    // slices summed in a fixed order
+  float sv = 0.f;                                  // slices summed in a fixed order
 #pragma unroll
   for (int q = 0; q < SQ; ++q) {
     if (4 * q + 0 < S) sv += p[q].x;
@@ -350,38 +323,46 @@ __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
   return sv;
 }
 
-template <int SQ>
-__global__ __launch_bounds__(kMergeSmallThreads) void k_merge_small(const float* __restrict__ part, int S, int n_max,
-                                                                    const int32_t* __restrict__ row_ids,
-                                                                    const int32_t* __restrict__ n_dev, int V, int k,
-                                                                    float* __restrict__ logits_out,
-                                                                    int32_t* __restrict__ out_ids,
-                                                                    float* __restrict__ out_vals) {
-  constexpr int NT = kMergeSmallThreads, U = kMergeSmallCols;
-  __shared__ uint64_t rmax[NS_WAVE];                 // (NT / 64 waves) x (4 rows of 16 lanes)
-  __shared__ uint64_t cand[kCandCap];
-  __shared__ uint64_t sh_red[NT / NS_WAVE];
-  __shared__ uint64_t sh_T;
-  __shared__ int sh_cnt;
-  static_assert(NT / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
-  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
+// k_merge_cols: block (m, c) sums the S partials of columns
+// [c * kMergeChunk, (c + 1) * kMergeChunk) of hidden row m (at most four per
+// thread), optionally writes the logits, and selects that chunk's top k.
+// With one chunk (n_max <= kMergeChunk) the winners go straight to the
+// outputs; otherwise each chunk's k keys go to cand_out[m][c][k] for
+// k_merge_keys.  The first column of every thread is requested in the same
+// round as |I|, so the partial sums are in flight before |I| is known.
+template <int SQ, bool FINAL>
+__global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __restrict__ part, int S, int n_max,
+                                                              const int32_t* __restrict__ row_ids,
+                                                              const int32_t* __restrict__ n_dev, int V, int k,
+                                                              float* __restrict__ logits_out,
+                                                              int32_t* __restrict__ out_ids,
+                                                              float* __restrict__ out_vals,
+                                                              uint64_t* __restrict__ cand_out) {
+  constexpr int NT = kMergeThreads, U = kMergeCols;
+  __shared__ SelectSmem sm;
+  const int m = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int col0 = c * kMergeChunk;
+  const int cend = min(n_max, col0 + kMergeChunk);   // > col0
   const float4* prow = (const float4*)(part + (size_t)m * n_max * (SQ * 4));
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
   float4 pv[U][SQ];
   {
-    const int jc = tid < n_max ? tid : n_max - 1;
+    const int j = col0 + tid;
+    const int jc = j < cend ? j : cend - 1;
     gv[0] = row_ids ? row_ids[jc] : jc;
 #pragma unroll
     for (int q = 0; q < SQ; ++q) pv[0][q] = prow[(size_t)jc * SQ + q];
   }
   NS_ISSUE_FENCE();
   const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
-  if (n > NT) {                                      // block-uniform
+  const int lim = min(n, cend);                      // live columns of this chunk end here
+  const bool more = lim > col0 + NT;                 // block-uniform
+  if (more) {
 #pragma unroll
     for (int u = 1; u < U; ++u) {
-      const int j = tid + u * NT;
-      const int jc = j < n ? j : n - 1;
+      const int j = col0 + tid + u * NT;
+      const int jc = j < lim ? j : lim - 1;
       gv[u] = row_ids ? row_ids[jc] : jc;
 #pragma unroll
       for (int q = 0; q < SQ; ++q) pv[u][q] = prow[(size_t)jc * SQ + q];
@@ -389,70 +370,52 @@ __global__ __launch_bounds__(kMergeSmallThreads) void k_merge_small(const float*
     NS_ISSUE_FENCE();
   }
   uint64_t key[U];
-  uint64_t best = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int j = tid + u * NT;
+    const int j = col0 + tid + u * NT;
     key[u] = 0;
-    if (u == 0 || n > NT) {
+    if (u == 0 || more) {
       const float sv = sum_slices<SQ>(pv[u], S);
-      if (j < n && gv[u] >= 0 && gv[u] < V) {
+      if (j < lim && gv[u] >= 0 && gv[u] < V) {
         if (logits_out) logits_out[(size_t)m * n_max + j] = sv;
         key[u] = ns::make_key(sv, gv[u]);
       }
     }
-    best = key[u] > best ? key[u] : best;
   }
-  const uint64_t rm = ns::row16_max_u64(best);
-  if ((lane & 15) == 15) rmax[(tid / NS_WAVE) * 4 + (lane >> 4)] = rm;
-  if (tid == 0) sh_cnt = 0;
-  __syncthreads();
-  // Wave 0 finds T: lane l ranks row maximum l among the 64.
-  if (tid < NS_WAVE) {
-    const uint64_t mine = rmax[lane];
-    int rank = 0;
-#pragma unroll 16
-    for (int q = 0; q < NS_WAVE; ++q) rank += rmax[q] > mine;
-    const unsigned long long ball = __ballot(mine != 0 && rank == k - 1);
-    if (lane == 0) sh_T = ball ? rmax[__ffsll(ball) - 1] : 0;
-  }
-  __syncthreads();
-  const uint64_t T = sh_T;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (key[u] != 0 && key[u] >= T) {
-      const int slot = atomicAdd(&sh_cnt, 1);
-      if (slot < kCandCap) cand[slot] = key[u];
-    }
-  }
-  __syncthreads();
-  const int C = sh_cnt;
-  if (C <= kCandCap) {
-    for (int q = tid; q < C; q += NT) {
-      const uint64_t x = cand[q];
-      int r = 0;
-#pragma unroll 8
-      for (int p = 0; p < C; ++p) r += cand[p] > x;
-      if (r < k) {
-        out_ids[(size_t)m * k + r] = ns::key_id(x);
-        out_vals[(size_t)m * k + r] = ns::key_val(x);
-      }
-    }
-    for (int r = C + tid; r < k; r += NT) {
-      out_ids[(size_t)m * k + r] = -1;
-      out_vals[(size_t)m * k + r] = -INFINITY;
-    }
-  } else {                                           // block-uniform: too many keys at T
-    uint64_t lst[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) lst[u] = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) ns::list_insert(lst, key[u]);
-    ns::block_pop_topk<NT, U>(lst, k, sh_red, [&](int r, uint64_t x) {
+  if (FINAL) {
+    block_select_topk<U>(key, k, sm, [&](int r, uint64_t x) {
       out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
       out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
     });
+  } else {
+    uint64_t* dst = cand_out + ((size_t)m * gridDim.y + c) * k;
+    block_select_topk<U>(key, k, sm, [&](int r, uint64_t x) { dst[r] = x; });
   }
+}
+
+// k_merge_keys: the final top k of hidden row m over the C chunks' keys
+// (nk = C * k of them, at most PER per thread).
+template <int PER>
+__global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __restrict__ cand, int nk, int k,
+                                                              int32_t* __restrict__ out_ids,
+                                                              float* __restrict__ out_vals) {
+  __shared__ SelectSmem sm;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const uint64_t* src = cand + (size_t)m * nk;
+  uint64_t key[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int j = tid + u * kMergeThreads;
+    key[u] = src[j < nk ? j : 0];
+  }
+  NS_ISSUE_FENCE();
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (tid + u * kMergeThreads >= nk) key[u] = 0;
+  block_select_topk<PER>(key, k, sm, [&](int r, uint64_t x) {
+    out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
+    out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -479,11 +442,6 @@ int pick_splits(int n_max, int M, int d, int dtype) {
   if (s > smax) s = smax;
   if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : s;
-}
-
-size_t merge_lds_bytes(int k) {
-  const int cap = k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
-  return (size_t)kMergeThreads * (k < cap ? k : cap) * sizeof(uint64_t);
 }
 
 template <bool BF16>
@@ -531,43 +489,43 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   return ns_launch_status();
 }
 
-template <int CAP>
-int launch_merge_t(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V, int M,
-                   int k, float* logits, int32_t* ids, float* vals, hipStream_t stream) {
-  const size_t lds = merge_lds_bytes(k);
-  if (lds > 65536) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      if (hipFuncSetAttribute((const void*)k_merge<CAP>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-          hipSuccess)
-        return NS_EHIP;
-      attr_set = true;
-    }
-  }
-  hipLaunchKernelGGL((k_merge<CAP>), dim3(M), dim3(kMergeThreads), lds, stream, part, S, SP, n_max, row_ids, n_dev,
-                     V, M, k, logits, ids, vals);
-  return ns_launch_status();
-}
+int merge_chunks(int n_max) { return (n_max + kMergeChunk - 1) / kMergeChunk; }
+
+// Workspace layout: [0, 256) reserved; partial sums float[M][n_max][SP] at
+// 256; for n_max > kMergeChunk, chunk keys uint64[M][C][k] after them.
+size_t partial_bytes(int n_max, int M, int SP) { return align256((size_t)SP * M * n_max * sizeof(float)); }
 
 int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
-                 int M, int k, float* logits, int32_t* ids, float* vals, hipStream_t stream) {
-  if (n_max <= kMergeSmallThreads * kMergeSmallCols) {
-#define NS_LAUNCH_MERGE_SMALL(SQV)                                                                                   \
-  hipLaunchKernelGGL((k_merge_small<SQV>), dim3(M), dim3(kMergeSmallThreads), 0, stream, part, S, n_max, row_ids, \
-                     n_dev, V, k, logits, ids, vals)
-    switch (SP / 4) {
-      case 1: NS_LAUNCH_MERGE_SMALL(1); break;
-      case 2: NS_LAUNCH_MERGE_SMALL(2); break;
-      case 3: NS_LAUNCH_MERGE_SMALL(3); break;
-      default: NS_LAUNCH_MERGE_SMALL(4); break;
-    }
-#undef NS_LAUNCH_MERGE_SMALL
+                 int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, hipStream_t stream) {
+  const int C = merge_chunks(n_max);
+#define NS_LAUNCH_COLS(SQV, FIN)                                                                                 \
+  hipLaunchKernelGGL((k_merge_cols<SQV, FIN>), dim3(M, C), dim3(kMergeThreads), 0, stream, part, S, n_max, row_ids, \
+                     n_dev, V, k, logits, ids, vals, cand)
+#define NS_LAUNCH_COLS_SQ(FIN)                 \
+  switch (SP / 4) {                            \
+    case 1: NS_LAUNCH_COLS(1, FIN); break;     \
+    case 2: NS_LAUNCH_COLS(2, FIN); break;     \
+    case 3: NS_LAUNCH_COLS(3, FIN); break;     \
+    default: NS_LAUNCH_COLS(4, FIN); break;    \
+  }
+  if (C == 1) {
+    NS_LAUNCH_COLS_SQ(true);
     return ns_launch_status();
   }
-  if (k <= 8) return launch_merge_t<8>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
-  if (k <= 16) return launch_merge_t<16>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
-  if (k <= 32) return launch_merge_t<32>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
-  return launch_merge_t<64>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, stream);
+  NS_LAUNCH_COLS_SQ(false);
+#undef NS_LAUNCH_COLS_SQ
+#undef NS_LAUNCH_COLS
+  const int nk = C * k;
+  const int per = (nk + kMergeThreads - 1) / kMergeThreads;
+#define NS_LAUNCH_KEYS(PERV) \
+  hipLaunchKernelGGL((k_merge_keys<PERV>), dim3(M), dim3(kMergeThreads), 0, stream, cand, nk, k, ids, vals)
+  if (per <= 1) NS_LAUNCH_KEYS(1);
+  else if (per <= 2) NS_LAUNCH_KEYS(2);
+  else if (per <= 4) NS_LAUNCH_KEYS(4);
+  else if (per <= 8) NS_LAUNCH_KEYS(8);
+  else NS_LAUNCH_KEYS(16);
+#undef NS_LAUNCH_KEYS
+  return ns_launch_status();
 }
 
 bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
@@ -584,7 +542,9 @@ extern "C" {
 size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d) {
   if (!draft_dims_ok(n_max, M, k, d)) return 0;
   const int SP = (pick_splits(n_max, M, d, NS_BF16) + 3) & ~3;
-  return 256 + align256((size_t)SP * M * n_max * sizeof(float));
+  const int C = merge_chunks(n_max);
+  const size_t keys = C > 1 ? align256((size_t)M * C * k * sizeof(uint64_t)) : 0;
+  return 256 + partial_bytes(n_max, M, SP) + keys;
 }
 
 int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
@@ -611,7 +571,8 @@ int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* ro
     rc = launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, SP, part, stream);
   }
   if (rc != NS_OK) return rc;
-  return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, stream);
+  uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP));
+  return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, stream);
 }
 
 }  // extern "C"

@@ -179,14 +179,16 @@ int nanospec_gather_rows(const void* w, int32_t V, int32_t d, int32_t dtype,
  *             rows = W_head and n_max = V this is the full-vocabulary head).
  *   n_dev   : [1] int32 active row count (NULL -> n_max), clamped to n_max.
  *   h       : [M x d] hidden rows, same dtype as rows, 16-byte aligned.
- *   logits  : optional [M x n_max] float32 output (NULL -> kept in the
- *             workspace); columns j >= n and holes are left untouched.
+ *   logits  : optional [M x n_max] float32 output (NULL -> not written);
+ *             columns j >= n and holes are left untouched.
  *   topk_ids/topk_vals : [M x k] int32 / float32 outputs; row m holds the k
  *             largest logits of hidden row m, ordered by (value desc, global
  *             id asc), with the global ids.
  *   ws      : workspace of >= nanospec_draft_workspace_bytes(n_max, M, k, d)
- *             bytes, 256-byte aligned (partial sums; no initialisation
- *             needed).  Calls sharing a workspace must be ordered.
+ *             bytes, 256-byte aligned (partial sums over slices of d and,
+ *             when n_max > 4096, each 4096-column chunk's top-k keys; no
+ *             initialisation needed).  Calls sharing a workspace must be
+ *             ordered.
  * Arithmetic: bf16 products are exact in float32 and summed in float32 on the
  * matrix cores (v_mfma_f32_16x16x32_bf16), in slices of d whose partial sums
  * are added in a fixed order; fp32 inputs use float32 FMAs.  No float
