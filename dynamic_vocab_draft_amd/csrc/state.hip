@@ -222,6 +222,18 @@ __host__ __device__ __forceinline__ int fast_wpt(int V) {
 
 __device__ __forceinline__ void bm_set(uint32_t* bm, int id) { atomicOr(&bm[id >> 5], 1u << (id & 31)); }
 
+__device__ __forceinline__ void bm_store8(uint32_t* __restrict__ dst, int w, int words, uint4 a, uint4 b, bool vec) {
+  if (vec && w + 8 <= words) {
+    ((uint4*)(dst + w))[0] = a;
+    ((uint4*)(dst + w))[1] = b;
+    return;
+  }
+  const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (w + e < words) dst[w + e] = x[e];
+}
+
 template <typename T, int RU>
 __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, const int32_t* draft_ids,
                                                             int n_draft, const int32_t* ver_ids, int n_ver,
@@ -233,12 +245,14 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
   extern __shared__ int4 lds4[];
   __shared__ int sh_scan[NW + 1];
   __shared__ int sh_flag;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), wv = tid / NS_WAVE;
   const int w_max = v.w_max, V = v.V;
   const int words = (V + 31) >> 5;
   const int wpt = fast_wpt(V);
+  const int nd64 = (n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1);
   uint32_t* bm = (uint32_t*)lds4;                                 // kFastThreads * wpt words
-  int32_t* dids = (int32_t*)(bm + (size_t)kFastThreads * wpt);    // n_draft rounded up to 64
+  int32_t* dids = (int32_t*)(bm + (size_t)kFastThreads * wpt);    // nd64 ids (-1 padding)
+  int32_t* sfp = dids + nd64;                                     // nd64 first positions
   // ---- one round of global loads --------------------------------------
   // An index the compiler cannot prove uniform keeps |S| in a vector
   // register, so no early wait is placed on it ahead of the other loads.
@@ -257,35 +271,46 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
   const int v_in = ver_ids[tid < n_ver ? tid : 0];
   NS_ISSUE_FENCE();
   for (int w = tid; w < kFastThreads * wpt; w += kFastThreads) bm[w] = 0u;
-  const int nd64 = (n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1);
-  for (int q = tid; q < nd64; q += kFastThreads) dids[q] = q < n_draft ? d_in : -1;
+  for (int q = tid; q < nd64; q += kFastThreads) {
+    dids[q] = q < n_draft ? d_in : -1;
+    sfp[q] = q;
+  }
   if (tid == 0) sh_flag = 0;
+  __syncthreads();
+  // ---- C_draft first occurrences ---------------------------------------
+  // Position i keeps its id iff no earlier position holds it.  The j range
+  // is split over the waves (wave w compares against ids
+  // [w * nd64 / 8, (w + 1) * nd64 / 8), read as broadcast 4-id LDS words) and
+  // each lane takes positions lane, lane + 64, ...; a smaller equal position
+  // is folded into sfp[i] with an LDS atomicMin.
+  {
+    const int cj = nd64 / NW;                                   // a multiple of 8
+    const int4* d4 = (const int4*)(dids + wv * cj);
+    for (int i = lane; i < n_draft; i += NS_WAVE) {
+      const int x = dids[i];
+      int fp = INT32_MAX;
+      for (int c4 = 0; c4 < cj / 4; c4 += 2) {
+        const int4 qa = d4[c4], qb = d4[c4 + 1];
+        const int j = wv * cj + 4 * c4;
+        fp = min(fp, qa.x == x ? j : INT32_MAX);
+        fp = min(fp, qa.y == x ? j + 1 : INT32_MAX);
+        fp = min(fp, qa.z == x ? j + 2 : INT32_MAX);
+        fp = min(fp, qa.w == x ? j + 3 : INT32_MAX);
+        fp = min(fp, qb.x == x ? j + 4 : INT32_MAX);
+        fp = min(fp, qb.y == x ? j + 5 : INT32_MAX);
+        fp = min(fp, qb.z == x ? j + 6 : INT32_MAX);
+        fp = min(fp, qb.w == x ? j + 7 : INT32_MAX);
+      }
+      if (fp < i) atomicMin(&sfp[i], fp);
+    }
+  }
   __syncthreads();
   // ---- tuple positions (C_draft deduplicated, then C_ver as given) ----
   bool keep_d = false, keep_v = false, bad = false;
   if (tid < n_draft) {
     keep_d = d_in >= 0 && d_in < V;
     bad |= !keep_d;
-  }
-  // First occurrence: keep iff no earlier position holds the same id.  All
-  // lanes read the same LDS words (broadcast), sixteen 4-id reads per batch.
-  if ((tid & ~(NS_WAVE - 1)) < n_draft) {
-    const int4* d4 = (const int4*)dids;
-    int fp = tid;
-    for (int c = 0; c < nd64; c += NS_WAVE) {
-      int4 q[NS_WAVE / 4];
-#pragma unroll
-      for (int i = 0; i < NS_WAVE / 4; ++i) q[i] = d4[(c >> 2) + i];
-#pragma unroll
-      for (int i = 0; i < NS_WAVE / 4; ++i) {
-        const int j = c + 4 * i;
-        fp = min(fp, q[i].x == d_in ? j : INT32_MAX);
-        fp = min(fp, q[i].y == d_in ? j + 1 : INT32_MAX);
-        fp = min(fp, q[i].z == d_in ? j + 2 : INT32_MAX);
-        fp = min(fp, q[i].w == d_in ? j + 3 : INT32_MAX);
-      }
-    }
-    keep_d &= fp == tid;
+    keep_d &= sfp[tid] == tid;
   }
   if (tid < n_ver) {
     keep_v = v_in >= 0 && v_in < V;
@@ -296,19 +321,27 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
   const int pre = ns::block_excl_scan<kFastThreads>((keep_d ? 1 : 0) | (keep_v ? 0x10000 : 0), sh_scan, &total);
   const int Cd = total & 0xFFFF, Cv = total >> 16, C = Cd + Cv;
   const int64_t len = len_in;
-  const int lm = (int)(len % (int64_t)w_max);         // slot of position |S|
+  int lm;                                               // slot of position |S|
+  if (len < ((int64_t)1 << 31)) lm = (int)((uint32_t)len % (uint32_t)w_max);
+  else lm = (int)(len % (int64_t)w_max);
+  auto slot_of = [&](int p) {                           // (lm + p) mod w_max, p < 2^16
+    int x = lm + p;
+    if (x >= w_max) x -= w_max;
+    if (x >= w_max) x %= w_max;
+    return x;
+  };
   // New entries: only the last w_max of this step can be inside the window.
   if (keep_d) {
     const int p = pre & 0xFFFF;
     if (p >= C - w_max) {
-      v.ring[(lm + p) % w_max] = d_in;
+      v.ring[slot_of(p)] = d_in;
       bm_set(bm, d_in);
     }
   }
   if (keep_v) {
     const int p = Cd + (pre >> 16);
     if (p >= C - w_max) {
-      v.ring[(lm + p) % w_max] = v_in;
+      v.ring[slot_of(p)] = v_in;
       bm_set(bm, v_in);
     }
   }
@@ -331,19 +364,25 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
     }
   }
   __syncthreads();
-  // ---- ascending compaction ------------------------------------------
+  // ---- ascending compaction; the bitmap goes out from registers ---------
+  const bool out_vec = bitmap_out && ((((uintptr_t)bitmap_out) & 15u) == 0);
   const uint4* bm4 = (const uint4*)(bm + (size_t)tid * wpt);
+  const int wbase = tid * wpt;
   int pc = 0;
   uint4 c0a = bm4[0], c0b = bm4[1];                   // first 8 words stay in registers
   pc += __popc(c0a.x) + __popc(c0a.y) + __popc(c0a.z) + __popc(c0a.w);
   pc += __popc(c0b.x) + __popc(c0b.y) + __popc(c0b.z) + __popc(c0b.w);
-  for (int c = 2; c < wpt / 4; ++c) {
-    const uint4 x = bm4[c];
+  bm_store8(v.bitmap, wbase, words, c0a, c0b, true);
+  if (bitmap_out) bm_store8(bitmap_out, wbase, words, c0a, c0b, out_vec);
+  for (int c = 2; c < wpt / 4; c += 2) {
+    const uint4 x = bm4[c], y = bm4[c + 1];
     pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+    pc += __popc(y.x) + __popc(y.y) + __popc(y.z) + __popc(y.w);
+    bm_store8(v.bitmap, wbase + 4 * c, words, x, y, true);
+    if (bitmap_out) bm_store8(bitmap_out, wbase + 4 * c, words, x, y, out_vec);
   }
   int n_tot = 0;
   int off = ns::block_excl_scan<kFastThreads>(pc, sh_scan, &n_tot);
-  const int wbase = tid * wpt;
   auto emit = [&](uint32_t b, int w) {
     while (b) {
       active_ids[off++] = (w << 5) + (__ffs(b) - 1);
@@ -357,20 +396,6 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
     const int w = wbase + 4 * c;
     emit(x.x, w); emit(x.y, w + 1); emit(x.z, w + 2); emit(x.w, w + 3);
   }
-  // Bitmap copies: coalesced, eight LDS reads in flight per thread.
-  for (int w0 = tid; w0 < words; w0 += kFastThreads * 8) {
-    uint32_t b[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) b[u] = bm[w0 + u * kFastThreads];   // < kFastThreads * wpt
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int w = w0 + u * kFastThreads;
-      if (w < words) {
-        v.bitmap[w] = b[u];
-        if (bitmap_out) bitmap_out[w] = b[u];
-      }
-    }
-  }
   if (tid == 0) {
     *n_active = n_tot;
     *v.len = len + C;
@@ -379,7 +404,7 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
 }
 
 size_t fast_lds_bytes(int V, int n_draft) {
-  return ((size_t)kFastThreads * fast_wpt(V) + (size_t)((n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1))) * 4;
+  return ((size_t)kFastThreads * fast_wpt(V) + 2 * (size_t)((n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1))) * 4;
 }
 
 typedef void (*step_fast_fn)(ns_state_view, const int32_t*, int, const int32_t*, int, int32_t*, int32_t*, uint32_t*);
