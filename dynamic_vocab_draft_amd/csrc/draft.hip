@@ -239,13 +239,16 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 // Merge.  Keys are (ordered f32 bits << 32) | ~id, so one 64-bit compare
 // orders by (value desc, id asc); 0 is the empty key.
 //
-// block_select_topk: the k largest keys held by a 1024-thread block (U keys
-// per thread).  T = the k-th largest of the 64 maxima of 16-lane DPP rows;
-// each of those is a real key, so the k-th largest key overall is >= T and
-// the top k are among the keys >= T.  Those are collected in LDS and ranked
+// block_select_topk: the k largest (value, id) pairs held by a 1024-thread
+// block (U per thread; id < 0 marks an empty slot), by the key order.
+// T = the k-th largest of the 64 maxima of 16-lane DPP rows, or of the 16
+// wave maxima when k <= 16 (float values, counted with multiplicity).  Each
+// of those is a real value, so the k-th
+// largest value overall is >= T and the top k are among the pairs with value
+// >= T.  Only those are turned into 64-bit keys, collected in LDS and ranked
 // by counting; if more than kCandCap reach T, the block falls back to k
 // rounds of block-wide maxima.  emit(r, key) is called once for every rank
-// r < k (key 0 when fewer than r + 1 keys exist).
+// r < k (key 0 when fewer than r + 1 pairs exist).
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCols = 4;                      // columns per thread
@@ -253,40 +256,72 @@ constexpr int kMergeChunk = kMergeThreads * kMergeCols;
 constexpr int kCandCap = 1024;
 
 struct SelectSmem {
-  uint64_t rmax[NS_WAVE];                          // (1024 / 64 waves) x (4 rows of 16 lanes)
+  float rmax[NS_WAVE];                             // (1024 / 64 waves) x (4 rows of 16 lanes)
   uint64_t cand[kCandCap];
   uint64_t red[kMergeThreads / NS_WAVE];
-  uint64_t T;
+  float T;
   int cnt;
 };
 
 template <int U, typename Emit>
-__device__ __forceinline__ void block_select_topk(const uint64_t (&key)[U], int k, SelectSmem& sm, Emit emit) {
+__device__ __forceinline__ void block_select_topk(const float (&val)[U], const int (&id)[U], int k, SelectSmem& sm,
+                                                  Emit emit) {
   static_assert(kMergeThreads / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
   const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
-  uint64_t best = 0;
+  const int ninf = __float_as_int(-INFINITY);
+  float best = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < U; ++u) best = key[u] > best ? key[u] : best;
-  const uint64_t rm = ns::row16_max_u64(best);
-  if ((lane & 15) == 15) sm.rmax[(tid / NS_WAVE) * 4 + (lane >> 4)] = rm;
+  for (int u = 0; u < U; ++u)
+    if (id[u] >= 0) best = fmaxf(best, val[u]);
+  best = fmaxf(best, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(best), 0x111, 0xf, 0xf, false)));
+  best = fmaxf(best, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(best), 0x112, 0xf, 0xf, false)));
+  best = fmaxf(best, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(best), 0x114, 0xf, 0xf, false)));
+  best = fmaxf(best, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(best), 0x118, 0xf, 0xf, false)));
+  constexpr int NW = kMergeThreads / NS_WAVE;
+  // For k <= NW the 16 wave maxima are enough (fewer compares for wave 0);
+  // otherwise the 64 row maxima are used.
+  const bool by_wave = k <= NW;
+  if (by_wave) {
+    const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 15));
+    const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 31));
+    const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 47));
+    const float w3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 63));
+    if (lane == 0) sm.rmax[tid / NS_WAVE] = fmaxf(fmaxf(w0, w1), fmaxf(w2, w3));
+  } else if ((lane & 15) == 15) {
+    sm.rmax[(tid / NS_WAVE) * 4 + (lane >> 4)] = best;
+  }
   if (tid == 0) sm.cnt = 0;
   __syncthreads();
-  // Wave 0 finds T: lane l ranks row maximum l among the 64.
+  // Wave 0 finds T: the maximum x with #{> x} < k <= #{>= x}.
   if (tid < NS_WAVE) {
-    const uint64_t mine = sm.rmax[lane];
-    int rank = 0;
+    const int nv = by_wave ? NW : NS_WAVE;
+    const float mine = lane < nv ? sm.rmax[lane] : -INFINITY;
+    int gt = 0, ge = 0;
+    if (by_wave) {
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const float o = sm.rmax[q];
+        gt += o > mine;
+        ge += o >= mine;
+      }
+    } else {
 #pragma unroll 16
-    for (int q = 0; q < NS_WAVE; ++q) rank += sm.rmax[q] > mine;
-    const unsigned long long ball = __ballot(mine != 0 && rank == k - 1);
-    if (lane == 0) sm.T = ball ? sm.rmax[__ffsll(ball) - 1] : 0;
+      for (int q = 0; q < NS_WAVE; ++q) {
+        const float o = sm.rmax[q];
+        gt += o > mine;
+        ge += o >= mine;
+      }
+    }
+    const unsigned long long ball = __ballot(mine != -INFINITY && gt < k && ge >= k);
+    if (lane == 0) sm.T = ball ? sm.rmax[__ffsll(ball) - 1] : -INFINITY;
   }
   __syncthreads();
-  const uint64_t T = sm.T;
+  const float T = sm.T;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (key[u] != 0 && key[u] >= T) {
+    if (id[u] >= 0 && val[u] >= T) {
       const int slot = atomicAdd(&sm.cnt, 1);
-      if (slot < kCandCap) sm.cand[slot] = key[u];
+      if (slot < kCandCap) sm.cand[slot] = ns::make_key(val[u], id[u]);
     }
   }
   __syncthreads();
@@ -300,12 +335,13 @@ __device__ __forceinline__ void block_select_topk(const uint64_t (&key)[U], int 
       if (r < k) emit(r, x);
     }
     for (int r = C + tid; r < k; r += kMergeThreads) emit(r, (uint64_t)0);
-  } else {                                         // block-uniform: too many keys at T
+  } else {                                         // block-uniform: too many pairs at T
     uint64_t lst[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) lst[u] = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) ns::list_insert(lst, key[u]);
+    for (int u = 0; u < U; ++u)
+      if (id[u] >= 0) ns::list_insert(lst, ns::make_key(val[u], id[u]));
     ns::block_pop_topk<kMergeThreads, U>(lst, k, sm.red, emit);
   }
 }
@@ -369,27 +405,30 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     }
     NS_ISSUE_FENCE();
   }
-  uint64_t key[U];
+  float val[U];
+  int gid[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = col0 + tid + u * NT;
-    key[u] = 0;
+    val[u] = 0.f;
+    gid[u] = -1;
     if (u == 0 || more) {
       const float sv = sum_slices<SQ>(pv[u], S);
       if (j < lim && gv[u] >= 0 && gv[u] < V) {
         if (logits_out) logits_out[(size_t)m * n_max + j] = sv;
-        key[u] = ns::make_key(sv, gv[u]);
+        val[u] = sv;
+        gid[u] = gv[u];
       }
     }
   }
   if (FINAL) {
-    block_select_topk<U>(key, k, sm, [&](int r, uint64_t x) {
+    block_select_topk<U>(val, gid, k, sm, [&](int r, uint64_t x) {
       out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
       out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
     });
   } else {
     uint64_t* dst = cand_out + ((size_t)m * gridDim.y + c) * k;
-    block_select_topk<U>(key, k, sm, [&](int r, uint64_t x) { dst[r] = x; });
+    block_select_topk<U>(val, gid, k, sm, [&](int r, uint64_t x) { dst[r] = x; });
   }
 }
 
@@ -409,10 +448,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __
     key[u] = src[j < nk ? j : 0];
   }
   NS_ISSUE_FENCE();
+  float val[PER];
+  int gid[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (tid + u * kMergeThreads >= nk) key[u] = 0;
-  block_select_topk<PER>(key, k, sm, [&](int r, uint64_t x) {
+  for (int u = 0; u < PER; ++u) {
+    const bool live = tid + u * kMergeThreads < nk && key[u] != 0;
+    val[u] = live ? ns::key_val(key[u]) : 0.f;
+    gid[u] = live ? ns::key_id(key[u]) : -1;
+  }
+  block_select_topk<PER>(val, gid, k, sm, [&](int r, uint64_t x) {
     out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
     out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
   });
