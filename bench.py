@@ -238,7 +238,7 @@ def main():
                    "mean_active": n_mean, "timing": "hipGraph replay of the timed steps"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name, mname[best]),
-                     "kernel": "nanospec_draft_logits_topk = k_proj_mfma + k_merge",
+                     "kernel": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols",
                      "bytes_per_launch": draft_bytes, "avg_launch_us": r["draft_ms"] * 1e3},
         "step": {"alg_bytes": step_bytes, "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
                  "state_update_us": r["state_ms"] * 1e3, "draft_us": r["draft_ms"] * 1e3,
