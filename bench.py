@@ -276,7 +276,8 @@ def copy_probe(torch, nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 3}), flush=True)
 
 
-DRAFT_SOURCES = ("dynamic_vocab_draft_amd/csrc/draft.hip", "dynamic_vocab_draft_amd/csrc/common.hpp")
+DRAFT_SOURCES = ("dynamic_vocab_draft_amd/csrc/draft.hip", "dynamic_vocab_draft_amd/csrc/select.hpp",
+                 "dynamic_vocab_draft_amd/csrc/common.hpp")
 
 
 def kernel_source_hash():

@@ -481,10 +481,6 @@ int fill_grid(const ns_state_view& v) {
 
 }  // namespace
 
-struct nanospec_state {
-  ns_state_view view;
-};
-
 extern "C" {
 
 const char* nanospec_strerror(int code) {

@@ -11,3 +11,8 @@ struct ns_state_view {
   int V;
   int w_max;
 };
+
+// The opaque host handle behind nanospec_state*.
+struct nanospec_state {
+  ns_state_view view;
+};
