@@ -53,6 +53,18 @@ constexpr int kTargetBlocks = 1536;               // MFMA blocks aimed for when 
 constexpr int kMaxSplits = 16;
 
 
+// Per-sequence element strides of a batched call (sequence b = blockIdx.z,
+// or blockIdx.y for k_merge_keys); all zero for a single sequence.
+struct BatchStrides {
+  size_t rows;     // uint4 units (0: W_head shared by all sequences)
+  size_t ids;      // row_ids / n_dev: ids per sequence (n_dev advances by 1)
+  size_t h;        // uint4 units
+  size_t part;     // floats
+  size_t logits;   // floats
+  size_t out;      // top-k entries
+  size_t cand;     // chunk keys
+};
+
 __device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
   int n = n_dev ? *n_dev : n_max;
   return n < 0 ? 0 : (n > n_max ? n_max : n);
@@ -83,8 +95,16 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
                                                             const int32_t* __restrict__ row_ids,
                                                             const int32_t* __restrict__ n_dev, int n_max, int V,
                                                             int dvec, const uint4* __restrict__ h, int M,
-                                                            int SP, float* __restrict__ part) {
+                                                            int SP, float* __restrict__ part, BatchStrides bs) {
   extern __shared__ uint4 hs[];   // [mt][dvec]
+  {
+    const size_t b = blockIdx.z;
+    rows += b * bs.rows;
+    if (row_ids) row_ids += b * bs.ids;
+    if (n_dev) n_dev += b;
+    h += b * bs.h;
+    part += b * bs.part;
+  }
   const int n = clamp_n(n_dev, n_max);
   if ((int)blockIdx.x * kProjWaves >= n) return;      // block-uniform
   const int m0 = blockIdx.y * MT;
@@ -136,8 +156,17 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
-                                                         int ks_per_split, int SP, float* __restrict__ part) {
+                                                         int ks_per_split, int SP, float* __restrict__ part,
+                                                         BatchStrides bs) {
   __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
+  {
+    const size_t b = blockIdx.z;
+    rows += b * bs.rows;
+    if (row_ids) row_ids += b * bs.ids;
+    if (n_dev) n_dev += b;
+    h += b * bs.h;
+    part += b * bs.part;
+  }
   __shared__ int sh_ok[RT * kTile];
   const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), w = tid / NS_WAVE;
   const int i = lane & 15, g = lane >> 4;
@@ -270,9 +299,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
                                                               float* __restrict__ logits_out,
                                                               int32_t* __restrict__ out_ids,
                                                               float* __restrict__ out_vals,
-                                                              uint64_t* __restrict__ cand_out) {
+                                                              uint64_t* __restrict__ cand_out, BatchStrides bs) {
   constexpr int NT = kMergeThreads, U = kMergeCols;
   __shared__ SelectSmem sm;
+  {
+    const size_t b = blockIdx.z;
+    part += b * bs.part;
+    if (row_ids) row_ids += b * bs.ids;
+    if (n_dev) n_dev += b;
+    if (logits_out) logits_out += b * bs.logits;
+    out_ids += b * bs.out;
+    out_vals += b * bs.out;
+    cand_out += b * bs.cand;
+  }
   const int m = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int col0 = c * kMergeChunk;
   const int cend = min(n_max, col0 + kMergeChunk);   // > col0
@@ -334,8 +373,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
 template <int PER>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __restrict__ cand, int nk, int k,
                                                               int32_t* __restrict__ out_ids,
-                                                              float* __restrict__ out_vals) {
+                                                              float* __restrict__ out_vals, BatchStrides bs) {
   __shared__ SelectSmem sm;
+  {
+    const size_t b = blockIdx.y;
+    cand += b * bs.cand;
+    out_ids += b * bs.out;
+    out_vals += b * bs.out;
+  }
   const int m = blockIdx.x, tid = threadIdx.x;
   const uint64_t* src = cand + (size_t)m * nk;
   uint64_t key[PER];
@@ -374,11 +419,11 @@ int pick_rt(int M) { return M <= 16 ? 1 : 2; }
 
 // Number of d-slices for the MFMA path: enough blocks to spread a call over
 // the chip, each wave keeping at least one batch of kKC steps.
-int pick_splits(int n_max, int M, int d, int dtype) {
+int pick_splits(int n_max, int M, int d, int dtype, int B) {
   if (dtype != NS_BF16) return 1;
   const int ksteps = (d / 8 + 3) / 4;
-  const int tiles = (n_max + kTile * pick_rt(M) - 1) / (kTile * pick_rt(M));
-  int s = (kTargetBlocks + tiles - 1) / tiles;
+  const long tiles = (long)((n_max + kTile * pick_rt(M) - 1) / (kTile * pick_rt(M))) * B;
+  int s = (int)((kTargetBlocks + tiles - 1) / tiles);
   const int smax = ksteps / (kPW * kKC) > 0 ? ksteps / (kPW * kKC) : 1;
   if (s > smax) s = smax;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -387,16 +432,16 @@ int pick_splits(int n_max, int M, int d, int dtype) {
 
 template <bool BF16>
 int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V,
-                int d, const void* h, int M, int SP, float* part, hipStream_t stream) {
+                int d, const void* h, int M, int SP, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
   const int esz = BF16 ? 2 : 4;
   const int dvec = d * esz / 16;
   const int quads = (n_max + kProjWaves - 1) / kProjWaves;
   const int gx = quads < 2048 ? quads : 2048;
-  const dim3 grid(gx, (M + mt - 1) / mt);
+  const dim3 grid(gx, (M + mt - 1) / mt, B);
   const size_t lds = (size_t)mt * dvec * 16;
 #define NS_LAUNCH_VALU(MTV)                                                                                     \
   hipLaunchKernelGGL((k_proj_valu<BF16, MTV>), grid, dim3(kProjThreads), lds, stream, (const uint4*)rows, mode, \
-                     row_ids, n_dev, n_max, V, dvec, (const uint4*)h, M, SP, part)
+                     row_ids, n_dev, n_max, V, dvec, (const uint4*)h, M, SP, part, bs)
   switch (mt) {
     case 1: NS_LAUNCH_VALU(1); break;
     case 2: NS_LAUNCH_VALU(2); break;
@@ -409,39 +454,47 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 
 template <int NMT, int RT>
 void launch_mfma_t(dim3 grid, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
-                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int ks, int SP, float* part) {
+                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int ks, int SP, float* part,
+                   const BatchStrides& bs) {
   hipLaunchKernelGGL((k_proj_mfma<NMT, RT>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
-                     n_dev, n_max, V, dv, (const uint4*)h, M, ks, SP, part);
+                     n_dev, n_max, V, dv, (const uint4*)h, M, ks, SP, part, bs);
 }
 
 int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
-                const void* h, int M, int S, int SP, float* part, hipStream_t stream) {
+                const void* h, int M, int S, int SP, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
   const int dv = d / 8;
   const int ksteps = (dv + 3) / 4;
   const int ks = (ksteps + S - 1) / S;
   const int rt = pick_rt(M);
-  const dim3 grid((n_max + kTile * rt - 1) / (kTile * rt), S);
+  const dim3 grid((n_max + kTile * rt - 1) / (kTile * rt), S, B);
+#define NS_LAUNCH_MFMA(NMTV, RTV) \
+  launch_mfma_t<NMTV, RTV>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part, bs)
   switch ((M + 15) / 16) {
-    case 1: launch_mfma_t<1, 1>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
-    case 2: launch_mfma_t<2, 2>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
-    case 3: launch_mfma_t<3, 2>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
-    default: launch_mfma_t<4, 2>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part); break;
+    case 1: NS_LAUNCH_MFMA(1, 1); break;
+    case 2: NS_LAUNCH_MFMA(2, 2); break;
+    case 3: NS_LAUNCH_MFMA(3, 2); break;
+    default: NS_LAUNCH_MFMA(4, 2); break;
   }
+#undef NS_LAUNCH_MFMA
   return ns_launch_status();
 }
 
 int merge_chunks(int n_max) { return (n_max + kMergeChunk - 1) / kMergeChunk; }
 
-// Workspace layout: [0, 256) reserved; partial sums float[M][n_max][SP] at
-// 256; for n_max > kMergeChunk, chunk keys uint64[M][C][k] after them.
-size_t partial_bytes(int n_max, int M, int SP) { return align256((size_t)SP * M * n_max * sizeof(float)); }
+// Workspace layout: [0, 256) reserved; partial sums float[B][M][n_max][SP]
+// at 256; for n_max > kMergeChunk, chunk keys uint64[B][M][C][k] after them.
+size_t partial_floats(int n_max, int M, int SP) { return (size_t)SP * M * n_max; }
+size_t partial_bytes(int n_max, int M, int SP, int B) {
+  return align256(partial_floats(n_max, M, SP) * B * sizeof(float));
+}
 
 int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
-                 int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, hipStream_t stream) {
+                 int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
+                 const BatchStrides& bs, hipStream_t stream) {
   const int C = merge_chunks(n_max);
-#define NS_LAUNCH_COLS(SQV, FIN)                                                                                 \
-  hipLaunchKernelGGL((k_merge_cols<SQV, FIN>), dim3(M, C), dim3(kMergeThreads), 0, stream, part, S, n_max, row_ids, \
-                     n_dev, V, k, logits, ids, vals, cand)
+#define NS_LAUNCH_COLS(SQV, FIN)                                                                                    \
+  hipLaunchKernelGGL((k_merge_cols<SQV, FIN>), dim3(M, C, B), dim3(kMergeThreads), 0, stream, part, S, n_max,      \
+                     row_ids, n_dev, V, k, logits, ids, vals, cand, bs)
 #define NS_LAUNCH_COLS_SQ(FIN)                 \
   switch (SP / 4) {                            \
     case 1: NS_LAUNCH_COLS(1, FIN); break;     \
@@ -459,7 +512,7 @@ int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row
   const int nk = C * k;
   const int per = (nk + kMergeThreads - 1) / kMergeThreads;
 #define NS_LAUNCH_KEYS(PERV) \
-  hipLaunchKernelGGL((k_merge_keys<PERV>), dim3(M), dim3(kMergeThreads), 0, stream, cand, nk, k, ids, vals)
+  hipLaunchKernelGGL((k_merge_keys<PERV>), dim3(M, B), dim3(kMergeThreads), 0, stream, cand, nk, k, ids, vals, bs)
   if (per <= 1) NS_LAUNCH_KEYS(1);
   else if (per <= 2) NS_LAUNCH_KEYS(2);
   else if (per <= 4) NS_LAUNCH_KEYS(4);
@@ -478,42 +531,81 @@ bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
 
 extern "C" {
 
-// Workspace: partial sums [M x n_max x SP] float32 (SP = S rounded up to 4)
-// at offset 256.
-size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d) {
-  if (!draft_dims_ok(n_max, M, k, d)) return 0;
-  const int SP = (pick_splits(n_max, M, d, NS_BF16) + 3) & ~3;
+// Workspace: partial sums [B x M x n_max x SP] float32 (SP = S rounded up to
+// 4) at offset 256, then the chunk keys when n_max > 4096.
+size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M, int32_t k, int32_t d) {
+  if (B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return 0;
+  const int SP = (pick_splits(n_max, M, d, NS_BF16, B) + 3) & ~3;
   const int C = merge_chunks(n_max);
-  const size_t keys = C > 1 ? align256((size_t)M * C * k * sizeof(uint64_t)) : 0;
-  return 256 + partial_bytes(n_max, M, SP) + keys;
+  const size_t keys = C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0;
+  return 256 + partial_bytes(n_max, M, SP, B) + keys;
 }
+
+size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d) {
+  return nanospec_batch_draft_workspace_bytes(1, n_max, M, k, d);
+}
+
+}  // extern "C"
+
+namespace {
+
+int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
+               int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k, float* logits,
+               int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (mode != NS_PACKED && mode != NS_INDEXED) return NS_EDTYPE;
+  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (!rows || !h || !topk_ids || !topk_vals || !ws) return NS_EINVAL;
+  if (mode == NS_INDEXED && !row_ids) return NS_EINVAL;
+  if (V < 1 || B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
+  if ((((uintptr_t)rows) & 15u) || (((uintptr_t)h) & 15u) || (((uintptr_t)ws) & 255u)) return NS_EINVAL;
+  if (ws_bytes < nanospec_batch_draft_workspace_bytes(B, n_max, M, k, d)) return NS_ECAPACITY;
+  float* part = (float*)((char*)ws + 256);
+  (void)hipGetLastError();
+  const int S = pick_splits(n_max, M, d, dtype, B);
+  const int SP = (S + 3) & ~3;
+  const int esz = dtype == NS_BF16 ? 2 : 4;
+  const int C = merge_chunks(n_max);
+  BatchStrides bs;
+  bs.rows = 0;                                   // W_head (or one packed buffer) shared
+  bs.ids = (size_t)n_max;
+  bs.h = (size_t)M * d * esz / 16;
+  bs.part = partial_floats(n_max, M, SP);
+  bs.logits = (size_t)M * n_max;
+  bs.out = (size_t)M * k;
+  bs.cand = (size_t)M * C * k;
+  int rc;
+  if (dtype == NS_BF16) {
+    rc = launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, S, SP, part, B, bs, stream);
+  } else {
+    const int mt = pick_mt(M, d, 4);
+    if (mt == 0) return NS_EINVAL;
+    rc = launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, SP, part, B, bs, stream);
+  }
+  if (rc != NS_OK) return rc;
+  uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP, B));
+  return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, B, bs,
+                      stream);
+}
+
+}  // namespace
+
+extern "C" {
 
 int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
                                int32_t n_max, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
                                int32_t k, float* logits, int32_t* topk_ids, float* topk_vals, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
-  if (mode != NS_PACKED && mode != NS_INDEXED) return NS_EDTYPE;
-  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
-  if (!rows || !h || !topk_ids || !topk_vals || !ws) return NS_EINVAL;
-  if (mode == NS_INDEXED && !row_ids) return NS_EINVAL;
-  if (V < 1 || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
-  if ((((uintptr_t)rows) & 15u) || (((uintptr_t)h) & 15u) || (((uintptr_t)ws) & 255u)) return NS_EINVAL;
-  if (ws_bytes < nanospec_draft_workspace_bytes(n_max, M, k, d)) return NS_ECAPACITY;
-  float* part = (float*)((char*)ws + 256);
-  (void)hipGetLastError();
-  const int S = pick_splits(n_max, M, d, dtype);
-  const int SP = (S + 3) & ~3;
-  int rc;
-  if (dtype == NS_BF16) {
-    rc = launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, S, SP, part, stream);
-  } else {
-    const int mt = pick_mt(M, d, 4);
-    if (mt == 0) return NS_EINVAL;
-    rc = launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, SP, part, stream);
-  }
-  if (rc != NS_OK) return rc;
-  uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP));
-  return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, stream);
+  return draft_call(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
+                    ws_bytes, stream);
+}
+
+int nanospec_batch_draft_logits_topk(const void* w, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
+                                     int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
+                                     int32_t k, float* logits, int32_t* topk_ids, float* topk_vals, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!n_dev) return NS_EINVAL;
+  return draft_call(w, NS_INDEXED, row_ids, n_dev, n_max, B, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
+                    ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -235,11 +235,9 @@ __device__ __forceinline__ void bm_store8(uint32_t* __restrict__ dst, int w, int
 }
 
 template <typename T, int RU>
-__global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, const int32_t* draft_ids,
-                                                            int n_draft, const int32_t* ver_ids, int n_ver,
-                                                            int32_t* __restrict__ active_ids,
-                                                            int32_t* __restrict__ n_active,
-                                                            uint32_t* __restrict__ bitmap_out) {
+__device__ __forceinline__ void step_fast_body(const ns_state_view& v, const int32_t* draft_ids, int n_draft,
+                                               const int32_t* ver_ids, int n_ver, int32_t* __restrict__ active_ids,
+                                               int32_t* __restrict__ n_active, uint32_t* __restrict__ bitmap_out) {
   constexpr int EPT = (int)(sizeof(T) / 4);     // ring entries per load
   constexpr int NW = kFastThreads / NS_WAVE;
   extern __shared__ int4 lds4[];
@@ -403,6 +401,44 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, con
   }
 }
 
+template <typename T, int RU>
+__global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, const int32_t* draft_ids,
+                                                            int n_draft, const int32_t* ver_ids, int n_ver,
+                                                            int32_t* __restrict__ active_ids,
+                                                            int32_t* __restrict__ n_active,
+                                                            uint32_t* __restrict__ bitmap_out) {
+  step_fast_body<T, RU>(v, draft_ids, n_draft, ver_ids, n_ver, active_ids, n_active, bitmap_out);
+}
+
+// B sequences, one workgroup each: sequence b's state is sequence 0's moved
+// by b * stride bytes; its tuples start at b * {draft,ver}_stride and hold
+// n_draft[b] / n_ver[b] ids (device counts, clamped to [0, nd_max] /
+// [0, nv_max]); its outputs are the b-th W_max / 1 / ceil(V/32) blocks.
+template <typename T, int RU>
+__global__ __launch_bounds__(kFastThreads) void k_step_fast_batch(ns_state_view v0, size_t stride,
+                                                                  const int32_t* draft_ids, int draft_stride,
+                                                                  const int32_t* n_draft, int nd_max,
+                                                                  const int32_t* ver_ids, int ver_stride,
+                                                                  const int32_t* n_ver, int nv_max,
+                                                                  int32_t* __restrict__ active_ids,
+                                                                  int32_t* __restrict__ n_active,
+                                                                  uint32_t* __restrict__ bitmap_out) {
+  const int b = blockIdx.x;
+  const size_t off = (size_t)b * stride;
+  ns_state_view v = v0;
+  v.len = (int64_t*)((char*)v0.len + off);
+  v.status = (uint32_t*)((char*)v0.status + off);
+  v.ring = (int32_t*)((char*)v0.ring + off);
+  v.first = (int32_t*)((char*)v0.first + off);
+  v.bitmap = (uint32_t*)((char*)v0.bitmap + off);
+  const int nd = min(max(n_draft[b], 0), nd_max);
+  const int nv = min(max(n_ver[b], 0), nv_max);
+  const int words = (v0.V + 31) >> 5;
+  step_fast_body<T, RU>(v, draft_ids + (size_t)b * draft_stride, nd, ver_ids + (size_t)b * ver_stride, nv,
+                        active_ids + (size_t)b * v0.w_max, n_active + b,
+                        bitmap_out ? bitmap_out + (size_t)b * words : nullptr);
+}
+
 size_t fast_lds_bytes(int V, int n_draft) {
   return ((size_t)kFastThreads * fast_wpt(V) + 2 * (size_t)((n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1))) * 4;
 }
@@ -410,6 +446,27 @@ size_t fast_lds_bytes(int V, int n_draft) {
 typedef void (*step_fast_fn)(ns_state_view, const int32_t*, int, const int32_t*, int, int32_t*, int32_t*, uint32_t*);
 
 // Kernel instance holding ring entries of a w_max-slot ring in registers.
+typedef void (*step_fast_batch_fn)(ns_state_view, size_t, const int32_t*, int, const int32_t*, int, const int32_t*,
+                                   int, const int32_t*, int, int32_t*, int32_t*, uint32_t*);
+
+step_fast_batch_fn pick_step_fast_batch(int w_max) {
+  if (w_max > kFastMaxRing) return nullptr;
+  if ((w_max & 3) == 0) {
+    const int per = (w_max / 4 + kFastThreads - 1) / kFastThreads;
+    if (per <= 1) return k_step_fast_batch<int4, 1>;
+    if (per <= 2) return k_step_fast_batch<int4, 2>;
+    if (per <= 4) return k_step_fast_batch<int4, 4>;
+    return k_step_fast_batch<int4, 8>;
+  }
+  const int per = (w_max + kFastThreads - 1) / kFastThreads;
+  if (per <= 1) return k_step_fast_batch<int, 1>;
+  if (per <= 2) return k_step_fast_batch<int, 2>;
+  if (per <= 4) return k_step_fast_batch<int, 4>;
+  if (per <= 8) return k_step_fast_batch<int, 8>;
+  if (per <= 16) return k_step_fast_batch<int, 16>;
+  return k_step_fast_batch<int, 32>;
+}
+
 step_fast_fn pick_step_fast(int w_max) {
   if (w_max > kFastMaxRing) return nullptr;
   if ((w_max & 3) == 0) {
@@ -505,16 +562,13 @@ size_t nanospec_state_bytes(int32_t V, int32_t w_max) {
   return b;
 }
 
-int nanospec_state_create(nanospec_state** out, int32_t V, int32_t w_max, void* dev_mem, size_t dev_bytes,
-                          hipStream_t stream) {
-  if (!out || !dev_mem || !state_dims_ok(V, w_max)) return NS_EINVAL;
-  if (((uintptr_t)dev_mem & 255u) != 0) return NS_EINVAL;
-  size_t need = nanospec_state_bytes(V, w_max);
-  if (dev_bytes < need) return NS_ECAPACITY;
-  nanospec_state* st = new (std::nothrow) nanospec_state;
-  if (!st) return NS_EINVAL;
-  char* p = (char*)dev_mem;
-  ns_state_view& v = st->view;
+}  // extern "C"
+
+namespace {
+
+// Device pointers of a state laid out at p (256-byte aligned).
+ns_state_view make_view(char* p, int32_t V, int32_t w_max) {
+  ns_state_view v;
   v.len = (int64_t*)p;
   v.status = (uint32_t*)(p + 8);
   size_t off = 256;
@@ -525,19 +579,105 @@ int nanospec_state_create(nanospec_state** out, int32_t V, int32_t w_max, void* 
   v.bitmap = (uint32_t*)(p + off);
   v.V = V;
   v.w_max = w_max;
+  return v;
+}
+
+// Raises the dynamic-LDS limits of the state kernels for this V / W_max.
+int prepare_kernels(int32_t V, int32_t w_max) {
   int rc = set_lds_limit((const void*)k_active, lds_bitmap_bytes(V));
   if (rc == NS_OK) rc = set_lds_limit((const void*)k_step, lds_bitmap_bytes(V));
   const size_t fast_max = fast_lds_bytes(V, kFastMaxIds);
+  const size_t lim = fast_max < kFastLdsMax ? fast_max : kFastLdsMax;
   step_fast_fn fast_fn = pick_step_fast(w_max);
-  if (rc == NS_OK && fast_fn)
-    rc = set_lds_limit((const void*)fast_fn, fast_max < kFastLdsMax ? fast_max : kFastLdsMax);
-  if (rc != NS_OK) { delete st; return rc; }
+  if (rc == NS_OK && fast_fn) rc = set_lds_limit((const void*)fast_fn, lim);
+  step_fast_batch_fn batch_fn = pick_step_fast_batch(w_max);
+  if (rc == NS_OK && batch_fn) rc = set_lds_limit((const void*)batch_fn, lim);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nanospec_state_create(nanospec_state** out, int32_t V, int32_t w_max, void* dev_mem, size_t dev_bytes,
+                          hipStream_t stream) {
+  if (!out || !dev_mem || !state_dims_ok(V, w_max)) return NS_EINVAL;
+  if (((uintptr_t)dev_mem & 255u) != 0) return NS_EINVAL;
+  size_t need = nanospec_state_bytes(V, w_max);
+  if (dev_bytes < need) return NS_ECAPACITY;
+  int rc = prepare_kernels(V, w_max);
+  if (rc != NS_OK) return rc;
+  nanospec_state* st = new (std::nothrow) nanospec_state;
+  if (!st) return NS_EINVAL;
+  st->view = make_view((char*)dev_mem, V, w_max);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(k_init, dim3(fill_grid(v)), dim3(256), 0, stream, v);
+  hipLaunchKernelGGL(k_init, dim3(fill_grid(st->view)), dim3(256), 0, stream, st->view);
   rc = ns_launch_status();
   if (rc != NS_OK) { delete st; return rc; }
   *out = st;
   return NS_OK;
+}
+
+// ---- batches of independent sequences ------------------------------------
+
+size_t nanospec_batch_state_bytes(int32_t B, int32_t V, int32_t w_max) {
+  if (B < 1 || B > NS_MAX_BATCH) return 0;
+  const size_t one = nanospec_state_bytes(V, w_max);
+  return one * (size_t)B;
+}
+
+int nanospec_batch_create(nanospec_batch** out, int32_t B, int32_t V, int32_t w_max, void* dev_mem,
+                          size_t dev_bytes, hipStream_t stream) {
+  if (!out || !dev_mem || B < 1 || B > NS_MAX_BATCH || !state_dims_ok(V, w_max)) return NS_EINVAL;
+  if (((uintptr_t)dev_mem & 255u) != 0) return NS_EINVAL;
+  if (dev_bytes < nanospec_batch_state_bytes(B, V, w_max)) return NS_ECAPACITY;
+  int rc = prepare_kernels(V, w_max);
+  if (rc != NS_OK) return rc;
+  nanospec_batch* bt = new (std::nothrow) nanospec_batch;
+  if (!bt) return NS_EINVAL;
+  bt->members = new (std::nothrow) nanospec_state[B];
+  if (!bt->members) { delete bt; return NS_EINVAL; }
+  bt->B = B;
+  bt->stride = nanospec_state_bytes(V, w_max);
+  (void)hipGetLastError();
+  for (int b = 0; b < B; ++b) {
+    bt->members[b].view = make_view((char*)dev_mem + (size_t)b * bt->stride, V, w_max);
+    hipLaunchKernelGGL(k_init, dim3(fill_grid(bt->members[b].view)), dim3(256), 0, stream, bt->members[b].view);
+  }
+  rc = ns_launch_status();
+  if (rc != NS_OK) { delete[] bt->members; delete bt; return rc; }
+  *out = bt;
+  return NS_OK;
+}
+
+int nanospec_batch_destroy(nanospec_batch* bt) {
+  if (!bt) return NS_EINVAL;
+  delete[] bt->members;
+  delete bt;
+  return NS_OK;
+}
+
+int nanospec_batch_member(nanospec_batch* bt, int32_t b, nanospec_state** out) {
+  if (!bt || !out || b < 0 || b >= bt->B) return NS_EINVAL;
+  *out = &bt->members[b];
+  return NS_OK;
+}
+
+int nanospec_batch_step_update(nanospec_batch* bt, const int32_t* draft_ids, int32_t draft_stride,
+                               const int32_t* n_draft, int32_t nd_max, const int32_t* ver_ids, int32_t ver_stride,
+                               const int32_t* n_ver, int32_t nv_max, int32_t* active_ids, int32_t* n_active,
+                               uint32_t* bitmap, hipStream_t stream) {
+  if (!bt || !draft_ids || !ver_ids || !n_draft || !n_ver || !active_ids || !n_active) return NS_EINVAL;
+  if (nd_max < 0 || nv_max < 0 || nd_max > kFastMaxIds || nv_max > kFastMaxIds) return NS_EINVAL;
+  if (draft_stride < nd_max || ver_stride < nv_max) return NS_EINVAL;
+  const ns_state_view& v0 = bt->members[0].view;
+  step_fast_batch_fn fn = pick_step_fast_batch(v0.w_max);
+  const size_t lds = fast_lds_bytes(v0.V, nd_max);
+  if (!fn || lds > kFastLdsMax) return NS_EINVAL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(fn, dim3(bt->B), dim3(kFastThreads), lds, stream, v0, bt->stride, draft_ids, draft_stride, n_draft,
+                     nd_max, ver_ids, ver_stride, n_ver, nv_max, active_ids, n_active, bitmap);
+  return ns_launch_status();
 }
 
 int nanospec_state_reset(nanospec_state* st, hipStream_t stream) {

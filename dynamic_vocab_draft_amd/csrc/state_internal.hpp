@@ -16,3 +16,11 @@ struct ns_state_view {
 struct nanospec_state {
   ns_state_view view;
 };
+
+// B states laid out back to back at a fixed stride; members[b] is the
+// ordinary handle of sequence b.
+struct nanospec_batch {
+  int B;
+  size_t stride;
+  nanospec_state* members;
+};

@@ -28,6 +28,7 @@ NS_STATUS_BAD_ID = 0x1
 NS_MAX_M = NS_MAX_K = 64
 NS_MAX_V = NS_MAX_WMAX = 1 << 20
 NS_MAX_D = 16384
+NS_MAX_BATCH = 4096
 
 
 class NanoSpecError(RuntimeError):
@@ -78,6 +79,16 @@ _SIGS = {
     "nanospec_draft_logits_topk": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
                                                   c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "nanospec_prefill_topk": (ctypes.c_int, [c_vp, c_int32, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp]),
+    "nanospec_batch_state_bytes": (c_size, [c_int32, c_int32, c_int32]),
+    "nanospec_batch_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_int32, c_vp, c_size, c_vp]),
+    "nanospec_batch_destroy": (ctypes.c_int, [c_vp]),
+    "nanospec_batch_member": (ctypes.c_int, [c_vp, c_int32, ctypes.POINTER(c_vp)]),
+    "nanospec_batch_step_update": (ctypes.c_int, [c_vp, c_vp, c_int32, c_vp, c_int32, c_vp, c_int32, c_vp, c_int32,
+                                                  c_vp, c_vp, c_vp, c_vp]),
+    "nanospec_batch_draft_workspace_bytes": (c_size, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "nanospec_batch_draft_logits_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
+                                                        c_int32, c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp,
+                                                        c_size, c_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -219,6 +230,86 @@ def nanospec_prefill_topk(logits: torch.Tensor, L: int, V: int, dtype: int, k: i
                           out_vals: torch.Tensor, stream=None) -> None:
     _check(_lib.nanospec_prefill_topk(_ptr(logits), L, V, dtype, k, _ptr(out_ids), _ptr(out_vals),
                                       _stream(stream)), "nanospec_prefill_topk")
+
+
+# ---------------------------------------------------------------------------
+# Batches of independent sequences
+# ---------------------------------------------------------------------------
+
+
+def nanospec_batch_state_bytes(B: int, V: int, w_max: int) -> int:
+    return _lib.nanospec_batch_state_bytes(B, V, w_max)
+
+
+class _Member:
+    """A borrowed per-sequence handle of a batch (the batch owns it)."""
+
+    def __init__(self, handle, V, w_max):
+        self.handle, self.V, self.w_max = handle, V, w_max
+
+
+class NanoSpecBatch:
+    """B window states in one caller-owned device buffer."""
+
+    def __init__(self, B: int, V: int, w_max: int, device="cuda", stream=None):
+        nbytes = nanospec_batch_state_bytes(B, V, w_max)
+        if nbytes == 0:
+            raise NanoSpecError(NS_EINVAL, f"nanospec_batch_state_bytes(B={B}, V={V}, w_max={w_max})")
+        self.B, self.V, self.w_max = B, V, w_max
+        self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.mem.data_ptr()) % 256
+        self.buf = self.mem[off:off + nbytes]
+        h = ctypes.c_void_p()
+        _check(_lib.nanospec_batch_create(ctypes.byref(h), B, V, w_max, _ptr(self.buf), nbytes, _stream(stream)),
+               "nanospec_batch_create")
+        self.handle = h
+
+    def member(self, b: int) -> "_Member":
+        out = ctypes.c_void_p()
+        _check(_lib.nanospec_batch_member(self.handle, b, ctypes.byref(out)), "nanospec_batch_member")
+        return _Member(out, self.V, self.w_max)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _lib.nanospec_batch_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def nanospec_batch_step_update(bt: NanoSpecBatch, draft_ids: torch.Tensor, draft_stride: int, n_draft: torch.Tensor,
+                               nd_max: int, ver_ids: torch.Tensor, ver_stride: int, n_ver: torch.Tensor, nv_max: int,
+                               active_ids: torch.Tensor, n_active: torch.Tensor,
+                               bitmap: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(_lib.nanospec_batch_step_update(bt.handle, _ptr(draft_ids), draft_stride, _ptr(n_draft), nd_max,
+                                           _ptr(ver_ids), ver_stride, _ptr(n_ver), nv_max, _ptr(active_ids),
+                                           _ptr(n_active), _ptr(bitmap), _stream(stream)),
+           "nanospec_batch_step_update")
+
+
+def nanospec_batch_draft_workspace_bytes(B: int, n_max: int, M: int, k: int, d: int) -> int:
+    return _lib.nanospec_batch_draft_workspace_bytes(B, n_max, M, k, d)
+
+
+def nanospec_batch_draft_logits_topk(w: torch.Tensor, row_ids: torch.Tensor, n_dev: torch.Tensor, n_max: int,
+                                     B: int, V: int, d: int, dtype: int, h: torch.Tensor, M: int, k: int,
+                                     logits: Optional[torch.Tensor], topk_ids: torch.Tensor,
+                                     topk_vals: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_batch_draft_logits_topk(_ptr(w), _ptr(row_ids), _ptr(n_dev), n_max, B, V, d, dtype,
+                                                 _ptr(h), M, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_vals),
+                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nanospec_batch_draft_logits_topk")
+
+
+def alloc_batch_workspace(B: int, n_max: int, M: int, k: int, d: int, device="cuda") -> torch.Tensor:
+    """A 256-byte-aligned uint8 workspace of nanospec_batch_draft_workspace_bytes."""
+    nbytes = nanospec_batch_draft_workspace_bytes(B, n_max, M, k, d)
+    if nbytes == 0:
+        raise NanoSpecError(NS_EINVAL, "nanospec_batch_draft_workspace_bytes")
+    mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-mem.data_ptr()) % 256
+    return mem[off:off + nbytes]
 
 
 def alloc_workspace(n_max: int, M: int, k: int, d: int, device="cuda") -> torch.Tensor:

@@ -72,8 +72,10 @@ extern "C" {
 #define NS_MAX_V      1048576   /* vocabulary size (the bitmap is built in LDS) */
 #define NS_MAX_WMAX   1048576   /* sliding-window length */
 #define NS_MAX_D      16384     /* hidden size; d % 8 == 0 */
+#define NS_MAX_BATCH  4096      /* sequences in one batch */
 
 typedef struct nanospec_state nanospec_state;   /* opaque host handle */
+typedef struct nanospec_batch nanospec_batch;   /* opaque host handle of B states */
 
 /* Human-readable text for a return code (static storage, never NULL). */
 const char* nanospec_strerror(int code);
@@ -154,6 +156,41 @@ int nanospec_step_update(nanospec_state* st,
                          hipStream_t stream);
 
 /* ======================================================================
+ * Batches of independent sequences (data parallel over sequences).  Each
+ * sequence has its own window state, exactly as above; a batch lays B of them
+ * back to back in one caller-owned buffer so that one launch serves all B.
+ * nanospec_batch_member returns the ordinary handle of sequence b, which every
+ * single-sequence call above accepts (prompt appends, window, status, reset).
+ *   nanospec_batch_state_bytes : B * nanospec_state_bytes(V, w_max) (0 if B
+ *             is not in [1, NS_MAX_BATCH] or the dims are invalid).
+ *   nanospec_batch_create      : as nanospec_state_create for all B members.
+ *   nanospec_batch_step_update : nanospec_step_update for every sequence b,
+ *             one workgroup per sequence:
+ *               draft_ids + b * draft_stride : C_draft ids of sequence b,
+ *                   n_draft[b] of them (device int32 [B], clamped to
+ *                   [0, nd_max]); the same for ver_ids / ver_stride / n_ver.
+ *                   draft_ids and ver_ids must point to readable memory even
+ *                   when a count is 0.
+ *               active_ids [B x w_max], n_active [B], bitmap [B x ceil(V/32)]
+ *                   or NULL: sequence b's outputs are the b-th blocks.
+ *             Limits: nd_max, nv_max <= 512, w_max <= 16384 and the bitmap
+ *             in LDS (V <= about 1.1M); NS_EINVAL otherwise (use the
+ *             single-sequence call per member).
+ * Errors: NS_EINVAL, NS_ECAPACITY, NS_EHIP. */
+size_t nanospec_batch_state_bytes(int32_t B, int32_t V, int32_t w_max);
+int nanospec_batch_create(nanospec_batch** out, int32_t B, int32_t V, int32_t w_max,
+                          void* dev_mem, size_t dev_bytes, hipStream_t stream);
+int nanospec_batch_destroy(nanospec_batch* bt);
+int nanospec_batch_member(nanospec_batch* bt, int32_t b, nanospec_state** out);
+int nanospec_batch_step_update(nanospec_batch* bt,
+                               const int32_t* draft_ids, int32_t draft_stride,
+                               const int32_t* n_draft, int32_t nd_max,
+                               const int32_t* ver_ids, int32_t ver_stride,
+                               const int32_t* n_ver, int32_t nv_max,
+                               int32_t* active_ids, int32_t* n_active, uint32_t* bitmap,
+                               hipStream_t stream);
+
+/* ======================================================================
  * Row gather ("pack").  NanoSpec "Avoiding Sparse Computation via
  * Asynchronous Gathering": out[j, :] = w[ids[j], :] for j < n, a bit copy.
  *   w     : W_head, [V x d] row-major, elements of `dtype`, 16-byte aligned.
@@ -203,6 +240,28 @@ int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* ro
                                int32_t k, float* logits, int32_t* topk_ids,
                                float* topk_vals, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* ======================================================================
+ * The draft head for a batch of B independent sequences sharing W_head, in
+ * NS_INDEXED mode: for every b, the result of nanospec_draft_logits_topk on
+ * sequence b's inputs.  One pair of launches serves all B sequences, so a
+ * call moves B times the bytes of a single-sequence call for the same launch
+ * and round-trip latency.
+ *   w        : W_head [V x d], shared.
+ *   row_ids  : [B x n_max] (sequence b's active ids in row b), holes skipped.
+ *   n_dev    : [B] device counts (required), each clamped to n_max.
+ *   h        : [B x M x d]; logits : [B x M x n_max] or NULL;
+ *   topk_ids, topk_vals : [B x M x k].
+ *   ws       : >= nanospec_batch_draft_workspace_bytes(B, n_max, M, k, d)
+ *              bytes, 256-byte aligned, no initialisation needed.
+ * B in [1, NS_MAX_BATCH]; other limits and errors as for
+ * nanospec_draft_logits_topk (NS_EINVAL also for n_dev == NULL). */
+size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M, int32_t k, int32_t d);
+int nanospec_batch_draft_logits_topk(const void* w, const int32_t* row_ids, const int32_t* n_dev,
+                                     int32_t n_max, int32_t B, int32_t V, int32_t d, int32_t dtype,
+                                     const void* h, int32_t M, int32_t k, float* logits,
+                                     int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /* ======================================================================
  * Prefill candidates.  Sec. 3.2 prefill: P[i] = T_Kpre(z_i) for every prompt

@@ -56,6 +56,14 @@ def test_codes_and_sizes(ns):
     assert L.nanospec_draft_workspace_bytes(3072, 65, 8, 4096) == 0
     assert L.nanospec_draft_workspace_bytes(3072, 8, 65, 4096) == 0
     assert L.nanospec_draft_workspace_bytes(3072, 8, 8, 4100) == 0      # d % 8 != 0
+    # batches: B copies of one state; the batched workspace grows with B
+    assert L.nanospec_batch_state_bytes(8, 128256, 3072) == 8 * b
+    assert L.nanospec_batch_state_bytes(0, 128256, 3072) == 0
+    assert L.nanospec_batch_state_bytes(ns.NS_MAX_BATCH + 1, 128256, 3072) == 0
+    w1 = L.nanospec_batch_draft_workspace_bytes(1, 3072, 8, 8, 4096)
+    assert w1 == L.nanospec_draft_workspace_bytes(3072, 8, 8, 4096)
+    assert L.nanospec_batch_draft_workspace_bytes(8, 3072, 8, 8, 4096) >= 8 * 3072 * 8 * 4
+    assert L.nanospec_batch_draft_workspace_bytes(0, 3072, 8, 8, 4096) == 0
 
 
 def test_host_validation_rejects_before_launch(ns):
@@ -95,6 +103,18 @@ def test_host_validation_rejects_before_launch(ns):
     assert call(h=None) == ns.NS_EINVAL
     assert call(ws_bytes=64) == ns.NS_ECAPACITY
     assert call(ws=ctypes.c_void_p(0x1010)) == ns.NS_EINVAL
+    # batches
+    assert L.nanospec_batch_create(None, 2, 10, 4, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_batch_create(ctypes.byref(h), 0, 10, 4, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_batch_create(ctypes.byref(h), 2, 10, 4, fake, 16, None) == ns.NS_ECAPACITY
+    assert L.nanospec_batch_destroy(None) == ns.NS_EINVAL
+    assert L.nanospec_batch_member(None, 0, ctypes.byref(h)) == ns.NS_EINVAL
+    assert L.nanospec_batch_step_update(None, fake, 8, fake, 8, fake, 8, fake, 8, fake, fake, None,
+                                        None) == ns.NS_EINVAL
+    assert L.nanospec_batch_draft_logits_topk(fake, fake, None, 16, 2, 100, 64, 0, fake, 8, 8, None, fake, fake,
+                                              fake, 1 << 20, None) == ns.NS_EINVAL       # n_dev required
+    assert L.nanospec_batch_draft_logits_topk(fake, fake, fake, 16, 0, 100, 64, 0, fake, 8, 8, None, fake, fake,
+                                              fake, 1 << 20, None) == ns.NS_EINVAL       # B = 0
     # prefill
     assert L.nanospec_prefill_topk(fake, 4, 10, 0, 0, fake, fake, None) == ns.NS_EINVAL
     assert L.nanospec_prefill_topk(fake, 4, 10, 0, 11, fake, fake, None) == ns.NS_EINVAL
