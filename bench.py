@@ -51,7 +51,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--no-extras", action="store_true", help="skip the prefill and overlap legs")
+    p.add_argument("--no-extras", action="store_true", help="skip the prefill, overlap and batch legs")
+    p.add_argument("--batches", default="1,8,32", help="sequence counts of the batched leg")
     p.add_argument("--sweep", action="store_true",
                    help="only sweep the draft head over |I| x M (cold) and print one JSON line per point")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -255,6 +256,8 @@ def main():
         progress("gather / backbone overlap leg")
         out["overlap"] = overlap_leg(torch, ns, cfg, W, ids, n_act, packed, hs[Wm], ws, dcode, copy_stream,
                                      flush_fn)
+        progress("batched-sequences leg")
+        out["batched"] = batch_leg(torch, ns, WL, cfg, W, dcode, flush_fn, [int(x) for x in args.batches.split(",")])
     if not args.no_dense:
         out["dense"] = dense_compare(torch, ns, cfg, W, hs[Wm], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
     if not args.no_cpu_baseline:
@@ -439,6 +442,101 @@ def overlap_leg(torch, ns, cfg, W, ids, n_act, packed, h, ws, dcode, copy_stream
             "T_serial_ms": r["serial"], "T_overlap_ms": r["overlap"], "T_forkjoin_no_gather_ms": r["forkjoin"],
             "hidden_fraction": (r["serial"] - r["overlap"]) / r["gather"] if r["gather"] > 0 else None,
             "note": "cold, hipGraph replay of 20 repetitions per variant, cache-streaming read subtracted"}
+
+
+def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
+    """B independent sequences of the same workload (seeds differ), one
+    batched step update and one batched draft head (INDEXED) per step, cold,
+    graph replay; the step-update-only graph is subtracted for the draft
+    time.  Algorithmic bytes of a batched draft call: the sum over sequences
+    of n_b*d*s + M*d*s + 4*n_b + 8*M*k."""
+    res = []
+    s = cfg.elem_bytes
+    for B in Bs:
+        cfgs = [WL.get_config(cfg.name, seed=cfg.seed + 1000 * (b + 1)) for b in range(B)]
+        T = warm + steps
+        scripts = [WL.make_id_script(c, steps=T) for c in cfgs]
+        nd = cfg.n_tree
+        nv = cfg.k_ver
+        trees = torch.as_tensor(np.stack([np.stack(sc.tree) for sc in scripts], 1), dtype=torch.int32).cuda()
+        vers = torch.as_tensor(np.stack([np.stack(sc.ver) for sc in scripts], 1), dtype=torch.int32).cuda()
+        n_d = torch.full((B,), nd, dtype=torch.int32, device="cuda")
+        n_v = torch.full((B,), nv, dtype=torch.int32, device="cuda")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(cfg.seed + 5)
+        hs = (torch.randn((T, B, cfg.M, cfg.d), generator=g, device="cuda")).to(W.dtype)
+        bt = ns.NanoSpecBatch(B, cfg.V, cfg.w_max)
+        ids = torch.empty((B, cfg.w_max), dtype=torch.int32, device="cuda")
+        n = torch.zeros(B, dtype=torch.int32, device="cuda")
+        wsb = ns.alloc_batch_workspace(B, cfg.w_max, cfg.M, cfg.k, cfg.d)
+        tids = torch.empty((B, cfg.M, cfg.k), dtype=torch.int32, device="cuda")
+        tvals = torch.empty((B, cfg.M, cfg.k), device="cuda")
+        prompts = [torch.as_tensor(sc.prompt, dtype=torch.int32).cuda() for sc in scripts]
+
+        def init():
+            for b in range(B):
+                m = bt.member(b)
+                ns.nanospec_state_reset(m)
+                ns.nanospec_stream_append(m, prompts[b], prompts[b].numel(), 0)
+            for t in range(warm):
+                ns.nanospec_batch_step_update(bt, trees[t], nd, n_d, nd, vers[t], nv, n_v, nv, ids, n)
+
+        sizes = []
+
+        def body(with_draft, record=False):
+            def run():
+                for t in range(warm, T):
+                    flush(t)
+                    ns.nanospec_batch_step_update(bt, trees[t], nd, n_d, nd, vers[t], nv, n_v, nv, ids, n)
+                    if record:
+                        sizes.append(n.clone())
+                    if with_draft:
+                        ns.nanospec_batch_draft_logits_topk(W, ids, n, cfg.w_max, B, cfg.V, cfg.d, dcode, hs[t],
+                                                            cfg.M, cfg.k, None, tids, tvals, wsb)
+            return run
+
+        init()
+        body(False, record=True)()                       # eager pass: |I| per sequence and step
+        torch.cuda.synchronize()
+        n_mean = float(torch.stack(sizes).float().mean().item())
+
+        def timed(fn):
+            init()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn()
+            ts = []
+            for _ in range(3):
+                init()
+                torch.cuda.synchronize()
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                gr.replay()
+                b_.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b_))
+            del gr
+            return float(np.median(ts))
+
+        def flush_only():
+            for t in range(warm, T):
+                flush(t)
+
+        t_f = timed(flush_only)
+        t_s = timed(body(False))
+        t_a = timed(body(True))
+        step_us = (t_a - t_f) / steps * 1e3
+        draft_us = (t_a - t_s) / steps * 1e3
+        draft_bytes = B * (n_mean * cfg.d * s + cfg.M * cfg.d * s + 4 * n_mean + 8 * cfg.M * cfg.k)
+        res.append({"B": B, "step_us": step_us, "sequence_steps_per_s": B / (step_us * 1e-6),
+                    "state_update_us": (t_s - t_f) / steps * 1e3, "draft_us": draft_us,
+                    "draft_GBps": draft_bytes / (draft_us * 1e-6) / 1e9,
+                    "draft_frac_of_peak": draft_bytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "mean_active": n_mean})
+        del bt, hs, wsb
+    return {"workload": f"{cfg.name} x B independent sequences (seeds differ), batched step update + batched "
+                        f"INDEXED draft head, cold, hipGraph replay of {steps} steps", "per_B": res}
 
 
 def sweep(torch, ns, WL, args):
