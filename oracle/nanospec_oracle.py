@@ -21,6 +21,8 @@ involved.  Sources (cited by page title and section/equation):
   I_{t+1} = Unique(Suffix(S_new, W_max)).
 * NanoSpec, "Eliminating Overhead via GPU-Resident State Management": the
   active set is held as a bitmap.
+* NanoSpec, "Avoiding Sparse Computation via Asynchronous Gathering": a
+  preallocated buffer of W_max rows receives only the rows of newly active ids.
 
 Readings taken where the pages leave a step open (each also listed in the
 design notes):
@@ -35,6 +37,9 @@ design notes):
 * R4 ``Unique`` returns ascending ids; ties in T_K go to the lower index
   (for the draft head: the lower *global* id).
 * R5 k larger than the candidate count pads with (id -1, value -inf).
+* R6 slot-stable packing (see packed_update): rows keep their slot while
+  their id stays active; entering ids fill the lowest free slots in ascending
+  id order; slots of ids that left are holes.
 
 Parity pins for every function live in ``tests/test_oracle_pins.py``.
 """
@@ -218,6 +223,56 @@ def draft_head(h: np.ndarray, W: np.ndarray, I: np.ndarray, k: int, dtype: str):
     logits = project(h, gather_rows(W, I), dtype)
     ids, vals = draft_topk(logits, I, k)
     return logits, ids, vals
+
+
+# ---------------------------------------------------------------------------
+# Slot-stable packed buffer
+# ---------------------------------------------------------------------------
+#
+# NanoSpec, "Avoiding Sparse Computation via Asynchronous Gathering": a
+# preallocated buffer of W_max rows holds W_head[I_t, :]; at each step only the
+# rows of ids that became active are gathered into it.  The pages fix neither
+# where an entering row goes nor what happens to the rows of ids that left.
+# Reading R6: a row stays in its slot for as long as its id stays active; the
+# slots of ids that left become holes (id -1); the ids that entered, taken in
+# ascending id order, fill the free slots in ascending slot order; the head
+# reads slots [0, n_slots), n_slots = 1 + the highest occupied slot (0 when
+# none), and skips holes.
+
+
+def packed_update(slot_ids: np.ndarray, I: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray, int]:
+    """One update of the slot map to a new active set I.
+
+    slot_ids: int [n_slot_cap], the global id held in each slot, -1 for a
+    hole.  Returns (new slot ids, entering slots, entering ids, n_slots); the
+    entering lists are in ascending id order and are the rows to gather."""
+    old = np.asarray(slot_ids, dtype=np.int64)
+    active = set(int(x) for x in np.asarray(I).reshape(-1))
+    new = old.copy()
+    for s in range(len(new)):                      # ids that left free their slot
+        if new[s] >= 0 and int(new[s]) not in active:
+            new[s] = -1
+    held = set(int(x) for x in new if x >= 0)
+    entering = sorted(active - held)
+    free = [s for s in range(len(new)) if new[s] < 0]
+    if len(entering) > len(free):
+        raise ValueError("active set larger than the buffer")
+    slots = np.array(free[:len(entering)], dtype=np.int64)
+    new[slots] = np.array(entering, dtype=np.int64)
+    occupied = [s for s in range(len(new)) if new[s] >= 0]
+    n_slots = occupied[-1] + 1 if occupied else 0
+    return new, slots, np.array(entering, dtype=np.int64), n_slots
+
+
+def packed_draft_head(h: np.ndarray, W: np.ndarray, slot_ids: np.ndarray, n_slots: int, k: int,
+                      dtype: str):
+    """The draft head over the packed buffer: column j of slots [0, n_slots) is
+    W[slot_ids[j]]; holes are not candidates.  Returns (ids, vals) as
+    draft_topk."""
+    ids = np.asarray(slot_ids, dtype=np.int64)[:n_slots]
+    live = ids[ids >= 0]
+    logits = project(h, gather_rows(W, live), dtype)
+    return draft_topk(logits, live, k)
 
 
 # ---------------------------------------------------------------------------

@@ -119,6 +119,49 @@ def _gather_transposed_index(W, I):
     return np.asarray(W)[np.asarray(I)[::-1]]
 
 
+def _packed_generic(slot_ids, I, *, order=sorted, pick_free=lambda f: f, free_leaving=True,
+                    keep_slots=True, count_slots=False):
+    old = np.asarray(slot_ids, dtype=np.int64)
+    act = set(int(x) for x in np.asarray(I).reshape(-1))
+    new = old.copy()
+    if not keep_slots:
+        new[:] = -1
+    elif free_leaving:
+        new[[s for s in range(len(new)) if new[s] >= 0 and int(new[s]) not in act]] = -1
+    held = set(int(x) for x in new if x >= 0)
+    ent = order(act - held)
+    free = pick_free([s for s in range(len(new)) if new[s] < 0])[:len(ent)]
+    new[free] = ent
+    occ = [s for s in range(len(new)) if new[s] >= 0]
+    n = len(occ) if count_slots else (occ[-1] + 1 if occ else 0)
+    return new, np.array(free, dtype=np.int64), np.array(ent, dtype=np.int64), n
+
+
+def _packed_highest_free(slot_ids, I):
+    return _packed_generic(slot_ids, I, pick_free=lambda f: f[::-1])
+
+
+def _packed_descending(slot_ids, I):
+    return _packed_generic(slot_ids, I, order=lambda x: sorted(x, reverse=True))
+
+
+def _packed_repack(slot_ids, I):
+    return _packed_generic(slot_ids, I, keep_slots=False)
+
+
+def _packed_keep_leaving(slot_ids, I):
+    return _packed_generic(slot_ids, I, free_leaving=False)
+
+
+def _packed_count_slots(slot_ids, I):
+    return _packed_generic(slot_ids, I, count_slots=True)
+
+
+def _packed_head_with_holes(h, W, slot_ids, n_slots, k, dtype):
+    ids = np.asarray(slot_ids, dtype=np.int64)[:n_slots]
+    return O.draft_topk(O.project(h, O.gather_rows(W, ids), dtype), ids, k)
+
+
 MUTATIONS = [
     ("top_k", _topk_tie_desc),
     ("top_k", _topk_ascending),
@@ -137,6 +180,12 @@ MUTATIONS = [
     ("init_stream", _init_stream_sorted_union),
     ("init_stream", _init_stream_rank_major),
     ("gather_rows", _gather_transposed_index),
+    ("packed_update", _packed_highest_free),
+    ("packed_update", _packed_descending),
+    ("packed_update", _packed_repack),
+    ("packed_update", _packed_keep_leaving),
+    ("packed_update", _packed_count_slots),
+    ("packed_draft_head", _packed_head_with_holes),
 ]
 
 

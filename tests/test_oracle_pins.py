@@ -246,10 +246,80 @@ def pin_draft_topk_global_ids(o):
     assert ids.tolist() == [[7, 9, 3]] and vals.tolist() == [[2.0, 2.0, 1.0]]
 
 
+GOLDEN_PACKED = os.path.join(os.path.dirname(__file__), "golden", "packed_slots.json")
+
+
+def pin_packed_worked_example(o):
+    """The hand-worked slot placements of tests/golden/packed_slots.json."""
+    with open(GOLDEN_PACKED) as f:
+        g = json.load(f)
+    slots = np.full(g["capacity"], -1, dtype=np.int64)
+    for st in g["steps"]:
+        slots, es, ei, n = o.packed_update(slots, np.array(st["I"], dtype=np.int64))
+        assert slots.tolist() == st["slot_ids"], st["why"]
+        assert list(es) == st["enter_slots"] and list(ei) == st["enter_ids"], st["why"]
+        assert n == st["n_slots"], st["why"]
+
+
+def pin_packed_invariants(o):
+    """Random churn on a small vocabulary, checked against properties the
+    placement rule implies on its own: the held ids are exactly I, an id that
+    stays keeps its slot, the entering list is I minus what was held (ascending)
+    and is what the update wrote, and every occupied slot lies below the largest
+    |I| seen so far (entering ids take the lowest free slots, so the r-th of
+    them lands below the count of ids held afterwards)."""
+    rng = np.random.default_rng(23)
+    V, cap = 60, 24
+    slots = np.full(cap, -1, dtype=np.int64)
+    peak = 0
+    prev = {}
+    for _ in range(300):
+        n = int(rng.integers(0, cap + 1))
+        I = np.sort(rng.choice(V, size=n, replace=False)) if rng.random() < 0.3 or not prev else \
+            np.sort(np.array(list(set(rng.choice(list(prev), size=min(len(prev), max(0, n - 4)),
+                                                    replace=False).tolist())
+                                  | set(rng.choice(V, size=4, replace=False).tolist())))[:cap])
+        new, es, ei, n_slots = o.packed_update(slots, I)
+        held = {int(x): s for s, x in enumerate(new) if x >= 0}
+        assert sorted(held) == I.tolist() and len(held) == int(np.sum(new >= 0))
+        for x, s in prev.items():
+            if x in held:
+                assert held[x] == s
+        assert list(ei) == sorted(set(I.tolist()) - set(prev)), "entering ids"
+        assert all(new[s] == x for s, x in zip(es, ei))
+        assert all(s < len(I) for s in es)
+        peak = max(peak, len(I))
+        assert all(s < peak for s in held.values())
+        assert n_slots == (max(held.values()) + 1 if held else 0)
+        slots, prev = new, held
+
+
+def pin_packed_head(o):
+    """The head over a slot map with holes equals the brute-force top-k of the
+    dense logits restricted to the held ids, whatever their slots."""
+    rng = np.random.default_rng(29)
+    V, d, M, k = 70, 24, 3, 6
+    W = rng.standard_normal((V, d)).astype(np.float32)
+    h = rng.standard_normal((M, d)).astype(np.float32)
+    dense = h.astype(np.float64) @ W.astype(np.float64).T
+    slot_ids = np.full(40, -1, dtype=np.int64)
+    held = rng.choice(V, size=25, replace=False)
+    slot_ids[rng.choice(40, size=25, replace=False)] = held
+    n_slots = int(np.flatnonzero(slot_ids >= 0).max()) + 1
+    ids, vals = o.packed_draft_head(h, W, slot_ids, n_slots, k, "fp32")
+    for m in range(M):
+        col = np.full(V, -np.inf)
+        col[held] = dense[m, held]
+        ref = _rank_topk(col.tolist(), k)
+        assert ids[m].tolist() == ref
+        np.testing.assert_allclose(vals[m], dense[m, ref], rtol=0, atol=1e-9)
+
+
 PINS = [pin_worked_example, pin_widen_bf16, pin_topk_bruteforce, pin_topk_library_cases,
         pin_prefill_planted, pin_first_occurrence, pin_stream_update,
         pin_active_set_bruteforce, pin_active_full_coverage, pin_bitmap_tail,
-        pin_projection_exact, pin_gather, pin_subset_equals_dense, pin_draft_topk_global_ids]
+        pin_projection_exact, pin_gather, pin_subset_equals_dense, pin_draft_topk_global_ids,
+        pin_packed_worked_example, pin_packed_invariants, pin_packed_head]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
