@@ -6,6 +6,7 @@ hidden rows, top-8, 60 raw draft-tree ids + 8 verify ids appended per step):
 
   nanospec_step_update        append C_draft (dedup) and C_ver, rebuild I
   nanospec_gather_rows        PACKED mode only, on a second stream
+  nanospec_packed_update      SLOTS mode only: slot-stable buffer, entering rows
   nanospec_draft_logits_topk  projection on W_head[I,:], top-k, map back
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
@@ -46,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--config", default="llama3_8b")
-    p.add_argument("--mode", choices=["auto", "packed", "indexed"], default="auto")
+    p.add_argument("--mode", choices=["auto", "packed", "indexed", "slots"], default="auto")
     p.add_argument("--reps", type=int, default=5, help="graph replays per measurement (median)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
@@ -103,6 +104,9 @@ def main():
     ids = torch.empty(cfg.w_max, dtype=torch.int32, device="cuda")
     n_act = torch.zeros(1, dtype=torch.int32, device="cuda")
     packed = torch.zeros((cfg.w_max, cfg.d), dtype=tdt, device="cuda")
+    pk = ns.NanoSpecPacked(cfg.V, cfg.w_max)
+    slot_rows = torch.zeros((cfg.w_max, cfg.d), dtype=tdt, device="cuda")
+    SLOTS = "slots"
     ws = ns.alloc_workspace(cfg.w_max, cfg.M, cfg.k, cfg.d)
     tids = torch.empty((T, cfg.M, cfg.k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((T, cfg.M, cfg.k), dtype=torch.float32, device="cuda")
@@ -116,20 +120,33 @@ def main():
         ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
         ns.nanospec_active_vocab(st, ids, n_act)
 
-    # |I| per step from an untimed pass of the state update alone.
-    init_state()
-    sizes = []
-    for t in range(T):
-        ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n_act)
-        sizes.append(int(n_act.item()))
-    sizes = np.array(sizes)
+    def pack_update(stream=None):
+        ns.nanospec_packed_update(pk, st, W, cfg.d, dcode, slot_rows, stream=stream)
 
     def state_part(t):
         ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n_act)
 
+    # |I|, entering rows and slots in use per step, from an untimed pass.
+    init_state()
+    ns.nanospec_packed_reset(pk)
+    pack_update()
+    sizes, enters, n_slots = [], [], []
+    for t in range(T):
+        state_part(t)
+        pack_update()
+        sizes.append(int(n_act.item()))
+        enters.append(int(pk.n_enter.item()))
+        n_slots.append(int(pk.n_slots.item()))
+    sizes = np.array(sizes)
+
     def draft_part(t, mode):
         comp = torch.cuda.current_stream()
         rows = W
+        if mode == SLOTS:
+            pack_update()
+            ns.nanospec_draft_logits_topk(slot_rows, ns.NS_PACKED, pk.slot_ids, pk.n_slots, cfg.w_max, cfg.V, cfg.d,
+                                          dcode, hs[t], cfg.M, cfg.k, None, tids[t], tvals[t], ws)
+            return
         if mode == ns.NS_PACKED:
             copy_stream.wait_stream(comp)
             ns.nanospec_gather_rows(W, cfg.V, cfg.d, dcode, ids, n_act, cfg.w_max, packed, stream=copy_stream)
@@ -149,13 +166,18 @@ def main():
                     draft_part(t, mode)
         return run
 
-    def warm_up_state():
+    def warm_up_state(mode=None):
         init_state()
+        if mode == SLOTS:
+            ns.nanospec_packed_reset(pk)
+            pack_update()
         for t in range(Wm):
             state_part(t)
+            if mode == SLOTS:
+                pack_update()
 
-    def capture(fn):
-        warm_up_state()
+    def capture(fn, mode=None):
+        warm_up_state(mode)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -163,11 +185,11 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def time_graph(g, needs_state=True):
+    def time_graph(g, needs_state=True, mode=None):
         ts = []
         for _ in range(args.reps):
             if needs_state:
-                warm_up_state()
+                warm_up_state(mode)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -177,35 +199,36 @@ def main():
             ts.append(a.elapsed_time(b))
         return float(np.median(ts))
 
-    def time_eager(fn):
-        warm_up_state()
+    def time_eager(fn, mode=None):
+        warm_up_state(mode)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         fn()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3
 
-    modes = {"packed": [ns.NS_PACKED], "indexed": [ns.NS_INDEXED], "auto": [ns.NS_PACKED, ns.NS_INDEXED]}[args.mode]
-    mname = {ns.NS_PACKED: "packed", ns.NS_INDEXED: "indexed"}
+    modes = {"packed": [ns.NS_PACKED], "indexed": [ns.NS_INDEXED], "slots": [SLOTS],
+             "auto": [ns.NS_PACKED, ns.NS_INDEXED, SLOTS]}[args.mode]
+    mname = {ns.NS_PACKED: "packed", ns.NS_INDEXED: "indexed", SLOTS: "slots"}
     g_flush = capture(body(None, True, False, False))
     t_flush = time_graph(g_flush, needs_state=False)
 
     res = {}
     for m in modes:
         # eager reference outputs for the replay check
-        time_eager(body(m, False))
+        time_eager(body(m, False), m)
         ref_ids, ref_vals = tids.clone(), tvals.clone()
         tids.fill_(-7)
-        g_cold = capture(body(m, True))
-        g_warm = capture(body(m, False))
-        g_state = capture(body(m, True, True, False))
-        t_cold = time_graph(g_cold)
+        g_cold = capture(body(m, True), m)
+        g_warm = capture(body(m, False), m)
+        g_state = capture(body(m, True, True, False), m)
+        t_cold = time_graph(g_cold, mode=m)
         ok = bool(torch.equal(tids[Wm:], ref_ids[Wm:]) and torch.equal(tvals[Wm:], ref_vals[Wm:]))
-        t_warm = time_graph(g_warm)
-        t_state = time_graph(g_state)
+        t_warm = time_graph(g_warm, mode=m)
+        t_state = time_graph(g_state, mode=m)
         res[m] = dict(cold_ms=(t_cold - t_flush) / K, warm_ms=t_warm / K,
                       draft_ms=(t_cold - t_state) / K, state_ms=(t_state - t_flush) / K,
-                      eager_warm_ms=time_eager(body(m, False)) / K, replay_matches_eager=ok)
+                      eager_warm_ms=time_eager(body(m, False), m) / K, replay_matches_eager=ok)
         del g_cold, g_warm, g_state
         progress(f"mode {mname[m]}: {res[m]['cold_ms'] * 1e3:.2f} us/step cold")
     best = min(modes, key=lambda m: res[m]["cold_ms"])
@@ -246,7 +269,11 @@ def main():
                  "warm_ms": r["warm_ms"], "eager_warm_ms": r["eager_warm_ms"],
                  "per_mode": {mname[m]: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res[m].items()}
                               for m in modes},
-                 "flush_ms": t_flush / K},
+                 "flush_ms": t_flush / K,
+                 "slots": {"mean_entering_rows": float(np.mean(enters[Wm:])),
+                           "mean_slots_in_use": float(np.mean(n_slots[Wm:])),
+                           "gather_bytes_per_step": float(np.mean(enters[Wm:])) * 2 * cfg.d * s,
+                           "full_gather_bytes_per_step": n_mean * 2 * cfg.d * s}},
         "cpu_baseline": None,
     }
     if not args.no_extras:
@@ -256,6 +283,49 @@ def main():
         progress("gather / backbone overlap leg")
         out["overlap"] = overlap_leg(torch, ns, cfg, W, ids, n_act, packed, hs[Wm], ws, dcode, copy_stream,
                                      flush_fn)
+        progress("decode pipeline leg")
+        backbone = make_backbone(torch, cfg)
+
+        class Head:
+            def __init__(self, mode, fn):
+                self.mode, self.fn = mode, fn
+
+            def __call__(self, t, comp, copy):
+                self.fn(t, comp, copy)
+
+        def head_indexed(t, comp, copy):
+            backbone()
+            ns.nanospec_draft_logits_topk(W, ns.NS_INDEXED, ids, n_act, cfg.w_max, cfg.V, cfg.d, dcode, hs[t],
+                                          cfg.M, cfg.k, None, tids[t], tvals[t], ws)
+
+        def head_slots(overlap):
+            def f(t, comp, copy):
+                if overlap:
+                    copy.wait_stream(comp)
+                    pack_update(copy)
+                    backbone()
+                    comp.wait_stream(copy)
+                else:
+                    backbone()
+                    pack_update()
+                ns.nanospec_draft_logits_topk(slot_rows, ns.NS_PACKED, pk.slot_ids, pk.n_slots, cfg.w_max, cfg.V,
+                                              cfg.d, dcode, hs[t], cfg.M, cfg.k, None, tids[t], tvals[t], ws)
+            return f
+
+        def head_full_gather(t, comp, copy):
+            copy.wait_stream(comp)
+            ns.nanospec_gather_rows(W, cfg.V, cfg.d, dcode, ids, n_act, cfg.w_max, packed, stream=copy)
+            backbone()
+            comp.wait_stream(copy)
+            ns.nanospec_draft_logits_topk(packed, ns.NS_PACKED, ids, n_act, cfg.w_max, cfg.V, cfg.d, dcode, hs[t],
+                                          cfg.M, cfg.k, None, tids[t], tvals[t], ws)
+
+        heads = {"indexed": Head(ns.NS_INDEXED, head_indexed),
+                 "slots_serial": Head(SLOTS, head_slots(False)),
+                 "slots_overlap": Head(SLOTS, head_slots(True)),
+                 "full_gather_overlap": Head(ns.NS_PACKED, head_full_gather)}
+        out["pipeline"] = pipeline_leg(torch, cfg, backbone, warm_up_state, state_part, heads, flush_fn, Wm,
+                                       min(K, 40), copy_stream)
         progress("batched-sequences leg")
         out["batched"] = batch_leg(torch, ns, WL, cfg, W, dcode, flush_fn, [int(x) for x in args.batches.split(",")])
     if not args.no_dense:
@@ -354,6 +424,75 @@ def prefill_leg(torch, ns, WL, flush):
             "bytes": nbytes, "values_match_torch_topk_first_64_rows": ok, "cache": "cold"}
 
 
+def make_backbone(torch, cfg):
+    """Stand-in for the draft model's backbone: the seven bf16 GEMMs of one
+    Llama-3-8B decoder layer (q, k, v, o, gate, up, down weight shapes) on M
+    rows, as one EAGLE-style draft layer would run them."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed + 7)
+    shapes = [(4096, 4096), (4096, 4096), (4096, 1024), (4096, 1024), (4096, 14336), (4096, 14336), (14336, 4096)]
+    Ws = [(torch.randn((i, o), generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for i, o in shapes]
+    xs = {n: torch.randn((cfg.M, n), generator=gen, device="cuda").to(torch.bfloat16) for n in (4096, 14336)}
+    outs = [torch.empty((cfg.M, o), dtype=torch.bfloat16, device="cuda") for _, o in shapes]
+
+    def backbone():
+        for (i, _), w, o in zip(shapes, Ws, outs):
+            torch.matmul(xs[i], w, out=o)
+    return backbone
+
+
+def pipeline_leg(torch, cfg, backbone, warm_up, state_part, heads, flush, Wm, R, copy_stream, reps=5):
+    """Decode steps with the state advancing: per step the state update, the
+    draft backbone stand-in, and the draft head in one of several variants
+    (``heads[name](t, comp, copy)`` enqueues the head's part after the state
+    update: it may fork work to the copy stream and must join it before the
+    head).  ``base`` runs the state update and the backbone only.  Graph
+    replay of R steps, cold, the cache-streaming read subtracted; per-step ms."""
+    def run_fn(name):
+        def run():
+            comp = torch.cuda.current_stream()
+            for t in range(Wm, Wm + R):
+                flush(t)
+                state_part(t)
+                if name == "flush":
+                    continue
+                if name == "base":
+                    backbone()
+                else:
+                    heads[name](t, comp, copy_stream)
+        return run
+
+    names = ["flush", "base"] + list(heads)
+    out = {}
+    for name in names:
+        mode = heads[name].mode if name in heads else None
+        warm_up(mode)
+        run_fn(name)()                                 # eager pass first
+        warm_up(mode)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_fn(name)()
+        ts = []
+        for _ in range(reps):
+            warm_up(mode)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[name] = float(np.median(ts)) / R
+        del g
+    flush_ms = out.pop("flush")
+    res = {name: v - flush_ms for name, v in out.items()}
+    return {"backbone": "bf16 GEMM chain, Llama-3-8B decoder-layer weight shapes, M rows",
+            "steps": R, "step_ms": res,
+            "head_cost_ms": {name: res[name] - res["base"] for name in heads},
+            "note": "per step: state update, backbone, draft head variant; cold; hipGraph replay"}
+
+
 def overlap_leg(torch, ns, cfg, W, ids, n_act, packed, h, ws, dcode, copy_stream, flush):
     """a7: the gather on a second stream while a backbone stand-in runs on the
     compute stream (a chain of bf16 GEMMs with one Llama-3-8B decoder layer's
@@ -363,18 +502,9 @@ def overlap_leg(torch, ns, cfg, W, ids, n_act, packed, h, ws, dcode, copy_stream
     hidden = (T_serial - T_overlap) / T_gather."""
     M, d = cfg.M, cfg.d
     R = 20
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(cfg.seed + 7)
-    shapes = [(4096, 4096), (4096, 4096), (4096, 1024), (4096, 1024), (4096, 14336), (4096, 14336), (14336, 4096)]
-    Ws = [(torch.randn((i, o), generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for i, o in shapes]
-    xs = {n: torch.randn((M, n), generator=gen, device="cuda").to(torch.bfloat16) for n in (4096, 14336)}
-    outs = [torch.empty((M, o), dtype=torch.bfloat16, device="cuda") for _, o in shapes]
+    backbone = make_backbone(torch, cfg)
     tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((cfg.M, cfg.k), dtype=torch.float32, device="cuda")
-
-    def backbone():
-        for (i, _), w, o in zip(shapes, Ws, outs):
-            torch.matmul(xs[i], w, out=o)
 
     def gather(stream):
         ns.nanospec_gather_rows(W, cfg.V, d, dcode, ids, n_act, cfg.w_max, packed, stream=stream)

@@ -29,6 +29,7 @@ NS_MAX_M = NS_MAX_K = 64
 NS_MAX_V = NS_MAX_WMAX = 1 << 20
 NS_MAX_D = 16384
 NS_MAX_BATCH = 4096
+NS_MAX_SLOTS = 16384
 
 
 class NanoSpecError(RuntimeError):
@@ -89,6 +90,12 @@ _SIGS = {
     "nanospec_batch_draft_logits_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
                                                         c_int32, c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp,
                                                         c_size, c_vp]),
+    "nanospec_packed_bytes": (c_size, [c_int32, c_int32]),
+    "nanospec_packed_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_vp, c_size, c_vp]),
+    "nanospec_packed_reset": (ctypes.c_int, [c_vp, c_vp]),
+    "nanospec_packed_destroy": (ctypes.c_int, [c_vp]),
+    "nanospec_packed_slots": (ctypes.c_int, [c_vp] + [ctypes.POINTER(c_vp)] * 5),
+    "nanospec_packed_update": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_vp, c_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -300,6 +307,66 @@ def nanospec_batch_draft_logits_topk(w: torch.Tensor, row_ids: torch.Tensor, n_d
                                                  _ptr(h), M, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_vals),
                                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "nanospec_batch_draft_logits_topk")
+
+
+# ---------------------------------------------------------------------------
+# Slot-stable packed buffer
+# ---------------------------------------------------------------------------
+
+
+def nanospec_packed_bytes(V: int, w_max: int) -> int:
+    return _lib.nanospec_packed_bytes(V, w_max)
+
+
+class NanoSpecPacked:
+    """Host handle plus the caller-owned device memory of one slot map.  The
+    int32 tensors ``slot_ids`` [w_max], ``n_slots`` [1], ``enter_slots``
+    [w_max], ``enter_ids`` [w_max] and ``n_enter`` [1] view that memory at the
+    addresses nanospec_packed_slots reports."""
+
+    def __init__(self, V: int, w_max: int, device="cuda", stream=None):
+        nbytes = nanospec_packed_bytes(V, w_max)
+        if nbytes == 0:
+            raise NanoSpecError(NS_EINVAL, f"nanospec_packed_bytes(V={V}, w_max={w_max})")
+        self.V, self.w_max = V, w_max
+        self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.mem.data_ptr()) % 256
+        self.buf = self.mem[off:off + nbytes]
+        h = ctypes.c_void_p()
+        _check(_lib.nanospec_packed_create(ctypes.byref(h), V, w_max, _ptr(self.buf), nbytes, _stream(stream)),
+               "nanospec_packed_create")
+        self.handle = h
+        ptrs = [c_vp() for _ in range(5)]
+        _check(_lib.nanospec_packed_slots(h, *[ctypes.byref(p) for p in ptrs]), "nanospec_packed_slots")
+        base = self.buf.data_ptr()
+
+        def view(p, n):
+            o = p.value - base
+            return self.buf[o:o + 4 * n].view(torch.int32)
+
+        self.slot_ids = view(ptrs[0], w_max)
+        self.n_slots = view(ptrs[1], 1)
+        self.enter_slots = view(ptrs[2], w_max)
+        self.enter_ids = view(ptrs[3], w_max)
+        self.n_enter = view(ptrs[4], 1)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _lib.nanospec_packed_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def nanospec_packed_reset(pk: NanoSpecPacked, stream=None) -> None:
+    _check(_lib.nanospec_packed_reset(pk.handle, _stream(stream)), "nanospec_packed_reset")
+
+
+def nanospec_packed_update(pk: NanoSpecPacked, st, w: torch.Tensor, d: int, dtype: int, rows: torch.Tensor,
+                           stream=None) -> None:
+    _check(_lib.nanospec_packed_update(pk.handle, st.handle, _ptr(w), d, dtype, _ptr(rows), _stream(stream)),
+           "nanospec_packed_update")
 
 
 def alloc_batch_workspace(B: int, n_max: int, M: int, k: int, d: int, device="cuda") -> torch.Tensor:

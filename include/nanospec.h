@@ -73,9 +73,11 @@ extern "C" {
 #define NS_MAX_WMAX   1048576   /* sliding-window length */
 #define NS_MAX_D      16384     /* hidden size; d % 8 == 0 */
 #define NS_MAX_BATCH  4096      /* sequences in one batch */
+#define NS_MAX_SLOTS  16384     /* slots of a slot-stable packed buffer */
 
 typedef struct nanospec_state nanospec_state;   /* opaque host handle */
 typedef struct nanospec_batch nanospec_batch;   /* opaque host handle of B states */
+typedef struct nanospec_packed nanospec_packed; /* opaque host handle of a slot map */
 
 /* Human-readable text for a return code (static storage, never NULL). */
 const char* nanospec_strerror(int code);
@@ -205,6 +207,55 @@ int nanospec_batch_step_update(nanospec_batch* bt,
 int nanospec_gather_rows(const void* w, int32_t V, int32_t d, int32_t dtype,
                          const int32_t* ids, const int32_t* n_dev, int32_t n_max,
                          void* out, hipStream_t stream);
+
+/* ======================================================================
+ * Slot-stable packed buffer.  NanoSpec "Avoiding Sparse Computation via
+ * Asynchronous Gathering": one buffer of W_max rows is allocated up front and
+ * each step gathers into it only the rows of ids that became active.
+ * Placement (the pages leave it open): a row stays in its slot while its id
+ * stays active; the slots of ids that left become holes (id -1); the entering
+ * ids, in ascending id order, take the free slots in ascending slot order.
+ * n_slots is one past the highest occupied slot; it never exceeds the
+ * largest |I| seen since the last reset.
+ *   nanospec_packed_bytes  : device bytes of the slot map for (V, w_max slots):
+ *             a 256-byte header (int32 n_slots, int32 n_enter), int32
+ *             slot_ids[w_max], int32 enter_slots[w_max], int32
+ *             enter_ids[w_max] and the held-id bitmap uint32[ceil(V/32)].
+ *             0 if V or w_max is outside [1, NS_MAX_V] / [1, NS_MAX_SLOTS].
+ *   nanospec_packed_create : binds a slot map to caller-owned device memory
+ *             (256-byte aligned) and enqueues its reset (all holes, nothing
+ *             held).  The row buffer itself, [w_max x d] elements, is also
+ *             the caller's and is passed to every update.
+ *   nanospec_packed_update : for the active set of the state's latest rebuild
+ *             (its bitmap), updates the slot map and enqueues the copy
+ *             rows[enter_slots[r], :] = w[enter_ids[r], :] for r < n_enter.
+ *             Rows of slots that stay occupied are not touched; hole rows hold
+ *             whatever they held.  st must have the same V and a w_max no
+ *             larger than the slot count; w and rows are 16-byte aligned, d %
+ *             8 == 0, and d, dtype and rows must stay the same from one update
+ *             to the next (until a reset).
+ *   nanospec_packed_slots  : (host call) the device addresses of slot_ids,
+ *             n_slots, enter_slots, enter_ids and n_enter (each output may be
+ *             NULL).  The head over the buffer is
+ *             nanospec_draft_logits_topk(rows, NS_PACKED, slot_ids, n_slots,
+ *             w_max, ...), which skips holes.
+ *   nanospec_packed_reset / _destroy : reset to empty / free the host handle.
+ * The update is two launches (the slot plan on one workgroup, then the row
+ * copy); like the plain gather it may run on a copy stream, ordered after the
+ * state update that produced the active set.
+ * Errors: NS_EINVAL (nulls, limits, misalignment, V / w_max mismatch),
+ * NS_EDTYPE, NS_ECAPACITY (dev_bytes too small), NS_EHIP. */
+size_t nanospec_packed_bytes(int32_t V, int32_t w_max);
+int nanospec_packed_create(nanospec_packed** out, int32_t V, int32_t w_max,
+                           void* dev_mem, size_t dev_bytes, hipStream_t stream);
+int nanospec_packed_reset(nanospec_packed* pk, hipStream_t stream);
+int nanospec_packed_destroy(nanospec_packed* pk);
+int nanospec_packed_slots(const nanospec_packed* pk, const int32_t** slot_ids,
+                          const int32_t** n_slots, const int32_t** enter_slots,
+                          const int32_t** enter_ids, const int32_t** n_enter);
+int nanospec_packed_update(nanospec_packed* pk, const nanospec_state* st,
+                           const void* w, int32_t d, int32_t dtype, void* rows,
+                           hipStream_t stream);
 
 /* ======================================================================
  * Restricted LM head + top-k + map back to global ids.  Sec. 3.1, Eq. 1 on

@@ -115,6 +115,22 @@ def test_host_validation_rejects_before_launch(ns):
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # n_dev required
     assert L.nanospec_batch_draft_logits_topk(fake, fake, fake, 16, 0, 100, 64, 0, fake, 8, 8, None, fake, fake,
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # B = 0
+    # slot-stable packed buffer
+    pb = L.nanospec_packed_bytes(128256, 3072)
+    assert pb == 256 + 3 * 12288 + 16128          # header, three [w_max] int32 arrays, bitmap (256-aligned)
+    assert L.nanospec_packed_bytes(0, 16) == 0
+    assert L.nanospec_packed_bytes(100, 0) == 0
+    assert L.nanospec_packed_bytes(100, ns.NS_MAX_SLOTS + 1) == 0
+    assert L.nanospec_packed_bytes(100, ns.NS_MAX_SLOTS) > 0
+    assert L.nanospec_packed_create(None, 10, 4, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_packed_create(ctypes.byref(h), 10, 4, None, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_packed_create(ctypes.byref(h), 10, 4, ctypes.c_void_p(0x1010), 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_packed_create(ctypes.byref(h), 10, 4, fake, 16, None) == ns.NS_ECAPACITY
+    assert L.nanospec_packed_create(ctypes.byref(h), 10, ns.NS_MAX_SLOTS + 1, fake, 1 << 30, None) == ns.NS_EINVAL
+    assert L.nanospec_packed_update(None, fake, fake, 64, 0, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_packed_reset(None, None) == ns.NS_EINVAL
+    assert L.nanospec_packed_destroy(None) == ns.NS_EINVAL
+    assert L.nanospec_packed_slots(None, None, None, None, None, None) == ns.NS_EINVAL
     # prefill
     assert L.nanospec_prefill_topk(fake, 4, 10, 0, 0, fake, fake, None) == ns.NS_EINVAL
     assert L.nanospec_prefill_topk(fake, 4, 10, 0, 11, fake, fake, None) == ns.NS_EINVAL
