@@ -280,22 +280,37 @@ def packed_draft_head(h: np.ndarray, W: np.ndarray, slot_ids: np.ndarray, n_slot
 # ---------------------------------------------------------------------------
 
 
+STREAM_MODES = ("full", "ctx_only", "ext_only")
+
+
 class Sequence_:
     """Keeps the full stream S of one sequence and derives each step's active
-    set from scratch."""
+    set from scratch.
 
-    def __init__(self, w_max: int):
+    ``mode`` selects the stream sources of the ablation study (NanoSpec
+    Sec. 4, ablation, Table 5): "full" is the method; "ctx_only" keeps only
+    the prompt and the prefill candidates, S^(0), and adds nothing while
+    decoding; "ext_only" keeps only the decoding tuples C_draft and C_ver and
+    ignores the prompt context (the window rule is unchanged)."""
+
+    def __init__(self, w_max: int, mode: str = "full"):
+        if mode not in STREAM_MODES:
+            raise ValueError(mode)
         self.w_max = int(w_max)
+        self.mode = mode
         self.S: List[int] = []
 
     def append_prompt(self, prompt: Sequence[int]) -> None:
-        self.S = self.S + [int(x) for x in prompt]
+        if self.mode != "ext_only":
+            self.S = self.S + [int(x) for x in prompt]
 
     def append_prefill_union(self, P: np.ndarray) -> None:
-        self.S = self.S + first_occurrence(np.asarray(P).reshape(-1))
+        if self.mode != "ext_only":
+            self.S = self.S + first_occurrence(np.asarray(P).reshape(-1))
 
     def step(self, tree_ids: Sequence[int], ver_ids: Sequence[int]) -> None:
-        self.S = stream_update(self.S, tree_ids, ver_ids)
+        if self.mode != "ctx_only":
+            self.S = stream_update(self.S, tree_ids, ver_ids)
 
     def active(self) -> np.ndarray:
         return active_set(self.S, self.w_max)

@@ -162,6 +162,23 @@ def _packed_head_with_holes(h, W, slot_ids, n_slots, k, dtype):
     return O.draft_topk(O.project(h, O.gather_rows(W, ids), dtype), ids, k)
 
 
+class _SequenceCtxKeepsVerify(O.Sequence_):
+    """Ctx-only read as 'no draft-tree ids', still appending C_ver."""
+
+    def step(self, tree_ids, ver_ids):
+        if self.mode == "ctx_only":
+            self.S = O.stream_update(self.S, [], ver_ids)
+        else:
+            super().step(tree_ids, ver_ids)
+
+
+class _SequenceExtKeepsPrompt(O.Sequence_):
+    """Ext-only that forgets to drop the prompt."""
+
+    def append_prompt(self, prompt):
+        self.S = self.S + [int(x) for x in prompt]
+
+
 MUTATIONS = [
     ("top_k", _topk_tie_desc),
     ("top_k", _topk_ascending),
@@ -186,6 +203,8 @@ MUTATIONS = [
     ("packed_update", _packed_keep_leaving),
     ("packed_update", _packed_count_slots),
     ("packed_draft_head", _packed_head_with_holes),
+    ("Sequence_", _SequenceCtxKeepsVerify),
+    ("Sequence_", _SequenceExtKeepsPrompt),
 ]
 
 

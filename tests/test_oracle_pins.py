@@ -246,6 +246,36 @@ def pin_draft_topk_global_ids(o):
     assert ids.tolist() == [[7, 9, 3]] and vals.tolist() == [[2.0, 2.0, 1.0]]
 
 
+def pin_stream_modes(o):
+    """Ablation modes, from their descriptions: with the context only, the
+    active set after any number of steps is the prompt's (capped by the window
+    over the prompt); with the decoding tuples only, it is the window over the
+    concatenated deduplicated tuples, as if the prompt had never been seen."""
+    rng = np.random.default_rng(31)
+    V, w = 40, 12
+    prompt = rng.integers(0, V, size=20).tolist()
+    steps = [(rng.integers(0, V, size=7).tolist(), rng.choice(V, size=3, replace=False).tolist())
+             for _ in range(6)]
+    ctx = o.Sequence_(w, "ctx_only")
+    ctx.append_prompt(prompt)
+    ext = o.Sequence_(w, "ext_only")
+    ext.append_prompt(prompt)
+    tail = []
+    for tree, ver in steps:
+        ctx.step(tree, ver)
+        ext.step(tree, ver)
+        seen = []
+        for x in tree:                              # C_draft: first occurrences
+            if x not in seen:
+                seen.append(x)
+        tail = tail + seen + list(ver)
+        assert ctx.active().tolist() == sorted(set(prompt[-w:]))
+        assert ext.active().tolist() == sorted(set(tail[-w:]))
+    full = o.Sequence_(w)
+    full.append_prompt(prompt)
+    assert full.active().tolist() == sorted(set(prompt[-w:]))
+
+
 GOLDEN_PACKED = os.path.join(os.path.dirname(__file__), "golden", "packed_slots.json")
 
 
@@ -319,7 +349,7 @@ PINS = [pin_worked_example, pin_widen_bf16, pin_topk_bruteforce, pin_topk_librar
         pin_prefill_planted, pin_first_occurrence, pin_stream_update,
         pin_active_set_bruteforce, pin_active_full_coverage, pin_bitmap_tail,
         pin_projection_exact, pin_gather, pin_subset_equals_dense, pin_draft_topk_global_ids,
-        pin_packed_worked_example, pin_packed_invariants, pin_packed_head]
+        pin_packed_worked_example, pin_packed_invariants, pin_packed_head, pin_stream_modes]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
