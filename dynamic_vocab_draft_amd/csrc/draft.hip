@@ -24,13 +24,19 @@
 //       they cost no extra traffic, and are zeroed.  Each block writes its
 //       partial sums (deterministic; no atomics) to partial[m][j][s], the S
 //       slices of one column side by side (row stride SP = S rounded up to
-//       4) so the merge reads them with 16-byte loads.
+//       4) so the merge reads them with 16-byte loads.  The grid is 1-D per
+//       sequence, in groups of 8 tiles x S slices, one tile per XCD: the
+//       blocks of the live tiles come first in dispatch order and are dealt
+//       evenly over the 8 XCDs and their CUs however large n_max is, and
+//       each row is read whole by one XCD.
 //   k_merge_cols (+ k_merge_keys when n_max > 4096): per hidden row m and
 //       4096-column chunk, a 1024-thread block sums the S partials of each
 //       active column in a fixed order and selects the chunk's k best
-//       (value, id) keys with a threshold from 64 row maxima and a rank
+//       (value, id) keys with a threshold from wave or row maxima and a rank
 //       count in LDS; with several chunks a second kernel selects the final
-//       k from the chunks' keys.  No k rounds of cross-lane reductions.
+//       k from the chunks' keys, unless every live column is in chunk 0,
+//       which then writes the result itself.  No k rounds of cross-lane
+//       reductions.
 #include "common.hpp"
 #include "select.hpp"
 
@@ -51,6 +57,7 @@ constexpr int kTile = 16;                         // rows per MFMA tile
 constexpr int kKC = 4;                            // 32-column steps loaded per batch
 constexpr int kTargetBlocks = 1536;               // MFMA blocks aimed for when choosing S
 constexpr int kMaxSplits = 16;
+constexpr int kLiveRowsHint = 3072;               // live rows assumed when sizing S without n
 
 
 // Per-sequence element strides of a batched call (sequence b = blockIdx.z,
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
-                                                         int ks_per_split, int SP, float* __restrict__ part,
+                                                         int S, int SP, float* __restrict__ part,
                                                          BatchStrides bs) {
   __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
   {
@@ -170,8 +177,14 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   __shared__ int sh_ok[RT * kTile];
   const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), w = tid / NS_WAVE;
   const int i = lane & 15, g = lane >> 4;
-  const int r0 = blockIdx.x * (kTile * RT);
-  const int split = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin (block L to XCD L % 8).
+  // Block L takes row tile 8 (L / 8S) + L % 8 and slice (L / 8) % S: each
+  // XCD owns whole rows (every slice of its tiles, so a row is read as one
+  // 8 KiB run in one L2), and the tiles are dispatched in ascending order,
+  // so the live ones (the lowest) come first and spread over every XCD and
+  // its CUs, whatever n_max is.
+  const int r0 = (int)((blockIdx.x / (8 * S)) * 8 + (blockIdx.x & 7)) * (kTile * RT);
+  const int split = (int)((blockIdx.x >> 3) % S);
   // Independent loads first: the active count and this lane's row ids.
   const int n = clamp_n(n_dev, n_max);
   int gid[RT];
@@ -200,6 +213,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   }
   // This wave's 32-column steps: the split's range, divided among the waves.
   const int ksteps = (dv + 3) >> 2;
+  const int ks_per_split = (ksteps + S - 1) / S;
   const int kb = split * ks_per_split;
   const int ke = min(ksteps, kb + ks_per_split);
   const int per = (ke - kb + kPW - 1) / kPW;
@@ -329,6 +343,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   NS_ISSUE_FENCE();
   const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
   const int lim = min(n, cend);                      // live columns of this chunk end here
+  // With several chunks but every live column in chunk 0, chunk 0 writes the
+  // final result and k_merge_keys does nothing; the other chunks are idle.
+  const bool final_here = FINAL || n <= kMergeChunk;
+  if (!FINAL && final_here && c > 0) return;         // block-uniform
   const bool more = lim > col0 + NT;                 // block-uniform
   if (more) {
 #pragma unroll
@@ -357,14 +375,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
       }
     }
   }
-  if (FINAL) {
-    block_select_topk<U>(val, gid, k, sm, [&](int r, uint64_t x) {
+  const int nlive = lim > col0 ? lim - col0 : 0;     // live slots lead: thread t, then t + NT, ...
+  if (final_here) {
+    block_select_topk<U>(val, gid, k, nlive, sm, [&](int r, uint64_t x) {
       out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
       out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
     });
   } else {
     uint64_t* dst = cand_out + ((size_t)m * gridDim.y + c) * k;
-    block_select_topk<U>(val, gid, k, sm, [&](int r, uint64_t x) { dst[r] = x; });
+    block_select_topk<U>(val, gid, k, nlive, sm, [&](int r, uint64_t x) { dst[r] = x; });
   }
 }
 
@@ -372,15 +391,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
 // (nk = C * k of them, at most PER per thread).
 template <int PER>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __restrict__ cand, int nk, int k,
+                                                              const int32_t* __restrict__ n_dev, int n_max,
                                                               int32_t* __restrict__ out_ids,
                                                               float* __restrict__ out_vals, BatchStrides bs) {
   __shared__ SelectSmem sm;
   {
     const size_t b = blockIdx.y;
     cand += b * bs.cand;
+    if (n_dev) n_dev += b;
     out_ids += b * bs.out;
     out_vals += b * bs.out;
   }
+  if (clamp_n(n_dev, n_max) <= kMergeChunk) return;   // chunk 0 already wrote the result
   const int m = blockIdx.x, tid = threadIdx.x;
   const uint64_t* src = cand + (size_t)m * nk;
   uint64_t key[PER];
@@ -398,7 +420,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __
     val[u] = live ? ns::key_val(key[u]) : 0.f;
     gid[u] = live ? ns::key_id(key[u]) : -1;
   }
-  block_select_topk<PER>(val, gid, k, sm, [&](int r, uint64_t x) {
+  block_select_topk<PER>(val, gid, k, nk, sm, [&](int r, uint64_t x) {
     out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
     out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
   });
@@ -417,17 +439,32 @@ int pick_mt(int M, int d, int esz) {
 
 int pick_rt(int M) { return M <= 16 ? 1 : 2; }
 
-// Number of d-slices for the MFMA path: enough blocks to spread a call over
-// the chip, each wave keeping at least one batch of kKC steps.
-int pick_splits(int n_max, int M, int d, int dtype, int B) {
+// Number of d-slices S for the MFMA path: about kTargetBlocks blocks, each
+// wave keeping at least one batch of kKC steps.  When the live row count is
+// only known on the device (n_dev given) and M <= 16, S is sized as if at
+// most kLiveRowsHint rows of each sequence were live, so a few live rows out
+// of a large n_max still spread over the chip; the partial sums then cost at
+// most 4 M S / d of the row bytes (6% at d = 4096, M = 8, S = 8).  Larger M,
+// whose partial sums cost more, and calls with n known on the host use n_max.
+// Other dtypes use one slice.
+int launch_splits(bool n_known, int n_max, int M, int d, int dtype, int B) {
   if (dtype != NS_BF16) return 1;
   const int ksteps = (d / 8 + 3) / 4;
-  const long tiles = (long)((n_max + kTile * pick_rt(M) - 1) / (kTile * pick_rt(M))) * B;
-  int s = (int)((kTargetBlocks + tiles - 1) / tiles);
-  const int smax = ksteps / (kPW * kKC) > 0 ? ksteps / (kPW * kKC) : 1;
-  if (s > smax) s = smax;
-  if (s > kMaxSplits) s = kMaxSplits;
-  return s < 1 ? 1 : s;
+  int s_hi = ksteps / (kPW * kKC);
+  s_hi = s_hi < 1 ? 1 : (s_hi > kMaxSplits ? kMaxSplits : s_hi);
+  const int rt = kTile * pick_rt(M);
+  long tiles = (n_max + rt - 1) / rt;
+  if (!n_known && M <= 16 && tiles > kLiveRowsHint / rt) tiles = kLiveRowsHint / rt;
+  tiles *= B;
+  const long s = (kTargetBlocks + tiles - 1) / tiles;
+  return s < 1 ? 1 : (s > s_hi ? s_hi : (int)s);
+}
+
+// Largest S any call with these dims may launch (sizes the workspace).
+int max_splits(int n_max, int M, int d, int B) {
+  const int a = launch_splits(false, n_max, M, d, NS_BF16, B);
+  const int b = launch_splits(true, n_max, M, d, NS_BF16, B);
+  return a > b ? a : b;
 }
 
 template <bool BF16>
@@ -454,21 +491,20 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 
 template <int NMT, int RT>
 void launch_mfma_t(dim3 grid, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
-                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int ks, int SP, float* part,
-                   const BatchStrides& bs) {
+                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int SP,
+                   float* part, const BatchStrides& bs) {
   hipLaunchKernelGGL((k_proj_mfma<NMT, RT>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
-                     n_dev, n_max, V, dv, (const uint4*)h, M, ks, SP, part, bs);
+                     n_dev, n_max, V, dv, (const uint4*)h, M, S, SP, part, bs);
 }
 
 int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
                 const void* h, int M, int S, int SP, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
   const int dv = d / 8;
-  const int ksteps = (dv + 3) / 4;
-  const int ks = (ksteps + S - 1) / S;
   const int rt = pick_rt(M);
-  const dim3 grid((n_max + kTile * rt - 1) / (kTile * rt), S, B);
+  // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and exit).
+  const dim3 grid((unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8 * S, 1, B);
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
-  launch_mfma_t<NMTV, RTV>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, ks, SP, part, bs)
+  launch_mfma_t<NMTV, RTV>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, SP, part, bs)
   switch ((M + 15) / 16) {
     case 1: NS_LAUNCH_MFMA(1, 1); break;
     case 2: NS_LAUNCH_MFMA(2, 2); break;
@@ -512,7 +548,8 @@ int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row
   const int nk = C * k;
   const int per = (nk + kMergeThreads - 1) / kMergeThreads;
 #define NS_LAUNCH_KEYS(PERV) \
-  hipLaunchKernelGGL((k_merge_keys<PERV>), dim3(M, B), dim3(kMergeThreads), 0, stream, cand, nk, k, ids, vals, bs)
+  hipLaunchKernelGGL((k_merge_keys<PERV>), dim3(M, B), dim3(kMergeThreads), 0, stream, cand, nk, k, n_dev, n_max, \
+                     ids, vals, bs)
   if (per <= 1) NS_LAUNCH_KEYS(1);
   else if (per <= 2) NS_LAUNCH_KEYS(2);
   else if (per <= 4) NS_LAUNCH_KEYS(4);
@@ -535,7 +572,7 @@ extern "C" {
 // 4) at offset 256, then the chunk keys when n_max > 4096.
 size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M, int32_t k, int32_t d) {
   if (B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return 0;
-  const int SP = (pick_splits(n_max, M, d, NS_BF16, B) + 3) & ~3;
+  const int SP = (max_splits(n_max, M, d, B) + 3) & ~3;
   const int C = merge_chunks(n_max);
   const size_t keys = C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0;
   return 256 + partial_bytes(n_max, M, SP, B) + keys;
@@ -561,7 +598,7 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   if (ws_bytes < nanospec_batch_draft_workspace_bytes(B, n_max, M, k, d)) return NS_ECAPACITY;
   float* part = (float*)((char*)ws + 256);
   (void)hipGetLastError();
-  const int S = pick_splits(n_max, M, d, dtype, B);
+  const int S = launch_splits(n_dev == nullptr, n_max, M, d, dtype, B);
   const int SP = (S + 3) & ~3;
   const int esz = dtype == NS_BF16 ? 2 : 4;
   const int C = merge_chunks(n_max);

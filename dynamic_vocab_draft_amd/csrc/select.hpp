@@ -1,5 +1,5 @@
 // Block-wide top-k selection over (value, id) pairs held by a 1024-thread
-// block; shared by the draft-head merge and the fused decode step.
+// block, used by the draft-head merges.
 #pragma once
 #include "common.hpp"
 
@@ -11,13 +11,18 @@ namespace {
 //
 // block_select_topk: the k largest (value, id) pairs held by a 1024-thread
 // block (U per thread; id < 0 marks an empty slot), by the key order.
-// T = the k-th largest of the 64 maxima of 16-lane DPP rows, or of the 16
-// wave maxima when k <= 16 (float values, counted with multiplicity).  Each
-// of those is a real value, so the k-th largest value overall is >= T and
-// the top k are among the pairs with value >= T.  Only those are turned into 64-bit keys, collected in LDS and ranked
-// by counting; if more than kCandCap reach T, the block falls back to k
-// rounds of block-wide maxima.  emit(r, key) is called once for every rank
-// r < k (key 0 when fewer than r + 1 pairs exist).
+// T = the k-th largest of the 16 wave maxima (k <= 16) or of the 64 maxima of
+// 16-lane DPP rows (float values, counted with multiplicity).  Each of those
+// is a real value, so the k-th largest value overall is >= T and the top k
+// are among the pairs with value >= T.  Only those are turned into 64-bit
+// keys, collected in LDS and ranked by counting; if more than kCandCap reach
+// T, the block falls back to k rounds of block-wide maxima.
+// `nlive` (block-uniform) bounds the live slots, which lead: slot u of
+// thread t is index t + u * 1024.  The maxima only give a threshold when at
+// least k of them are live, so wave maxima are used when more than 64 (k - 1)
+// slots may be live, row maxima when more than 16 (k - 1), and otherwise
+// every live pair (at most 16 k) is ranked.  emit(r, key) is called once for
+// every rank r < k (key 0 when fewer than r + 1 pairs exist).
 // ---------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
 constexpr int kCandCap = 1024;
@@ -31,8 +36,8 @@ struct SelectSmem {
 };
 
 template <int U, typename Emit>
-__device__ __forceinline__ void block_select_topk(const float (&val)[U], const int (&id)[U], int k, SelectSmem& sm,
-                                                  Emit emit) {
+__device__ __forceinline__ void block_select_topk(const float (&val)[U], const int (&id)[U], int k, int nlive,
+                                                  SelectSmem& sm, Emit emit) {
   static_assert(kSelectThreads / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
   const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
   const int ninf = __float_as_int(-INFINITY);
@@ -45,9 +50,11 @@ __device__ __forceinline__ void block_select_topk(const float (&val)[U], const i
   best = fmaxf(best, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(best), 0x114, 0xf, 0xf, false)));
   best = fmaxf(best, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(best), 0x118, 0xf, 0xf, false)));
   constexpr int NW = kSelectThreads / NS_WAVE;
-  // For k <= NW the 16 wave maxima are enough (fewer compares for wave 0);
-  // otherwise the 64 row maxima are used.
-  const bool by_wave = k <= NW;
+  // Wave maxima when k <= NW and at least k waves can hold a live pair (fewer
+  // compares for wave 0); else row maxima when at least k rows can; else no
+  // threshold (T = -inf, all live pairs ranked).
+  const bool by_wave = k <= NW && nlive > NS_WAVE * (k - 1);
+  const bool by_row = !by_wave && nlive > 16 * (k - 1);
   if (by_wave) {
     const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 15));
     const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 31));
@@ -80,7 +87,7 @@ __device__ __forceinline__ void block_select_topk(const float (&val)[U], const i
       }
     }
     const unsigned long long ball = __ballot(mine != -INFINITY && gt < k && ge >= k);
-    if (lane == 0) sm.T = ball ? sm.rmax[__ffsll(ball) - 1] : -INFINITY;
+    if (lane == 0) sm.T = (ball && (by_wave || by_row)) ? sm.rmax[__ffsll(ball) - 1] : -INFINITY;
   }
   __syncthreads();
   const float T = sm.T;

@@ -355,6 +355,61 @@ def test_merge_paths(ns):
         check_draft(out, h, Wa, I, 64, dtype, f"{dtype} fallback")
 
 
+def test_live_count_below_capacity(ns):
+    """Few live columns in a large n_max: the slice count follows the live n
+    on the device (a larger grid is launched), with several 4096-column merge
+    chunks only chunk 0 may be live (it then writes the result and the key
+    merge stands down), and small n at k = 8 / 16 / 64 takes the selection's
+    row-maxima or no-threshold paths."""
+    say("live count below capacity")
+    rng = np.random.default_rng(13)
+    V, d = 20000, 256
+    W = WL.f32_to_bf16_bits((rng.standard_normal((V, d)) * 0.1).astype(np.float32))
+    W_dev = dev_elems(W, "bf16")
+    cases = [(8, 8, 0, 6000), (8, 8, 5, 6000), (8, 8, 300, 6000), (4, 16, 4096, 9000), (4, 16, 4097, 9000),
+             (3, 64, 900, 12000), (8, 8, 100, 3072), (8, 16, 200, 3072), (2, 64, 70, 3072), (2, 64, 1000, 1000),
+             (20, 10, 600, 8192), (64, 16, 2000, 16384)]
+    for M, k, n, n_max in cases:
+        h = WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+        I = np.sort(rng.choice(V, size=n, replace=False))
+        for mode in (ns.NS_INDEXED, ns.NS_PACKED):
+            out = run_draft(ns, W_dev, dev_elems(h, "bf16"), I, n_max, V, d, "bf16", M, k, mode)
+            check_draft(out, h, W, I, k, "bf16", f"M={M} k={k} n={n} n_max={n_max} mode={mode}")
+
+
+def test_batch_mixed_merge_paths(ns):
+    """One batched call whose sequences take different merge paths: n <= 4096
+    (chunk 0 final, key merge idle) next to n > 4096 (key merge), with
+    per-sequence slice counts from each n."""
+    say("batch: mixed merge paths")
+    rng = np.random.default_rng(37)
+    V, d, M, k, n_max = 30000, 128, 4, 8, 9000
+    W = WL.f32_to_bf16_bits((rng.standard_normal((V, d)) * 0.1).astype(np.float32))
+    W_dev = dev_elems(W, "bf16")
+    sizes = (9000, 40, 4096, 4097, 0, 2500)
+    B = len(sizes)
+    Is = [np.sort(rng.choice(V, size=s, replace=False)) for s in sizes]
+    ids = np.full((B, n_max), -1, np.int32)
+    for b, I in enumerate(Is):
+        ids[b, :len(I)] = I
+    hs = [WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32)) for _ in range(B)]
+    ws = ns.alloc_batch_workspace(B, n_max, M, k, d)
+    tids = torch.empty((B, M, k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((B, M, k), device="cuda")
+    logits = torch.full((B, M, n_max), float("nan"), device="cuda")
+    ns.nanospec_batch_draft_logits_topk(W_dev, dev_i32(ids.reshape(-1)), dev_i32(np.array(sizes, np.int32)), n_max,
+                                        B, V, d, ns.NS_BF16, dev_elems(np.stack(hs), "bf16"), M, k, logits, tids,
+                                        tvals, ws)
+    torch.cuda.synchronize()
+    lg, ti, tv = logits.cpu().numpy(), tids.cpu().numpy(), tvals.cpu().numpy()
+    for b, I in enumerate(Is):
+        ref, o_ids, o_vals = O.draft_head(hs[b], W, I, k, "bf16")
+        what = f"mixed batch seq {b} n={len(I)}"
+        check_logits(lg[b][:, :len(I)], ref, what)
+        assert np.isnan(lg[b][:, len(I):]).all(), what
+        check_topk(ti[b], tv[b], ref, I, o_ids, o_vals, k, what)
+
+
 def test_draft_deterministic(ns):
     say("determinism")
     cfg = WL.get_config("tiny")
