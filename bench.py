@@ -326,6 +326,8 @@ def main():
                  "full_gather_overlap": Head(ns.NS_PACKED, head_full_gather)}
         out["pipeline"] = pipeline_leg(torch, cfg, backbone, warm_up_state, state_part, heads, flush_fn, Wm,
                                        min(K, 40), copy_stream)
+        progress("stream-source ablation and W_max leg")
+        out["ablation"] = ablation_leg(torch, ns, WL, cfg, W, dcode, flush_fn)
         progress("batched-sequences leg")
         out["batched"] = batch_leg(torch, ns, WL, cfg, W, dcode, flush_fn, [int(x) for x in args.batches.split(",")])
     if not args.no_dense:
@@ -667,6 +669,93 @@ def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
         del bt, hs, wsb
     return {"workload": f"{cfg.name} x B independent sequences (seeds differ), batched step update + batched "
                         f"INDEXED draft head, cold, hipGraph replay of {steps} steps", "per_B": res}
+
+
+def ablation_leg(torch, ns, WL, cfg, W, dcode, flush, steps=48, warm=16):
+    """Stream sources of the ablation study (full, context only, decoding
+    tuples only) at the workload's W_max, then the full stream over W_max in
+    [1024, 8192]: per configuration the mean |I| and the cold per-step times
+    of the state update and the INDEXED draft head (graph replay, the
+    cache-streaming read and the state-only graph subtracted)."""
+    T = warm + steps
+    script = WL.make_id_script(cfg, steps=T)
+    trees = [torch.as_tensor(t, dtype=torch.int32).cuda() for t in script.tree]
+    vers = [torch.as_tensor(v, dtype=torch.int32).cuda() for v in script.ver]
+    prompt = torch.as_tensor(script.prompt, dtype=torch.int32).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 11)
+    hs = torch.randn((T, cfg.M, cfg.d), generator=g, device="cuda").to(W.dtype)
+    tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((cfg.M, cfg.k), device="cuda")
+    s = cfg.elem_bytes
+    modes = {"full": ns.NS_STREAM_FULL, "ctx_only": ns.NS_STREAM_CTX_ONLY, "ext_only": ns.NS_STREAM_EXT_ONLY}
+    points = [(m, cfg.w_max) for m in modes] + [("full", w) for w in (1024, 2048, 4096, 6144, 8192)
+                                                  if w != cfg.w_max]
+    out = []
+    for mode, w_max in points:
+        st = ns.NanoSpecState(cfg.V, w_max)
+        ns.nanospec_state_set_mode(st, modes[mode])
+        ids = torch.empty(w_max, dtype=torch.int32, device="cuda")
+        n = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ws = ns.alloc_workspace(w_max, cfg.M, cfg.k, cfg.d)
+
+        def init():
+            ns.nanospec_state_reset(st)
+            ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
+            ns.nanospec_active_vocab(st, ids, n)
+            for t in range(warm):
+                ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n)
+
+        sizes = []
+
+        def body(with_state, with_draft, record=False):
+            def run():
+                for t in range(warm, T):
+                    flush(t)
+                    if with_state:
+                        ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n)
+                    if record:
+                        sizes.append(n.clone())
+                    if with_draft:
+                        ns.nanospec_draft_logits_topk(W, ns.NS_INDEXED, ids, n, w_max, cfg.V, cfg.d, dcode, hs[t],
+                                                      cfg.M, cfg.k, None, tids, tvals, ws)
+            return run
+
+        init()
+        body(True, False, record=True)()
+        torch.cuda.synchronize()
+        n_mean = float(torch.stack(sizes).float().mean().item())
+
+        def timed(fn):
+            init()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn()
+            ts = []
+            for _ in range(3):
+                init()
+                torch.cuda.synchronize()
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                gr.replay()
+                b_.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b_))
+            del gr
+            return float(np.median(ts))
+
+        t_f = timed(body(False, False))
+        t_s = timed(body(True, False))
+        t_a = timed(body(True, True))
+        draft_us = (t_a - t_s) / steps * 1e3
+        draft_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + 4 * n_mean + 8 * cfg.M * cfg.k
+        out.append({"mode": mode, "w_max": w_max, "mean_active": n_mean,
+                    "step_us": (t_a - t_f) / steps * 1e3, "state_update_us": (t_s - t_f) / steps * 1e3,
+                    "draft_us": draft_us, "draft_GBps": draft_bytes / (draft_us * 1e-6) / 1e9})
+        del st, ws
+    return {"workload": f"{cfg.name} id stream under each stream source, and the full stream over W_max; "
+                        f"cold, hipGraph replay of {steps} steps", "points": out}
 
 
 def sweep(torch, ns, WL, args):

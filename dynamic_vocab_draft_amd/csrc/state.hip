@@ -670,6 +670,8 @@ int nanospec_batch_step_update(nanospec_batch* bt, const int32_t* draft_ids, int
   if (!bt || !draft_ids || !ver_ids || !n_draft || !n_ver || !active_ids || !n_active) return NS_EINVAL;
   if (nd_max < 0 || nv_max < 0 || nd_max > kFastMaxIds || nv_max > kFastMaxIds) return NS_EINVAL;
   if (draft_stride < nd_max || ver_stride < nv_max) return NS_EINVAL;
+  for (int b = 0; b < bt->B; ++b)                     // the batched kernel appends for every member
+    if (bt->members[b].mode == NS_STREAM_CTX_ONLY) return NS_EINVAL;
   const ns_state_view& v0 = bt->members[0].view;
   step_fast_batch_fn fn = pick_step_fast_batch(v0.w_max);
   const size_t lds = fast_lds_bytes(v0.V, nd_max);
@@ -685,6 +687,13 @@ int nanospec_state_reset(nanospec_state* st, hipStream_t stream) {
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_init, dim3(fill_grid(st->view)), dim3(256), 0, stream, st->view);
   return ns_launch_status();
+}
+
+int nanospec_state_set_mode(nanospec_state* st, int32_t mode) {
+  if (!st) return NS_EINVAL;
+  if (mode != NS_STREAM_FULL && mode != NS_STREAM_CTX_ONLY && mode != NS_STREAM_EXT_ONLY) return NS_EINVAL;
+  st->mode = mode;
+  return NS_OK;
 }
 
 int nanospec_state_destroy(nanospec_state* st) {
@@ -718,7 +727,7 @@ int nanospec_stream_append(nanospec_state* st, const int32_t* ids, int32_t n, in
                            hipStream_t stream) {
   if (!st || n < 0 || (n > 0 && !ids)) return NS_EINVAL;
   if (dedup_first != 0 && dedup_first != 1) return NS_EINVAL;
-  if (n == 0) return NS_OK;
+  if (n == 0 || st->mode == NS_STREAM_EXT_ONLY) return NS_OK;   // ext-only: no prompt context
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_append, dim3(1), dim3(kStateThreads), 0, stream, st->view, ids, n, dedup_first);
   return ns_launch_status();
@@ -738,6 +747,7 @@ int nanospec_step_update(nanospec_state* st, const int32_t* draft_ids, int32_t n
                          hipStream_t stream) {
   if (!st || !active_ids || !n_active || n_draft < 0 || n_ver < 0) return NS_EINVAL;
   if ((n_draft > 0 && !draft_ids) || (n_ver > 0 && !ver_ids)) return NS_EINVAL;
+  if (st->mode == NS_STREAM_CTX_ONLY) n_draft = n_ver = 0;     // ctx-only: nothing added while decoding
   (void)hipGetLastError();
   const size_t fast = fast_lds_bytes(st->view.V, n_draft);
   step_fast_fn fast_fn = pick_step_fast(st->view.w_max);

@@ -12,9 +12,11 @@ struct ns_state_view {
   int w_max;
 };
 
-// The opaque host handle behind nanospec_state*.
+// The opaque host handle behind nanospec_state*.  `mode` is the stream-source
+// setting of nanospec_state_set_mode (NS_STREAM_*), applied on the host.
 struct nanospec_state {
   ns_state_view view;
+  int mode = 0;
 };
 
 // B states laid out back to back at a fixed stride; members[b] is the

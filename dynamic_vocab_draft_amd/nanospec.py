@@ -25,6 +25,7 @@ NS_OK, NS_EINVAL, NS_EDTYPE, NS_ECAPACITY, NS_EHIP = 0, 1, 2, 3, 4
 NS_BF16, NS_FP32 = 0, 1
 NS_PACKED, NS_INDEXED = 0, 1
 NS_STATUS_BAD_ID = 0x1
+NS_STREAM_FULL, NS_STREAM_CTX_ONLY, NS_STREAM_EXT_ONLY = 0, 1, 2
 NS_MAX_M = NS_MAX_K = 64
 NS_MAX_V = NS_MAX_WMAX = 1 << 20
 NS_MAX_D = 16384
@@ -70,6 +71,7 @@ _SIGS = {
     "nanospec_state_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_vp, c_size, c_vp]),
     "nanospec_state_reset": (ctypes.c_int, [c_vp, c_vp]),
     "nanospec_state_destroy": (ctypes.c_int, [c_vp]),
+    "nanospec_state_set_mode": (ctypes.c_int, [c_vp, c_int32]),
     "nanospec_state_status": (ctypes.c_int, [c_vp, c_u32p, c_vp]),
     "nanospec_state_window": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp]),
     "nanospec_stream_append": (ctypes.c_int, [c_vp, c_vp, c_int32, c_int32, c_vp]),
@@ -169,6 +171,10 @@ class NanoSpecState:
 
     def __del__(self):
         self.close()
+
+
+def nanospec_state_set_mode(st, mode: int) -> None:
+    _check(_lib.nanospec_state_set_mode(st.handle, mode), "nanospec_state_set_mode")
 
 
 def nanospec_state_reset(st: NanoSpecState, stream=None) -> None:

@@ -63,6 +63,11 @@ extern "C" {
 #define NS_PACKED  0     /* rows = packed buffer [n_max x d]; row j is rows[j] */
 #define NS_INDEXED 1     /* rows = W_head [V x d]; row j is W_head[row_ids[j]] */
 
+/* ---- stream sources (nanospec_state_set_mode) -------------------------- */
+#define NS_STREAM_FULL     0   /* prompt, prefill candidates and decoding tuples */
+#define NS_STREAM_CTX_ONLY 1   /* prompt and prefill candidates only */
+#define NS_STREAM_EXT_ONLY 2   /* decoding tuples only */
+
 /* ---- sticky device status bits ---------------------------------------- */
 #define NS_STATUS_BAD_ID 0x1u   /* an appended id was outside [0, V) and was skipped */
 
@@ -110,6 +115,18 @@ int nanospec_state_reset(nanospec_state* st, hipStream_t stream);
 
 /* Frees the host handle (the device memory stays the caller's). */
 int nanospec_state_destroy(nanospec_state* st);
+
+/* Stream sources of the ablation study (NanoSpec Sec. 4, ablation, Table 5),
+ * a host-side setting of the handle (default NS_STREAM_FULL, kept by reset):
+ *   NS_STREAM_CTX_ONLY : I comes from the prompt and the prefill candidates
+ *       only; nanospec_step_update appends nothing (it ignores its tuples)
+ *       and still rebuilds I and writes its outputs.
+ *   NS_STREAM_EXT_ONLY : I comes from the decoding tuples C_draft and C_ver
+ *       only; nanospec_stream_append drops its ids and enqueues nothing.
+ * The same call sequence then yields each ablation's vocabulary.
+ * nanospec_batch_step_update refuses (NS_EINVAL) a batch with a CTX_ONLY
+ * member.  Errors: NS_EINVAL (null handle, unknown mode). */
+int nanospec_state_set_mode(nanospec_state* st, int32_t mode);
 
 /* Synchronises `stream`, then writes the sticky status bits to *flags (host)
  * and clears them. */

@@ -115,6 +115,8 @@ def test_host_validation_rejects_before_launch(ns):
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # n_dev required
     assert L.nanospec_batch_draft_logits_topk(fake, fake, fake, 16, 0, 100, 64, 0, fake, 8, 8, None, fake, fake,
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # B = 0
+    # stream modes
+    assert L.nanospec_state_set_mode(None, ns.NS_STREAM_CTX_ONLY) == ns.NS_EINVAL
     # slot-stable packed buffer
     pb = L.nanospec_packed_bytes(128256, 3072)
     assert pb == 256 + 3 * 12288 + 16128          # header, three [w_max] int32 arrays, bitmap (256-aligned)
