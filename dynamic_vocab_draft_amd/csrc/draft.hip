@@ -285,6 +285,9 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 constexpr int kMergeThreads = kSelectThreads;
 constexpr int kMergeCols = 4;                      // columns per thread
 constexpr int kMergeChunk = kMergeThreads * kMergeCols;
+// One block of 8 columns per thread covers n_max <= 8192 in a single chunk
+// (no key merge) when a column's partial sums are at most two 16-byte loads.
+constexpr int kMergeColsWide = 8;
 
 template <int SQ>
 __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
@@ -300,13 +303,13 @@ __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
 }
 
 // k_merge_cols: block (m, c) sums the S partials of columns
-// [c * kMergeChunk, (c + 1) * kMergeChunk) of hidden row m (at most four per
-// thread), optionally writes the logits, and selects that chunk's top k.
-// With one chunk (n_max <= kMergeChunk) the winners go straight to the
-// outputs; otherwise each chunk's k keys go to cand_out[m][c][k] for
-// k_merge_keys.  The first column of every thread is requested in the same
-// round as |I|, so the partial sums are in flight before |I| is known.
-template <int SQ, bool FINAL>
+// [c * 1024 U, (c + 1) * 1024 U) of hidden row m (at most U per thread),
+// optionally writes the logits, and selects that chunk's top k.  With one
+// chunk the winners go straight to the outputs; otherwise each chunk's k
+// keys go to cand_out[m][c][k] for k_merge_keys.  The first column of every
+// thread is requested in the same round as |I|, so the partial sums are in
+// flight before |I| is known.
+template <int SQ, bool FINAL, int U>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __restrict__ part, int S, int n_max,
                                                               const int32_t* __restrict__ row_ids,
                                                               const int32_t* __restrict__ n_dev, int V, int k,
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
                                                               int32_t* __restrict__ out_ids,
                                                               float* __restrict__ out_vals,
                                                               uint64_t* __restrict__ cand_out, BatchStrides bs) {
-  constexpr int NT = kMergeThreads, U = kMergeCols;
+  constexpr int NT = kMergeThreads, CHUNK = kMergeThreads * U;
   __shared__ SelectSmem sm;
   {
     const size_t b = blockIdx.z;
@@ -327,8 +330,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     cand_out += b * bs.cand;
   }
   const int m = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const int col0 = c * kMergeChunk;
-  const int cend = min(n_max, col0 + kMergeChunk);   // > col0
+  const int col0 = c * CHUNK;
+  const int cend = min(n_max, col0 + CHUNK);         // > col0
   const float4* prow = (const float4*)(part + (size_t)m * n_max * (SQ * 4));
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   const int lim = min(n, cend);                      // live columns of this chunk end here
   // With several chunks but every live column in chunk 0, chunk 0 writes the
   // final result and k_merge_keys does nothing; the other chunks are idle.
-  const bool final_here = FINAL || n <= kMergeChunk;
+  const bool final_here = FINAL || n <= CHUNK;
   if (!FINAL && final_here && c > 0) return;         // block-uniform
   const bool more = lim > col0 + NT;                 // block-uniform
   if (more) {
@@ -528,18 +531,24 @@ int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row
                  int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
                  const BatchStrides& bs, hipStream_t stream) {
   const int C = merge_chunks(n_max);
-#define NS_LAUNCH_COLS(SQV, FIN)                                                                                    \
-  hipLaunchKernelGGL((k_merge_cols<SQV, FIN>), dim3(M, C, B), dim3(kMergeThreads), 0, stream, part, S, n_max,      \
-                     row_ids, n_dev, V, k, logits, ids, vals, cand, bs)
-#define NS_LAUNCH_COLS_SQ(FIN)                 \
-  switch (SP / 4) {                            \
-    case 1: NS_LAUNCH_COLS(1, FIN); break;     \
-    case 2: NS_LAUNCH_COLS(2, FIN); break;     \
-    case 3: NS_LAUNCH_COLS(3, FIN); break;     \
-    default: NS_LAUNCH_COLS(4, FIN); break;    \
+#define NS_LAUNCH_COLS(SQV, FIN, UV)                                                                                 \
+  hipLaunchKernelGGL((k_merge_cols<SQV, FIN, UV>), dim3(M, (n_max + kMergeThreads * UV - 1) / (kMergeThreads * UV), \
+                     B), dim3(kMergeThreads), 0, stream, part, S, n_max, row_ids, n_dev, V, k, logits, ids, vals,  \
+                     cand, bs)
+#define NS_LAUNCH_COLS_SQ(FIN)                       \
+  switch (SP / 4) {                                  \
+    case 1: NS_LAUNCH_COLS(1, FIN, kMergeCols); break; \
+    case 2: NS_LAUNCH_COLS(2, FIN, kMergeCols); break; \
+    case 3: NS_LAUNCH_COLS(3, FIN, kMergeCols); break; \
+    default: NS_LAUNCH_COLS(4, FIN, kMergeCols); break; \
   }
   if (C == 1) {
     NS_LAUNCH_COLS_SQ(true);
+    return ns_launch_status();
+  }
+  if (C == 2 && SP <= 8) {                           // one wide chunk: no key merge
+    if (SP == 4) NS_LAUNCH_COLS(1, true, kMergeColsWide);
+    else NS_LAUNCH_COLS(2, true, kMergeColsWide);
     return ns_launch_status();
   }
   NS_LAUNCH_COLS_SQ(false);

@@ -356,11 +356,11 @@ def test_merge_paths(ns):
 
 
 def test_live_count_below_capacity(ns):
-    """Few live columns in a large n_max: the slice count follows the live n
-    on the device (a larger grid is launched), with several 4096-column merge
-    chunks only chunk 0 may be live (it then writes the result and the key
-    merge stands down), and small n at k = 8 / 16 / 64 takes the selection's
-    row-maxima or no-threshold paths."""
+    """Few live columns in a large n_max (the projection grid covers n_max,
+    the live tiles are dispatched first), n_max up to 8192 in one wide merge
+    chunk, several 4096-column chunks of which only chunk 0 may be live (it
+    then writes the result and the key merge stands down), and small n at
+    k = 8 / 16 / 64 (the selection's row-maxima or no-threshold paths)."""
     say("live count below capacity")
     rng = np.random.default_rng(13)
     V, d = 20000, 256
@@ -368,7 +368,8 @@ def test_live_count_below_capacity(ns):
     W_dev = dev_elems(W, "bf16")
     cases = [(8, 8, 0, 6000), (8, 8, 5, 6000), (8, 8, 300, 6000), (4, 16, 4096, 9000), (4, 16, 4097, 9000),
              (3, 64, 900, 12000), (8, 8, 100, 3072), (8, 16, 200, 3072), (2, 64, 70, 3072), (2, 64, 1000, 1000),
-             (20, 10, 600, 8192), (64, 16, 2000, 16384)]
+             (20, 10, 600, 8192), (64, 16, 2000, 16384), (8, 8, 7000, 8192), (4, 16, 8192, 8192),
+             (2, 64, 6000, 6100), (1, 1, 4500, 8000)]
     for M, k, n, n_max in cases:
         h = WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
         I = np.sort(rng.choice(V, size=n, replace=False))
