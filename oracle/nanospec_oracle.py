@@ -37,6 +37,9 @@ design notes):
 * R4 ``Unique`` returns ascending ids; ties in T_K go to the lower index
   (for the draft head: the lower *global* id).
 * R5 k larger than the candidate count pads with (id -1, value -inf).
+* R7 the draft head's values for the tree are log-probabilities renormalised
+  over I plus the parent's score; R8 the tree keeps the F best children of
+  each depth for expansion and the N best nodes overall (see draft_tree).
 * R6 slot-stable packing (see packed_update): rows keep their slot while
   their id stays active; entering ids fill the lowest free slots in ascending
   id order; slots of ids that left are holes.
@@ -223,6 +226,81 @@ def draft_head(h: np.ndarray, W: np.ndarray, I: np.ndarray, k: int, dtype: str):
     logits = project(h, gather_rows(W, I), dtype)
     ids, vals = draft_topk(logits, I, k)
     return logits, ids, vals
+
+
+# ---------------------------------------------------------------------------
+# Log-probabilities over the active set, and the multi-depth draft tree
+# ---------------------------------------------------------------------------
+#
+# NanoSpec, Sec. 4.1 "Experimental Setup": the draft tree has depth 5 and at
+# most 60 draft tokens; the results discussion notes that dropping tokens from
+# the draft vocabulary renormalises the draft softmax over the active set.
+# Readings R7 and R8: a node's children are the top K of its draft head, each
+# scored by the node's score plus the child's log-probability over I; the
+# next depth expands the F best children of the current depth (score
+# descending, then flat index m * K + r ascending); the final tree is the N
+# best of all generated nodes in the same order (pool index ascending on ties).
+
+
+def log_softmax_active(logits: np.ndarray) -> np.ndarray:
+    """logp[m, j] = z[m, j] - log(sum over active columns j' of exp(z[m, j'])),
+    in float64 (the softmax restricted to, and renormalised over, I)."""
+    z = np.atleast_2d(np.asarray(logits, dtype=np.float64))
+    if z.shape[1] == 0:
+        return z.copy()
+    mx = z.max(axis=1, keepdims=True)
+    return z - (mx + np.log(np.exp(z - mx).sum(axis=1, keepdims=True)))
+
+
+def draft_logprob_topk(h: np.ndarray, W: np.ndarray, I: np.ndarray, k: int, dtype: str,
+                       parent: np.ndarray = None):
+    """The draft head with log-probabilities over I: per hidden row m the top k
+    of logp[m] (the same ids as the top k of the logits), valued
+    parent[m] + logp.  Returns (logp [M x n], ids [M x k], vals [M x k])."""
+    logp = log_softmax_active(project(h, gather_rows(W, I), dtype))
+    ids, vals = draft_topk(logp, I, k)
+    if parent is not None:
+        vals = vals + np.asarray(parent, dtype=np.float64)[:, None]
+    return logp, ids, vals
+
+
+def select_best(vals: np.ndarray, ids: np.ndarray, k: int) -> np.ndarray:
+    """Flat indices of the k best candidates (value descending, flat index
+    ascending), skipping entries whose id is negative; padded with -1."""
+    v = np.asarray(vals, dtype=np.float64).reshape(-1)
+    live = np.flatnonzero(np.asarray(ids).reshape(-1) >= 0)
+    order = live[np.lexsort((live, -v[live]))][:k]
+    out = np.full(k, -1, dtype=np.int64)
+    out[:len(order)] = order
+    return out
+
+
+def draft_tree(hs: Sequence[np.ndarray], W: np.ndarray, I: np.ndarray, K: int, F: int, N: int, dtype: str):
+    """The multi-depth draft loop on one active set.  hs[t] holds the hidden
+    rows of depth t: one row (the root) at depth 0, one per frontier slot
+    after that.  Returns a dict with the node pool (ids, scores, parent pool
+    index, depth), the frontier of every depth (pool indices) and the final
+    N nodes (pool indices)."""
+    pool_ids, pool_vals, pool_parent, pool_depth = [], [], [], []
+    frontier = np.array([-1], dtype=np.int64)           # the root
+    frontiers = []
+    for t, h in enumerate(hs):
+        h = np.atleast_2d(np.asarray(h))
+        parent = np.array([pool_vals[f] if f >= 0 else 0.0 for f in frontier])
+        _, ids, vals = draft_logprob_topk(h[:len(frontier)], W, I, K, dtype, parent)
+        base = len(pool_ids)
+        for m in range(len(frontier)):
+            for r in range(K):
+                pool_ids.append(int(ids[m, r]))
+                pool_vals.append(float(vals[m, r]))
+                pool_parent.append(int(frontier[m]))
+                pool_depth.append(t)
+        best = select_best(vals, ids, F)
+        frontier = np.array([base + i for i in best if i >= 0], dtype=np.int64)
+        frontiers.append(frontier)
+    final = select_best(np.array(pool_vals), np.array(pool_ids), N)
+    return {"ids": np.array(pool_ids), "vals": np.array(pool_vals), "parent": np.array(pool_parent),
+            "depth": np.array(pool_depth), "frontiers": frontiers, "final": final}
 
 
 # ---------------------------------------------------------------------------

@@ -179,6 +179,45 @@ class _SequenceExtKeepsPrompt(O.Sequence_):
         self.S = self.S + [int(x) for x in prompt]
 
 
+def _log_softmax_raw(logits):
+    return np.atleast_2d(np.asarray(logits, np.float64)).copy()
+
+
+def _logprob_over_vocabulary(h, W, I, k, dtype, parent=None):
+    """Normalises over every row of W instead of the active set."""
+    dense = O.dense_logits(h, W, dtype)
+    lse = np.log(np.exp(dense - dense.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)) + \
+        dense.max(axis=1, keepdims=True)
+    logp = O.project(h, O.gather_rows(W, I), dtype) - lse
+    ids, vals = O.draft_topk(logp, I, k)
+    if parent is not None:
+        vals = vals + np.asarray(parent, np.float64)[:, None]
+    return logp, ids, vals
+
+
+def _logprob_no_parent(h, W, I, k, dtype, parent=None):
+    logp = O.log_softmax_active(O.project(h, O.gather_rows(W, I), dtype))
+    ids, vals = O.draft_topk(logp, I, k)
+    return logp, ids, vals
+
+
+def _select_ties_late(vals, ids, k):
+    v = np.asarray(vals, np.float64).reshape(-1)
+    live = np.flatnonzero(np.asarray(ids).reshape(-1) >= 0)
+    order = live[np.lexsort((-live, -v[live]))][:k]
+    out = np.full(k, -1, np.int64)
+    out[:len(order)] = order
+    return out
+
+
+def _select_keeps_holes(vals, ids, k):
+    v = np.asarray(vals, np.float64).reshape(-1)
+    order = np.lexsort((np.arange(len(v)), -v))[:k]
+    out = np.full(k, -1, np.int64)
+    out[:len(order)] = order
+    return out
+
+
 MUTATIONS = [
     ("top_k", _topk_tie_desc),
     ("top_k", _topk_ascending),
@@ -205,6 +244,11 @@ MUTATIONS = [
     ("packed_draft_head", _packed_head_with_holes),
     ("Sequence_", _SequenceCtxKeepsVerify),
     ("Sequence_", _SequenceExtKeepsPrompt),
+    ("log_softmax_active", _log_softmax_raw),
+    ("draft_logprob_topk", _logprob_over_vocabulary),
+    ("draft_logprob_topk", _logprob_no_parent),
+    ("select_best", _select_ties_late),
+    ("select_best", _select_keeps_holes),
 ]
 
 

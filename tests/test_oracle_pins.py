@@ -276,6 +276,79 @@ def pin_stream_modes(o):
     assert full.active().tolist() == sorted(set(prompt[-w:]))
 
 
+def pin_log_softmax(o):
+    """Closed forms: exp of the row sums to one over I, a constant added to a
+    row cancels, and logits (0, ln 2, ln 3) give log(1/6, 2/6, 3/6)."""
+    rng = np.random.default_rng(41)
+    z = rng.standard_normal((4, 9)) * 3
+    lp = o.log_softmax_active(z)
+    np.testing.assert_allclose(np.exp(lp).sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o.log_softmax_active(z + 7.5), lp, rtol=0, atol=1e-12)
+    got = o.log_softmax_active(np.array([[0.0, math.log(2), math.log(3)]]))[0]
+    np.testing.assert_allclose(got, np.log([1 / 6, 2 / 6, 3 / 6]), rtol=0, atol=1e-12)
+    assert (np.argsort(-lp, axis=1, kind="stable") == np.argsort(-z, axis=1, kind="stable")).all()
+
+
+def pin_select_best(o):
+    """Brute-force ranking of candidates with negative ids skipped."""
+    rng = np.random.default_rng(43)
+    for _ in range(20):
+        v = rng.integers(-3, 3, size=30).astype(np.float64)     # many ties
+        ids = rng.integers(-1, 5, size=30)
+        k = int(rng.integers(1, 35))
+        cand = [i for i in range(30) if ids[i] >= 0]
+        rank = {i: sum(1 for j in cand if v[j] > v[i] or (v[j] == v[i] and j < i)) for i in cand}
+        ref = sorted([i for i in cand if rank[i] < k], key=lambda i: rank[i])
+        got = o.select_best(v, ids, k)
+        assert got[:len(ref)].tolist() == ref and (got[len(ref):] == -1).all()
+
+
+GOLDEN_TREE = os.path.join(os.path.dirname(__file__), "golden", "draft_tree.json")
+
+
+def pin_draft_tree_worked_example(o):
+    """The hand-worked tree of tests/golden/draft_tree.json."""
+    from fractions import Fraction
+    with open(GOLDEN_TREE) as f:
+        g = json.load(f)
+    sym = {"ln2": math.log(2), "-ln3": -math.log(3), "0": 0.0}
+    hs = [np.array([[sym[x]] for x in row]) for row in g["h_symbolic"]]
+    W = np.asarray(g["W"], dtype=np.float32)
+    r = o.draft_tree(hs, W, np.asarray(g["I"]), g["K"], g["F"], g["N"], "fp32")
+    assert r["ids"].tolist() == g["expect_ids"]
+    probs = np.array([float(Fraction(p)) for p in g["expect_probs"]])
+    np.testing.assert_allclose(np.exp(r["vals"]), probs, rtol=1e-6, atol=0)
+    assert r["parent"].tolist() == g["expect_parent"] and r["depth"].tolist() == g["expect_depth"]
+    assert [f.tolist() for f in r["frontiers"]] == g["expect_frontiers"]
+    assert r["final"].tolist() == g["expect_final"]
+
+
+def pin_draft_tree_invariants(o):
+    """Random trees: every child's score is its parent's score plus its own
+    log-probability over I (so it never exceeds the parent's), each depth's
+    frontier is the brute-force best F of that depth's children, and the
+    final N nodes are closed under taking parents."""
+    rng = np.random.default_rng(47)
+    V, d, K, F, N = 60, 12, 3, 4, 9
+    W = rng.standard_normal((V, d)).astype(np.float32)
+    I = np.sort(rng.choice(V, size=25, replace=False))
+    hs = [rng.standard_normal((1, d))] + [rng.standard_normal((F, d)) for _ in range(3)]
+    r = o.draft_tree(hs, W, I, K, F, N, "fp32")
+    dense = W.astype(np.float64) @ np.asarray(hs[0], np.float64)[0].astype(np.float32).astype(np.float64)
+    lse = np.log(np.exp(dense[I] - dense[I].max()).sum()) + dense[I].max()
+    for i in range(K):
+        assert r["parent"][i] == -1 and abs(r["vals"][i] - (dense[r["ids"][i]] - lse)) < 1e-9
+    for i, p in enumerate(r["parent"]):
+        if p >= 0:
+            assert r["vals"][i] <= r["vals"][p] + 1e-12
+    for t, fr in enumerate(r["frontiers"]):
+        at = np.flatnonzero(r["depth"] == t)
+        best = sorted(at, key=lambda i: (-r["vals"][i], i))[:F]
+        assert fr.tolist() == best
+    chosen = set(r["final"].tolist())
+    assert all(r["parent"][i] < 0 or r["parent"][i] in chosen for i in chosen)
+
+
 GOLDEN_PACKED = os.path.join(os.path.dirname(__file__), "golden", "packed_slots.json")
 
 
@@ -349,7 +422,8 @@ PINS = [pin_worked_example, pin_widen_bf16, pin_topk_bruteforce, pin_topk_librar
         pin_prefill_planted, pin_first_occurrence, pin_stream_update,
         pin_active_set_bruteforce, pin_active_full_coverage, pin_bitmap_tail,
         pin_projection_exact, pin_gather, pin_subset_equals_dense, pin_draft_topk_global_ids,
-        pin_packed_worked_example, pin_packed_invariants, pin_packed_head, pin_stream_modes]
+        pin_packed_worked_example, pin_packed_invariants, pin_packed_head, pin_stream_modes,
+        pin_log_softmax, pin_select_best, pin_draft_tree_worked_example, pin_draft_tree_invariants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
