@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnanospec.so")
 
-SOURCES = ["state.hip", "gather.hip", "packed.hip", "draft.hip", "prefill.hip"]
+SOURCES = ["state.hip", "gather.hip", "packed.hip", "draft.hip", "tree.hip", "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

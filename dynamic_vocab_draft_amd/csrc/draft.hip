@@ -72,6 +72,41 @@ struct BatchStrides {
   size_t cand;     // chunk keys
 };
 
+// Log-probability outputs of nanospec_draft_logprob_topk (per sequence b the
+// pointers advance by M, or M * C for the chunk statistics).
+struct LogProb {
+  const float* parent;   // [B][M] score added to each row's log-probabilities (NULL: 0)
+  float* lse;            // [B][M] log-sum-exp of the row over the active columns (NULL: not written)
+  float2* stats;         // [B][M][C] per chunk: (max, sum of exp(z - max)) when C > 1
+};
+
+// Block-wide max and sum over a 1024-thread block in a fixed order; `sh`
+// holds one float per wave.  Both contain barriers and must be reached by
+// every thread.
+__device__ __forceinline__ float block_max_f32(float v, float* sh) {
+  const int tid = threadIdx.x;
+  v = ns::wave_max_f32(v);
+  if ((tid & (NS_WAVE - 1)) == 0) sh[tid / NS_WAVE] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kSelectThreads / NS_WAVE; ++i) r = fmaxf(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_sum_f32(float v, float* sh) {
+  const int tid = threadIdx.x;
+  v = ns::wave_sum_f32(v);
+  if ((tid & (NS_WAVE - 1)) == 0) sh[tid / NS_WAVE] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kSelectThreads / NS_WAVE; ++i) r += sh[i];
+  __syncthreads();
+  return r;
+}
+
 __device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
   int n = n_dev ? *n_dev : n_max;
   return n < 0 ? 0 : (n > n_max ? n_max : n);
@@ -308,15 +343,20 @@ __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
 // chunk the winners go straight to the outputs; otherwise each chunk's k
 // keys go to cand_out[m][c][k] for k_merge_keys.  The first column of every
 // thread is requested in the same round as |I|, so the partial sums are in
-// flight before |I| is known.
-template <int SQ, bool FINAL, int U>
+// flight before |I| is known.  With LOGP the emitted values are
+// parent[m] + z - lse[m], lse[m] being the log-sum-exp of row m over all
+// active columns (a block max and a sum of exp(z - max) per chunk, combined
+// by k_merge_keys when there are several); the selection itself runs on z,
+// whose order is the same.
+template <int SQ, bool FINAL, int U, bool LOGP>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __restrict__ part, int S, int n_max,
                                                               const int32_t* __restrict__ row_ids,
                                                               const int32_t* __restrict__ n_dev, int V, int k,
                                                               float* __restrict__ logits_out,
                                                               int32_t* __restrict__ out_ids,
                                                               float* __restrict__ out_vals,
-                                                              uint64_t* __restrict__ cand_out, BatchStrides bs) {
+                                                              uint64_t* __restrict__ cand_out, BatchStrides bs,
+                                                              LogProb lp) {
   constexpr int NT = kMergeThreads, CHUNK = kMergeThreads * U;
   __shared__ SelectSmem sm;
   {
@@ -379,10 +419,34 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     }
   }
   const int nlive = lim > col0 ? lim - col0 : 0;     // live slots lead: thread t, then t + NT, ...
+  float shift = 0.f;
+  if (LOGP) {
+    __shared__ float sh_red[NT / NS_WAVE];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (gid[u] >= 0) mx = fmaxf(mx, val[u]);
+    mx = block_max_f32(mx, sh_red);
+    float se = 0.f;
+    if (mx != -INFINITY) {                           // block-uniform
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (gid[u] >= 0) se += expf(val[u] - mx);
+    }
+    se = block_sum_f32(se, sh_red);
+    const size_t row = (size_t)blockIdx.z * gridDim.x + m;
+    if (final_here) {
+      const float lse = mx + logf(se);               // -inf with no live column
+      shift = (lp.parent ? lp.parent[row] : 0.f) - lse;
+      if (lp.lse && tid == 0) lp.lse[row] = lse;
+    } else if (tid == 0) {
+      lp.stats[row * gridDim.y + c] = make_float2(mx, se);
+    }
+  }
   if (final_here) {
     block_select_topk<U>(val, gid, k, nlive, sm, [&](int r, uint64_t x) {
       out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
-      out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
+      out_vals[(size_t)m * k + r] = x ? (LOGP ? ns::key_val(x) + shift : ns::key_val(x)) : -INFINITY;
     });
   } else {
     uint64_t* dst = cand_out + ((size_t)m * gridDim.y + c) * k;
@@ -391,12 +455,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
 }
 
 // k_merge_keys: the final top k of hidden row m over the C chunks' keys
-// (nk = C * k of them, at most PER per thread).
-template <int PER>
+// (nk = C * k of them, at most PER per thread).  With LOGP the chunks'
+// (max, sum) pairs give the row's log-sum-exp, combined in chunk order.
+template <int PER, bool LOGP>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __restrict__ cand, int nk, int k,
                                                               const int32_t* __restrict__ n_dev, int n_max,
                                                               int32_t* __restrict__ out_ids,
-                                                              float* __restrict__ out_vals, BatchStrides bs) {
+                                                              float* __restrict__ out_vals, BatchStrides bs,
+                                                              LogProb lp) {
   __shared__ SelectSmem sm;
   {
     const size_t b = blockIdx.y;
@@ -407,6 +473,21 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __
   }
   if (clamp_n(n_dev, n_max) <= kMergeChunk) return;   // chunk 0 already wrote the result
   const int m = blockIdx.x, tid = threadIdx.x;
+  float shift = 0.f;
+  if (LOGP) {
+    const int C = nk / k;
+    const size_t row = (size_t)blockIdx.y * gridDim.x + m;
+    const float2* st = lp.stats + row * C;
+    float mx = -INFINITY;
+    for (int c = 0; c < C; ++c) mx = fmaxf(mx, st[c].x);
+    float se = 0.f;
+    if (mx != -INFINITY)
+      for (int c = 0; c < C; ++c)
+        if (st[c].x != -INFINITY) se += st[c].y * expf(st[c].x - mx);
+    const float lse = mx + logf(se);
+    shift = (lp.parent ? lp.parent[row] : 0.f) - lse;
+    if (lp.lse && tid == 0) lp.lse[row] = lse;
+  }
   const uint64_t* src = cand + (size_t)m * nk;
   uint64_t key[PER];
 #pragma unroll
@@ -425,7 +506,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __
   }
   block_select_topk<PER>(val, gid, k, nk, sm, [&](int r, uint64_t x) {
     out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
-    out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
+    out_vals[(size_t)m * k + r] = x ? (LOGP ? ns::key_val(x) + shift : ns::key_val(x)) : -INFINITY;
   });
 }
 
@@ -527,14 +608,15 @@ size_t partial_bytes(int n_max, int M, int SP, int B) {
   return align256(partial_floats(n_max, M, SP) * B * sizeof(float));
 }
 
-int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
-                 int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
-                 const BatchStrides& bs, hipStream_t stream) {
+template <bool LOGP>
+int launch_merge_t(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
+                   int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
+                   const BatchStrides& bs, const LogProb& lp, hipStream_t stream) {
   const int C = merge_chunks(n_max);
 #define NS_LAUNCH_COLS(SQV, FIN, UV)                                                                                 \
-  hipLaunchKernelGGL((k_merge_cols<SQV, FIN, UV>), dim3(M, (n_max + kMergeThreads * UV - 1) / (kMergeThreads * UV), \
-                     B), dim3(kMergeThreads), 0, stream, part, S, n_max, row_ids, n_dev, V, k, logits, ids, vals,  \
-                     cand, bs)
+  hipLaunchKernelGGL((k_merge_cols<SQV, FIN, UV, LOGP>), dim3(M, (n_max + kMergeThreads * UV - 1) /                 \
+                     (kMergeThreads * UV), B), dim3(kMergeThreads), 0, stream, part, S, n_max, row_ids, n_dev, V, k, \
+                     logits, ids, vals, cand, bs, lp)
 #define NS_LAUNCH_COLS_SQ(FIN)                       \
   switch (SP / 4) {                                  \
     case 1: NS_LAUNCH_COLS(1, FIN, kMergeCols); break; \
@@ -556,9 +638,9 @@ int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row
 #undef NS_LAUNCH_COLS
   const int nk = C * k;
   const int per = (nk + kMergeThreads - 1) / kMergeThreads;
-#define NS_LAUNCH_KEYS(PERV) \
-  hipLaunchKernelGGL((k_merge_keys<PERV>), dim3(M, B), dim3(kMergeThreads), 0, stream, cand, nk, k, n_dev, n_max, \
-                     ids, vals, bs)
+#define NS_LAUNCH_KEYS(PERV)                                                                                       \
+  hipLaunchKernelGGL((k_merge_keys<PERV, LOGP>), dim3(M, B), dim3(kMergeThreads), 0, stream, cand, nk, k, n_dev, \
+                     n_max, ids, vals, bs, lp)
   if (per <= 1) NS_LAUNCH_KEYS(1);
   else if (per <= 2) NS_LAUNCH_KEYS(2);
   else if (per <= 4) NS_LAUNCH_KEYS(4);
@@ -566,6 +648,16 @@ int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row
   else NS_LAUNCH_KEYS(16);
 #undef NS_LAUNCH_KEYS
   return ns_launch_status();
+}
+
+int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
+                 int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
+                 const BatchStrides& bs, const LogProb* lp, hipStream_t stream) {
+  if (lp)
+    return launch_merge_t<true>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs, *lp,
+                                stream);
+  return launch_merge_t<false>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs,
+                               LogProb{nullptr, nullptr, nullptr}, stream);
 }
 
 bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
@@ -584,7 +676,8 @@ size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M,
   const int SP = (max_splits(n_max, M, d, B) + 3) & ~3;
   const int C = merge_chunks(n_max);
   const size_t keys = C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0;
-  return 256 + partial_bytes(n_max, M, SP, B) + keys;
+  const size_t stats = C > 1 ? align256((size_t)B * M * C * sizeof(float2)) : 0;
+  return 256 + partial_bytes(n_max, M, SP, B) + keys + stats;
 }
 
 size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d) {
@@ -597,7 +690,8 @@ namespace {
 
 int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
                int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k, float* logits,
-               int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream) {
+               int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream,
+               bool logp = false, const float* parent = nullptr, float* lse = nullptr) {
   if (mode != NS_PACKED && mode != NS_INDEXED) return NS_EDTYPE;
   if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
   if (!rows || !h || !topk_ids || !topk_vals || !ws) return NS_EINVAL;
@@ -629,8 +723,10 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   }
   if (rc != NS_OK) return rc;
   uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP, B));
+  float2* stats = (float2*)((char*)cand + (C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0));
+  const LogProb lp{parent, lse, stats};
   return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, B, bs,
-                      stream);
+                      logp ? &lp : nullptr, stream);
 }
 
 }  // namespace
@@ -652,6 +748,14 @@ int nanospec_batch_draft_logits_topk(const void* w, const int32_t* row_ids, cons
   if (!n_dev) return NS_EINVAL;
   return draft_call(w, NS_INDEXED, row_ids, n_dev, n_max, B, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
                     ws_bytes, stream);
+}
+
+int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
+                                int32_t n_max, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
+                                int32_t k, const float* parent, float* lse, float* logits, int32_t* topk_ids,
+                                float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return draft_call(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
+                    ws_bytes, stream, true, parent, lse);
 }
 
 }  // extern "C"

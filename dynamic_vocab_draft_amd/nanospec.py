@@ -31,6 +31,7 @@ NS_MAX_V = NS_MAX_WMAX = 1 << 20
 NS_MAX_D = 16384
 NS_MAX_BATCH = 4096
 NS_MAX_SLOTS = 16384
+NS_MAX_TREE_CAND = 4096
 
 
 class NanoSpecError(RuntimeError):
@@ -92,6 +93,10 @@ _SIGS = {
     "nanospec_batch_draft_logits_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
                                                         c_int32, c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp,
                                                         c_size, c_vp]),
+    "nanospec_draft_logprob_topk": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
+                                                   c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                   c_size, c_vp]),
+    "nanospec_tree_select": (ctypes.c_int, [c_vp, c_vp, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp]),
     "nanospec_packed_bytes": (c_size, [c_int32, c_int32]),
     "nanospec_packed_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_vp, c_size, c_vp]),
     "nanospec_packed_reset": (ctypes.c_int, [c_vp, c_vp]),
@@ -237,6 +242,23 @@ def nanospec_draft_logits_topk(rows: torch.Tensor, mode: int, row_ids: Optional[
                                            _ptr(h), M, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_vals),
                                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "nanospec_draft_logits_topk")
+
+
+def nanospec_draft_logprob_topk(rows: torch.Tensor, mode: int, row_ids: Optional[torch.Tensor],
+                                n_dev: Optional[torch.Tensor], n_max: int, V: int, d: int, dtype: int, h: torch.Tensor,
+                                M: int, k: int, parent: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                                logits: Optional[torch.Tensor], topk_ids: torch.Tensor, topk_vals: torch.Tensor,
+                                ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_draft_logprob_topk(_ptr(rows), mode, _ptr(row_ids), _ptr(n_dev), n_max, V, d, dtype, _ptr(h),
+                                            M, k, _ptr(parent), _ptr(lse), _ptr(logits), _ptr(topk_ids),
+                                            _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)), "nanospec_draft_logprob_topk")
+
+
+def nanospec_tree_select(vals: torch.Tensor, ids: torch.Tensor, C: int, B: int, k: int, out_idx: torch.Tensor,
+                         out_vals: torch.Tensor, out_ids: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_tree_select(_ptr(vals), _ptr(ids), C, B, k, _ptr(out_idx), _ptr(out_vals), _ptr(out_ids),
+                                     _stream(stream)), "nanospec_tree_select")
 
 
 def nanospec_prefill_topk(logits: torch.Tensor, L: int, V: int, dtype: int, k: int, out_ids: torch.Tensor,

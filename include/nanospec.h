@@ -79,6 +79,7 @@ extern "C" {
 #define NS_MAX_D      16384     /* hidden size; d % 8 == 0 */
 #define NS_MAX_BATCH  4096      /* sequences in one batch */
 #define NS_MAX_SLOTS  16384     /* slots of a slot-stable packed buffer */
+#define NS_MAX_TREE_CAND 4096   /* candidates of one nanospec_tree_select */
 
 typedef struct nanospec_state nanospec_state;   /* opaque host handle */
 typedef struct nanospec_batch nanospec_batch;   /* opaque host handle of B states */
@@ -330,6 +331,44 @@ int nanospec_batch_draft_logits_topk(const void* w, const int32_t* row_ids, cons
                                      const void* h, int32_t M, int32_t k, float* logits,
                                      int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
+
+/* ======================================================================
+ * Draft head with log-probabilities over the active set, for tree drafting.
+ * NanoSpec Sec. 4.1 (draft tree of depth 5) and its results discussion: with
+ * a dynamic vocabulary the draft softmax is renormalised over I.  Same
+ * arguments and rules as nanospec_draft_logits_topk, plus:
+ *   parent : [M] float32 (device) or NULL (zeros): score of hidden row m's
+ *            node in the tree;
+ *   lse    : [M] float32 output or NULL: log(sum over active j of
+ *            exp(z[m, j])), -INFINITY for an empty row;
+ * and topk_vals[m, r] = parent[m] + z[m, j_r] - lse[m] for the same top-k
+ * ids as the logits version (the shift does not change the order).  logits,
+ * when given, receives the raw z.  lse is computed in float32: a max, then a
+ * sum of exp(z - max) in a fixed order (per 4096-column chunk, combined in
+ * chunk order), so results are deterministic.  The workspace is the same as
+ * for nanospec_draft_logits_topk. */
+int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* row_ids,
+                                const int32_t* n_dev, int32_t n_max, int32_t V, int32_t d,
+                                int32_t dtype, const void* h, int32_t M, int32_t k,
+                                const float* parent, float* lse, float* logits,
+                                int32_t* topk_ids, float* topk_vals, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Best-k selection over draft-tree candidates, B independent selections:
+ *   vals, ids : [B x C] candidate scores and token ids (device); id -1 marks
+ *               an empty candidate, which is never selected;
+ *   out_idx   : [B x k] flat candidate indices of the k best, ordered by
+ *               (score desc, flat index asc); out_vals / out_ids : their
+ *               scores and token ids; padded with (-1, -INFINITY, -1) when
+ *               fewer than k candidates exist.
+ * Next frontier: the best F of the F x K children a depth's draft head wrote
+ * ([F x K] row-major, so flat index / K is the parent slot); final tree: the
+ * best N of all nodes kept so far.  C in [1, NS_MAX_TREE_CAND], k in
+ * [1, NS_MAX_K], B in [1, NS_MAX_BATCH].
+ * Errors: NS_EINVAL, NS_EHIP. */
+int nanospec_tree_select(const float* vals, const int32_t* ids, int32_t C, int32_t B,
+                         int32_t k, int32_t* out_idx, float* out_vals, int32_t* out_ids,
+                         hipStream_t stream);
 
 /* ======================================================================
  * Prefill candidates.  Sec. 3.2 prefill: P[i] = T_Kpre(z_i) for every prompt
