@@ -326,6 +326,8 @@ def main():
                  "full_gather_overlap": Head(ns.NS_PACKED, head_full_gather)}
         out["pipeline"] = pipeline_leg(torch, cfg, backbone, warm_up_state, state_part, heads, flush_fn, Wm,
                                        min(K, 40), copy_stream)
+        progress("tree drafting leg")
+        out["tree"] = tree_leg(torch, ns, cfg, W, ids, n_act, dcode, flush_fn)
         progress("stream-source ablation and W_max leg")
         out["ablation"] = ablation_leg(torch, ns, WL, cfg, W, dcode, flush_fn)
         progress("batched-sequences leg")
@@ -669,6 +671,77 @@ def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
         del bt, hs, wsb
     return {"workload": f"{cfg.name} x B independent sequences (seeds differ), batched step update + batched "
                         f"INDEXED draft head, cold, hipGraph replay of {steps} steps", "per_B": res}
+
+
+def tree_leg(torch, ns, cfg, W, ids, n_act, dcode, flush, K=10, F=10, N=60, D=5, R=20):
+    """Tree drafting on one active set (the state as the main loop left it):
+    per depth one log-probability head (1 hidden row at depth 0, F after)
+    and one best-F selection, then the best-N selection over all nodes.  The
+    cache-streaming read runs before every depth, as the draft backbone's
+    weight traffic would.  Graph replay of R trees; the reads alone are
+    subtracted.  The same loop with the plain logits head shows what the
+    log-softmax costs."""
+    P = K + (D - 1) * F * K
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 13)
+    hs = [torch.randn((1 if t == 0 else F, cfg.d), generator=g, device="cuda").to(W.dtype) for t in range(D)]
+    pool_ids = torch.empty(P, dtype=torch.int32, device="cuda")
+    pool_vals = torch.empty(P, device="cuda")
+    f_idx = torch.empty((D, F), dtype=torch.int32, device="cuda")
+    f_vals = torch.empty((D, F), device="cuda")
+    f_ids = torch.empty((D, F), dtype=torch.int32, device="cuda")
+    fin = [torch.empty(N, dtype=torch.int32, device="cuda"), torch.empty(N, device="cuda"),
+           torch.empty(N, dtype=torch.int32, device="cuda")]
+    ws = ns.alloc_workspace(cfg.w_max, F, K, cfg.d)
+
+    def tree(kind):
+        def run():
+            for i in range(R):
+                base = 0
+                for t in range(D):
+                    flush(i * D + t)
+                    if kind == "flush":
+                        continue
+                    M = 1 if t == 0 else F
+                    tv, ti = pool_vals[base:base + M * K], pool_ids[base:base + M * K]
+                    if kind == "logprob":
+                        ns.nanospec_draft_logprob_topk(W, ns.NS_INDEXED, ids, n_act, cfg.w_max, cfg.V, cfg.d, dcode,
+                                                       hs[t], M, K, None if t == 0 else f_vals[t - 1], None, None,
+                                                       ti, tv, ws)
+                    else:
+                        ns.nanospec_draft_logits_topk(W, ns.NS_INDEXED, ids, n_act, cfg.w_max, cfg.V, cfg.d, dcode,
+                                                      hs[t], M, K, None, ti, tv, ws)
+                    ns.nanospec_tree_select(tv, ti, M * K, 1, F, f_idx[t], f_vals[t], f_ids[t])
+                    base += M * K
+                if kind != "flush":
+                    ns.nanospec_tree_select(pool_vals, pool_ids, P, 1, N, fin[0], fin[1], fin[2])
+        return run
+
+    out = {}
+    for kind in ("flush", "logprob", "logits"):
+        tree(kind)()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            tree(kind)()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[kind] = float(np.median(ts)) / R
+        del gr
+    n_act_h = int(n_act.item())
+    per_tree = out["logprob"] - out["flush"]
+    return {"workload": f"{cfg.name}: depth {D}, {K} children per node, frontier {F}, final {N} nodes, "
+                        f"|I| = {n_act_h}; cold before every depth; hipGraph replay of {R} trees",
+            "tree_us": per_tree * 1e3, "per_depth_us": per_tree * 1e3 / D,
+            "tree_with_logits_head_us": (out["logits"] - out["flush"]) * 1e3,
+            "logsoftmax_cost_us_per_tree": (out["logprob"] - out["logits"]) * 1e3,
+            "draft_nodes_per_s": N / (per_tree * 1e-3)}
 
 
 def ablation_leg(torch, ns, WL, cfg, W, dcode, flush, steps=48, warm=16):

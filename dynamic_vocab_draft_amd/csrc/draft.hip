@@ -78,33 +78,20 @@ struct LogProb {
   const float* parent;   // [B][M] score added to each row's log-probabilities (NULL: 0)
   float* lse;            // [B][M] log-sum-exp of the row over the active columns (NULL: not written)
   float2* stats;         // [B][M][C] per chunk: (max, sum of exp(z - max)) when C > 1
+  int M;                 // hidden rows per sequence
 };
 
-// Block-wide max and sum over a 1024-thread block in a fixed order; `sh`
-// holds one float per wave.  Both contain barriers and must be reached by
-// every thread.
-__device__ __forceinline__ float block_max_f32(float v, float* sh) {
-  const int tid = threadIdx.x;
-  v = ns::wave_max_f32(v);
-  if ((tid & (NS_WAVE - 1)) == 0) sh[tid / NS_WAVE] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < kSelectThreads / NS_WAVE; ++i) r = fmaxf(r, sh[i]);
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ float block_sum_f32(float v, float* sh) {
-  const int tid = threadIdx.x;
-  v = ns::wave_sum_f32(v);
-  if ((tid & (NS_WAVE - 1)) == 0) sh[tid / NS_WAVE] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < kSelectThreads / NS_WAVE; ++i) r += sh[i];
-  __syncthreads();
-  return r;
+// Sum over the 64 lanes of a wave in a fixed order: an inclusive DPP scan
+// (row_shr 1, 2, 4, 8, then row_bcast 15 and 31), read from lane 63.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  const int z = __float_as_int(0.f);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x111, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x112, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x114, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x118, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(z, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
@@ -376,14 +363,26 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
   float4 pv[U][SQ];
+  // LOGP: the parent score is requested in the first round too, as a vector
+  // load (an opaque zero keeps it per lane): a scalar load would share the
+  // LDS wait counter and stall the selection's first LDS wait on memory.
+  // Without parents it reads a valid partial sum instead.
+  const size_t row = (size_t)blockIdx.z * lp.M + m;
+  float par_raw = 0.f;
   {
     const int j = col0 + tid;
     const int jc = j < cend ? j : cend - 1;
     gv[0] = row_ids ? row_ids[jc] : jc;
 #pragma unroll
     for (int q = 0; q < SQ; ++q) pv[0][q] = prow[(size_t)jc * SQ + q];
+    if (LOGP) {
+      int zero;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+      par_raw = (lp.parent ? lp.parent + row : part)[zero];
+    }
   }
   NS_ISSUE_FENCE();
+  const float par = (LOGP && lp.parent) ? par_raw : 0.f;
   const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
   const int lim = min(n, cend);                      // live columns of this chunk end here
   // With several chunks but every live column in chunk 0, chunk 0 writes the
@@ -419,38 +418,58 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     }
   }
   const int nlive = lim > col0 ? lim - col0 : 0;     // live slots lead: thread t, then t + NT, ...
-  float shift = 0.f;
+  // LOGP: each wave's (max, sum of exp(z - max)) goes to LDS before the
+  // selection, whose first barrier publishes it; wave 1 combines the 16 pairs
+  // in wave order while wave 0 finds the threshold, and the second barrier
+  // publishes the result to the emitters.  No barrier of its own.
+  __shared__ float sh_mx[NT / NS_WAVE], sh_se[NT / NS_WAVE], sh_lse;
   if (LOGP) {
-    __shared__ float sh_red[NT / NS_WAVE];
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (gid[u] >= 0) mx = fmaxf(mx, val[u]);
-    mx = block_max_f32(mx, sh_red);
+    mx = ns::wave_max_f32(mx);
     float se = 0.f;
-    if (mx != -INFINITY) {                           // block-uniform
+    if (mx != -INFINITY) {                           // wave-uniform
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (gid[u] >= 0) se += expf(val[u] - mx);
     }
-    se = block_sum_f32(se, sh_red);
-    const size_t row = (size_t)blockIdx.z * gridDim.x + m;
-    if (final_here) {
-      const float lse = mx + logf(se);               // -inf with no live column
-      shift = (lp.parent ? lp.parent[row] : 0.f) - lse;
-      if (lp.lse && tid == 0) lp.lse[row] = lse;
-    } else if (tid == 0) {
-      lp.stats[row * gridDim.y + c] = make_float2(mx, se);
+    se = wave_sum_dpp(se);
+    if ((tid & (NS_WAVE - 1)) == 0) {
+      sh_mx[tid / NS_WAVE] = mx;
+      sh_se[tid / NS_WAVE] = se;
     }
   }
+  const auto mid = [&]() {
+    if (LOGP && tid / NS_WAVE == 1) {                // wave 1: lane i takes wave i's pair
+      const int lane = tid & (NS_WAVE - 1);
+      const float wm = lane < NT / NS_WAVE ? sh_mx[lane] : -INFINITY;
+      const float ws = lane < NT / NS_WAVE ? sh_se[lane] : 0.f;
+      const float cm = ns::wave_max_f32(wm);
+      const float cs = wave_sum_dpp(wm != -INFINITY ? ws * expf(wm - cm) : 0.f);
+      if (lane == 0) {
+        if (final_here)
+          sh_lse = cm == -INFINITY ? -INFINITY : cm + logf(cs);
+        else                                         // this chunk's pair for k_merge_keys
+          lp.stats[row * gridDim.y + c] = make_float2(cm, cs);
+      }
+    }
+  };
   if (final_here) {
     block_select_topk<U>(val, gid, k, nlive, sm, [&](int r, uint64_t x) {
       out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
-      out_vals[(size_t)m * k + r] = x ? (LOGP ? ns::key_val(x) + shift : ns::key_val(x)) : -INFINITY;
-    });
+      if (LOGP) {
+        const float lse = sh_lse;
+        out_vals[(size_t)m * k + r] = x ? ns::key_val(x) + (par - lse) : -INFINITY;
+        if (r == 0 && lp.lse) lp.lse[row] = lse;
+      } else {
+        out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
+      }
+    }, mid);
   } else {
     uint64_t* dst = cand_out + ((size_t)m * gridDim.y + c) * k;
-    block_select_topk<U>(val, gid, k, nlive, sm, [&](int r, uint64_t x) { dst[r] = x; });
+    block_select_topk<U>(val, gid, k, nlive, sm, [&](int r, uint64_t x) { dst[r] = x; }, mid);
   }
 }
 
@@ -473,10 +492,12 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __
   }
   if (clamp_n(n_dev, n_max) <= kMergeChunk) return;   // chunk 0 already wrote the result
   const int m = blockIdx.x, tid = threadIdx.x;
+  const size_t row = (size_t)blockIdx.y * lp.M + m;
+  const float par_raw = *(LOGP && lp.parent ? lp.parent + row : (const float*)cand);
+  const float par = (LOGP && lp.parent) ? par_raw : 0.f;
   float shift = 0.f;
   if (LOGP) {
     const int C = nk / k;
-    const size_t row = (size_t)blockIdx.y * gridDim.x + m;
     const float2* st = lp.stats + row * C;
     float mx = -INFINITY;
     for (int c = 0; c < C; ++c) mx = fmaxf(mx, st[c].x);
@@ -484,8 +505,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_keys(const uint64_t* __
     if (mx != -INFINITY)
       for (int c = 0; c < C; ++c)
         if (st[c].x != -INFINITY) se += st[c].y * expf(st[c].x - mx);
-    const float lse = mx + logf(se);
-    shift = (lp.parent ? lp.parent[row] : 0.f) - lse;
+    const float lse = mx == -INFINITY ? -INFINITY : mx + logf(se);
+    shift = par - lse;
     if (lp.lse && tid == 0) lp.lse[row] = lse;
   }
   const uint64_t* src = cand + (size_t)m * nk;
@@ -657,7 +678,7 @@ int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row
     return launch_merge_t<true>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs, *lp,
                                 stream);
   return launch_merge_t<false>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs,
-                               LogProb{nullptr, nullptr, nullptr}, stream);
+                               LogProb{nullptr, nullptr, nullptr, M}, stream);
 }
 
 bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
@@ -724,7 +745,7 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   if (rc != NS_OK) return rc;
   uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP, B));
   float2* stats = (float2*)((char*)cand + (C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0));
-  const LogProb lp{parent, lse, stats};
+  const LogProb lp{parent, lse, stats, M};
   return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, B, bs,
                       logp ? &lp : nullptr, stream);
 }

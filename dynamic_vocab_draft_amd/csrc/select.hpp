@@ -22,7 +22,10 @@ namespace {
 // least k of them are live, so wave maxima are used when more than 64 (k - 1)
 // slots may be live, row maxima when more than 16 (k - 1), and otherwise
 // every live pair (at most 16 k) is ranked.  emit(r, key) is called once for
-// every rank r < k (key 0 when fewer than r + 1 pairs exist).
+// every rank r < k (key 0 when fewer than r + 1 pairs exist).  mid() is
+// called by every thread between the first two barriers, while wave 0 looks
+// for the threshold (work placed there by waves 1..15 is free; its LDS
+// writes are visible to every emit).
 // ---------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
 constexpr int kCandCap = 1024;
@@ -35,9 +38,13 @@ struct SelectSmem {
   int cnt;
 };
 
-template <int U, typename Emit>
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+template <int U, typename Emit, typename Mid = NoMid>
 __device__ __forceinline__ void block_select_topk(const float (&val)[U], const int (&id)[U], int k, int nlive,
-                                                  SelectSmem& sm, Emit emit) {
+                                                  SelectSmem& sm, Emit emit, Mid mid = Mid()) {
   static_assert(kSelectThreads / NS_WAVE * 4 == NS_WAVE, "one row maximum per lane of a wave");
   const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
   const int ninf = __float_as_int(-INFINITY);
@@ -89,6 +96,7 @@ __device__ __forceinline__ void block_select_topk(const float (&val)[U], const i
     const unsigned long long ball = __ballot(mine != -INFINITY && gt < k && ge >= k);
     if (lane == 0) sm.T = (ball && (by_wave || by_row)) ? sm.rmax[__ffsll(ball) - 1] : -INFINITY;
   }
+  mid();
   __syncthreads();
   const float T = sm.T;
 #pragma unroll
