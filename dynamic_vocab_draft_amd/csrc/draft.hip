@@ -771,6 +771,15 @@ int nanospec_batch_draft_logits_topk(const void* w, const int32_t* row_ids, cons
                     ws_bytes, stream);
 }
 
+int nanospec_batch_draft_logprob_topk(const void* w, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
+                                      int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
+                                      int32_t k, const float* parent, float* lse, float* logits, int32_t* topk_ids,
+                                      float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!n_dev) return NS_EINVAL;
+  return draft_call(w, NS_INDEXED, row_ids, n_dev, n_max, B, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
+                    ws_bytes, stream, true, parent, lse);
+}
+
 int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
                                 int32_t n_max, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
                                 int32_t k, const float* parent, float* lse, float* logits, int32_t* topk_ids,

@@ -97,6 +97,9 @@ _SIGS = {
                                                    c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                    c_size, c_vp]),
     "nanospec_tree_select": (ctypes.c_int, [c_vp, c_vp, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp]),
+    "nanospec_batch_draft_logprob_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                         c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                         c_size, c_vp]),
     "nanospec_packed_bytes": (c_size, [c_int32, c_int32]),
     "nanospec_packed_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_vp, c_size, c_vp]),
     "nanospec_packed_reset": (ctypes.c_int, [c_vp, c_vp]),
@@ -253,6 +256,17 @@ def nanospec_draft_logprob_topk(rows: torch.Tensor, mode: int, row_ids: Optional
                                             M, k, _ptr(parent), _ptr(lse), _ptr(logits), _ptr(topk_ids),
                                             _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
                                             _stream(stream)), "nanospec_draft_logprob_topk")
+
+
+def nanospec_batch_draft_logprob_topk(w: torch.Tensor, row_ids: torch.Tensor, n_dev: torch.Tensor, n_max: int,
+                                      B: int, V: int, d: int, dtype: int, h: torch.Tensor, M: int, k: int,
+                                      parent: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                                      logits: Optional[torch.Tensor], topk_ids: torch.Tensor, topk_vals: torch.Tensor,
+                                      ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_batch_draft_logprob_topk(_ptr(w), _ptr(row_ids), _ptr(n_dev), n_max, B, V, d, dtype, _ptr(h),
+                                                  M, k, _ptr(parent), _ptr(lse), _ptr(logits), _ptr(topk_ids),
+                                                  _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
+                                                  _stream(stream)), "nanospec_batch_draft_logprob_topk")
 
 
 def nanospec_tree_select(vals: torch.Tensor, ids: torch.Tensor, C: int, B: int, k: int, out_idx: torch.Tensor,

@@ -354,6 +354,16 @@ int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* r
                                 int32_t* topk_ids, float* topk_vals, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* nanospec_draft_logprob_topk for B independent sequences sharing W_head, in
+ * NS_INDEXED mode, with the batch layout of nanospec_batch_draft_logits_topk;
+ * parent and lse are [B x M] (parent may be NULL).  Workspace:
+ * nanospec_batch_draft_workspace_bytes. */
+int nanospec_batch_draft_logprob_topk(const void* w, const int32_t* row_ids, const int32_t* n_dev,
+                                      int32_t n_max, int32_t B, int32_t V, int32_t d, int32_t dtype,
+                                      const void* h, int32_t M, int32_t k, const float* parent,
+                                      float* lse, float* logits, int32_t* topk_ids, float* topk_vals,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Best-k selection over draft-tree candidates, B independent selections:
  *   vals, ids : [B x C] candidate scores and token ids (device); id -1 marks
  *               an empty candidate, which is never selected;

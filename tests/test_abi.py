@@ -115,6 +115,15 @@ def test_host_validation_rejects_before_launch(ns):
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # n_dev required
     assert L.nanospec_batch_draft_logits_topk(fake, fake, fake, 16, 0, 100, 64, 0, fake, 8, 8, None, fake, fake,
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # B = 0
+    # log-prob head and tree selection
+    assert L.nanospec_batch_draft_logprob_topk(fake, fake, None, 16, 2, 100, 64, 0, fake, 8, 8, None, None, None,
+                                               fake, fake, fake, 1 << 20, None) == ns.NS_EINVAL   # n_dev required
+    assert L.nanospec_draft_logprob_topk(fake, 5, fake, None, 16, 100, 64, 0, fake, 8, 8, None, None, None, fake,
+                                         fake, fake, 1 << 20, None) == ns.NS_EDTYPE               # bad mode
+    assert L.nanospec_tree_select(fake, fake, 0, 1, 8, fake, fake, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_tree_select(fake, fake, ns.NS_MAX_TREE_CAND + 1, 1, 8, fake, fake, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_tree_select(fake, fake, 10, 1, 65, fake, fake, fake, None) == ns.NS_EINVAL
+    assert L.nanospec_tree_select(None, fake, 10, 1, 8, fake, fake, fake, None) == ns.NS_EINVAL
     # stream modes
     assert L.nanospec_state_set_mode(None, ns.NS_STREAM_CTX_ONLY) == ns.NS_EINVAL
     # slot-stable packed buffer

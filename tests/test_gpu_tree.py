@@ -247,3 +247,51 @@ def test_draft_tree_loop_llama_invariants(ns):
     assert g["final"].tolist() == sorted(range(len(v)), key=lambda i: (-v[i], i))[:N]
     chosen = set(g["final"].tolist())
     assert all(p[i] < 0 or p[i] in chosen for i in chosen), "final tree not closed under parents"
+
+
+def test_batched_logprob_and_selection(ns):
+    """B sequences in one log-prob head call (different active sets and
+    counts, per-sequence parents) against the oracle by the set rule, and one
+    batched selection over the head's output, checked as the best F of its
+    own inputs."""
+    say("batched log-prob head and selection")
+    rng = np.random.default_rng(71)
+    V, d, M, k, n_max, F = 30000, 128, 6, 10, 9000, 8
+    W = WL.f32_to_bf16_bits((rng.standard_normal((V, d)) * 0.3).astype(np.float32))
+    W_dev = dev_elems(W, "bf16")
+    sizes = (3000, 40, 9000, 0, 5000)
+    B = len(sizes)
+    Is = [np.sort(rng.choice(V, size=s, replace=False)) for s in sizes]
+    ids = np.full((B, n_max), -1, np.int32)
+    for b, I in enumerate(Is):
+        ids[b, :len(I)] = I
+    hs = [WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32)) for _ in range(B)]
+    parent = rng.uniform(-5, 0, size=(B, M)).astype(np.float32)
+    ws = ns.alloc_batch_workspace(B, n_max, M, k, d)
+    tids = torch.empty((B, M, k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((B, M, k), device="cuda")
+    lse = torch.empty((B, M), device="cuda")
+    ns.nanospec_batch_draft_logprob_topk(W_dev, dev_i32(ids.reshape(-1)), dev_i32(np.array(sizes, np.int32)), n_max,
+                                         B, V, d, ns.NS_BF16, dev_elems(np.stack(hs), "bf16"), M, k,
+                                         torch.as_tensor(parent).cuda(), lse, None, tids, tvals, ws)
+    oi = torch.empty((B, F), dtype=torch.int32, device="cuda")
+    ov = torch.empty((B, F), device="cuda")
+    od = torch.empty((B, F), dtype=torch.int32, device="cuda")
+    ns.nanospec_tree_select(tvals, tids, M * k, B, F, oi, ov, od)
+    torch.cuda.synchronize()
+    ti, tv, gl = tids.cpu().numpy(), tvals.cpu().numpy(), lse.cpu().numpy()
+    gi, gv, gd = oi.cpu().numpy(), ov.cpu().numpy(), od.cpu().numpy()
+    for b, I in enumerate(Is):
+        what = f"batched log-prob seq {b} n={len(I)}"
+        p64 = parent[b].astype(np.float64)
+        logp, o_ids, o_vals = O.draft_logprob_topk(hs[b], W, I, k, "bf16", p64)
+        if len(I) == 0:
+            assert (ti[b] == -1).all() and np.isneginf(tv[b]).all() and np.isneginf(gl[b]).all(), what
+        else:
+            check_topk(ti[b], tv[b], logp + p64[:, None], I, o_ids, o_vals, k, what)
+        # The selection as a property of its own inputs: the best F of the
+        # head's candidates by (score desc, index asc), empty ones skipped.
+        cv, cid = tv[b].reshape(-1), ti[b].reshape(-1)
+        best = sorted([i for i in range(len(cv)) if cid[i] >= 0], key=lambda i: (-cv[i], i))[:F]
+        assert gi[b][:len(best)].tolist() == best and (gi[b][len(best):] == -1).all(), what
+        assert np.array_equal(gv[b][:len(best)], cv[best]) and np.array_equal(gd[b][:len(best)], cid[best]), what
