@@ -94,6 +94,17 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// d-slices for n live rows of each of B sequences: about kTargetBlocks
+// blocks, at most s_launch.  When the launch may over-split (n only known on
+// the device, n_max above kLiveRowsHint), the projection and the merge both
+// derive it from the n they read, so they agree.
+__host__ __device__ __forceinline__ int live_splits(int n, int M, int B, int s_launch) {
+  const int rt = M <= 16 ? kTile : 2 * kTile;
+  const int tiles = ((n > 0 ? n : 1) + rt - 1) / rt * B;
+  const int s = (kTargetBlocks + tiles - 1) / tiles;
+  return s < 1 ? 1 : (s > s_launch ? s_launch : s);
+}
+
 __device__ __forceinline__ int clamp_n(const int32_t* n_dev, int n_max) {
   int n = n_dev ? *n_dev : n_max;
   return n < 0 ? 0 : (n > n_max ? n_max : n);
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
-                                                         int S, int SP, float* __restrict__ part,
+                                                         int S, int adapt, int SP, float* __restrict__ part,
                                                          BatchStrides bs) {
   __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
   {
@@ -205,8 +216,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // 8 KiB run in one L2), and the tiles are dispatched in ascending order,
   // so the live ones (the lowest) come first and spread over every XCD and
   // its CUs, whatever n_max is.
-  const int r0 = (int)((blockIdx.x / (8 * S)) * 8 + (blockIdx.x & 7)) * (kTile * RT);
-  const int split = (int)((blockIdx.x >> 3) % S);
+  int r0 = (int)((blockIdx.x / (8 * S)) * 8 + (blockIdx.x & 7)) * (kTile * RT);
+  int split = (int)((blockIdx.x >> 3) % S);
   // Independent loads first: the active count and this lane's row ids.
   const int n = clamp_n(n_dev, n_max);
   int gid[RT];
@@ -214,6 +225,22 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   for (int r = 0; r < RT; ++r) {
     const int row = r0 + r * kTile + i;
     gid[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+  }
+  // With `adapt`, S was launched for a few live rows: if n calls for fewer
+  // slices, the block maps itself again and reloads its row ids (one more
+  // round trip, only when many rows are live).
+  if (adapt) {                                          // launch-uniform
+    const int S_live = live_splits(n, M, gridDim.z, S);
+    if (S_live != S) {                                  // block-uniform
+      S = S_live;
+      r0 = (int)((blockIdx.x / (8 * S)) * 8 + (blockIdx.x & 7)) * (kTile * RT);
+      split = (int)((blockIdx.x >> 3) % S);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int row = r0 + r * kTile + i;
+        gid[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+      }
+    }
   }
   if (r0 >= n) return;                                  // block-uniform: nothing live here
   bool ok[RT];
@@ -336,7 +363,8 @@ __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
 // by k_merge_keys when there are several); the selection itself runs on z,
 // whose order is the same.
 template <int SQ, bool FINAL, int U, bool LOGP>
-__global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __restrict__ part, int S, int n_max,
+__global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __restrict__ part, int S, int adapt,
+                                                              int n_max,
                                                               const int32_t* __restrict__ row_ids,
                                                               const int32_t* __restrict__ n_dev, int V, int k,
                                                               float* __restrict__ logits_out,
@@ -384,6 +412,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   NS_ISSUE_FENCE();
   const float par = (LOGP && lp.parent) ? par_raw : 0.f;
   const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
+  if (adapt) S = live_splits(n, (int)gridDim.x, gridDim.z, S);   // as the projection chose (grid: M x chunks x B)
   const int lim = min(n, cend);                      // live columns of this chunk end here
   // With several chunks but every live column in chunk 0, chunk 0 writes the
   // final result and k_merge_keys does nothing; the other chunks are idle.
@@ -596,20 +625,21 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 
 template <int NMT, int RT>
 void launch_mfma_t(dim3 grid, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
-                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int SP,
-                   float* part, const BatchStrides& bs) {
+                   const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
+                   int SP, float* part, const BatchStrides& bs) {
   hipLaunchKernelGGL((k_proj_mfma<NMT, RT>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
-                     n_dev, n_max, V, dv, (const uint4*)h, M, S, SP, part, bs);
+                     n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, SP, part, bs);
 }
 
 int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
-                const void* h, int M, int S, int SP, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
+                const void* h, int M, int S, int adapt, int SP, float* part, int B, const BatchStrides& bs,
+                hipStream_t stream) {
   const int dv = d / 8;
   const int rt = pick_rt(M);
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and exit).
   const dim3 grid((unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8 * S, 1, B);
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
-  launch_mfma_t<NMTV, RTV>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, SP, part, bs)
+  launch_mfma_t<NMTV, RTV>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
   switch ((M + 15) / 16) {
     case 1: NS_LAUNCH_MFMA(1, 1); break;
     case 2: NS_LAUNCH_MFMA(2, 2); break;
@@ -630,13 +660,14 @@ size_t partial_bytes(int n_max, int M, int SP, int B) {
 }
 
 template <bool LOGP>
-int launch_merge_t(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
+int launch_merge_t(const float* part, int S, int adapt, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
                    int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
                    const BatchStrides& bs, const LogProb& lp, hipStream_t stream) {
   const int C = merge_chunks(n_max);
 #define NS_LAUNCH_COLS(SQV, FIN, UV)                                                                                 \
   hipLaunchKernelGGL((k_merge_cols<SQV, FIN, UV, LOGP>), dim3(M, (n_max + kMergeThreads * UV - 1) /                 \
-                     (kMergeThreads * UV), B), dim3(kMergeThreads), 0, stream, part, S, n_max, row_ids, n_dev, V, k, \
+                     (kMergeThreads * UV), B), dim3(kMergeThreads), 0, stream, part, S, adapt, n_max, row_ids, n_dev, \
+                     V, k, \
                      logits, ids, vals, cand, bs, lp)
 #define NS_LAUNCH_COLS_SQ(FIN)                       \
   switch (SP / 4) {                                  \
@@ -671,13 +702,13 @@ int launch_merge_t(const float* part, int S, int SP, int n_max, const int32_t* r
   return ns_launch_status();
 }
 
-int launch_merge(const float* part, int S, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
+int launch_merge(const float* part, int S, int adapt, int SP, int n_max, const int32_t* row_ids, const int32_t* n_dev, int V,
                  int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
                  const BatchStrides& bs, const LogProb* lp, hipStream_t stream) {
   if (lp)
-    return launch_merge_t<true>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs, *lp,
+    return launch_merge_t<true>(part, S, adapt, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs, *lp,
                                 stream);
-  return launch_merge_t<false>(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs,
+  return launch_merge_t<false>(part, S, adapt, SP, n_max, row_ids, n_dev, V, M, k, logits, ids, vals, cand, B, bs,
                                LogProb{nullptr, nullptr, nullptr, M}, stream);
 }
 
@@ -724,6 +755,9 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   (void)hipGetLastError();
   const int S = launch_splits(n_dev == nullptr, n_max, M, d, dtype, B);
   const int SP = (S + 3) & ~3;
+  // Only a launch sized by kLiveRowsHint can over-split; the kernels then
+  // size S from the live n.
+  const int adapt = (dtype == NS_BF16 && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
   const int esz = dtype == NS_BF16 ? 2 : 4;
   const int C = merge_chunks(n_max);
   BatchStrides bs;
@@ -736,7 +770,7 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   bs.cand = (size_t)M * C * k;
   int rc;
   if (dtype == NS_BF16) {
-    rc = launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, S, SP, part, B, bs, stream);
+    rc = launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, S, adapt, SP, part, B, bs, stream);
   } else {
     const int mt = pick_mt(M, d, 4);
     if (mt == 0) return NS_EINVAL;
@@ -746,8 +780,8 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP, B));
   float2* stats = (float2*)((char*)cand + (C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0));
   const LogProb lp{parent, lse, stats, M};
-  return launch_merge(part, S, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, B, bs,
-                      logp ? &lp : nullptr, stream);
+  return launch_merge(part, S, adapt, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, B,
+                      bs, logp ? &lp : nullptr, stream);
 }
 
 }  // namespace
