@@ -142,6 +142,10 @@ def main():
     def draft_part(t, mode):
         comp = torch.cuda.current_stream()
         rows = W
+        if mode == "project":                      # the projection stage alone (timing)
+            ns.nanospec_draft_project(W, ns.NS_INDEXED, ids, n_act, cfg.w_max, cfg.V, cfg.d, dcode, hs[t], cfg.M,
+                                      cfg.k, ws)
+            return
         if mode == SLOTS:
             pack_update()
             ns.nanospec_draft_logits_topk(slot_rows, ns.NS_PACKED, pk.slot_ids, pk.n_slots, cfg.w_max, cfg.V, cfg.d,
@@ -233,6 +237,12 @@ def main():
         progress(f"mode {mname[m]}: {res[m]['cold_ms'] * 1e3:.2f} us/step cold")
     best = min(modes, key=lambda m: res[m]["cold_ms"])
     r = res[best]
+    # The dominant kernel, k_proj_mfma, timed on its own: the INDEXED
+    # projection stage after the state update, minus the state update alone.
+    g_proj = capture(body("project", True))
+    g_st = capture(body("project", True, True, False))
+    t_proj_ms = (time_graph(g_proj) - time_graph(g_st)) / K
+    del g_proj, g_st
 
     ms = r["cold_ms"]
     n_mean = float(np.mean(sizes[Wm:]))
@@ -240,6 +250,9 @@ def main():
     # Algorithmic bytes of one draft-head call: active rows, h, row ids, outputs.
     draft_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + n_mean * 4 + cfg.M * cfg.k * 8
     achieved = draft_bytes / (r["draft_ms"] * 1e-3) / 1e9
+    # The projection's own algorithmic bytes: active rows, h and row ids.
+    proj_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + n_mean * 4
+    proj_GBps = proj_bytes / (t_proj_ms * 1e-3) / 1e9
     # ... plus the state update: ring read, tuple ids, bitmap + id list writes.
     step_bytes = draft_bytes + cfg.w_max * 4 + (cfg.n_tree + cfg.k_ver) * 4 + ((cfg.V + 31) // 32) * 4 + n_mean * 4
 
@@ -260,10 +273,15 @@ def main():
                                f"{cfg.n_tree} draft-tree + {cfg.k_ver} verify ids per step",
                    "mode": mname[best], "cache": "cold (512 MiB streamed through the caches between steps)",
                    "mean_active": n_mean, "timing": "hipGraph replay of the timed steps"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name, mname[best]),
-                     "kernel": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols",
-                     "bytes_per_launch": draft_bytes, "avg_launch_us": r["draft_ms"] * 1e3},
+        "roofline": {"bound": "hbm", "achieved": proj_GBps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": proj_GBps / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg.name, "indexed", "traffic_bytes_per_projection"),
+                     "kernel": "k_proj_mfma (nanospec_draft_project, INDEXED)",
+                     "bytes_per_launch": proj_bytes, "avg_launch_us": t_proj_ms * 1e3,
+                     "draft_call": {"kernels": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols",
+                                    "mode": mname[best], "bytes": draft_bytes, "avg_us": r["draft_ms"] * 1e3,
+                                    "achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
+                                    "traffic": measured_traffic(cfg.name, mname[best])}},
         "step": {"alg_bytes": step_bytes, "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
                  "state_update_us": r["state_ms"] * 1e3, "draft_us": r["draft_ms"] * 1e3,
                  "warm_ms": r["warm_ms"], "eager_warm_ms": r["eager_warm_ms"],
@@ -366,11 +384,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, mode):
-    """HBM bytes per draft-head call from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when
-    there is none for this workload and mode or the kernel sources changed
-    since the counters were taken."""
+def measured_traffic(workload, mode, key="traffic_bytes_per_call"):
+    """HBM bytes per draft-head call (or, with key
+    traffic_bytes_per_projection, per k_proj_mfma launch) from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    calibration), or None when there is none for this workload and mode or
+    the kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"draft_head_{workload}_traffic.txt")
     try:
         with open(path) as f:
@@ -381,7 +400,7 @@ def measured_traffic(workload, mode):
     if kv.get("source_sha256") != kernel_source_hash() or kv.get("mode") != mode:
         return None
     try:
-        return float(kv["traffic_bytes_per_call"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -926,18 +945,20 @@ def dense_compare(torch, ns, cfg, W, h, dcode, flush, step_ms):
             "speedup_vs_dense": best / step_ms, "note": "event-bracketed single calls, cold"}
 
 
-def cpu_baseline(cfg, W, seconds):
-    """The CPU oracle as written (numpy, float64) on a bounded sample of the
-    same workload: as many decode steps as fit in about `seconds`."""
-    import oracle.nanospec_oracle as O
-    from dynamic_vocab_draft_amd import workloads as WL
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        used = max((int(i.get("num_threads", 1)) for i in threadpool_info()), default=1)
-    except ImportError:  # pragma: no cover
-        used = 1
-    script = WL.make_id_script(cfg)
-    hs = [WL.make_hidden(cfg, t) for t in range(cfg.steps)]
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_steps(cfg, W, seconds, script, hs):
+    """Decode steps of the oracle as written in about `seconds`."""
+    import oracle.nanospec_oracle as O
     done = passes = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
@@ -951,11 +972,39 @@ def cpu_baseline(cfg, W, seconds):
             if time.perf_counter() - t0 >= seconds:
                 break
         passes += 1
-    el = time.perf_counter() - t0
+    return done, passes, time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, W, seconds):
+    """The CPU oracle as written (numpy, float64) on a bounded sample of the
+    same workload: as many decode steps as fit in about `seconds` with the
+    BLAS pool on every host core, then a shorter sample on one thread, and
+    the full-vocabulary float64 head once (context for the dense
+    comparison)."""
+    import oracle.nanospec_oracle as O
+    from dynamic_vocab_draft_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        used = max((int(i.get("num_threads", 1)) for i in threadpool_info()), default=1)
+    except ImportError:  # pragma: no cover
+        threadpool_limits, used = None, 1
+    script = WL.make_id_script(cfg)
+    hs = [WL.make_hidden(cfg, t) for t in range(cfg.steps)]
+    done, passes, el = _oracle_steps(cfg, W, seconds, script, hs)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, _, e1 = _oracle_steps(cfg, W, seconds / 3, script, hs)
+        one = d1 / e1
+    t0 = time.perf_counter()
+    O.dense_logits(hs[0], W, cfg.dtype)
+    dense_s = time.perf_counter() - t0
     return {"value": done / el, "unit": "steps/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{done} decode steps of {cfg.name} ({passes} pass(es) over its {cfg.steps} steps: stream update, window, unique, gather, fp64 "
-                      f"projection, top-k) in {el:.1f} s; BLAS threads {used}, host has {os.cpu_count()} "
-                      f"logical CPUs"}
+            "sample": f"{done} decode steps of {cfg.name} ({passes} pass(es) over its {cfg.steps} steps: stream "
+                      f"update, window, unique, gather, fp64 projection, top-k) in {el:.1f} s; BLAS threads {used}, "
+                      f"host has {os.cpu_count()} logical CPUs",
+            "single_thread_steps_per_s": one, "cpu_model": _cpu_model(),
+            "dense_f64_head_s": dense_s}
 
 
 if __name__ == "__main__":

@@ -740,48 +740,84 @@ size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32
 
 namespace {
 
-int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
-               int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k, float* logits,
-               int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream,
-               bool logp = false, const float* parent = nullptr, float* lse = nullptr) {
+// Launch plan shared by the whole call and its two stages: slice count,
+// partial-sum layout and workspace regions follow from the arguments alone,
+// so nanospec_draft_project and nanospec_draft_select agree.
+struct DraftPlan {
+  int S, SP, adapt, C;
+  BatchStrides bs;
+  float* part;
+  uint64_t* cand;
+  float2* stats;
+};
+
+int draft_check(const void* rows, int32_t mode, const int32_t* row_ids, int32_t n_max, int32_t B, int32_t V,
+                int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k, void* ws, size_t ws_bytes) {
   if (mode != NS_PACKED && mode != NS_INDEXED) return NS_EDTYPE;
   if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
-  if (!rows || !h || !topk_ids || !topk_vals || !ws) return NS_EINVAL;
+  if (!rows || !h || !ws) return NS_EINVAL;
   if (mode == NS_INDEXED && !row_ids) return NS_EINVAL;
   if (V < 1 || B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
   if ((((uintptr_t)rows) & 15u) || (((uintptr_t)h) & 15u) || (((uintptr_t)ws) & 255u)) return NS_EINVAL;
   if (ws_bytes < nanospec_batch_draft_workspace_bytes(B, n_max, M, k, d)) return NS_ECAPACITY;
-  float* part = (float*)((char*)ws + 256);
-  (void)hipGetLastError();
-  const int S = launch_splits(n_dev == nullptr, n_max, M, d, dtype, B);
-  const int SP = (S + 3) & ~3;
+  return NS_OK;
+}
+
+DraftPlan draft_plan(const int32_t* n_dev, int32_t n_max, int32_t B, int32_t d, int32_t dtype, int32_t M, int32_t k,
+                     void* ws) {
+  DraftPlan p;
+  p.S = launch_splits(n_dev == nullptr, n_max, M, d, dtype, B);
+  p.SP = (p.S + 3) & ~3;
   // Only a launch sized by kLiveRowsHint can over-split; the kernels then
   // size S from the live n.
-  const int adapt = (dtype == NS_BF16 && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
+  p.adapt = (dtype == NS_BF16 && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
+  p.C = merge_chunks(n_max);
   const int esz = dtype == NS_BF16 ? 2 : 4;
-  const int C = merge_chunks(n_max);
-  BatchStrides bs;
-  bs.rows = 0;                                   // W_head (or one packed buffer) shared
-  bs.ids = (size_t)n_max;
-  bs.h = (size_t)M * d * esz / 16;
-  bs.part = partial_floats(n_max, M, SP);
-  bs.logits = (size_t)M * n_max;
-  bs.out = (size_t)M * k;
-  bs.cand = (size_t)M * C * k;
-  int rc;
-  if (dtype == NS_BF16) {
-    rc = launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, S, adapt, SP, part, B, bs, stream);
-  } else {
-    const int mt = pick_mt(M, d, 4);
-    if (mt == 0) return NS_EINVAL;
-    rc = launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, SP, part, B, bs, stream);
-  }
+  p.bs.rows = 0;                                 // W_head (or one packed buffer) shared
+  p.bs.ids = (size_t)n_max;
+  p.bs.h = (size_t)M * d * esz / 16;
+  p.bs.part = partial_floats(n_max, M, p.SP);
+  p.bs.logits = (size_t)M * n_max;
+  p.bs.out = (size_t)M * k;
+  p.bs.cand = (size_t)M * p.C * k;
+  p.part = (float*)((char*)ws + 256);
+  p.cand = (uint64_t*)((char*)p.part + partial_bytes(n_max, M, p.SP, B));
+  p.stats = (float2*)((char*)p.cand + (p.C > 1 ? align256((size_t)B * M * p.C * k * sizeof(uint64_t)) : 0));
+  return p;
+}
+
+int draft_project(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
+                  int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M, const DraftPlan& p,
+                  hipStream_t stream) {
+  (void)hipGetLastError();
+  if (dtype == NS_BF16)
+    return launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.SP, p.part, B, p.bs, stream);
+  const int mt = pick_mt(M, d, 4);
+  if (mt == 0) return NS_EINVAL;
+  return launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.SP, p.part, B, p.bs, stream);
+}
+
+int draft_select(const int32_t* row_ids, const int32_t* n_dev, int32_t n_max, int32_t B, int32_t V, int32_t M,
+                 int32_t k, float* logits, int32_t* topk_ids, float* topk_vals, const DraftPlan& p, bool logp,
+                 const float* parent, float* lse, hipStream_t stream) {
+  (void)hipGetLastError();
+  const LogProb lp{parent, lse, p.stats, M};
+  return launch_merge(p.part, p.S, p.adapt, p.SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals,
+                      p.cand, B, p.bs, logp ? &lp : nullptr, stream);
+}
+
+int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
+               int32_t B, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k, float* logits,
+               int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream,
+               bool logp = false, const float* parent = nullptr, float* lse = nullptr) {
+  int rc = draft_check(rows, mode, row_ids, n_max, B, V, d, dtype, h, M, k, ws, ws_bytes);
   if (rc != NS_OK) return rc;
-  uint64_t* cand = (uint64_t*)((char*)part + partial_bytes(n_max, M, SP, B));
-  float2* stats = (float2*)((char*)cand + (C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0));
-  const LogProb lp{parent, lse, stats, M};
-  return launch_merge(part, S, adapt, SP, n_max, row_ids, n_dev, V, M, k, logits, topk_ids, topk_vals, cand, B,
-                      bs, logp ? &lp : nullptr, stream);
+  if (!topk_ids || !topk_vals) return NS_EINVAL;
+  if (dtype != NS_BF16 && pick_mt(M, d, 4) == 0) return NS_EINVAL;
+  const DraftPlan p = draft_plan(n_dev, n_max, B, d, dtype, M, k, ws);
+  rc = draft_project(rows, mode, row_ids, n_dev, n_max, B, V, d, dtype, h, M, p, stream);
+  if (rc != NS_OK) return rc;
+  return draft_select(row_ids, n_dev, n_max, B, V, M, k, logits, topk_ids, topk_vals, p, logp, parent, lse, stream);
 }
 
 }  // namespace
@@ -812,6 +848,27 @@ int nanospec_batch_draft_logprob_topk(const void* w, const int32_t* row_ids, con
   if (!n_dev) return NS_EINVAL;
   return draft_call(w, NS_INDEXED, row_ids, n_dev, n_max, B, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
                     ws_bytes, stream, true, parent, lse);
+}
+
+int nanospec_draft_project(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
+                           int32_t n_max, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int rc = draft_check(rows, mode, row_ids, n_max, 1, V, d, dtype, h, M, k, ws, ws_bytes);
+  if (rc != NS_OK) return rc;
+  if (dtype != NS_BF16 && pick_mt(M, d, 4) == 0) return NS_EINVAL;
+  return draft_project(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M,
+                       draft_plan(n_dev, n_max, 1, d, dtype, M, k, ws), stream);
+}
+
+int nanospec_draft_select(const int32_t* row_ids, const int32_t* n_dev, int32_t n_max, int32_t V, int32_t d,
+                          int32_t dtype, int32_t M, int32_t k, float* logits, int32_t* topk_ids, float* topk_vals,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (!topk_ids || !topk_vals || !ws || V < 1 || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
+  if (((uintptr_t)ws) & 255u) return NS_EINVAL;
+  if (ws_bytes < nanospec_batch_draft_workspace_bytes(1, n_max, M, k, d)) return NS_ECAPACITY;
+  return draft_select(row_ids, n_dev, n_max, 1, V, M, k, logits, topk_ids, topk_vals,
+                      draft_plan(n_dev, n_max, 1, d, dtype, M, k, ws), false, nullptr, nullptr, stream);
 }
 
 int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,

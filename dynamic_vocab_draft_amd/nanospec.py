@@ -97,6 +97,10 @@ _SIGS = {
                                                    c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                    c_size, c_vp]),
     "nanospec_tree_select": (ctypes.c_int, [c_vp, c_vp, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp]),
+    "nanospec_draft_project": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32, c_vp,
+                                              c_int32, c_int32, c_vp, c_size, c_vp]),
+    "nanospec_draft_select": (ctypes.c_int, [c_vp, c_vp, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_vp,
+                                             c_vp, c_vp, c_vp, c_size, c_vp]),
     "nanospec_batch_draft_logprob_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                          c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                          c_size, c_vp]),
@@ -267,6 +271,22 @@ def nanospec_batch_draft_logprob_topk(w: torch.Tensor, row_ids: torch.Tensor, n_
                                                   M, k, _ptr(parent), _ptr(lse), _ptr(logits), _ptr(topk_ids),
                                                   _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
                                                   _stream(stream)), "nanospec_batch_draft_logprob_topk")
+
+
+def nanospec_draft_project(rows: torch.Tensor, mode: int, row_ids: Optional[torch.Tensor], n_dev: Optional[torch.Tensor],
+                           n_max: int, V: int, d: int, dtype: int, h: torch.Tensor, M: int, k: int, ws: torch.Tensor,
+                           stream=None) -> None:
+    _check(_lib.nanospec_draft_project(_ptr(rows), mode, _ptr(row_ids), _ptr(n_dev), n_max, V, d, dtype, _ptr(h), M, k,
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nanospec_draft_project")
+
+
+def nanospec_draft_select(row_ids: Optional[torch.Tensor], n_dev: Optional[torch.Tensor], n_max: int, V: int, d: int,
+                          dtype: int, M: int, k: int, logits: Optional[torch.Tensor], topk_ids: torch.Tensor,
+                          topk_vals: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_draft_select(_ptr(row_ids), _ptr(n_dev), n_max, V, d, dtype, M, k, _ptr(logits),
+                                      _ptr(topk_ids), _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "nanospec_draft_select")
 
 
 def nanospec_tree_select(vals: torch.Tensor, ids: torch.Tensor, C: int, B: int, k: int, out_idx: torch.Tensor,

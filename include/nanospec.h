@@ -310,6 +310,27 @@ int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* ro
                                float* topk_vals, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/* The two stages of nanospec_draft_logits_topk, for callers that place them
+ * separately (and to time the projection on its own):
+ *   nanospec_draft_project : the projection (Eq. 1 on the active rows) into
+ *       the workspace's partial sums; same arguments as the whole call minus
+ *       the outputs (k only sizes the workspace).
+ *   nanospec_draft_select  : the merge of those partial sums, top-k and the
+ *       map to global ids; writes logits / topk_ids / topk_vals exactly as
+ *       the whole call.
+ * select must follow a project call on the same workspace with the same
+ * n_dev (NULL or not), n_max, d, dtype, M and k; the pair then gives
+ * bit-identical results to nanospec_draft_logits_topk.  Errors as for the
+ * whole call. */
+int nanospec_draft_project(const void* rows, int32_t mode, const int32_t* row_ids,
+                           const int32_t* n_dev, int32_t n_max, int32_t V, int32_t d,
+                           int32_t dtype, const void* h, int32_t M, int32_t k, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+int nanospec_draft_select(const int32_t* row_ids, const int32_t* n_dev, int32_t n_max,
+                          int32_t V, int32_t d, int32_t dtype, int32_t M, int32_t k,
+                          float* logits, int32_t* topk_ids, float* topk_vals, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
 /* ======================================================================
  * The draft head for a batch of B independent sequences sharing W_head, in
  * NS_INDEXED mode: for every b, the result of nanospec_draft_logits_topk on

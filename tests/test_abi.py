@@ -115,6 +115,13 @@ def test_host_validation_rejects_before_launch(ns):
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # n_dev required
     assert L.nanospec_batch_draft_logits_topk(fake, fake, fake, 16, 0, 100, 64, 0, fake, 8, 8, None, fake, fake,
                                               fake, 1 << 20, None) == ns.NS_EINVAL       # B = 0
+    # two-stage draft head
+    assert L.nanospec_draft_project(fake, 0, fake, None, 16, 100, 60, 0, fake, 8, 8, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_draft_project(fake, 1, None, None, 16, 100, 64, 0, fake, 8, 8, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_draft_project(fake, 0, fake, None, 16, 100, 64, 0, fake, 8, 8, fake, 64, None) == ns.NS_ECAPACITY
+    assert L.nanospec_draft_select(fake, None, 16, 100, 64, 0, 8, 8, None, None, fake, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_draft_select(fake, None, 16, 100, 64, 3, 8, 8, None, fake, fake, fake, 1 << 20, None) == ns.NS_EDTYPE
+    assert L.nanospec_draft_select(fake, None, 16, 100, 64, 0, 8, 8, None, fake, fake, fake, 64, None) == ns.NS_ECAPACITY
     # log-prob head and tree selection
     assert L.nanospec_batch_draft_logprob_topk(fake, fake, None, 16, 2, 100, 64, 0, fake, 8, 8, None, None, None,
                                                fake, fake, fake, 1 << 20, None) == ns.NS_EINVAL   # n_dev required

@@ -411,6 +411,46 @@ def test_batch_mixed_merge_paths(ns):
         check_topk(ti[b], tv[b], ref, I, o_ids, o_vals, k, what)
 
 
+def test_two_stage_matches_call(ns):
+    """nanospec_draft_project + nanospec_draft_select give the whole call's
+    results bit for bit (both modes and dtypes, one and several merge
+    chunks, a live count far below n_max)."""
+    say("two-stage draft head")
+    rng = np.random.default_rng(19)
+    V, d = 20000, 128
+    for dtype in ("bf16", "fp32"):
+        Wf = (rng.standard_normal((V, d)) * 0.1).astype(np.float32)
+        W = WL.f32_to_bf16_bits(Wf) if dtype == "bf16" else Wf
+        W_dev = dev_elems(W, dtype)
+        dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
+        for M, k, n, n_max in ((8, 8, 967, 3072), (4, 16, 300, 9000), (3, 10, 9000, 12000)):
+            h = dev_elems(WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32)) if dtype == "bf16"
+                          else rng.standard_normal((M, d)).astype(np.float32), dtype)
+            I = np.sort(rng.choice(V, size=n, replace=False))
+            ids = torch.full((n_max,), -1, dtype=torch.int32, device="cuda")
+            ids[:n] = dev_i32(I)
+            n_dev = torch.tensor([n], dtype=torch.int32, device="cuda")
+            ws = ns.alloc_workspace(n_max, M, k, d)
+            outs = []
+            for staged in (False, True):
+                lg = torch.full((M, n_max), float("nan"), device="cuda")
+                ti = torch.empty((M, k), dtype=torch.int32, device="cuda")
+                tv = torch.empty((M, k), device="cuda")
+                if staged:
+                    ns.nanospec_draft_project(W_dev, ns.NS_INDEXED, ids, n_dev, n_max, V, d, dcode, h, M, k, ws)
+                    ns.nanospec_draft_select(ids, n_dev, n_max, V, d, dcode, M, k, lg, ti, tv, ws)
+                else:
+                    ns.nanospec_draft_logits_topk(W_dev, ns.NS_INDEXED, ids, n_dev, n_max, V, d, dcode, h, M, k, lg,
+                                                  ti, tv, ws)
+                torch.cuda.synchronize()
+                outs.append((lg.cpu().numpy(), ti.cpu().numpy(), tv.cpu().numpy()))
+            what = f"{dtype} M={M} k={k} n={n} n_max={n_max}"
+            assert np.array_equal(outs[0][1], outs[1][1]), what
+            assert np.array_equal(outs[0][2].view(np.uint32), outs[1][2].view(np.uint32)), what
+            assert np.array_equal(np.nan_to_num(outs[0][0], nan=7.0).view(np.uint32),
+                                  np.nan_to_num(outs[1][0], nan=7.0).view(np.uint32)), what
+
+
 def test_draft_deterministic(ns):
     say("determinism")
     cfg = WL.get_config("tiny")
