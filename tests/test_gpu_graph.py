@@ -1,7 +1,8 @@
 """HIP-graph capture of a whole decode step (state update, gather on a second
-stream, draft head in both row modes, and the batched calls): each replay,
-with eager work and synchronisations between replays, must give exactly the
-outputs of the same calls run eagerly on a twin state."""
+stream, draft head in both row modes), of the batched calls, of a step with
+the slot-stable buffer updated on a second stream, and of a tree-drafting
+step: each replay, with eager work and synchronisations between replays, must
+give exactly the outputs of the same calls run eagerly on a twin state."""
 import numpy as np
 import pytest
 import torch
@@ -146,3 +147,139 @@ def test_graph_replays_batched(ns):
         for b in range(B):                       # ids past n[b] are never written
             nb = int(sides[1]["n"][b].item())
             assert torch.equal(sides[0]["ids"][b, :nb], sides[1]["ids"][b, :nb]), f"batched replay {t}: ids"
+
+
+def test_graph_replays_slot_buffer(ns):
+    """State update, the slot-stable buffer's update on a second stream (fork
+    and join), and the head over the slot map, captured once and replayed
+    against an eager twin."""
+    cfg = WL.get_config("tiny", dtype="bf16")
+    say("graph capture of a slot-buffer step", cfg)
+    W = dev_elems(WL.make_weights(cfg), "bf16")
+    script = WL.make_id_script(cfg, 8)
+    prompt = dev_i32(script.prompt)
+    copy_stream = torch.cuda.Stream()
+
+    def side():
+        st = ns.NanoSpecState(cfg.V, cfg.w_max)
+        ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
+        d = dict(st=st, pk=ns.NanoSpecPacked(cfg.V, cfg.w_max),
+                 rows=torch.zeros((cfg.w_max, cfg.d), dtype=torch.bfloat16, device="cuda"),
+                 ids=torch.empty(cfg.w_max, dtype=torch.int32, device="cuda"),
+                 n=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                 ws=ns.alloc_workspace(cfg.w_max, cfg.M, cfg.k, cfg.d),
+                 tids=torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda"),
+                 tvals=torch.empty((cfg.M, cfg.k), device="cuda"))
+        ns.nanospec_active_vocab(st, d["ids"], d["n"])
+        ns.nanospec_packed_update(d["pk"], st, W, cfg.d, ns.NS_BF16, d["rows"])
+        return d
+
+    def step(d, tree, ver, h):
+        ns.nanospec_step_update(d["st"], tree, tree.numel(), ver, ver.numel(), d["ids"], d["n"])
+        comp = torch.cuda.current_stream()
+        copy_stream.wait_stream(comp)
+        ns.nanospec_packed_update(d["pk"], d["st"], W, cfg.d, ns.NS_BF16, d["rows"], stream=copy_stream)
+        comp.wait_stream(copy_stream)
+        ns.nanospec_draft_logits_topk(d["rows"], ns.NS_PACKED, d["pk"].slot_ids, d["pk"].n_slots, cfg.w_max, cfg.V,
+                                      cfg.d, ns.NS_BF16, h, cfg.M, cfg.k, None, d["tids"], d["tvals"], d["ws"])
+
+    g, e = side(), side()
+    tree_buf = torch.empty(cfg.n_tree, dtype=torch.int32, device="cuda")
+    ver_buf = torch.empty(cfg.k_ver, dtype=torch.int32, device="cuda")
+    h_buf = torch.empty((cfg.M, cfg.d), dtype=torch.bfloat16, device="cuda")
+
+    def load(t):
+        tree_buf.copy_(dev_i32(script.tree[t]))
+        ver_buf.copy_(dev_i32(script.ver[t]))
+        h_buf.copy_(dev_elems(WL.make_hidden(cfg, t), "bf16"))
+
+    load(0)
+    for d in (g, e):
+        step(d, tree_buf, ver_buf, h_buf)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g, tree_buf, ver_buf, h_buf)
+    torch.cuda.synchronize()
+    for t in range(1, 8):
+        load(t)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e, tree_buf, ver_buf, h_buf)
+        torch.cuda.synchronize()
+        for key in ("tids", "tvals"):
+            assert torch.equal(g[key], e[key]), f"slot replay {t}: {key}"
+        assert torch.equal(g["pk"].slot_ids, e["pk"].slot_ids), f"slot replay {t}: slot map"
+        assert torch.equal(g["pk"].n_slots, e["pk"].n_slots), f"slot replay {t}: n_slots"
+        occ = (e["pk"].slot_ids >= 0).nonzero().flatten()
+        assert torch.equal(g["rows"][occ].view(torch.int16), e["rows"][occ].view(torch.int16)), f"slot replay {t}"
+
+
+def test_graph_replays_tree(ns):
+    """A state update and a 3-depth draft tree (log-prob heads, frontier
+    selections, final selection) captured once and replayed against an
+    eager twin."""
+    cfg = WL.get_config("tiny", dtype="bf16")
+    K, F, N, D = 4, 4, 10, 3
+    say("graph capture of a tree-drafting step", cfg)
+    W = dev_elems(WL.make_weights(cfg), "bf16")
+    script = WL.make_id_script(cfg, 6)
+    prompt = dev_i32(script.prompt)
+    P = K + (D - 1) * F * K
+
+    def side():
+        st = ns.NanoSpecState(cfg.V, cfg.w_max)
+        ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
+        return dict(st=st, ids=torch.empty(cfg.w_max, dtype=torch.int32, device="cuda"),
+                    n=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    ws=ns.alloc_workspace(cfg.w_max, F, K, cfg.d),
+                    pid=torch.empty(P, dtype=torch.int32, device="cuda"), pv=torch.empty(P, device="cuda"),
+                    fi=torch.empty((D, F), dtype=torch.int32, device="cuda"), fv=torch.empty((D, F), device="cuda"),
+                    fd=torch.empty((D, F), dtype=torch.int32, device="cuda"),
+                    out=[torch.empty(N, dtype=torch.int32, device="cuda"), torch.empty(N, device="cuda"),
+                         torch.empty(N, dtype=torch.int32, device="cuda")])
+
+    hs = [torch.empty((1 if t == 0 else F, cfg.d), dtype=torch.bfloat16, device="cuda") for t in range(D)]
+    tree_buf = torch.empty(cfg.n_tree, dtype=torch.int32, device="cuda")
+    ver_buf = torch.empty(cfg.k_ver, dtype=torch.int32, device="cuda")
+
+    def step(d):
+        ns.nanospec_step_update(d["st"], tree_buf, tree_buf.numel(), ver_buf, ver_buf.numel(), d["ids"], d["n"])
+        base = 0
+        for t in range(D):
+            M = 1 if t == 0 else F
+            ti, tv = d["pid"][base:base + M * K], d["pv"][base:base + M * K]
+            ns.nanospec_draft_logprob_topk(W, ns.NS_INDEXED, d["ids"], d["n"], cfg.w_max, cfg.V, cfg.d, ns.NS_BF16,
+                                           hs[t], M, K, None if t == 0 else d["fv"][t - 1], None, None, ti, tv,
+                                           d["ws"])
+            ns.nanospec_tree_select(tv, ti, M * K, 1, F, d["fi"][t], d["fv"][t], d["fd"][t])
+            base += M * K
+        ns.nanospec_tree_select(d["pv"], d["pid"], P, 1, N, *d["out"])
+
+    def load(t):
+        tree_buf.copy_(dev_i32(script.tree[t]))
+        ver_buf.copy_(dev_i32(script.ver[t]))
+        for i, h in enumerate(hs):
+            h.copy_(dev_elems(WL.make_hidden(cfg, 10 * t + i, M=h.shape[0]), "bf16"))
+
+    g, e = side(), side()
+    load(0)
+    for d in (g, e):
+        step(d)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g)
+    torch.cuda.synchronize()
+    for t in range(1, 6):
+        load(t)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e)
+        torch.cuda.synchronize()
+        for key in ("pid", "pv", "fi", "fv", "fd"):
+            assert torch.equal(g[key], e[key]), f"tree replay {t}: {key}"
+        for a, b in zip(g["out"], e["out"]):
+            assert torch.equal(a, b), f"tree replay {t}: final"
