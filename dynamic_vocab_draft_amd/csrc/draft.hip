@@ -29,7 +29,7 @@
 //       blocks of the live tiles come first in dispatch order and are dealt
 //       evenly over the 8 XCDs and their CUs however large n_max is, and
 //       each row is read whole by one XCD.
-//   k_merge_cols (+ k_merge_keys when n_max > 4096): per hidden row m and
+//   k_merge_cols (+ k_merge_keys past one chunk): per hidden row m and
 //       4096-column chunk, a 1024-thread block sums the S partials of each
 //       active column in a fixed order and selects the chunk's k best
 //       (value, id) keys with a threshold from wave or row maxima and a rank
@@ -722,7 +722,8 @@ bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
 extern "C" {
 
 // Workspace: partial sums [B x M x n_max x SP] float32 (SP = S rounded up to
-// 4) at offset 256, then the chunk keys when n_max > 4096.
+// 4) at offset 256, then, when n_max > 4096, the chunk keys and the chunks'
+// log-sum-exp pairs.
 size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M, int32_t k, int32_t d) {
   if (B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return 0;
   const int SP = (max_splits(n_max, M, d, B) + 3) & ~3;
