@@ -376,11 +376,18 @@ DRAFT_SOURCES = ("dynamic_vocab_draft_amd/csrc/draft.hip", "dynamic_vocab_draft_
 
 
 def kernel_source_hash():
+    """sha256 of the draft-head sources with comments and blank space
+    removed, so that only a change to the code itself retires the committed
+    counter summary."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in DRAFT_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
