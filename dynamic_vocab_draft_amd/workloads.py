@@ -43,7 +43,7 @@ class Config:
     name: str
     V: int                 # vocabulary size (rows of W_head)
     d: int                 # hidden size (columns of W_head)
-    dtype: str             # "bf16" or "fp32" for W and h
+    dtype: str             # "bf16", "fp16" or "fp32" for W and h
     M: int                 # draft hidden rows per projection call
     k: int                 # draft top-k
     w_max: int             # sliding-window length W_max
@@ -67,7 +67,7 @@ class Config:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return 4 if self.dtype == "fp32" else 2
 
 
 CONFIGS = {
@@ -125,6 +125,23 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def f32_to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (round to nearest, ties to even, by
+    numpy's conversion); returns the 16-bit patterns as uint16.  Inputs stay
+    within the binary16 range (the generators' values are small)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 draws in the storage format of `dtype`: uint16 patterns for
+    bf16 and fp16, float32 itself for fp32."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "fp16":
+        return f32_to_fp16_bits(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns to float32 (input conversion for
     callers that want float views; not part of the method)."""
@@ -132,13 +149,15 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _blocked_normal(seed: np.random.SeedSequence, rows: int, cols: int, std: float,
-                    to_bf16: bool, post=None) -> np.ndarray:
+                    fmt, post=None) -> np.ndarray:
     """rows x cols N(0, std^2) in fixed blocks of rows, each block with its own
-    child seed (thread-count independent).  ``post(block_index, r0, block)``
-    may modify the float32 block before rounding."""
+    child seed (thread-count independent), stored as `fmt` ("bf16", "fp16" or
+    "fp32"; True means "bf16").  ``post(block_index, r0, block)`` may modify
+    the float32 block before rounding."""
+    fmt = "bf16" if fmt is True else ("fp32" if fmt is False else fmt)
     nblk = (rows + _BLOCK_ROWS - 1) // _BLOCK_ROWS
     seeds = seed.spawn(nblk)
-    out = np.empty((rows, cols), dtype=np.uint16 if to_bf16 else np.float32)
+    out = np.empty((rows, cols), dtype=np.float32 if fmt == "fp32" else np.uint16)
 
     def work(b):
         r0 = b * _BLOCK_ROWS
@@ -149,7 +168,7 @@ def _blocked_normal(seed: np.random.SeedSequence, rows: int, cols: int, std: flo
             blk *= np.float32(std)
         if post is not None:
             post(b, r0, blk)
-        out[r0:r1] = f32_to_bf16_bits(blk) if to_bf16 else blk
+        out[r0:r1] = to_bits(blk, fmt)
         return None
 
     if nblk == 1:
@@ -213,7 +232,7 @@ def _uniform_distinct(V: int, n: int, rng: np.random.Generator) -> np.ndarray:
 def make_weights(cfg: Config, V: Optional[int] = None) -> np.ndarray:
     """W_head [V x d]: uint16 bf16 bits (bf16 configs) or float32."""
     V = cfg.V if V is None else V
-    return _blocked_normal(_seq(cfg, 0), V, cfg.d, 0.02, cfg.dtype == "bf16")
+    return _blocked_normal(_seq(cfg, 0), V, cfg.d, 0.02, cfg.dtype)
 
 
 def make_hidden(cfg: Config, step: int, M: Optional[int] = None) -> np.ndarray:
@@ -221,7 +240,7 @@ def make_hidden(cfg: Config, step: int, M: Optional[int] = None) -> np.ndarray:
     M = cfg.M if M is None else M
     g = np.random.default_rng(_seq(cfg, 1, step))
     x = g.standard_normal((M, cfg.d), dtype=np.float32)
-    return f32_to_bf16_bits(x) if cfg.dtype == "bf16" else x
+    return to_bits(x, cfg.dtype)
 
 
 # --------------------------------------------------------------------------

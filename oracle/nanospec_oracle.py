@@ -64,12 +64,23 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 
     bf16 elements are given as their 16-bit patterns (uint16); a bf16 value is
     the float32 whose upper half is those bits, and float32 -> float64 is
-    exact.  fp32 elements widen exactly too."""
+    exact.  fp16 elements are uint16 patterns of IEEE binary16, decoded from
+    their fields.  fp32 elements widen exactly too."""
     if dtype == "bf16":
         b = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return b.view(np.float32).astype(np.float64)
     if dtype == "fp32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "fp16":
+        # IEEE-754 binary16 from its fields: sign, 5-bit exponent (bias 15),
+        # 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24).  Inputs
+        # are finite (the generators never make Inf or NaN).
+        u = np.asarray(x, dtype=np.uint16).astype(np.int64)
+        sign = np.where(u >> 15, -1.0, 1.0)
+        e = (u >> 10) & 0x1F
+        f = (u & 0x3FF).astype(np.float64)
+        mag = np.where(e == 0, f * 2.0 ** -24, (1024.0 + f) * np.exp2((e - 25).astype(np.float64)))
+        return sign * mag
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

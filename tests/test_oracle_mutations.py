@@ -82,6 +82,19 @@ def _widen_shift15(x, dtype):
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
+def _widen_fp16_bias14(x, dtype):
+    if dtype == "fp16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.int64)
+        sign = np.where(u >> 15, -1.0, 1.0)
+        e = (u >> 10) & 0x1F
+        f = (u & 0x3FF).astype(np.float64)
+        return sign * np.where(e == 0, f * 2.0 ** -24, (1024.0 + f) * np.exp2((e - 24).astype(np.float64)))
+    return _widen_orig(x, dtype)
+
+
+_widen_orig = O.widen
+
+
 def _draft_topk_by_column(logits, I, k):
     logits = np.atleast_2d(np.asarray(logits, np.float64))
     I = np.asarray(I, np.int64)
@@ -231,6 +244,7 @@ MUTATIONS = [
     ("project", _project_drop_last_col),
     ("project", _project_sign),
     ("widen", _widen_shift15),
+    ("widen", _widen_fp16_bias14),
     ("draft_topk", _draft_topk_by_column),
     ("draft_topk", _draft_topk_no_map),
     ("init_stream", _init_stream_sorted_union),

@@ -81,6 +81,21 @@ def pin_widen_bf16(o):
     assert o.widen(f, "fp32").tolist() == [float(x) for x in f]
 
 
+def pin_widen_fp16(o):
+    # Known IEEE binary16 bit patterns.
+    cases = {
+        0x3C00: 1.0, 0xBC00: -1.0, 0x4000: 2.0, 0xC200: -3.0, 0x3800: 0.5, 0x3555: 0.25 * (1 + 0x155 / 1024),
+        0x7BFF: 65504.0, 0x0400: 2.0 ** -14, 0x03FF: 1023 * 2.0 ** -24, 0x0001: 2.0 ** -24, 0x0000: 0.0,
+        0x4248: 3.140625,
+    }
+    bits = np.array(list(cases.keys()), dtype=np.uint16)
+    got = o.widen(bits, "fp16")
+    assert got.dtype == np.float64
+    assert got.tolist() == list(cases.values())
+    neg0 = o.widen(np.array([0x8000], np.uint16), "fp16")[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+
+
 def _rank_topk(z, K):
     """Brute force from the rank characterisation: index i is among the top K
     iff fewer than K entries beat it, where j beats i when z_j > z_i or
@@ -418,7 +433,7 @@ def pin_packed_head(o):
         np.testing.assert_allclose(vals[m], dense[m, ref], rtol=0, atol=1e-9)
 
 
-PINS = [pin_worked_example, pin_widen_bf16, pin_topk_bruteforce, pin_topk_library_cases,
+PINS = [pin_worked_example, pin_widen_bf16, pin_widen_fp16, pin_topk_bruteforce, pin_topk_library_cases,
         pin_prefill_planted, pin_first_occurrence, pin_stream_update,
         pin_active_set_bruteforce, pin_active_full_coverage, pin_bitmap_tail,
         pin_projection_exact, pin_gather, pin_subset_equals_dense, pin_draft_topk_global_ids,
