@@ -49,6 +49,13 @@ __device__ __forceinline__ float key_val(uint64_t k) { return unord_f32((uint32_
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+// IEEE binary16 halves of a 32-bit pair, widened exactly to float32.
+__device__ __forceinline__ float fp16_lo(uint32_t pair) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(pair & 0xFFFFu));
+}
+__device__ __forceinline__ float fp16_hi(uint32_t pair) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(pair >> 16));
+}
 
 // ---------------------------------------------------------------------------
 // Wave-level helpers

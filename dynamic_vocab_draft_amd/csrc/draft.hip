@@ -13,7 +13,8 @@
 // Two kernels per call:
 //   k_proj_mfma  (bf16) / k_proj_valu (fp32): partial products.  For bf16 a
 //       block owns 16*RT active rows (the A operand of
-//       v_mfma_f32_16x16x32_bf16, one row per lane group of 16) and all M
+//       v_mfma_f32_16x16x32_bf16, or _f16 for fp16, one row per lane group
+//       of 16) and all M
 //       hidden rows (the B operand, padded to 16*NMT), over one of S slices
 //       of d; its 4 waves split the slice further and their tiles are summed
 //       through LDS.  Splitting d across blocks is what puts enough blocks on
@@ -44,6 +45,10 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// bf16 and fp16 go through the matrix cores; fp32 through the VALU kernel.
+__host__ __device__ constexpr bool is_mfma_dtype(int dtype) { return dtype == NS_BF16 || dtype == NS_FP16; }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kProjThreads = 256;                 // VALU projection block
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
 // ---------------------------------------------------------------------------
 // bf16 MFMA projection over one slice of d.  grid = (row tiles, S slices).
 // ---------------------------------------------------------------------------
-template <int NMT, int RT>
+template <int NMT, int RT, bool F16>
 __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict__ rows, int mode,
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
@@ -297,8 +302,12 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           const uint4 av = (kok && ok[r]) ? a[kk][r] : z;
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                              __builtin_bit_cast(bf16x8_t, bv), acc[r][t], 0, 0, 0);
+          if (F16)
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av),
+                                                               __builtin_bit_cast(f16x8_t, bv), acc[r][t], 0, 0, 0);
+          else
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                __builtin_bit_cast(bf16x8_t, bv), acc[r][t], 0, 0, 0);
         }
       }
     }
@@ -582,7 +591,7 @@ int pick_rt(int M) { return M <= 16 ? 1 : 2; }
 // whose partial sums cost more, and calls with n known on the host use n_max.
 // Other dtypes use one slice.
 int launch_splits(bool n_known, int n_max, int M, int d, int dtype, int B) {
-  if (dtype != NS_BF16) return 1;
+  if (!is_mfma_dtype(dtype)) return 1;
   const int ksteps = (d / 8 + 3) / 4;
   int s_hi = ksteps / (kPW * kKC);
   s_hi = s_hi < 1 ? 1 : (s_hi > kMaxSplits ? kMaxSplits : s_hi);
@@ -623,14 +632,15 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   return ns_launch_status();
 }
 
-template <int NMT, int RT>
+template <int NMT, int RT, bool F16>
 void launch_mfma_t(dim3 grid, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
                    int SP, float* part, const BatchStrides& bs) {
-  hipLaunchKernelGGL((k_proj_mfma<NMT, RT>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
+  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
                      n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, SP, part, bs);
 }
 
+template <bool F16>
 int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
                 const void* h, int M, int S, int adapt, int SP, float* part, int B, const BatchStrides& bs,
                 hipStream_t stream) {
@@ -639,7 +649,7 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and exit).
   const dim3 grid((unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8 * S, 1, B);
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
-  launch_mfma_t<NMTV, RTV>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
+  launch_mfma_t<NMTV, RTV, F16>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
   switch ((M + 15) / 16) {
     case 1: NS_LAUNCH_MFMA(1, 1); break;
     case 2: NS_LAUNCH_MFMA(2, 2); break;
@@ -755,7 +765,7 @@ struct DraftPlan {
 int draft_check(const void* rows, int32_t mode, const int32_t* row_ids, int32_t n_max, int32_t B, int32_t V,
                 int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k, void* ws, size_t ws_bytes) {
   if (mode != NS_PACKED && mode != NS_INDEXED) return NS_EDTYPE;
-  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (dtype != NS_BF16 && dtype != NS_FP32 && dtype != NS_FP16) return NS_EDTYPE;
   if (!rows || !h || !ws) return NS_EINVAL;
   if (mode == NS_INDEXED && !row_ids) return NS_EINVAL;
   if (V < 1 || B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
@@ -771,9 +781,9 @@ DraftPlan draft_plan(const int32_t* n_dev, int32_t n_max, int32_t B, int32_t d, 
   p.SP = (p.S + 3) & ~3;
   // Only a launch sized by kLiveRowsHint can over-split; the kernels then
   // size S from the live n.
-  p.adapt = (dtype == NS_BF16 && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
+  p.adapt = (is_mfma_dtype(dtype) && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
   p.C = merge_chunks(n_max);
-  const int esz = dtype == NS_BF16 ? 2 : 4;
+  const int esz = dtype == NS_FP32 ? 4 : 2;
   p.bs.rows = 0;                                 // W_head (or one packed buffer) shared
   p.bs.ids = (size_t)n_max;
   p.bs.h = (size_t)M * d * esz / 16;
@@ -792,7 +802,11 @@ int draft_project(const void* rows, int32_t mode, const int32_t* row_ids, const 
                   hipStream_t stream) {
   (void)hipGetLastError();
   if (dtype == NS_BF16)
-    return launch_mfma(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.SP, p.part, B, p.bs, stream);
+    return launch_mfma<false>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.SP, p.part, B, p.bs,
+                              stream);
+  if (dtype == NS_FP16)
+    return launch_mfma<true>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.SP, p.part, B, p.bs,
+                             stream);
   const int mt = pick_mt(M, d, 4);
   if (mt == 0) return NS_EINVAL;
   return launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.SP, p.part, B, p.bs, stream);
@@ -814,7 +828,7 @@ int draft_call(const void* rows, int32_t mode, const int32_t* row_ids, const int
   int rc = draft_check(rows, mode, row_ids, n_max, B, V, d, dtype, h, M, k, ws, ws_bytes);
   if (rc != NS_OK) return rc;
   if (!topk_ids || !topk_vals) return NS_EINVAL;
-  if (dtype != NS_BF16 && pick_mt(M, d, 4) == 0) return NS_EINVAL;
+  if (!is_mfma_dtype(dtype) && pick_mt(M, d, 4) == 0) return NS_EINVAL;
   const DraftPlan p = draft_plan(n_dev, n_max, B, d, dtype, M, k, ws);
   rc = draft_project(rows, mode, row_ids, n_dev, n_max, B, V, d, dtype, h, M, p, stream);
   if (rc != NS_OK) return rc;
@@ -856,7 +870,7 @@ int nanospec_draft_project(const void* rows, int32_t mode, const int32_t* row_id
                            void* ws, size_t ws_bytes, hipStream_t stream) {
   const int rc = draft_check(rows, mode, row_ids, n_max, 1, V, d, dtype, h, M, k, ws, ws_bytes);
   if (rc != NS_OK) return rc;
-  if (dtype != NS_BF16 && pick_mt(M, d, 4) == 0) return NS_EINVAL;
+  if (!is_mfma_dtype(dtype) && pick_mt(M, d, 4) == 0) return NS_EINVAL;
   return draft_project(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M,
                        draft_plan(n_dev, n_max, 1, d, dtype, M, k, ws), stream);
 }
@@ -864,7 +878,7 @@ int nanospec_draft_project(const void* rows, int32_t mode, const int32_t* row_id
 int nanospec_draft_select(const int32_t* row_ids, const int32_t* n_dev, int32_t n_max, int32_t V, int32_t d,
                           int32_t dtype, int32_t M, int32_t k, float* logits, int32_t* topk_ids, float* topk_vals,
                           void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (dtype != NS_BF16 && dtype != NS_FP32 && dtype != NS_FP16) return NS_EDTYPE;
   if (!topk_ids || !topk_vals || !ws || V < 1 || !draft_dims_ok(n_max, M, k, d)) return NS_EINVAL;
   if (((uintptr_t)ws) & 255u) return NS_EINVAL;
   if (ws_bytes < nanospec_batch_draft_workspace_bytes(1, n_max, M, k, d)) return NS_ECAPACITY;

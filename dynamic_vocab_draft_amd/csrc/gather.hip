@@ -59,8 +59,8 @@ int ns::launch_row_copy(const void* w, int V, int dvec, const int32_t* ids, cons
 extern "C" int nanospec_gather_rows(const void* w, int32_t V, int32_t d, int32_t dtype, const int32_t* ids,
                                     const int32_t* n_dev, int32_t n_max, void* out, hipStream_t stream) {
   if (!w || !ids || !out || V < 1 || n_max < 1 || d < 8 || d > NS_MAX_D || (d % 8) != 0) return NS_EINVAL;
-  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (dtype != NS_BF16 && dtype != NS_FP32 && dtype != NS_FP16) return NS_EDTYPE;
   if ((((uintptr_t)w) & 15u) || (((uintptr_t)out) & 15u)) return NS_EINVAL;
-  const int esz = dtype == NS_BF16 ? 2 : 4;
+  const int esz = dtype == NS_FP32 ? 4 : 2;
   return ns::launch_row_copy(w, V, d * esz / 16, ids, nullptr, n_dev, n_max, out, stream);
 }

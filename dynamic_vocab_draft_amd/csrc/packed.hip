@@ -289,7 +289,7 @@ int nanospec_packed_slots(const nanospec_packed* pk, const int32_t** slot_ids, c
 int nanospec_packed_update(nanospec_packed* pk, const nanospec_state* st, const void* w, int32_t d,
                            int32_t dtype, void* rows, hipStream_t stream) {
   if (!pk || !st || !w || !rows || d < 8 || d > NS_MAX_D || (d % 8) != 0) return NS_EINVAL;
-  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (dtype != NS_BF16 && dtype != NS_FP32 && dtype != NS_FP16) return NS_EDTYPE;
   if ((((uintptr_t)w) & 15u) || (((uintptr_t)rows) & 15u)) return NS_EINVAL;
   if (st->view.V != pk->V || st->view.w_max > pk->cap) return NS_EINVAL;
   (void)hipGetLastError();
@@ -297,7 +297,7 @@ int nanospec_packed_update(nanospec_packed* pk, const nanospec_state* st, const 
                      stream, (const uint32_t*)st->view.bitmap, view_of(pk));
   int rc = ns_launch_status();
   if (rc != NS_OK) return rc;
-  const int esz = dtype == NS_BF16 ? 2 : 4;
+  const int esz = dtype == NS_FP32 ? 4 : 2;
   return ns::launch_row_copy(w, pk->V, d * esz / 16, pk->enter_id, pk->enter_slot, pk->hdr + 1, pk->cap, rows,
                              stream, kCopyBlocks);
 }

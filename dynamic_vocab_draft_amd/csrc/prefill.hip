@@ -53,11 +53,22 @@ struct Cands {
   }
 };
 
+// Element types are the NS_* dtype codes: NS_BF16 and NS_FP16 (2 bytes,
+// 8 per 16-byte vector) and NS_FP32 (4 bytes, 4 per vector).
+__host__ __device__ constexpr int elem_bytes(int ET) { return ET == NS_FP32 ? 4 : 2; }
+
+// Element e of a 32-bit word pair (e = 0: low half) widened to float32.
+template <int ET>
+__device__ __forceinline__ float half_elem(uint32_t w, int e) {
+  if (ET == NS_BF16) return e ? ns::bf16_hi(w) : ns::bf16_lo(w);
+  return e ? ns::fp16_hi(w) : ns::fp16_lo(w);
+}
+
 // Scans one batch of 16-byte vectors (vector q0 + u * threads for u < U);
 // vectors past the row were loaded clamped and are skipped.
-template <bool BF16, int CAP>
+template <int ET, int CAP>
 __device__ __forceinline__ void scan_batch(const uint4 (&x)[kPrefillUnroll], int q0, int nvec, Cands<CAP>& c) {
-  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int EPV = 16 / elem_bytes(ET);
 #pragma unroll
   for (int u = 0; u < kPrefillUnroll; ++u) {
     const int q = q0 + u * kPrefillThreads;
@@ -66,9 +77,9 @@ __device__ __forceinline__ void scan_batch(const uint4 (&x)[kPrefillUnroll], int
     float v[EPV];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (BF16) {
-        v[2 * e] = ns::bf16_lo(wv[e]);
-        v[2 * e + 1] = ns::bf16_hi(wv[e]);
+      if (ET != NS_FP32) {
+        v[2 * e] = half_elem<ET>(wv[e], 0);
+        v[2 * e + 1] = half_elem<ET>(wv[e], 1);
       } else {
         v[e] = __uint_as_float(wv[e]);
       }
@@ -83,7 +94,7 @@ __device__ __forceinline__ void scan_batch(const uint4 (&x)[kPrefillUnroll], int
   }
 }
 
-template <bool BF16, bool VEC, int CAP>
+template <int ET, bool VEC, int CAP>
 __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restrict__ Z, int V, int k,
                                                              int32_t* __restrict__ out_ids,
                                                              float* __restrict__ out_vals) {
@@ -93,10 +104,10 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
   Cands<CAP> c;
   c.init();
   if (VEC) {
-    constexpr int EPV = BF16 ? 8 : 4;     // elements per 16-byte vector
+    constexpr int EPV = 16 / elem_bytes(ET);   // elements per 16-byte vector
     constexpr int STEP = kPrefillThreads * kPrefillUnroll;
     const int nvec = V / EPV;
-    const uint4* __restrict__ p = (const uint4*)((const char*)Z + row * (size_t)V * (BF16 ? 2 : 4));
+    const uint4* __restrict__ p = (const uint4*)((const char*)Z + row * (size_t)V * elem_bytes(ET));
     // Two register batches, a and b, alternate so that the loads of one are
     // in flight while the other is scanned.  Indices are clamped into the row,
     // so every load is in bounds.  The loop trip count is the same for all
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
         b[u] = p[q < nvec ? q : 0];
       }
       NS_ISSUE_FENCE();
-      scan_batch<BF16, CAP>(a, base + tid, nvec, c);
+      scan_batch<ET, CAP>(a, base + tid, nvec, c);
       c.floor = fmaxf(c.floor, ns::wave_max_f32(c.kth(k)));
       if (base + STEP >= nvec) break;                   // uniform
 #pragma unroll
@@ -125,13 +136,13 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
         a[u] = p[q < nvec ? q : 0];
       }
       NS_ISSUE_FENCE();
-      scan_batch<BF16, CAP>(b, base + STEP + tid, nvec, c);
+      scan_batch<ET, CAP>(b, base + STEP + tid, nvec, c);
       c.floor = fmaxf(c.floor, ns::wave_max_f32(c.kth(k)));
     }
   } else {
-    if (BF16) {
+    if (ET != NS_FP32) {
       const uint16_t* __restrict__ p = (const uint16_t*)Z + row * (size_t)V;
-      for (int e = tid; e < V; e += kPrefillThreads) c.add(__uint_as_float((uint32_t)p[e] << 16), e);
+      for (int e = tid; e < V; e += kPrefillThreads) c.add(half_elem<ET>((uint32_t)p[e], 0), e);
     } else {
       const float* __restrict__ p = (const float*)Z + row * (size_t)V;
       for (int e = tid; e < V; e += kPrefillThreads) c.add(p[e], e);
@@ -143,10 +154,10 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
   });
 }
 
-template <bool BF16, bool VEC>
+template <int ET, bool VEC>
 void launch_cap(int cap, const void* Z, int L, int V, int k, int32_t* ids, float* vals, hipStream_t s) {
 #define NS_LAUNCH_PREFILL(C) \
-  hipLaunchKernelGGL((k_prefill<BF16, VEC, C>), dim3(L), dim3(kPrefillThreads), 0, s, Z, V, k, ids, vals)
+  hipLaunchKernelGGL((k_prefill<ET, VEC, C>), dim3(L), dim3(kPrefillThreads), 0, s, Z, V, k, ids, vals)
   switch (cap) {
     case 4: NS_LAUNCH_PREFILL(4); break;
     case 8: NS_LAUNCH_PREFILL(8); break;
@@ -161,20 +172,23 @@ void launch_cap(int cap, const void* Z, int L, int V, int k, int32_t* ids, float
 
 extern "C" int nanospec_prefill_topk(const void* logits, int32_t L, int32_t V, int32_t dtype, int32_t k,
                                      int32_t* out_ids, float* out_vals, hipStream_t stream) {
-  if (dtype != NS_BF16 && dtype != NS_FP32) return NS_EDTYPE;
+  if (dtype != NS_BF16 && dtype != NS_FP32 && dtype != NS_FP16) return NS_EDTYPE;
   if (L < 0 || V < 1 || k < 1 || k > NS_MAX_K || k > V) return NS_EINVAL;
   if (L == 0) return NS_OK;
   if (!logits || !out_ids || !out_vals) return NS_EINVAL;
-  const int esz = dtype == NS_BF16 ? 2 : 4;
+  const int esz = elem_bytes(dtype);
   const bool vec = (((uintptr_t)logits) & 15u) == 0 && (((size_t)V * esz) % 16) == 0;
   const int cap = k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64;
   (void)hipGetLastError();
   if (dtype == NS_BF16) {
-    if (vec) launch_cap<true, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
-    else launch_cap<true, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    if (vec) launch_cap<NS_BF16, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    else launch_cap<NS_BF16, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
+  } else if (dtype == NS_FP16) {
+    if (vec) launch_cap<NS_FP16, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    else launch_cap<NS_FP16, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
   } else {
-    if (vec) launch_cap<false, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
-    else launch_cap<false, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    if (vec) launch_cap<NS_FP32, true>(cap, logits, L, V, k, out_ids, out_vals, stream);
+    else launch_cap<NS_FP32, false>(cap, logits, L, V, k, out_ids, out_vals, stream);
   }
   return ns_launch_status();
 }

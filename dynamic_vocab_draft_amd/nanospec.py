@@ -22,7 +22,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnanospec.so")
 
 NS_OK, NS_EINVAL, NS_EDTYPE, NS_ECAPACITY, NS_EHIP = 0, 1, 2, 3, 4
-NS_BF16, NS_FP32 = 0, 1
+NS_BF16, NS_FP32, NS_FP16 = 0, 1, 2
 NS_PACKED, NS_INDEXED = 0, 1
 NS_STATUS_BAD_ID = 0x1
 NS_STREAM_FULL, NS_STREAM_CTX_ONLY, NS_STREAM_EXT_ONLY = 0, 1, 2
@@ -140,6 +140,8 @@ def dtype_code(t: torch.Tensor) -> int:
         return NS_BF16
     if t.dtype == torch.float32:
         return NS_FP32
+    if t.dtype == torch.float16:
+        return NS_FP16
     raise NanoSpecError(NS_EDTYPE, f"dtype {t.dtype}")
 
 

@@ -58,6 +58,7 @@ extern "C" {
 /* ---- element types of W_head, h and logits ---------------------------- */
 #define NS_BF16 0        /* bfloat16, stored as 16-bit patterns */
 #define NS_FP32 1        /* IEEE float32 */
+#define NS_FP16 2        /* IEEE binary16, stored as 16-bit patterns */
 
 /* ---- row modes of nanospec_draft_logits_topk --------------------------- */
 #define NS_PACKED  0     /* rows = packed buffer [n_max x d]; row j is rows[j] */
@@ -295,9 +296,10 @@ int nanospec_packed_update(nanospec_packed* pk, const nanospec_state* st,
  *             when n_max > 4096, room for per-chunk top-k keys and
  *             log-sum-exp pairs; no initialisation needed).  Calls sharing a workspace must be
  *             ordered.
- * Arithmetic: bf16 products are exact in float32 and summed in float32 on the
- * matrix cores (v_mfma_f32_16x16x32_bf16), in slices of d whose partial sums
- * are added in a fixed order; fp32 inputs use float32 FMAs.  No float
+ * Arithmetic: bf16 and fp16 products are exact in float32 and summed in
+ * float32 on the matrix cores (v_mfma_f32_16x16x32_bf16 / _f16), in slices of
+ * d whose partial sums are added in a fixed order; fp32 inputs use float32
+ * FMAs.  No float
  * atomics: the same arguments and inputs give the same results (the slice
  * count depends on n_max, M, d and the live count).
  * row_ids must be distinct apart from holes.
@@ -405,7 +407,7 @@ int nanospec_tree_select(const float* vals, const int32_t* ids, int32_t C, int32
 /* ======================================================================
  * Prefill candidates.  Sec. 3.2 prefill: P[i] = T_Kpre(z_i) for every prompt
  * position i.
- *   logits   : [L x V] target logits, NS_BF16 or NS_FP32, row-major.
+ *   logits   : [L x V] target logits, NS_BF16, NS_FP16 or NS_FP32, row-major.
  *   out_ids  : [L x k] int32, out_vals : [L x k] float32 (exact: the stored
  *              logits widened to float32), each row ordered by (value desc,
  *              id asc).  out_ids may be fed to nanospec_stream_append with

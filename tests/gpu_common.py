@@ -32,16 +32,21 @@ def dev_i32(x):
 
 
 def dev_elems(x: np.ndarray, dtype: str) -> torch.Tensor:
-    """bf16 bit patterns (uint16) or float32 array -> device tensor."""
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16)).cuda().view(torch.bfloat16)
+    """bf16 / fp16 bit patterns (uint16) or float32 array -> device tensor."""
+    if dtype in ("bf16", "fp16"):
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16)).cuda()
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
 
 
 def host_elems(t: torch.Tensor, dtype: str) -> np.ndarray:
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp16"):
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
+
+
+def dcode_of(ns, dtype: str) -> int:
+    return {"bf16": ns.NS_BF16, "fp32": ns.NS_FP32, "fp16": ns.NS_FP16}[dtype]
 
 
 def tol(ref):

@@ -7,7 +7,7 @@ import torch
 
 import oracle.nanospec_oracle as O
 from dynamic_vocab_draft_amd import workloads as WL
-from tests.gpu_common import bitmap_from_ids, check_logits, check_topk, dev_elems, dev_i32, say
+from tests.gpu_common import dcode_of, bitmap_from_ids, check_logits, check_topk, dev_elems, dev_i32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,7 @@ def run_batch(ns, name, B, steps, check_steps, dtype=None, vary=False):
         h_dev = dev_elems(np.stack(hs), base.dtype)
         logits.fill_(float("nan"))
         ns.nanospec_batch_draft_logits_topk(W_dev, ids, n, w_max, B, V, d,
-                                            ns.NS_BF16 if base.dtype == "bf16" else ns.NS_FP32, h_dev, M, k, logits,
+                                            dcode_of(ns, base.dtype), h_dev, M, k, logits,
                                             tids, tvals, ws)
         torch.cuda.synchronize()
         n_h, ids_h, bm_h = n.cpu().numpy(), ids.cpu().numpy(), bm.cpu().numpy().view(np.uint32)

@@ -8,7 +8,7 @@ import torch
 
 import oracle.nanospec_oracle as O
 from dynamic_vocab_draft_amd import workloads as WL
-from tests.gpu_common import check_logits, check_topk, dev_elems, dev_i32, say
+from tests.gpu_common import dcode_of, check_logits, check_topk, dev_elems, dev_i32, say
 from tests.test_gpu_parity import GpuSeq, check_state
 
 pytestmark = pytest.mark.gpu
@@ -58,7 +58,7 @@ def run_mode(ns, name, mode, steps, head_steps, prefill_k=0):
             tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
             tvals = torch.empty((cfg.M, cfg.k), device="cuda")
             ns.nanospec_draft_logits_topk(dev, ns.NS_INDEXED, g.ids, g.n, cfg.w_max, cfg.V, cfg.d,
-                                          ns.NS_BF16 if cfg.dtype == "bf16" else ns.NS_FP32,
+                                          dcode_of(ns, cfg.dtype),
                                           dev_elems(h, cfg.dtype), cfg.M, cfg.k, logits, tids, tvals, ws)
             torch.cuda.synchronize()
             ref, o_ids, o_vals = O.draft_head(h, W, I, cfg.k, cfg.dtype)

@@ -10,7 +10,7 @@ import torch
 
 import oracle.nanospec_oracle as O
 from dynamic_vocab_draft_amd import workloads as WL
-from tests.gpu_common import check_logits, check_topk, dev_elems, dev_i32, host_elems, say
+from tests.gpu_common import dcode_of, check_logits, check_topk, dev_elems, dev_i32, host_elems, say
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ class Packed:
         self.V, self.d = cfg.V, cfg.d
         self.w_max = w_max or cfg.w_max
         self.cap = cap or self.w_max
-        self.dcode = ns.NS_BF16 if cfg.dtype == "bf16" else ns.NS_FP32
+        self.dcode = dcode_of(ns, cfg.dtype)
         self.st = ns.NanoSpecState(self.V, self.w_max)
         self.pk = ns.NanoSpecPacked(self.V, self.cap)
         self.rows = new_rows(self.cap, self.d, cfg.dtype)

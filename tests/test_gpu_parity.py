@@ -7,7 +7,8 @@ import torch
 
 import oracle.nanospec_oracle as O
 from dynamic_vocab_draft_amd import workloads as WL
-from tests.gpu_common import (bitmap_from_ids, check_logits, check_topk, dev_elems, dev_i32, host_elems, say)
+from tests.gpu_common import (bitmap_from_ids, check_logits, check_topk, dcode_of, dev_elems, dev_i32, host_elems,
+                               say)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +73,7 @@ def run_draft(ns, W_dev, h_dev, I, n_max, V, d, dtype, M, k, mode, packed=None, 
     ids[:len(I)] = dev_i32(I)
     if n_dev is None:
         n_dev = torch.tensor([len(I)], dtype=torch.int32, device="cuda")
-    dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
+    dcode = dcode_of(ns, dtype)
     logits = torch.full((M, n_max), float("nan"), device="cuda") if with_logits else None
     tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((M, k), dtype=torch.float32, device="cuda")
@@ -308,7 +309,7 @@ def test_draft_edges(ns):
         check_topk(out["ids"], out["vals"], ref_logits, valid, o_ids, o_vals, k, "holes")
         # n_dev = NULL means n = n_max; row_ids = NULL (PACKED) means id = row index
         Wsub_dev = W_dev[:64].contiguous()
-        dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
+        dcode = dcode_of(ns, dtype)
         tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
         tvals = torch.empty((M, k), dtype=torch.float32, device="cuda")
         ws = ns.alloc_workspace(64, M, k, d)
@@ -422,7 +423,7 @@ def test_two_stage_matches_call(ns):
         Wf = (rng.standard_normal((V, d)) * 0.1).astype(np.float32)
         W = WL.f32_to_bf16_bits(Wf) if dtype == "bf16" else Wf
         W_dev = dev_elems(W, dtype)
-        dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
+        dcode = dcode_of(ns, dtype)
         for M, k, n, n_max in ((8, 8, 967, 3072), (4, 16, 300, 9000), (3, 10, 9000, 12000)):
             h = dev_elems(WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32)) if dtype == "bf16"
                           else rng.standard_normal((M, d)).astype(np.float32), dtype)
@@ -473,7 +474,7 @@ def test_prefill_edges(ns):
             Z = WL.f32_to_bf16_bits(Zf) if dtype == "bf16" else Zf
             pid = torch.empty((L, k), dtype=torch.int32, device="cuda")
             pval = torch.empty((L, k), dtype=torch.float32, device="cuda")
-            ns.nanospec_prefill_topk(dev_elems(Z, dtype), L, V, ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32, k,
+            ns.nanospec_prefill_topk(dev_elems(Z, dtype), L, V, dcode_of(ns, dtype), k,
                                      pid, pval)
             torch.cuda.synchronize()
             o_ids, o_vals = O.prefill_topk(Z, k, dtype)
@@ -580,3 +581,51 @@ def test_prefill_config(ns):
     out = run_draft(ns, dev_elems(W, "bf16"), dev_elems(h, "bf16"), I, cfg.w_max, cfg.V, cfg.d, "bf16", cfg.M,
                     cfg.k, ns.NS_INDEXED)
     check_draft(out, h, W, I, cfg.k, "bf16", "prefill projection")
+
+
+def test_fp16_paths(ns):
+    """IEEE binary16 weights, hidden rows and logits: the draft head in both
+    modes (one and several merge chunks, M above 16), the row gather and the
+    prefill top-k (bit-exact), and the log-prob head."""
+    say("fp16 paths")
+    rng = np.random.default_rng(23)
+    V, d = 12000, 256
+    W = WL.f32_to_fp16_bits((rng.standard_normal((V, d)) * 0.05).astype(np.float32))
+    W_dev = dev_elems(W, "fp16")
+    for M, k, n, n_max in ((8, 8, 967, 3072), (20, 10, 2000, 2048), (4, 16, 5000, 9000)):
+        h = WL.f32_to_fp16_bits(rng.standard_normal((M, d)).astype(np.float32))
+        I = np.sort(rng.choice(V, size=n, replace=False))
+        for mode in (ns.NS_INDEXED, ns.NS_PACKED):
+            out = run_draft(ns, W_dev, dev_elems(h, "fp16"), I, n_max, V, d, "fp16", M, k, mode)
+            check_draft(out, h, W, I, k, "fp16", f"fp16 M={M} k={k} n={n} n_max={n_max} mode={mode}")
+            if mode == ns.NS_PACKED:
+                got = host_elems(out["packed"], "fp16")[:n]
+                assert np.array_equal(got, W[I]), "fp16 gather"
+    # prefill over fp16 logits: exact ids and values
+    L, Vp, kp = 64, 5003, 4
+    Z = WL.f32_to_fp16_bits((rng.standard_normal((L, Vp)) * 3).astype(np.float32))
+    for vec in (False, True):
+        Vq = Vp if not vec else 5000                  # 5000 * 2 bytes is a multiple of 16
+        Zq = np.ascontiguousarray(Z[:, :Vq])
+        oi = torch.empty((L, kp), dtype=torch.int32, device="cuda")
+        ov = torch.empty((L, kp), device="cuda")
+        ns.nanospec_prefill_topk(dev_elems(Zq, "fp16"), L, Vq, dcode_of(ns, "fp16"), kp, oi, ov)
+        torch.cuda.synchronize()
+        ref_ids, ref_vals = O.prefill_topk(Zq, kp, "fp16")
+        assert np.array_equal(oi.cpu().numpy(), ref_ids), f"fp16 prefill ids (vector path {vec})"
+        assert np.array_equal(ov.cpu().numpy().astype(np.float64), ref_vals), f"fp16 prefill values ({vec})"
+    # log-prob head
+    M, k, n = 6, 10, 1500
+    h = WL.f32_to_fp16_bits(rng.standard_normal((M, d)).astype(np.float32))
+    I = np.sort(rng.choice(V, size=n, replace=False))
+    ids = torch.full((3072,), -1, dtype=torch.int32, device="cuda")
+    ids[:n] = dev_i32(I)
+    tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((M, k), device="cuda")
+    ws = ns.alloc_workspace(3072, M, k, d)
+    ns.nanospec_draft_logprob_topk(W_dev, ns.NS_INDEXED, ids, torch.tensor([n], dtype=torch.int32, device="cuda"),
+                                   3072, V, d, ns.NS_FP16, dev_elems(h, "fp16"), M, k, None, None, None, tids, tvals,
+                                   ws)
+    torch.cuda.synchronize()
+    logp, o_ids, o_vals = O.draft_logprob_topk(h, W, I, k, "fp16")
+    check_topk(tids.cpu().numpy(), tvals.cpu().numpy(), logp, I, o_ids, o_vals, k, "fp16 log-prob head")

@@ -19,7 +19,7 @@ import torch
 
 import oracle.nanospec_oracle as O
 from dynamic_vocab_draft_amd import workloads as WL
-from tests.gpu_common import check_topk, dev_elems, dev_i32, say, tol
+from tests.gpu_common import dcode_of, check_topk, dev_elems, dev_i32, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def logprob_call(ns, W_dev, I, n_max, V, d, dtype, h, M, k, parent, mode=None, w
     ids = torch.full((n_max,), -1, dtype=torch.int32, device="cuda")
     ids[:len(I)] = dev_i32(I)
     n_dev = torch.tensor([len(I)], dtype=torch.int32, device="cuda")
-    dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
+    dcode = dcode_of(ns, dtype)
     rows = W_dev
     if mode == ns.NS_PACKED:
         rows = torch.zeros((n_max, d), dtype=W_dev.dtype, device="cuda")
@@ -124,7 +124,7 @@ def gpu_tree(ns, W_dev, I, n_max, V, d, dtype, hs, K, F, N):
     ids = torch.full((n_max,), -1, dtype=torch.int32, device="cuda")
     ids[:len(I)] = dev_i32(I)
     n_dev = torch.tensor([len(I)], dtype=torch.int32, device="cuda")
-    dcode = ns.NS_BF16 if dtype == "bf16" else ns.NS_FP32
+    dcode = dcode_of(ns, dtype)
     pool_ids = torch.full((P,), -7, dtype=torch.int32, device="cuda")
     pool_vals = torch.full((P,), float("nan"), device="cuda")
     f_idx = torch.empty((D, F), dtype=torch.int32, device="cuda")
