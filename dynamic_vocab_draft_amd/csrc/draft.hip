@@ -19,10 +19,11 @@
 //       of d; its 4 waves split the slice further and their tiles are summed
 //       through LDS.  Splitting d across blocks is what puts enough blocks on
 //       the 256 CUs: ~1k active rows x 8 KiB is only ~60 row tiles, and one
-//       CU alone cannot pull a tile's 128 KiB fast enough.  Every load of a
-//       wave's slice is issued before the first MFMA waits on it.  Padded
-//       B-operand lanes (m >= M) read the same address as a real lane, so
-//       they cost no extra traffic, and are zeroed.  Each block writes its
+//       CU alone cannot pull a tile's 128 KiB fast enough.  Both operands
+//       reach the matrix cores through per-wave LDS buffers filled by direct
+//       global->LDS loads that read each row as a contiguous 128-byte run
+//       (double-buffered batches of two k-steps).  Padded B-operand lanes
+//       (m >= M) are zeroed.  Each block writes its
 //       partial sums (deterministic; no atomics) to partial[m][j][s], the S
 //       slices of one column side by side (row stride SP = S rounded up to
 //       4) so the merge reads them with 16-byte loads.  The grid is 1-D per
@@ -50,6 +51,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 // bf16 and fp16 go through the matrix cores; fp32 through the VALU kernel.
 __host__ __device__ constexpr bool is_mfma_dtype(int dtype) { return dtype == NS_BF16 || dtype == NS_FP16; }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kProjThreads = 256;                 // VALU projection block
 constexpr int kProjWaves = kProjThreads / NS_WAVE;
@@ -59,7 +61,7 @@ constexpr size_t kHLdsBytes = 65536;              // LDS budget for staged hidde
 constexpr int kPW = 4;                            // waves per MFMA projection block
 constexpr int kPThreads = kPW * NS_WAVE;
 constexpr int kTile = 16;                         // rows per MFMA tile
-constexpr int kKC = 4;                            // 32-column steps loaded per batch
+constexpr int kKC = 4;                            // 32-column steps per wave and slice, at least
 constexpr int kTargetBlocks = 1536;               // MFMA blocks aimed for when choosing S
 constexpr int kMaxSplits = 16;
 constexpr int kLiveRowsHint = 3072;               // live rows assumed when sizing S without n
@@ -194,8 +196,51 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA projection over one slice of d.  grid = (row tiles, S slices).
+// bf16 / fp16 MFMA projection over one slice of d, with both operands staged
+// through LDS by direct global->LDS loads (global_load_lds_dwordx4).
+//
+// A wave owns RT tiles of 16 rows and a range of 32-column k-steps, taken in
+// batches of kDmaKC.  One load instruction of a batch fills 16 * 4 kDmaKC
+// bytes of LDS: lane L reads row q RPI + L / CPR of the tile at 16-byte
+// position p = L % CPR of the batch window, so each row is read as one
+// contiguous 16 CPR-byte run (8 rows x 128 B per instruction instead of the
+// 16 rows x 64 B that the MFMA lane layout would ask of a direct load; the
+// load units then touch half as many cache lines).  The LDS image is
+// row-major; position p of row r holds window chunk p ^ (r mod CPR), so the
+// ds_read_b128 of an MFMA fragment (lane (i, g) wants chunk 4 kk + g of row
+// i) spreads 8 consecutive lanes over distinct banks.  Hidden rows (M <= 16)
+// take the same route, aliased to row M - 1 past M.
+//
+// Buffers are per wave and double-buffered: the next batch is requested
+// before the current one is read, and the wait is an explicit vmcnt of one
+// batch's load count.  The LDS reads are inline-asm ds_read_b128 followed by
+// an explicit lgkmcnt(0): the compiler would otherwise wait for every load
+// still in flight (it cannot tell the two buffers' loads apart across the
+// loop).  No block barrier until the four waves' tiles are summed.
 // ---------------------------------------------------------------------------
+constexpr int kDmaKC = 2;                          // k-steps per batch (128-byte row runs)
+
+__device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)p;
+}
+
+__device__ __forceinline__ uint4 lds_read_b128(const uint4* p) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(lds_addr(p)));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Ties a value read by lds_read_b128 to the point after the lgkmcnt wait.
+__device__ __forceinline__ void lds_ready(uint4& x) {
+  u32x4 v = {x.x, x.y, x.z, x.w};
+  asm volatile("" : "+v"(v));
+  x = make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void dma16(const uint4* src, uint4* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
 template <int NMT, int RT, bool F16>
 __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict__ rows, int mode,
                                                          const int32_t* __restrict__ row_ids,
@@ -203,7 +248,18 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          int dv, const uint4* __restrict__ h, int M,
                                                          int S, int adapt, int SP, float* __restrict__ part,
                                                          BatchStrides bs) {
+  constexpr int KC = kDmaKC;
+  constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
+  constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction
+  constexpr int NI = kTile / RPI;                  // load instructions per 16 rows
+  constexpr int TB = kTile * CPR;                  // uint4 of one tile's batch window
+  constexpr bool BDMA = NMT == 1;                  // hidden rows through LDS too (M <= 16)
+  __shared__ uint4 abuf0[kPW][RT * TB];
+  __shared__ uint4 abuf1[kPW][RT * TB];
+  __shared__ uint4 bbuf0[kPW][BDMA ? TB : 1];
+  __shared__ uint4 bbuf1[kPW][BDMA ? TB : 1];
   __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
+  __shared__ int sh_ok[RT * kTile];
   {
     const size_t b = blockIdx.z;
     rows += b * bs.rows;
@@ -212,8 +268,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
     h += b * bs.h;
     part += b * bs.part;
   }
-  __shared__ int sh_ok[RT * kTile];
-  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), w = tid / NS_WAVE;
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / NS_WAVE);   // wave-uniform, so branches on it are scalar
   const int i = lane & 15, g = lane >> 4;
   // Workgroups are dealt to the 8 XCDs round-robin (block L to XCD L % 8).
   // Block L takes row tile 8 (L / 8S) + L % 8 and slice (L / 8) % S: each
@@ -249,13 +305,37 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   }
   if (r0 >= n) return;                                  // block-uniform: nothing live here
   bool ok[RT];
-  const uint4* src[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const int row = r0 + r * kTile + i;
     ok[r] = row < n && gid[r] >= 0 && gid[r] < V;
-    src[r] = rows + (size_t)(ok[r] ? (mode == NS_INDEXED ? gid[r] : row) : 0) * dv;
     if (w == 0 && lane < kTile) sh_ok[r * kTile + lane] = ok[r];
+  }
+  // Load sources.  Row tr of a tile is requested by the lanes of instruction
+  // tr / RPI with L / CPR == tr % RPI; lanes 0..15 hold the tile's row ids.
+  // Rows that are not live read row 0 of `rows` (in bounds) and are zeroed
+  // as MFMA operands.
+  const int rsub = lane / CPR, cpos = lane % CPR;
+  const uint4* asrc[RT][NI];
+  int apos[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int tr = q * RPI + rsub;
+    apos[q] = cpos ^ (tr & (CPR - 1));                  // window chunk this lane fetches
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int gsh = __shfl(gid[r], tr, NS_WAVE);
+      const int oks = __shfl((int)ok[r], tr, NS_WAVE);
+      asrc[r][q] = rows + (size_t)(oks ? (mode == NS_INDEXED ? gsh : r0 + r * kTile + tr) : 0) * dv;
+    }
+  }
+  const uint4* hsrc[BDMA ? NI : 1];
+  if constexpr (BDMA) {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int m = q * RPI + rsub;
+      hsrc[q] = h + (size_t)(m < M ? m : M - 1) * dv;
+    }
   }
   const uint4* hrow[NMT];
   bool m_ok[NMT];
@@ -279,29 +359,58 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
     for (int t = 0; t < NMT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int s0 = s_begin; s0 < s_end; s0 += kKC) {
-    uint4 a[kKC][RT];
-    uint4 b[kKC][NMT];
+  const int swz_i = i & (CPR - 1);
+
+  // Requests batch s0 into one buffer pair.  Chunks past the wave's range
+  // or past d load column 0 of the same row (their products are zeroed).
+  auto issue = [&](int s0, uint4 (&ab)[kPW][RT * TB], uint4 (&bb)[kPW][BDMA ? TB : 1],
+                   uint4 (&bq)[KC][NMT]) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): earlier reads of these buffers done
 #pragma unroll
-    for (int kk = 0; kk < kKC; ++kk) {
-      const int c8 = (s0 + kk) * 4 + g;
-      const int cc = ((s0 + kk) < s_end && c8 < dv) ? c8 : 0;
+    for (int q = 0; q < NI; ++q) {
+      const int c = s0 * 4 + apos[q];
+      const int cc = (c < s_end * 4 && c < dv) ? c : 0;
 #pragma unroll
-      for (int r = 0; r < RT; ++r) a[kk][r] = src[r][cc];
-#pragma unroll
-      for (int t = 0; t < NMT; ++t) b[kk][t] = hrow[t][cc];
+      for (int r = 0; r < RT; ++r) dma16(asrc[r][q] + cc, &ab[w][r * TB + q * NS_WAVE]);
+      if constexpr (BDMA) dma16(hsrc[q] + cc, &bb[w][q * NS_WAVE]);
     }
-    NS_ISSUE_FENCE();
+    if constexpr (!BDMA) {
 #pragma unroll
-    for (int kk = 0; kk < kKC; ++kk) {
+      for (int kk = 0; kk < KC; ++kk) {
+        const int c8 = (s0 + kk) * 4 + g;
+        const int cc = ((s0 + kk) < s_end && c8 < dv) ? c8 : 0;
+#pragma unroll
+        for (int t = 0; t < NMT; ++t) bq[kk][t] = hrow[t][cc];
+      }
+    }
+  };
+  auto compute = [&](int s0, const uint4 (&ab)[kPW][RT * TB], const uint4 (&bb)[kPW][BDMA ? TB : 1],
+                     const uint4 (&bq)[KC][NMT]) {
+    uint4 af[KC][RT], bf[KC];
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const int off = i * CPR + ((4 * kk + g) ^ swz_i);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) af[kk][r] = lds_read_b128(&ab[w][r * TB + off]);
+      if constexpr (BDMA) bf[kk] = lds_read_b128(&bb[w][off]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) lds_ready(af[kk][r]);
+      if constexpr (BDMA) lds_ready(bf[kk]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
       const int c8 = (s0 + kk) * 4 + g;
       const bool kok = (s0 + kk) < s_end && c8 < dv;
 #pragma unroll
       for (int t = 0; t < NMT; ++t) {
-        const uint4 bv = (kok && m_ok[t]) ? b[kk][t] : z;
+        const uint4 bv = (kok && m_ok[t]) ? (BDMA ? bf[kk] : bq[kk][t]) : z;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-          const uint4 av = (kok && ok[r]) ? a[kk][r] : z;
+          const uint4 av = (kok && ok[r]) ? af[kk][r] : z;
           if (F16)
             acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av),
                                                                __builtin_bit_cast(f16x8_t, bv), acc[r][t], 0, 0, 0);
@@ -310,6 +419,36 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                                 __builtin_bit_cast(bf16x8_t, bv), acc[r][t], 0, 0, 0);
         }
       }
+    }
+  };
+  // vmcnt immediate (gfx9 encoding, expcnt and lgkmcnt left at their maxima)
+  // that waits until at most one batch's loads are outstanding.
+  constexpr int NLOADS = NI * RT + (BDMA ? NI : KC * NMT);
+  static_assert(NLOADS < 64, "vmcnt range");
+  constexpr int kWaitOneBatch = (NLOADS & 0xF) | (0x7 << 4) | (0xF << 8) | ((NLOADS >> 4) << 14);
+  constexpr int kWaitAll = 0x0F70;
+  uint4 b0[KC][NMT], b1[KC][NMT];
+  if (s_begin < s_end) {                                // wave-uniform
+    issue(s_begin, abuf0, bbuf0, b0);
+    NS_ISSUE_FENCE();
+    for (int s0 = s_begin; s0 < s_end; s0 += 2 * KC) {
+      if (s0 + KC < s_end) {
+        issue(s0 + KC, abuf1, bbuf1, b1);
+        NS_ISSUE_FENCE();
+        __builtin_amdgcn_s_waitcnt(kWaitOneBatch);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+      }
+      compute(s0, abuf0, bbuf0, b0);
+      if (s0 + KC >= s_end) break;
+      if (s0 + 2 * KC < s_end) {
+        issue(s0 + 2 * KC, abuf0, bbuf0, b0);
+        NS_ISSUE_FENCE();
+        __builtin_amdgcn_s_waitcnt(kWaitOneBatch);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+      }
+      compute(s0 + KC, abuf1, bbuf1, b1);
     }
   }
 #pragma unroll
@@ -583,7 +722,7 @@ int pick_mt(int M, int d, int esz) {
 int pick_rt(int M) { return M <= 16 ? 1 : 2; }
 
 // Number of d-slices S for the MFMA path: about kTargetBlocks blocks, each
-// wave keeping at least one batch of kKC steps.  When the live row count is
+// wave keeping at least kKC k-steps.  When the live row count is
 // only known on the device (n_dev given) and M <= 16, S is sized as if at
 // most kLiveRowsHint rows of each sequence were live, so a few live rows out
 // of a large n_max still spread over the chip; the partial sums then cost at
