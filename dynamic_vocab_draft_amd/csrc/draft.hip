@@ -67,8 +67,9 @@ constexpr int kMaxSplits = 16;
 constexpr int kLiveRowsHint = 3072;               // live rows assumed when sizing S without n
 
 
-// Per-sequence element strides of a batched call (sequence b = blockIdx.z,
-// or blockIdx.y for k_merge_keys); all zero for a single sequence.
+// Per-sequence element strides of a batched call (sequence b = blockIdx.z in
+// the merge and the fp32 projection, blockIdx.y in k_merge_keys, decoded from
+// the 1-D grid in k_proj_mfma); all zero for a single sequence.
 struct BatchStrides {
   size_t rows;     // uint4 units (0: W_head shared by all sequences)
   size_t ids;      // row_ids / n_dev: ids per sequence (n_dev advances by 1)
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
                                                          int S, int adapt, int SP, float* __restrict__ part,
-                                                         BatchStrides bs) {
+                                                         BatchStrides bs, int B) {
   constexpr int KC = kDmaKC;
   constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
   constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction
@@ -260,8 +261,17 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   __shared__ uint4 bbuf1[kPW][BDMA ? TB : 1];
   __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
   __shared__ int sh_ok[RT * kTile];
+  // The 1-D grid is read as (tile group, sequence, slice, XCD lane), tile
+  // group slowest: L = ((tg B + b) S + s) 8 + x.  Row tile tg 8 + x of
+  // sequence b and slice s.  Dispatch then runs over the low (live) tiles of
+  // every sequence before any sequence's high tiles, and every slice of a
+  // tile goes to the same XCD (L mod 8).  kblk = (tg S + s) 8 + x is the
+  // block's index among its sequence's blocks; for B = 1 it is L.
+  const unsigned L = blockIdx.x;
+  const int seq = (int)((L / (8u * (unsigned)S)) % (unsigned)B);
+  const unsigned kblk = (L / (8u * (unsigned)S * (unsigned)B)) * (8u * (unsigned)S) + L % (8u * (unsigned)S);
   {
-    const size_t b = blockIdx.z;
+    const size_t b = (size_t)seq;
     rows += b * bs.rows;
     if (row_ids) row_ids += b * bs.ids;
     if (n_dev) n_dev += b;
@@ -277,8 +287,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // 8 KiB run in one L2), and the tiles are dispatched in ascending order,
   // so the live ones (the lowest) come first and spread over every XCD and
   // its CUs, whatever n_max is.
-  int r0 = (int)((blockIdx.x / (8 * S)) * 8 + (blockIdx.x & 7)) * (kTile * RT);
-  int split = (int)((blockIdx.x >> 3) % S);
+  int r0 = (int)((kblk / (8 * S)) * 8 + (kblk & 7)) * (kTile * RT);
+  int split = (int)((kblk >> 3) % S);
   // Independent loads first: the active count and this lane's row ids.
   const int n = clamp_n(n_dev, n_max);
   int gid[RT];
@@ -291,11 +301,11 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // slices, the block maps itself again and reloads its row ids (one more
   // round trip, only when many rows are live).
   if (adapt) {                                          // launch-uniform
-    const int S_live = live_splits(n, M, gridDim.z, S);
+    const int S_live = live_splits(n, M, B, S);
     if (S_live != S) {                                  // block-uniform
       S = S_live;
-      r0 = (int)((blockIdx.x / (8 * S)) * 8 + (blockIdx.x & 7)) * (kTile * RT);
-      split = (int)((blockIdx.x >> 3) % S);
+      r0 = (int)((kblk / (8 * S)) * 8 + (kblk & 7)) * (kTile * RT);
+      split = (int)((kblk >> 3) % S);
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const int row = r0 + r * kTile + i;
@@ -772,11 +782,11 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 }
 
 template <int NMT, int RT, bool F16>
-void launch_mfma_t(dim3 grid, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
+void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
                    int SP, float* part, const BatchStrides& bs) {
-  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16>), grid, dim3(kPThreads), 0, stream, (const uint4*)rows, mode, row_ids,
-                     n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, SP, part, bs);
+  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows, mode,
+                     row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, SP, part, bs, B);
 }
 
 template <bool F16>
@@ -785,10 +795,13 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
                 hipStream_t stream) {
   const int dv = d / 8;
   const int rt = pick_rt(M);
-  // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and exit).
-  const dim3 grid((unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8 * S, 1, B);
+  // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and
+  // exit), times S slices, per sequence; one 1-D grid for all B sequences.
+  // S > 1 only while tiles x B < kTargetBlocks, so the grid stays below 2^31.
+  const unsigned per_seq = (unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8u * (unsigned)S;
+  const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
-  launch_mfma_t<NMTV, RTV, F16>(grid, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
+  launch_mfma_t<NMTV, RTV, F16>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
   switch ((M + 15) / 16) {
     case 1: NS_LAUNCH_MFMA(1, 1); break;
     case 2: NS_LAUNCH_MFMA(2, 2); break;

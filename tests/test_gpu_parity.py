@@ -321,6 +321,40 @@ def test_draft_edges(ns):
         check_topk(tids.cpu().numpy(), tvals.cpu().numpy(), ref_logits, I, o_ids, o_vals, k, "identity rows")
 
 
+def test_projection_shapes(ns):
+    """The projection kernel's edges: d / 8 of 1, 5, 33, 65 and 131 sixteen-
+    byte chunks (the two-k-step batch window runs past d, and a wave's range
+    can be shorter than a batch or empty), M across the 16-row hidden tiles
+    (hidden rows staged in LDS for M <= 16, loaded directly above), ragged
+    row tiles, both row modes, bf16 and fp16, and a large n_max whose blocks
+    re-map themselves to the live row count."""
+    say("projection shapes")
+    rng = np.random.default_rng(31)
+    V = 2600
+    for d in (8, 40, 264, 520, 1048):
+        for dtype in ("bf16", "fp16"):
+            bits = WL.f32_to_bf16_bits if dtype == "bf16" else WL.f32_to_fp16_bits
+            W = bits((rng.standard_normal((V, d)) * 0.1).astype(np.float32))
+            W_dev = dev_elems(W, dtype)
+            for M, n in ((1, 1), (7, 15), (16, 33), (17, 300), (40, 47), (64, 129)):
+                h = bits(rng.standard_normal((M, d)).astype(np.float32))
+                I = np.sort(rng.choice(V, size=n, replace=False))
+                k = min(8, n)
+                for mode in (ns.NS_INDEXED, ns.NS_PACKED):
+                    out = run_draft(ns, W_dev, dev_elems(h, dtype), I, n + 7, V, d, dtype, M, k, mode)
+                    check_draft(out, h, W, I, k, dtype, f"{dtype} d={d} M={M} n={n} mode={mode}")
+    # n_max above the live-row hint with M <= 16: blocks size their slices
+    # from the live n read on the device.
+    d = 264
+    W = WL.f32_to_bf16_bits((rng.standard_normal((V, d)) * 0.1).astype(np.float32))
+    W_dev = dev_elems(W, "bf16")
+    for M, n, n_max in ((8, 2500, 5000), (16, 40, 4000), (3, 2599, 8000)):
+        h = WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+        I = np.sort(rng.choice(V, size=n, replace=False))
+        out = run_draft(ns, W_dev, dev_elems(h, "bf16"), I, n_max, V, d, "bf16", M, 8, ns.NS_INDEXED)
+        check_draft(out, h, W, I, 8, "bf16", f"adaptive slices M={M} n={n} n_max={n_max}")
+
+
 def test_merge_paths(ns):
     """Column counts around the merge kernel's limits (one column per thread,
     up to four per thread, the general kernel past 4096) and a logit pattern
