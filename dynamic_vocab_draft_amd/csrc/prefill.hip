@@ -4,20 +4,23 @@
 // Initialization": the stream starts as the prompt followed by the union of
 // each position's top-K_pre logits.  The pass reads L x V logits once, so it
 // is HBM-bound.  One wave owns one row and streams it with 16-byte loads, in
-// batches of four per lane that alternate between two register sets.  Each
-// lane scans its elements in ascending id order and keeps a sorted list of its
-// CAP best (value, id) keys; an element that only ties the list's last value
-// has a larger id and is dropped.  After every batch the wave shares the
+// batches of four per lane that alternate between two register sets; a block
+// holds the waves of four adjacent rows (measured faster than one-wave
+// blocks and than several waves sharing a row).  Each lane scans its
+// elements in ascending id order and keeps a sorted list of its CAP best
+// (value, id) keys; an element that only ties the list's last value has a
+// larger id and is dropped.  After every batch the wave shares the
 // largest k-th best value held by any lane as a floor (the row's k-th largest
 // cannot be below it), so most vectors cost a conversion and one compare of
-// their 8-element maximum.  A pop over the lanes then emits the k winners
-// ordered by (value desc, id asc).  Values are the stored logits widened to
-// float32, so the result is exact.
+// their 8-element maximum.  A pop over the wave's lanes (no block barrier)
+// then emits the k winners ordered by (value desc, id asc).  Values are the
+// stored logits widened to float32, so the result is exact.
 #include "common.hpp"
 
 namespace {
 
-constexpr int kPrefillThreads = 64;       // one wave per row: all rows resident at once
+constexpr int kPrefillThreads = NS_WAVE;  // lanes per row: one wave per row, all rows resident at once
+constexpr int kPrefillRows = 4;           // rows (waves) per block
 constexpr int kPrefillUnroll = 4;
 
 template <int CAP>
@@ -95,12 +98,12 @@ __device__ __forceinline__ void scan_batch(const uint4 (&x)[kPrefillUnroll], int
 }
 
 template <int ET, bool VEC, int CAP>
-__global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restrict__ Z, int V, int k,
-                                                             int32_t* __restrict__ out_ids,
-                                                             float* __restrict__ out_vals) {
-  __shared__ uint64_t sh[kPrefillThreads / NS_WAVE];
-  const size_t row = blockIdx.x;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kPrefillThreads * kPrefillRows) void k_prefill(const void* __restrict__ Z, int L, int V,
+                                                                            int k, int32_t* __restrict__ out_ids,
+                                                                            float* __restrict__ out_vals) {
+  const size_t row = (size_t)blockIdx.x * kPrefillRows + threadIdx.x / NS_WAVE;
+  const int tid = threadIdx.x & (NS_WAVE - 1);
+  if (row >= (size_t)L) return;                        // wave-uniform; no barrier below
   Cands<CAP> c;
   c.init();
   if (VEC) {
@@ -148,16 +151,18 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill(const void* __restr
       for (int e = tid; e < V; e += kPrefillThreads) c.add(p[e], e);
     }
   }
-  ns::block_pop_topk<kPrefillThreads, CAP>(c.lst, k, sh, [&](int r, uint64_t key) {
-    out_ids[row * k + r] = key ? ns::key_id(key) : -1;
-    out_vals[row * k + r] = key ? ns::key_val(key) : -INFINITY;
-  });
+  const uint64_t key = ns::wave_pop_topk<CAP>(c.lst, k, tid);   // lane r < k holds the r-th winner
+  if (tid < k) {
+    out_ids[row * k + tid] = key ? ns::key_id(key) : -1;
+    out_vals[row * k + tid] = key ? ns::key_val(key) : -INFINITY;
+  }
 }
 
 template <int ET, bool VEC>
 void launch_cap(int cap, const void* Z, int L, int V, int k, int32_t* ids, float* vals, hipStream_t s) {
-#define NS_LAUNCH_PREFILL(C) \
-  hipLaunchKernelGGL((k_prefill<ET, VEC, C>), dim3(L), dim3(kPrefillThreads), 0, s, Z, V, k, ids, vals)
+#define NS_LAUNCH_PREFILL(C)                                                                                  \
+  hipLaunchKernelGGL((k_prefill<ET, VEC, C>), dim3((L + kPrefillRows - 1) / kPrefillRows),                     \
+                     dim3(kPrefillThreads * kPrefillRows), 0, s, Z, L, V, k, ids, vals)
   switch (cap) {
     case 4: NS_LAUNCH_PREFILL(4); break;
     case 8: NS_LAUNCH_PREFILL(8); break;
