@@ -487,6 +487,190 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Projection for 48 < M <= 64 over many rows: the four waves split M (wave
+// w owns hidden rows 16w .. 16w+15) instead of k, so a block's 16 RT rows
+// are read once and shared, and the hidden rows cost one load per row
+// tile group instead of one per 32 rows.  Each batch (two k-steps) of the rows is filled into a
+// block-shared LDS window by all four waves (RT/4 tiles each, direct
+// global->LDS loads, 128-byte row runs, XOR-swizzled as in k_proj_mfma);
+// each wave also fills its own hidden-row window.  Three buffers: batch
+// it+2 is requested after the barrier of batch it, so two batches are in
+// flight while one is multiplied.  Each wave owns complete sums of its
+// hidden tile over the block's slice and writes them without a reduction.
+// ---------------------------------------------------------------------------
+template <int RT, bool F16>
+__global__ __launch_bounds__(kPThreads) void k_proj_msplit(const uint4* __restrict__ rows, int mode,
+                                                           const int32_t* __restrict__ row_ids,
+                                                           const int32_t* __restrict__ n_dev, int n_max, int V,
+                                                           int dv, const uint4* __restrict__ h, int M,
+                                                           int S, int SP, float* __restrict__ part,
+                                                           BatchStrides bs, int B) {
+  constexpr int KC = kDmaKC;
+  constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
+  constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction (8)
+  constexpr int NI = kTile / RPI;                  // load instructions per 16 rows (2)
+  constexpr int TB = kTile * CPR;                  // uint4 of one tile's batch window
+  constexpr int TPW = RT / kPW;                    // row tiles loaded by each wave
+  static_assert(RT % kPW == 0, "each wave loads whole tiles");
+  constexpr int NBUF = 3;
+  __shared__ uint4 ab0[RT * TB], ab1[RT * TB], ab2[RT * TB];
+  __shared__ uint4 hb0[kPW][TB], hb1[kPW][TB], hb2[kPW][TB];
+  __shared__ int sh_ok[RT * kTile];
+  const unsigned L = blockIdx.x;
+  const int seq = (int)((L / (8u * (unsigned)S)) % (unsigned)B);
+  const unsigned kblk = (L / (8u * (unsigned)S * (unsigned)B)) * (8u * (unsigned)S) + L % (8u * (unsigned)S);
+  {
+    const size_t b = (size_t)seq;
+    rows += b * bs.rows;
+    if (row_ids) row_ids += b * bs.ids;
+    if (n_dev) n_dev += b;
+    h += b * bs.h;
+    part += b * bs.part;
+  }
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / NS_WAVE);
+  const int i = lane & 15, g = lane >> 4;
+  const int r0 = (int)((kblk / (8 * S)) * 8 + (kblk & 7)) * (kTile * RT);
+  const int split = (int)((kblk >> 3) % S);
+  const int n = clamp_n(n_dev, n_max);
+  // This wave loads tiles w TPW .. w TPW + TPW - 1; lanes 0..15 of each hold
+  // the tile's row ids.
+  int gid[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = r0 + (w * TPW + t) * kTile + i;
+    gid[t] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+  }
+  if (r0 >= n) return;                                  // block-uniform
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = r0 + (w * TPW + t) * kTile + i;
+    const bool okv = row < n && gid[t] >= 0 && gid[t] < V;
+    if (lane < kTile) sh_ok[(w * TPW + t) * kTile + lane] = okv;
+  }
+  const int rsub = lane / CPR, cpos = lane % CPR;
+  const uint4* asrc[TPW][NI];
+  int apos[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int tr = q * RPI + rsub;
+    apos[q] = cpos ^ (tr & (CPR - 1));
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int row = r0 + (w * TPW + t) * kTile + tr;
+      const int gsh = __shfl(gid[t], tr, NS_WAVE);
+      const bool oks = row < n && gsh >= 0 && gsh < V;
+      asrc[t][q] = rows + (size_t)(oks ? (mode == NS_INDEXED ? gsh : row) : 0) * dv;
+    }
+  }
+  const uint4* hsrc[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int m = w * kTile + q * RPI + rsub;
+    hsrc[q] = h + (size_t)(m < M ? m : M - 1) * dv;
+  }
+  const bool m_ok = w * kTile + i < M;
+  const int ksteps = (dv + 3) >> 2;
+  const int ks_per_split = (ksteps + S - 1) / S;
+  const int kb = split * ks_per_split;
+  const int ke = min(ksteps, kb + ks_per_split);
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const int swz_i = i & (CPR - 1);
+  auto issue = [&](int s0, uint4 (&ab)[RT * TB], uint4 (&hb)[kPW][TB]) {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int c = s0 * 4 + apos[q];
+      const int cc = (c < ke * 4 && c < dv) ? c : 0;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) dma16(asrc[t][q] + cc, &ab[(w * TPW + t) * TB + q * NS_WAVE]);
+      dma16(hsrc[q] + cc, &hb[w][q * NS_WAVE]);
+    }
+  };
+  bool okr[RT];
+  auto compute = [&](int s0, const uint4 (&ab)[RT * TB], const uint4 (&hb)[kPW][TB]) {
+    uint4 af[KC][RT], bf[KC];
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const int off = i * CPR + ((4 * kk + g) ^ swz_i);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) af[kk][r] = lds_read_b128(&ab[r * TB + off]);
+      bf[kk] = lds_read_b128(&hb[w][off]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) lds_ready(af[kk][r]);
+      lds_ready(bf[kk]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const int c8 = (s0 + kk) * 4 + g;
+      const bool kok = (s0 + kk) < ke && c8 < dv;
+      const uint4 bv = (kok && m_ok) ? bf[kk] : z;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const uint4 av = (kok && okr[r]) ? af[kk][r] : z;
+        if (F16)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av),
+                                                          __builtin_bit_cast(f16x8_t, bv), acc[r], 0, 0, 0);
+        else
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                           __builtin_bit_cast(bf16x8_t, bv), acc[r], 0, 0, 0);
+      }
+    }
+  };
+  constexpr int NLOADS = NI * (TPW + 1);                   // this wave's loads of one batch
+  constexpr int kWaitOne = (NLOADS & 0xF) | (0x7 << 4) | (0xF << 8) | ((NLOADS >> 4) << 14);
+  constexpr int kWaitAll = 0x0F70;
+  // Batch b lives in buffer b mod 3.  Iteration it: wait for this wave's
+  // loads of batch it (batch it+1 may stay in flight), barrier (every
+  // wave's part of batch it has landed, and every wave is done with batch
+  // it-1, whose buffer batch it+2 reuses), request batch it+2, multiply.
+  if (kb < ke) {                                        // block-uniform
+    issue(kb, ab0, hb0);
+    if (kb + KC < ke) issue(kb + KC, ab1, hb1);
+    NS_ISSUE_FENCE();
+    int it = 0;
+    for (int s0 = kb; s0 < ke; s0 += KC, ++it) {
+      if (s0 + KC < ke) __builtin_amdgcn_s_waitcnt(kWaitOne);
+      else __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __syncthreads();
+      if (it == 0) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) okr[r] = sh_ok[r * kTile + i] != 0;
+      }
+      const int b = it % NBUF;                          // uniform
+      if (s0 + 2 * KC < ke) {
+        if (b == 0) issue(s0 + 2 * KC, ab2, hb2);
+        else if (b == 1) issue(s0 + 2 * KC, ab0, hb0);
+        else issue(s0 + 2 * KC, ab1, hb1);
+        NS_ISSUE_FENCE();
+      }
+      if (b == 0) compute(s0, ab0, hb0);
+      else if (b == 1) compute(s0, ab1, hb1);
+      else compute(s0, ab2, hb2);
+    }
+  }
+  __syncthreads();                                      // sh_ok complete even when the slice is empty
+  // Lane L of a 16x16 result tile holds rows 4 (L / 16) .. +3 of column L % 16;
+  // an empty slice (kb >= ke) writes its zeros so the merge can sum all S.
+  const int m = w * kTile + i;
+  if (m < M) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ri = r * kTile + g * 4 + v;
+        if (sh_ok[ri]) part[((size_t)m * n_max + r0 + ri) * SP + split] = acc[r][v];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge (the block selection routine is in select.hpp).
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = kSelectThreads;
@@ -729,7 +913,19 @@ int pick_mt(int M, int d, int esz) {
   return ((size_t)mt * d * esz > kHLdsBytes) ? 0 : mt;
 }
 
-int pick_rt(int M) { return M <= 16 ? 1 : 2; }
+// The M-split kernel (k_proj_msplit, 64-row groups) serves 48 < M <= 64 once
+// the launch spans at least kMsplitMinTiles row groups (over all sequences);
+// below that the k-split kernel, with more blocks per row, is faster (at
+// ~900 live rows of 3072 it is 11 us against 13 us).
+constexpr int kMsplitRT = 4;
+constexpr int kMsplitMinTiles = 128;
+constexpr int kMsplitTargetBlocks = 384;
+
+bool use_msplit(int n_max, int M, int B) {
+  return M > 48 && (long)((n_max + kTile * kMsplitRT - 1) / (kTile * kMsplitRT)) * B >= kMsplitMinTiles;
+}
+
+int pick_rt(int M, int n_max, int B) { return use_msplit(n_max, M, B) ? kMsplitRT : (M <= 16 ? 1 : 2); }
 
 // Number of d-slices S for the MFMA path: about kTargetBlocks blocks, each
 // wave keeping at least kKC k-steps.  When the live row count is
@@ -742,9 +938,19 @@ int pick_rt(int M) { return M <= 16 ? 1 : 2; }
 int launch_splits(bool n_known, int n_max, int M, int d, int dtype, int B) {
   if (!is_mfma_dtype(dtype)) return 1;
   const int ksteps = (d / 8 + 3) / 4;
+  if (use_msplit(n_max, M, B)) {
+    // Each wave runs the whole slice; at least two slices, few enough blocks
+    // that the partial sums (M S floats per row) stay a small share.
+    const long tiles = (long)((n_max + kTile * kMsplitRT - 1) / (kTile * kMsplitRT)) * B;
+    int s = (int)((kMsplitTargetBlocks + tiles - 1) / tiles);
+    const int s_hi = ksteps / kKC < kMaxSplits ? ksteps / kKC : kMaxSplits;
+    s = s < 2 ? 2 : s;
+    s = s > s_hi ? s_hi : s;
+    return s < 1 ? 1 : s;
+  }
   int s_hi = ksteps / (kPW * kKC);
   s_hi = s_hi < 1 ? 1 : (s_hi > kMaxSplits ? kMaxSplits : s_hi);
-  const int rt = kTile * pick_rt(M);
+  const int rt = kTile * pick_rt(M, n_max, B);
   long tiles = (n_max + rt - 1) / rt;
   if (!n_known && M <= 16 && tiles > kLiveRowsHint / rt) tiles = kLiveRowsHint / rt;
   tiles *= B;
@@ -794,7 +1000,7 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
                 const void* h, int M, int S, int adapt, int SP, float* part, int B, const BatchStrides& bs,
                 hipStream_t stream) {
   const int dv = d / 8;
-  const int rt = pick_rt(M);
+  const int rt = pick_rt(M, n_max, B);
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and
   // exit), times S slices, per sequence; one 1-D grid for all B sequences.
   // S > 1 only while tiles x B < kTargetBlocks, so the grid stays below 2^31.
@@ -802,6 +1008,11 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
   launch_mfma_t<NMTV, RTV, F16>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
+  if (rt == kMsplitRT) {
+    hipLaunchKernelGGL((k_proj_msplit<kMsplitRT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows,
+                       mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, SP, part, bs, B);
+    return ns_launch_status();
+  }
   switch ((M + 15) / 16) {
     case 1: NS_LAUNCH_MFMA(1, 1); break;
     case 2: NS_LAUNCH_MFMA(2, 2); break;

@@ -322,12 +322,13 @@ def test_draft_edges(ns):
 
 
 def test_projection_shapes(ns):
-    """The projection kernel's edges: d / 8 of 1, 5, 33, 65 and 131 sixteen-
+    """The projection kernels' edges: d / 8 of 1, 5, 33, 65 and 131 sixteen-
     byte chunks (the two-k-step batch window runs past d, and a wave's range
     can be shorter than a batch or empty), M across the 16-row hidden tiles
     (hidden rows staged in LDS for M <= 16, loaded directly above), ragged
-    row tiles, both row modes, bf16 and fp16, and a large n_max whose blocks
-    re-map themselves to the live row count."""
+    row tiles, both row modes, bf16 and fp16, the M-split kernel for
+    48 < M <= 64 over many rows, and a large n_max whose blocks re-map
+    themselves to the live row count."""
     say("projection shapes")
     rng = np.random.default_rng(31)
     V = 2600
@@ -343,6 +344,22 @@ def test_projection_shapes(ns):
                 for mode in (ns.NS_INDEXED, ns.NS_PACKED):
                     out = run_draft(ns, W_dev, dev_elems(h, dtype), I, n + 7, V, d, dtype, M, k, mode)
                     check_draft(out, h, W, I, k, dtype, f"{dtype} d={d} M={M} n={n} mode={mode}")
+    # 48 < M <= 64 over at least 128 groups of 64 rows: the M-split kernel
+    # (shared row windows, one hidden tile per wave), including a d whose
+    # two slices end inside a batch window, and few live rows in a large
+    # n_max.
+    Vm = 9000
+    for dtype in ("bf16", "fp16"):
+        bits = WL.f32_to_bf16_bits if dtype == "bf16" else WL.f32_to_fp16_bits
+        for d in (40, 264):
+            W = bits((rng.standard_normal((Vm, d)) * 0.1).astype(np.float32))
+            W_dev = dev_elems(W, dtype)
+            for M, n, n_max in ((49, 8150, 8192), (64, 300, 8192), (60, 8192, 8192)):
+                h = bits(rng.standard_normal((M, d)).astype(np.float32))
+                I = np.sort(rng.choice(Vm, size=n, replace=False))
+                for mode in (ns.NS_INDEXED, ns.NS_PACKED):
+                    out = run_draft(ns, W_dev, dev_elems(h, dtype), I, n_max, Vm, d, dtype, M, 16, mode)
+                    check_draft(out, h, W, I, 16, dtype, f"M-split {dtype} d={d} M={M} n={n} mode={mode}")
     # n_max above the live-row hint with M <= 16: blocks size their slices
     # from the live n read on the device.
     d = 264
