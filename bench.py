@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-extras", action="store_true", help="skip the prefill, overlap and batch legs")
-    p.add_argument("--batches", default="1,8,32", help="sequence counts of the batched leg")
+    p.add_argument("--batches", default="1,8,32,64", help="sequence counts of the batched leg")
     p.add_argument("--sweep", action="store_true",
                    help="only sweep the draft head over |I| x M (cold) and print one JSON line per point")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",

@@ -23,14 +23,15 @@
 //       reach the matrix cores through per-wave LDS buffers filled by direct
 //       global->LDS loads that read each row as a contiguous 128-byte run
 //       (double-buffered batches of two k-steps).  Padded B-operand lanes
-//       (m >= M) are zeroed.  Each block writes its
-//       partial sums (deterministic; no atomics) to partial[m][j][s], the S
-//       slices of one column side by side (row stride SP = S rounded up to
-//       4) so the merge reads them with 16-byte loads.  The grid is 1-D per
-//       sequence, in groups of 8 tiles x S slices, one tile per XCD: the
+//       (m >= M) are zeroed.  Each block writes its partial sums
+//       (deterministic; no atomics) to partial[m][j][s], the S slices of one
+//       column side by side (row stride SP = S for S <= 2, else S rounded up
+//       to 4) so the merge reads them with one load.  The grid is 1-D, in
+//       groups of 8 tiles x S slices per sequence, one tile per XCD: the
 //       blocks of the live tiles come first in dispatch order and are dealt
 //       evenly over the 8 XCDs and their CUs however large n_max is, and
-//       each row is read whole by one XCD.
+//       each row is read whole by one XCD.  For 48 < M <= 64 over many rows
+//       k_proj_msplit splits M across the waves instead of k.
 //   k_merge_cols (+ k_merge_keys past one chunk): per hidden row m and
 //       4096-column chunk, a 1024-thread block sums the S partials of each
 //       active column in a fixed order and selects the chunk's k best
@@ -680,15 +681,36 @@ constexpr int kMergeChunk = kMergeThreads * kMergeCols;
 // (no key merge) when a column's partial sums are at most two 16-byte loads.
 constexpr int kMergeColsWide = 8;
 
-template <int SQ>
-__device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
+// A column's S partial sums sit side by side at a pitch of SPT floats (S
+// for S <= 2, else S rounded up to 4), read as one float, one float2 or
+// SPT / 4 float4.
+template <int SPT>
+struct Pitch {
+  static constexpr int NQ = SPT >= 4 ? SPT / 4 : 1;
+};
+
+template <int SPT>
+__device__ __forceinline__ void load_slices(const float* __restrict__ col, float4 (&p)[Pitch<SPT>::NQ]) {
+  if constexpr (SPT >= 4) {
+#pragma unroll
+    for (int q = 0; q < SPT / 4; ++q) p[q] = ((const float4*)col)[q];
+  } else if constexpr (SPT == 2) {
+    const float2 x = *(const float2*)col;
+    p[0] = make_float4(x.x, x.y, 0.f, 0.f);
+  } else {
+    p[0] = make_float4(*col, 0.f, 0.f, 0.f);
+  }
+}
+
+template <int SPT>
+__device__ __forceinline__ float sum_slices(const float4 (&p)[Pitch<SPT>::NQ], int S) {
   float sv = 0.f;                                  // slices summed in a fixed order
 #pragma unroll
-  for (int q = 0; q < SQ; ++q) {
+  for (int q = 0; q < Pitch<SPT>::NQ; ++q) {
     if (4 * q + 0 < S) sv += p[q].x;
-    if (4 * q + 1 < S) sv += p[q].y;
-    if (4 * q + 2 < S) sv += p[q].z;
-    if (4 * q + 3 < S) sv += p[q].w;
+    if (4 * q + 1 < S && 4 * q + 1 < SPT) sv += p[q].y;
+    if (4 * q + 2 < S && 4 * q + 2 < SPT) sv += p[q].z;
+    if (4 * q + 3 < S && 4 * q + 3 < SPT) sv += p[q].w;
   }
   return sv;
 }
@@ -704,7 +726,7 @@ __device__ __forceinline__ float sum_slices(const float4 (&p)[SQ], int S) {
 // active columns (a block max and a sum of exp(z - max) per chunk, combined
 // by k_merge_keys when there are several); the selection itself runs on z,
 // whose order is the same.
-template <int SQ, bool FINAL, int U, bool LOGP>
+template <int SPT, bool FINAL, int U, bool LOGP>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __restrict__ part, int S, int adapt,
                                                               int n_max,
                                                               const int32_t* __restrict__ row_ids,
@@ -729,10 +751,11 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   const int m = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int col0 = c * CHUNK;
   const int cend = min(n_max, col0 + CHUNK);         // > col0
-  const float4* prow = (const float4*)(part + (size_t)m * n_max * (SQ * 4));
+  const float* prow = part + (size_t)m * n_max * SPT;
+  constexpr int NQ = Pitch<SPT>::NQ;
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
-  float4 pv[U][SQ];
+  float4 pv[U][NQ];
   // LOGP: the parent score is requested in the first round too, as a vector
   // load (an opaque zero keeps it per lane): a scalar load would share the
   // LDS wait counter and stall the selection's first LDS wait on memory.
@@ -743,8 +766,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     const int j = col0 + tid;
     const int jc = j < cend ? j : cend - 1;
     gv[0] = row_ids ? row_ids[jc] : jc;
-#pragma unroll
-    for (int q = 0; q < SQ; ++q) pv[0][q] = prow[(size_t)jc * SQ + q];
+    load_slices<SPT>(prow + (size_t)jc * SPT, pv[0]);
     if (LOGP) {
       int zero;
       asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
@@ -767,8 +789,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
       const int j = col0 + tid + u * NT;
       const int jc = j < lim ? j : lim - 1;
       gv[u] = row_ids ? row_ids[jc] : jc;
-#pragma unroll
-      for (int q = 0; q < SQ; ++q) pv[u][q] = prow[(size_t)jc * SQ + q];
+      load_slices<SPT>(prow + (size_t)jc * SPT, pv[u]);
     }
     NS_ISSUE_FENCE();
   }
@@ -780,7 +801,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     val[u] = 0.f;
     gid[u] = -1;
     if (u == 0 || more) {
-      const float sv = sum_slices<SQ>(pv[u], S);
+      const float sv = sum_slices<SPT>(pv[u], S);
       if (j < lim && gv[u] >= 0 && gv[u] < V) {
         if (logits_out) logits_out[(size_t)m * n_max + j] = sv;
         val[u] = sv;
@@ -1025,6 +1046,10 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
 
 int merge_chunks(int n_max) { return (n_max + kMergeChunk - 1) / kMergeChunk; }
 
+// Floats per column of the partial sums for S slices (monotonic in S, so a
+// workspace sized for the largest S fits every smaller one).
+int slice_pitch(int S) { return S <= 2 ? S : (S + 3) & ~3; }
+
 // Workspace layout: [0, 256) reserved; partial sums float[B][M][n_max][SP]
 // at 256; for n_max > kMergeChunk, chunk keys uint64[B][M][C][k] after them.
 size_t partial_floats(int n_max, int M, int SP) { return (size_t)SP * M * n_max; }
@@ -1037,29 +1062,35 @@ int launch_merge_t(const float* part, int S, int adapt, int SP, int n_max, const
                    int M, int k, float* logits, int32_t* ids, float* vals, uint64_t* cand, int B,
                    const BatchStrides& bs, const LogProb& lp, hipStream_t stream) {
   const int C = merge_chunks(n_max);
-#define NS_LAUNCH_COLS(SQV, FIN, UV)                                                                                 \
-  hipLaunchKernelGGL((k_merge_cols<SQV, FIN, UV, LOGP>), dim3(M, (n_max + kMergeThreads * UV - 1) /                 \
+#define NS_LAUNCH_COLS(SPV, FIN, UV)                                                                                 \
+  hipLaunchKernelGGL((k_merge_cols<SPV, FIN, UV, LOGP>), dim3(M, (n_max + kMergeThreads * UV - 1) /                 \
                      (kMergeThreads * UV), B), dim3(kMergeThreads), 0, stream, part, S, adapt, n_max, row_ids, n_dev, \
                      V, k, \
                      logits, ids, vals, cand, bs, lp)
-#define NS_LAUNCH_COLS_SQ(FIN)                       \
-  switch (SP / 4) {                                  \
-    case 1: NS_LAUNCH_COLS(1, FIN, kMergeCols); break; \
-    case 2: NS_LAUNCH_COLS(2, FIN, kMergeCols); break; \
-    case 3: NS_LAUNCH_COLS(3, FIN, kMergeCols); break; \
-    default: NS_LAUNCH_COLS(4, FIN, kMergeCols); break; \
+#define NS_LAUNCH_COLS_SP(FIN)                        \
+  switch (SP) {                                       \
+    case 1: NS_LAUNCH_COLS(1, FIN, kMergeCols); break;  \
+    case 2: NS_LAUNCH_COLS(2, FIN, kMergeCols); break;  \
+    case 4: NS_LAUNCH_COLS(4, FIN, kMergeCols); break;  \
+    case 8: NS_LAUNCH_COLS(8, FIN, kMergeCols); break;  \
+    case 12: NS_LAUNCH_COLS(12, FIN, kMergeCols); break; \
+    default: NS_LAUNCH_COLS(16, FIN, kMergeCols); break; \
   }
   if (C == 1) {
-    NS_LAUNCH_COLS_SQ(true);
+    NS_LAUNCH_COLS_SP(true);
     return ns_launch_status();
   }
   if (C == 2 && SP <= 8) {                           // one wide chunk: no key merge
-    if (SP == 4) NS_LAUNCH_COLS(1, true, kMergeColsWide);
-    else NS_LAUNCH_COLS(2, true, kMergeColsWide);
+    switch (SP) {
+      case 1: NS_LAUNCH_COLS(1, true, kMergeColsWide); break;
+      case 2: NS_LAUNCH_COLS(2, true, kMergeColsWide); break;
+      case 4: NS_LAUNCH_COLS(4, true, kMergeColsWide); break;
+      default: NS_LAUNCH_COLS(8, true, kMergeColsWide); break;
+    }
     return ns_launch_status();
   }
-  NS_LAUNCH_COLS_SQ(false);
-#undef NS_LAUNCH_COLS_SQ
+  NS_LAUNCH_COLS_SP(false);
+#undef NS_LAUNCH_COLS_SP
 #undef NS_LAUNCH_COLS
   const int nk = C * k;
   const int per = (nk + kMergeThreads - 1) / kMergeThreads;
@@ -1094,12 +1125,12 @@ bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
 
 extern "C" {
 
-// Workspace: partial sums [B x M x n_max x SP] float32 (SP = S rounded up to
-// 4) at offset 256, then, when n_max > 4096, the chunk keys and the chunks'
-// log-sum-exp pairs.
+// Workspace: partial sums [B x M x n_max x SP] float32 (SP = S for S <= 2,
+// else S rounded up to 4) at offset 256, then, when n_max > 4096, the chunk
+// keys and the chunks' log-sum-exp pairs.
 size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M, int32_t k, int32_t d) {
   if (B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return 0;
-  const int SP = (max_splits(n_max, M, d, B) + 3) & ~3;
+  const int SP = slice_pitch(max_splits(n_max, M, d, B));
   const int C = merge_chunks(n_max);
   const size_t keys = C > 1 ? align256((size_t)B * M * C * k * sizeof(uint64_t)) : 0;
   const size_t stats = C > 1 ? align256((size_t)B * M * C * sizeof(float2)) : 0;
@@ -1141,7 +1172,7 @@ DraftPlan draft_plan(const int32_t* n_dev, int32_t n_max, int32_t B, int32_t d, 
                      void* ws) {
   DraftPlan p;
   p.S = launch_splits(n_dev == nullptr, n_max, M, d, dtype, B);
-  p.SP = (p.S + 3) & ~3;
+  p.SP = slice_pitch(p.S);
   // Only a launch sized by kLiveRowsHint can over-split; the kernels then
   // size S from the live n.
   p.adapt = (is_mfma_dtype(dtype) && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
