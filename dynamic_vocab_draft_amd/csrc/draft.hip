@@ -1025,7 +1025,17 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and
   // exit), times S slices, per sequence; one 1-D grid for all B sequences.
   // S > 1 only while tiles x B < kTargetBlocks, so the grid stays below 2^31.
-  const unsigned per_seq = (unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8u * (unsigned)S;
+  unsigned per_seq = (unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8u * (unsigned)S;
+  if (adapt) {
+    // Blocks re-map to the live n with S_live = live_splits(n) slices, and
+    // tiles(n) x S_live < kTargetBlocks / B + tiles(n) (plus the rounding
+    // of tiles to 8), so the rest of a full tiles x S grid would only exit.
+    const unsigned tiles_max = (unsigned)((n_max + kTile * rt - 1) / (kTile * rt));
+    const unsigned bound = (unsigned)((kTargetBlocks + B - 1) / B) + tiles_max + 56u;
+    const unsigned group = 8u * (unsigned)S;
+    const unsigned trimmed = (bound + group - 1) / group * group;
+    per_seq = trimmed < per_seq ? trimmed : per_seq;
+  }
   const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
   launch_mfma_t<NMTV, RTV, F16>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
