@@ -360,6 +360,12 @@ def test_projection_shapes(ns):
                 for mode in (ns.NS_INDEXED, ns.NS_PACKED):
                     out = run_draft(ns, W_dev, dev_elems(h, dtype), I, n_max, Vm, d, dtype, M, 16, mode)
                     check_draft(out, h, W, I, 16, dtype, f"M-split {dtype} d={d} M={M} n={n} mode={mode}")
+            # every row of a large n_max live with M <= 16: the most blocks a
+            # trimmed adaptive grid has to re-map
+            h = bits(rng.standard_normal((8, d)).astype(np.float32))
+            I = np.sort(rng.choice(Vm, size=8192, replace=False))
+            out = run_draft(ns, W_dev, dev_elems(h, dtype), I, 8192, Vm, d, dtype, 8, 8, ns.NS_INDEXED)
+            check_draft(out, h, W, I, 8, dtype, f"adaptive full {dtype} d={d}")
     # n_max above the live-row hint with M <= 16: blocks size their slices
     # from the live n read on the device.
     d = 264
