@@ -396,14 +396,17 @@ DRAFT_SOURCES = ("dynamic_vocab_draft_amd/csrc/draft.hip", "dynamic_vocab_draft_
                  "dynamic_vocab_draft_amd/csrc/common.hpp")
 
 
-def kernel_source_hash():
-    """sha256 of the draft-head sources with comments and blank space
-    removed, so that only a change to the code itself retires the committed
-    counter summary."""
+PREFILL_SOURCES = ("dynamic_vocab_draft_amd/csrc/prefill.hip", "dynamic_vocab_draft_amd/csrc/common.hpp")
+
+
+def kernel_source_hash(sources=DRAFT_SOURCES):
+    """sha256 of the given kernel sources (the draft head by default) with
+    comments and blank space removed, so that only a change to the code
+    itself retires the committed counter summary."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for rel in DRAFT_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel)) as f:
             src = f.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
@@ -429,6 +432,25 @@ def measured_traffic(workload, mode, key="traffic_bytes_per_call"):
         return None
     try:
         return float(kv[key])
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_prefill_traffic():
+    """HBM bytes per k_prefill launch on the prefill workload (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy calibration) from the committed counter
+    summary, or None once the prefill sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "prefill_topk_4096x128256_traffic.txt")
+    try:
+        with open(path) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != kernel_source_hash(PREFILL_SOURCES):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_call"])
     except (KeyError, ValueError):
         return None
 
@@ -472,7 +494,8 @@ def prefill_leg(torch, ns, WL, flush):
     del Zb
     return {"workload": f"prefill: L={cfg.L} V={cfg.V} bf16, K_pre={cfg.k_pre}", "ms": ms,
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "bytes": nbytes, "values_match_torch_topk_first_64_rows": ok, "cache": "cold"}
+            "bytes": nbytes, "traffic": measured_prefill_traffic(), "values_match_torch_topk_first_64_rows": ok,
+            "cache": "cold"}
 
 
 def make_backbone(torch, cfg):
