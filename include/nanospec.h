@@ -294,14 +294,13 @@ int nanospec_packed_update(nanospec_packed* pk, const nanospec_state* st,
  *   ws      : workspace of >= nanospec_draft_workspace_bytes(n_max, M, k, d)
  *             bytes, 256-byte aligned (partial sums over slices of d and,
  *             when n_max > 4096, room for per-chunk top-k keys and
- *             log-sum-exp pairs; no initialisation needed).  Calls sharing a workspace must be
- *             ordered.
+ *             log-sum-exp pairs; no initialisation needed).  Calls sharing
+ *             a workspace must be ordered.
  * Arithmetic: bf16 and fp16 products are exact in float32 and summed in
  * float32 on the matrix cores (v_mfma_f32_16x16x32_bf16 / _f16), in slices of
  * d whose partial sums are added in a fixed order; fp32 inputs use float32
- * FMAs.  No float
- * atomics: the same arguments and inputs give the same results (the slice
- * count depends on n_max, M, d and the live count).
+ * FMAs.  No float atomics: the same arguments and inputs give the same
+ * results (the slice count depends on n_max, M, d and the live count).
  * row_ids must be distinct apart from holes.
  * Errors: NS_EINVAL (nulls, M not in [1,64], k not in [1,64], d % 8 != 0,
  * n_max < 1), NS_EDTYPE, NS_ECAPACITY (ws too small), NS_EHIP. */
