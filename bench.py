@@ -371,6 +371,8 @@ def main():
         out["ablation"] = ablation_leg(torch, ns, WL, cfg, W, dcode, flush_fn)
         progress("batched-sequences leg")
         out["batched"] = batch_leg(torch, ns, WL, cfg, W, dcode, flush_fn, [int(x) for x in args.batches.split(",")])
+        progress("stress leg")
+        out["stress"] = stress_leg(torch, ns, WL, flush_fn)
     if not args.no_dense:
         out["dense"] = dense_compare(torch, ns, cfg, W, hs[Wm], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
     if not args.no_cpu_baseline:
@@ -899,6 +901,111 @@ def ablation_leg(torch, ns, WL, cfg, W, dcode, flush, steps=48, warm=16):
         del st, ws
     return {"workload": f"{cfg.name} id stream under each stream source, and the full stream over W_max; "
                         f"cold, hipGraph replay of {steps} steps", "points": out}
+
+
+def stress_leg(torch, ns, WL, flush, steps=32, warm=16):
+    """The stress workload (V=151936, d=4096, W_max=16384, M=64, k=16; a
+    uniform id stream keeps about 15.5k ids active): cold per-step times of
+    the state update and the INDEXED draft head (graph replay, the
+    cache-streaming read and the state-only graph subtracted), and the
+    full-vocabulary head at the same M.  W and h are drawn on the GPU from a
+    seeded generator with the workload's distributions (N(0, 0.02^2) and
+    N(0, 1), bf16)."""
+    cfg = WL.get_config("stress")
+    T = warm + steps
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    W = torch.randn((cfg.V, cfg.d), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+    hs = torch.randn((T, cfg.M, cfg.d), generator=g, device="cuda").to(torch.bfloat16)
+    script = WL.make_id_script(cfg, steps=T)
+    trees = [torch.as_tensor(t, dtype=torch.int32).cuda() for t in script.tree]
+    vers = [torch.as_tensor(v, dtype=torch.int32).cuda() for v in script.ver]
+    prompt = torch.as_tensor(script.prompt, dtype=torch.int32).cuda()
+    st = ns.NanoSpecState(cfg.V, cfg.w_max)
+    ids = torch.empty(cfg.w_max, dtype=torch.int32, device="cuda")
+    n = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = ns.alloc_workspace(cfg.w_max, cfg.M, cfg.k, cfg.d)
+    tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((cfg.M, cfg.k), device="cuda")
+
+    def init():
+        ns.nanospec_state_reset(st)
+        ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
+        ns.nanospec_active_vocab(st, ids, n)
+        for t in range(warm):
+            ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n)
+
+    sizes = []
+
+    def body(with_state, with_draft, record=False):
+        def run():
+            for t in range(warm, T):
+                flush(t)
+                if with_state:
+                    ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n)
+                if record:
+                    sizes.append(n.clone())
+                if with_draft:
+                    ns.nanospec_draft_logits_topk(W, ns.NS_INDEXED, ids, n, cfg.w_max, cfg.V, cfg.d, ns.NS_BF16,
+                                                  hs[t], cfg.M, cfg.k, None, tids, tvals, ws)
+        return run
+
+    init()
+    body(True, False, record=True)()
+    torch.cuda.synchronize()
+    n_mean = float(torch.stack(sizes).float().mean().item())
+
+    def timed(fn):
+        init()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        ts = []
+        for _ in range(5):
+            init()
+            torch.cuda.synchronize()
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b_.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b_))
+        del gr
+        return float(np.median(ts))
+
+    t_f = timed(body(False, False))
+    t_s = timed(body(True, False))
+    t_a = timed(body(True, True))
+    draft_us = (t_a - t_s) / steps * 1e3
+    s = cfg.elem_bytes
+    draft_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + 4 * n_mean + 8 * cfg.M * cfg.k
+
+    # Full-vocabulary head at M = 64: our kernels over every row, and torch.
+    wsd = ns.alloc_workspace(cfg.V, cfg.M, cfg.k, cfg.d)
+    h0 = hs[warm]
+
+    def ours():
+        ns.nanospec_draft_logits_topk(W, ns.NS_PACKED, None, None, cfg.V, cfg.V, cfg.d, ns.NS_BF16, h0, cfg.M,
+                                      cfg.k, None, tids, tvals, wsd)
+
+    def vendor():
+        z = h0 @ W.t()
+        torch.topk(z.float(), cfg.k, dim=1)
+
+    t_ours = _event_time(torch, ours, flush, 10)
+    t_vendor = _event_time(torch, vendor, flush, 10)
+    step_us = (t_a - t_f) / steps * 1e3
+    res = {"workload": f"stress: V={cfg.V} d={cfg.d} W_max={cfg.w_max} M={cfg.M} k={cfg.k}, uniform id stream, "
+                       f"cold, hipGraph replay of {steps} steps",
+           "mean_active": n_mean, "step_us": step_us, "state_update_us": (t_s - t_f) / steps * 1e3,
+           "draft_us": draft_us, "draft_GBps": draft_bytes / (draft_us * 1e-6) / 1e9,
+           "draft_frac_of_peak": draft_bytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "dense_ours_ms": t_ours, "dense_torch_ms": t_vendor,
+           "dense_ours_GBps": cfg.V * cfg.d * s / (t_ours * 1e-3) / 1e9,
+           "speedup_vs_dense": min(t_ours, t_vendor) * 1e3 / step_us}
+    del st, ws, wsd, W, hs
+    return res
 
 
 def sweep(torch, ns, WL, args):
