@@ -214,10 +214,22 @@ constexpr int kFastThreads = 512;
 constexpr int kFastMaxIds = kFastThreads;      // one tuple entry per thread
 constexpr int kFastMaxRing = 32 * kFastThreads; // ring entries held in registers
 constexpr size_t kFastLdsMax = 144 * 1024;
+constexpr int kFastStageMinIds = 4096;          // ids from which the compaction is staged in LDS
 
 __host__ __device__ __forceinline__ int fast_wpt(int V) {
   const int words = (V + 31) >> 5;
   return ((words + kFastThreads * 8 - 1) / (kFastThreads * 8)) * 8;
+}
+
+// Ints of LDS that stage the ascending active ids before one coalesced copy
+// to active_ids (at most min(W_max, V) ids), or 0 when the bitmap, the
+// staging area and the largest tuples would not fit kFastLdsMax; then the
+// ids are written to global memory directly from the compaction.
+__host__ __device__ __forceinline__ int fast_stage_ints(int V, int w_max) {
+  const int n = w_max < V ? w_max : V;
+  const int ints = (n + 3) & ~3;
+  const size_t need = ((size_t)kFastThreads * fast_wpt(V) + (size_t)ints + 2 * (size_t)kFastMaxIds) * 4;
+  return need <= kFastLdsMax ? ints : 0;
 }
 
 __device__ __forceinline__ void bm_set(uint32_t* bm, int id) { atomicOr(&bm[id >> 5], 1u << (id & 31)); }
@@ -248,8 +260,10 @@ __device__ __forceinline__ void step_fast_body(const ns_state_view& v, const int
   const int words = (V + 31) >> 5;
   const int wpt = fast_wpt(V);
   const int nd64 = (n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1);
+  const int stage = fast_stage_ints(V, w_max);
   uint32_t* bm = (uint32_t*)lds4;                                 // kFastThreads * wpt words
-  int32_t* dids = (int32_t*)(bm + (size_t)kFastThreads * wpt);    // nd64 ids (-1 padding)
+  int32_t* sids = (int32_t*)(bm + (size_t)kFastThreads * wpt);    // stage ids (16-byte aligned)
+  int32_t* dids = sids + stage;                                   // nd64 ids (-1 padding)
   int32_t* sfp = dids + nd64;                                     // nd64 first positions
   // ---- one round of global loads --------------------------------------
   // An index the compiler cannot prove uniform keeps |S| in a vector
@@ -381,9 +395,16 @@ __device__ __forceinline__ void step_fast_body(const ns_state_view& v, const int
   }
   int n_tot = 0;
   int off = ns::block_excl_scan<kFastThreads>(pc, sh_scan, &n_tot);
+  // Each thread writes its ids at its prefix offset, straight to active_ids
+  // (every lane of a store then hits its own cache line) or, for many ids,
+  // into the LDS staging area followed by one coalesced copy.  Measured on
+  // the same GPU: 967 ids, 4.90 us direct vs 5.21 staged; 15.5k ids, 14.7 us
+  // direct vs 12.2 staged.  n_tot is block-uniform after the scan.
+  const bool staged = stage && n_tot >= kFastStageMinIds;
+  int32_t* const dst = staged ? sids : active_ids;
   auto emit = [&](uint32_t b, int w) {
     while (b) {
-      active_ids[off++] = (w << 5) + (__ffs(b) - 1);
+      dst[off++] = (w << 5) + (__ffs(b) - 1);
       b &= b - 1u;
     }
   };
@@ -393,6 +414,16 @@ __device__ __forceinline__ void step_fast_body(const ns_state_view& v, const int
     const uint4 x = bm4[c];
     const int w = wbase + 4 * c;
     emit(x.x, w); emit(x.y, w + 1); emit(x.z, w + 2); emit(x.w, w + 3);
+  }
+  if (staged) {                                         // block-uniform
+    __syncthreads();
+    if ((((uintptr_t)active_ids) & 15u) == 0) {
+      const int n4 = n_tot >> 2;
+      for (int i = tid; i < n4; i += kFastThreads) ((int4*)active_ids)[i] = ((const int4*)sids)[i];
+      for (int i = (n4 << 2) + tid; i < n_tot; i += kFastThreads) active_ids[i] = sids[i];
+    } else {
+      for (int i = tid; i < n_tot; i += kFastThreads) active_ids[i] = sids[i];
+    }
   }
   if (tid == 0) {
     *n_active = n_tot;
@@ -439,8 +470,9 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast_batch(ns_state_view 
                         bitmap_out ? bitmap_out + (size_t)b * words : nullptr);
 }
 
-size_t fast_lds_bytes(int V, int n_draft) {
-  return ((size_t)kFastThreads * fast_wpt(V) + 2 * (size_t)((n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1))) * 4;
+size_t fast_lds_bytes(int V, int w_max, int n_draft) {
+  return ((size_t)kFastThreads * fast_wpt(V) + (size_t)fast_stage_ints(V, w_max) +
+          2 * (size_t)((n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1))) * 4;
 }
 
 typedef void (*step_fast_fn)(ns_state_view, const int32_t*, int, const int32_t*, int, int32_t*, int32_t*, uint32_t*);
@@ -586,7 +618,7 @@ ns_state_view make_view(char* p, int32_t V, int32_t w_max) {
 int prepare_kernels(int32_t V, int32_t w_max) {
   int rc = set_lds_limit((const void*)k_active, lds_bitmap_bytes(V));
   if (rc == NS_OK) rc = set_lds_limit((const void*)k_step, lds_bitmap_bytes(V));
-  const size_t fast_max = fast_lds_bytes(V, kFastMaxIds);
+  const size_t fast_max = fast_lds_bytes(V, w_max, kFastMaxIds);
   const size_t lim = fast_max < kFastLdsMax ? fast_max : kFastLdsMax;
   step_fast_fn fast_fn = pick_step_fast(w_max);
   if (rc == NS_OK && fast_fn) rc = set_lds_limit((const void*)fast_fn, lim);
@@ -674,7 +706,7 @@ int nanospec_batch_step_update(nanospec_batch* bt, const int32_t* draft_ids, int
     if (bt->members[b].mode == NS_STREAM_CTX_ONLY) return NS_EINVAL;
   const ns_state_view& v0 = bt->members[0].view;
   step_fast_batch_fn fn = pick_step_fast_batch(v0.w_max);
-  const size_t lds = fast_lds_bytes(v0.V, nd_max);
+  const size_t lds = fast_lds_bytes(v0.V, v0.w_max, nd_max);
   if (!fn || lds > kFastLdsMax) return NS_EINVAL;
   (void)hipGetLastError();
   hipLaunchKernelGGL(fn, dim3(bt->B), dim3(kFastThreads), lds, stream, v0, bt->stride, draft_ids, draft_stride, n_draft,
@@ -749,7 +781,7 @@ int nanospec_step_update(nanospec_state* st, const int32_t* draft_ids, int32_t n
   if ((n_draft > 0 && !draft_ids) || (n_ver > 0 && !ver_ids)) return NS_EINVAL;
   if (st->mode == NS_STREAM_CTX_ONLY) n_draft = n_ver = 0;     // ctx-only: nothing added while decoding
   (void)hipGetLastError();
-  const size_t fast = fast_lds_bytes(st->view.V, n_draft);
+  const size_t fast = fast_lds_bytes(st->view.V, st->view.w_max, n_draft);
   step_fast_fn fast_fn = pick_step_fast(st->view.w_max);
   if (fast_fn && n_draft <= kFastMaxIds && n_ver <= kFastMaxIds && fast <= kFastLdsMax) {
     // The kernel reads element 0 of an empty tuple unconditionally.

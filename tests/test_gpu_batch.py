@@ -167,3 +167,52 @@ def test_batch_member_calls_and_limits(ns):
         ns.nanospec_batch_step_update(bt, z, 600, c, 600, z, 8, c, 8, out, c)     # nd_max > 512
     with pytest.raises(ns.NanoSpecError):
         ns.nanospec_batch_step_update(bt, z, 4, c, 8, z, 8, c, 8, out, c)         # stride < nd_max
+
+
+def test_many_active_ids_staged(ns):
+    """More than 4096 active ids (the compaction staged in LDS, then copied
+    out), for a single state and for batch members whose active-id outputs
+    start off 16-byte alignment (W_max not a multiple of 4): ids, counts and
+    bitmaps bit-exact against the oracle at every step."""
+    say("many active ids: staged compaction")
+    rng = np.random.default_rng(41)
+    V = 200000                                        # uniform ids over a large V: nearly all distinct
+    for w_max, B in ((4403, 1), (5001, 3)):
+        bt = ns.NanoSpecBatch(B, V, w_max)
+        seqs = []
+        for b in range(B):
+            prompt = rng.integers(0, V, size=w_max + 500).astype(np.int32)
+            seq = O.Sequence_(w_max)
+            seq.append_prompt(prompt)
+            seqs.append(seq)
+            ns.nanospec_stream_append(bt.member(b), dev_i32(prompt), len(prompt), 0)
+        ids = torch.full((B, w_max), -7, dtype=torch.int32, device="cuda")
+        n = torch.zeros(B, dtype=torch.int32, device="cuda")
+        bm = torch.zeros((B, (V + 31) // 32), dtype=torch.int32, device="cuda")
+        for step in range(4):
+            trees = [rng.integers(0, V, size=400).astype(np.int32) for _ in range(B)]
+            vers = [rng.choice(V, size=8, replace=False).astype(np.int32) for _ in range(B)]
+            td, nd = pack(trees, 400)
+            tv, nv = pack(vers, 8)
+            ns.nanospec_batch_step_update(bt, td, 400, nd, 400, tv, 8, nv, 8, ids, n, bm)
+            torch.cuda.synchronize()
+            for b in range(B):
+                seqs[b].step(trees[b], vers[b])
+                I = seqs[b].active()
+                got_n = int(n[b].item())
+                assert len(I) > 4096, f"W_max={w_max}: only {len(I)} active ids"
+                assert got_n == len(I), f"W_max={w_max} seq {b} step {step}: n {got_n} vs {len(I)}"
+                assert np.array_equal(ids[b, :got_n].cpu().numpy(), I), f"W_max={w_max} seq {b} step {step}: ids"
+                assert np.array_equal(bm[b].cpu().numpy().view(np.uint32), bitmap_from_ids(I, V)), "bitmap"
+            if B == 1:
+                # the single-sequence entry point on the same state
+                m = bt.member(0)
+                ids1 = torch.full((w_max,), -7, dtype=torch.int32, device="cuda")
+                n1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+                tree, ver = rng.integers(0, V, size=300).astype(np.int32), rng.choice(V, size=8, replace=False)
+                ns.nanospec_step_update(m, dev_i32(tree), len(tree), dev_i32(ver), len(ver), ids1, n1)
+                torch.cuda.synchronize()
+                seqs[0].step(tree, ver)
+                I = seqs[0].active()
+                assert len(I) > 4096, f"few active ids: {len(I)}"
+                assert int(n1.item()) == len(I) and np.array_equal(ids1[:len(I)].cpu().numpy(), I), "single-state ids"
