@@ -680,38 +680,40 @@ constexpr int kMergeChunk = kMergeThreads * kMergeCols;
 // One block of 8 columns per thread covers n_max <= 8192 in a single chunk
 // (no key merge) when a column's partial sums are at most two 16-byte loads.
 constexpr int kMergeColsWide = 8;
+// With one or two slices (4-8 bytes of partial sums per column), 16 columns
+// per thread cover n_max <= 16384 in a single chunk: one launch instead of
+// the per-chunk selection and the key merge.
+constexpr int kMergeColsWide16 = 16;
 
 // A column's S partial sums sit side by side at a pitch of SPT floats (S
 // for S <= 2, else S rounded up to 4), read as one float, one float2 or
 // SPT / 4 float4.
 template <int SPT>
-struct Pitch {
-  static constexpr int NQ = SPT >= 4 ? SPT / 4 : 1;
-};
-
-template <int SPT>
-__device__ __forceinline__ void load_slices(const float* __restrict__ col, float4 (&p)[Pitch<SPT>::NQ]) {
+__device__ __forceinline__ void load_slices(const float* __restrict__ col, float (&p)[SPT]) {
   if constexpr (SPT >= 4) {
 #pragma unroll
-    for (int q = 0; q < SPT / 4; ++q) p[q] = ((const float4*)col)[q];
+    for (int q = 0; q < SPT / 4; ++q) {
+      const float4 x = ((const float4*)col)[q];
+      p[4 * q] = x.x;
+      p[4 * q + 1] = x.y;
+      p[4 * q + 2] = x.z;
+      p[4 * q + 3] = x.w;
+    }
   } else if constexpr (SPT == 2) {
     const float2 x = *(const float2*)col;
-    p[0] = make_float4(x.x, x.y, 0.f, 0.f);
+    p[0] = x.x;
+    p[1] = x.y;
   } else {
-    p[0] = make_float4(*col, 0.f, 0.f, 0.f);
+    p[0] = *col;
   }
 }
 
 template <int SPT>
-__device__ __forceinline__ float sum_slices(const float4 (&p)[Pitch<SPT>::NQ], int S) {
+__device__ __forceinline__ float sum_slices(const float (&p)[SPT], int S) {
   float sv = 0.f;                                  // slices summed in a fixed order
 #pragma unroll
-  for (int q = 0; q < Pitch<SPT>::NQ; ++q) {
-    if (4 * q + 0 < S) sv += p[q].x;
-    if (4 * q + 1 < S && 4 * q + 1 < SPT) sv += p[q].y;
-    if (4 * q + 2 < S && 4 * q + 2 < SPT) sv += p[q].z;
-    if (4 * q + 3 < S && 4 * q + 3 < SPT) sv += p[q].w;
-  }
+  for (int q = 0; q < SPT; ++q)
+    if (q < S) sv += p[q];
   return sv;
 }
 
@@ -752,10 +754,9 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   const int col0 = c * CHUNK;
   const int cend = min(n_max, col0 + CHUNK);         // > col0
   const float* prow = part + (size_t)m * n_max * SPT;
-  constexpr int NQ = Pitch<SPT>::NQ;
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
-  float4 pv[U][NQ];
+  float pv[U][SPT];
   // LOGP: the parent score is requested in the first round too, as a vector
   // load (an opaque zero keeps it per lane): a scalar load would share the
   // LDS wait counter and stall the selection's first LDS wait on memory.
@@ -1088,6 +1089,11 @@ int launch_merge_t(const float* part, int S, int adapt, int SP, int n_max, const
   }
   if (C == 1) {
     NS_LAUNCH_COLS_SP(true);
+    return ns_launch_status();
+  }
+  if (C <= 4 && SP <= 2 && C > 2) {                  // one 16384-column chunk: no key merge
+    if (SP == 1) NS_LAUNCH_COLS(1, true, kMergeColsWide16);
+    else NS_LAUNCH_COLS(2, true, kMergeColsWide16);
     return ns_launch_status();
   }
   if (C == 2 && SP <= 8) {                           // one wide chunk: no key merge

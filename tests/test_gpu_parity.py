@@ -390,7 +390,8 @@ def test_merge_paths(ns):
         W = WL.f32_to_bf16_bits(Wf) if dtype == "bf16" else Wf
         W_dev = dev_elems(W, dtype)
         for M, k, n, n_max in ((2, 8, 1024, 1024), (3, 8, 1025, 1100), (4, 16, 2900, 4096), (2, 64, 4096, 4096),
-                               (2, 8, 4097, 4097), (5, 10, 3000, 4500)):
+                               (2, 8, 4097, 4097), (5, 10, 3000, 4500), (3, 10, 4999, 12000), (2, 64, 5000, 16384),
+                               (2, 8, 100, 16000)):
             hf = rng.standard_normal((M, d)).astype(np.float32)
             h = WL.f32_to_bf16_bits(hf) if dtype == "bf16" else hf
             I = np.sort(rng.choice(V, size=n, replace=False))
@@ -411,6 +412,33 @@ def test_merge_paths(ns):
         I = np.arange(n)
         out = run_draft(ns, dev_elems(Wa, dtype), dev_elems(h, dtype), I, n, n, d, dtype, 1, 64, ns.NS_INDEXED)
         check_draft(out, h, Wa, I, 64, dtype, f"{dtype} fallback")
+    # One or two slices over 8192 < n_max <= 16384: a single merge chunk of
+    # 16 columns per thread (fp32 heads use one slice; the M-split bf16 head
+    # uses two), logits and log-probabilities.
+    V2, d2 = 20000, 264
+    Wf = (rng.standard_normal((V2, d2)) * 0.1).astype(np.float32)
+    for dtype in ("fp32", "bf16"):
+        W2 = WL.f32_to_bf16_bits(Wf) if dtype == "bf16" else Wf
+        W2_dev = dev_elems(W2, dtype)
+        M = 64 if dtype == "bf16" else 6
+        for n, n_max in ((12000, 12288), (9000, 16384)):
+            hf = rng.standard_normal((M, d2)).astype(np.float32)
+            h = WL.f32_to_bf16_bits(hf) if dtype == "bf16" else hf
+            I = np.sort(rng.choice(V2, size=n, replace=False))
+            out = run_draft(ns, W2_dev, dev_elems(h, dtype), I, n_max, V2, d2, dtype, M, 16, ns.NS_INDEXED)
+            check_draft(out, h, W2, I, 16, dtype, f"{dtype} one 16k chunk M={M} n={n} n_max={n_max}")
+            ids = torch.full((n_max,), -1, dtype=torch.int32, device="cuda")
+            ids[:n] = dev_i32(I)
+            tids = torch.empty((M, 16), dtype=torch.int32, device="cuda")
+            tvals = torch.empty((M, 16), device="cuda")
+            ws = ns.alloc_workspace(n_max, M, 16, d2)
+            ns.nanospec_draft_logprob_topk(W2_dev, ns.NS_INDEXED, ids, torch.tensor([n], dtype=torch.int32, device="cuda"),
+                                           n_max, V2, d2, dcode_of(ns, dtype), dev_elems(h, dtype), M, 16, None, None,
+                                           None, tids, tvals, ws)
+            torch.cuda.synchronize()
+            logp, o_ids, o_vals = O.draft_logprob_topk(h, W2, I, 16, dtype)
+            check_topk(tids.cpu().numpy(), tvals.cpu().numpy(), logp, I, o_ids, o_vals, 16,
+                       f"{dtype} log-prob one 16k chunk n={n}")
 
 
 def test_live_count_below_capacity(ns):
