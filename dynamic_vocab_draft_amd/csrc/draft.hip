@@ -24,9 +24,10 @@
 //       global->LDS loads that read each row as a contiguous 128-byte run
 //       (double-buffered batches of two k-steps).  Padded B-operand lanes
 //       (m >= M) are zeroed.  Each block writes its partial sums
-//       (deterministic; no atomics) to partial[m][j][s], the S slices of one
-//       column side by side (row stride SP = S for S <= 2, else S rounded up
-//       to 4) so the merge reads them with one load.  The grid is 1-D, in
+//       (deterministic; no atomics) to partial[s][m][j], slice-major with the
+//       column pitch rounded up to 4, so a lane's four rows of one hidden row
+//       leave as one 16-byte store and the merge reads each slice with
+//       coalesced loads over consecutive columns.  The grid is 1-D, in
 //       groups of 8 tiles x S slices per sequence, one tile per XCD: the
 //       blocks of the live tiles come first in dispatch order and are dealt
 //       evenly over the 8 XCDs and their CUs however large n_max is, and
@@ -51,6 +52,10 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // bf16 and fp16 go through the matrix cores; fp32 through the VALU kernel.
 __host__ __device__ constexpr bool is_mfma_dtype(int dtype) { return dtype == NS_BF16 || dtype == NS_FP16; }
+
+// Floats between the runs of consecutive hidden rows (and slices) in the
+// partial sums: n_max rounded up to 4, so every 4-row group is 16-byte aligned.
+__host__ __device__ inline int col_pitch(int n_max) { return (n_max + 3) & ~3; }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
                                                             const int32_t* __restrict__ row_ids,
                                                             const int32_t* __restrict__ n_dev, int n_max, int V,
                                                             int dvec, const uint4* __restrict__ h, int M,
-                                                            int SP, float* __restrict__ part, BatchStrides bs) {
+                                                            float* __restrict__ part, BatchStrides bs) {
   extern __shared__ uint4 hs[];   // [mt][dvec]
   {
     const size_t b = blockIdx.z;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
     if (lane == 0) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        if (m < mt) part[((size_t)(m0 + m) * n_max + j) * SP] = acc[m];
+        if (m < mt) part[(size_t)(m0 + m) * col_pitch(n_max) + j] = acc[m];
     }
   }
 }
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
-                                                         int S, int adapt, int SP, float* __restrict__ part,
+                                                         int S, int adapt, float* __restrict__ part,
                                                          BatchStrides bs, int B) {
   constexpr int KC = kDmaKC;
   constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
@@ -261,7 +266,6 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   __shared__ uint4 bbuf0[kPW][BDMA ? TB : 1];
   __shared__ uint4 bbuf1[kPW][BDMA ? TB : 1];
   __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
-  __shared__ int sh_ok[RT * kTile];
   // The 1-D grid is read as (tile group, sequence, slice, XCD lane), tile
   // group slowest: L = ((tg B + b) S + s) 8 + x.  Row tile tg 8 + x of
   // sequence b and slice s.  Dispatch then runs over the low (live) tiles of
@@ -320,7 +324,6 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   for (int r = 0; r < RT; ++r) {
     const int row = r0 + r * kTile + i;
     ok[r] = row < n && gid[r] >= 0 && gid[r] < V;
-    if (w == 0 && lane < kTile) sh_ok[r * kTile + lane] = ok[r];
   }
   // Load sources.  Row tr of a tile is requested by the lanes of instruction
   // tr / RPI with L / CPR == tr % RPI; lanes 0..15 hold the tile's row ids.
@@ -468,7 +471,10 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
     for (int t = 0; t < NMT; ++t) red[w][r][t][lane] = acc[r][t];
   __syncthreads();
   // Sum the wave tiles.  In a 16x16 result tile, lane L holds rows
-  // 4*(L/16) .. +3 (one per register) of column L%16.
+  // 4*(L/16) .. +3 (one per register) of column L%16: one 16-byte store into
+  // this slice's run of hidden row m (rows that are not live hold zeros and
+  // are never read; a quad that starts below n_max ends within the pitch).
+  const int NP = col_pitch(n_max);
   for (int e = tid; e < RT * NMT * NS_WAVE; e += kPThreads) {
     const int r = e / (NMT * NS_WAVE);
     const int t = (e / NS_WAVE) % NMT;
@@ -477,13 +483,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
     for (int ww = 1; ww < kPW; ++ww) sum += red[ww][r][t][l2];
     const int m = t * 16 + (l2 & 15);
-    if (m < M) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ri = r * kTile + (l2 >> 4) * 4 + v;
-        if (sh_ok[ri]) part[((size_t)m * n_max + r0 + ri) * SP + split] = sum[v];
-      }
-    }
+    const int q0 = r0 + r * kTile + (l2 >> 4) * 4;
+    if (m < M && q0 < n_max) *(f32x4_t*)(part + ((size_t)split * M + m) * NP + q0) = sum;
   }
 }
 
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_msplit(const uint4* __restri
                                                            const int32_t* __restrict__ row_ids,
                                                            const int32_t* __restrict__ n_dev, int n_max, int V,
                                                            int dv, const uint4* __restrict__ h, int M,
-                                                           int S, int SP, float* __restrict__ part,
+                                                           int S, float* __restrict__ part,
                                                            BatchStrides bs, int B) {
   constexpr int KC = kDmaKC;
   constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
@@ -656,18 +657,17 @@ __global__ __launch_bounds__(kPThreads) void k_proj_msplit(const uint4* __restri
       else compute(s0, ab2, hb2);
     }
   }
-  __syncthreads();                                      // sh_ok complete even when the slice is empty
-  // Lane L of a 16x16 result tile holds rows 4 (L / 16) .. +3 of column L % 16;
-  // an empty slice (kb >= ke) writes its zeros so the merge can sum all S.
+  // Lane L of a 16x16 result tile holds rows 4 (L / 16) .. +3 of column L % 16,
+  // stored as one 16-byte run (rows that are not live hold zeros and are never
+  // read); an empty slice (kb >= ke) writes its zeros so the merge can sum all S.
   const int m = w * kTile + i;
   if (m < M) {
+    float* dst = part + ((size_t)split * M + m) * col_pitch(n_max);
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ri = r * kTile + g * 4 + v;
-        if (sh_ok[ri]) part[((size_t)m * n_max + r0 + ri) * SP + split] = acc[r][v];
-      }
+    for (int r = 0; r < RT; ++r) {
+      const int q0 = r0 + r * kTile + g * 4;
+      if (q0 < n_max) *(f32x4_t*)(dst + q0) = acc[r];
+    }
   }
 }
 
@@ -685,27 +685,13 @@ constexpr int kMergeColsWide = 8;
 // the per-chunk selection and the key merge.
 constexpr int kMergeColsWide16 = 16;
 
-// A column's S partial sums sit side by side at a pitch of SPT floats (S
-// for S <= 2, else S rounded up to 4), read as one float, one float2 or
-// SPT / 4 float4.
+// A column's partial sums of slices 0 .. SPT-1, `stride` floats apart (one
+// slice's M runs of NP floats).  Slices at or past the launch's S lie inside
+// the workspace but hold nothing the sum uses.
 template <int SPT>
-__device__ __forceinline__ void load_slices(const float* __restrict__ col, float (&p)[SPT]) {
-  if constexpr (SPT >= 4) {
+__device__ __forceinline__ void load_slices(const float* __restrict__ col, size_t stride, float (&p)[SPT]) {
 #pragma unroll
-    for (int q = 0; q < SPT / 4; ++q) {
-      const float4 x = ((const float4*)col)[q];
-      p[4 * q] = x.x;
-      p[4 * q + 1] = x.y;
-      p[4 * q + 2] = x.z;
-      p[4 * q + 3] = x.w;
-    }
-  } else if constexpr (SPT == 2) {
-    const float2 x = *(const float2*)col;
-    p[0] = x.x;
-    p[1] = x.y;
-  } else {
-    p[0] = *col;
-  }
+  for (int q = 0; q < SPT; ++q) p[q] = col[q * stride];
 }
 
 template <int SPT>
@@ -753,7 +739,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   const int m = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int col0 = c * CHUNK;
   const int cend = min(n_max, col0 + CHUNK);         // > col0
-  const float* prow = part + (size_t)m * n_max * SPT;
+  const float* prow = part + (size_t)m * col_pitch(n_max);   // slice 0 of hidden row m
+  const size_t sstride = (size_t)gridDim.x * col_pitch(n_max);
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
   float pv[U][SPT];
@@ -767,7 +754,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
     const int j = col0 + tid;
     const int jc = j < cend ? j : cend - 1;
     gv[0] = row_ids ? row_ids[jc] : jc;
-    load_slices<SPT>(prow + (size_t)jc * SPT, pv[0]);
+    load_slices<SPT>(prow + jc, sstride, pv[0]);
     if (LOGP) {
       int zero;
       asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
@@ -790,7 +777,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
       const int j = col0 + tid + u * NT;
       const int jc = j < lim ? j : lim - 1;
       gv[u] = row_ids ? row_ids[jc] : jc;
-      load_slices<SPT>(prow + (size_t)jc * SPT, pv[u]);
+      load_slices<SPT>(prow + jc, sstride, pv[u]);
     }
     NS_ISSUE_FENCE();
   }
@@ -989,7 +976,7 @@ int max_splits(int n_max, int M, int d, int B) {
 
 template <bool BF16>
 int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V,
-                int d, const void* h, int M, int SP, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
+                int d, const void* h, int M, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
   const int esz = BF16 ? 2 : 4;
   const int dvec = d * esz / 16;
   const int quads = (n_max + kProjWaves - 1) / kProjWaves;
@@ -998,7 +985,7 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   const size_t lds = (size_t)mt * dvec * 16;
 #define NS_LAUNCH_VALU(MTV)                                                                                     \
   hipLaunchKernelGGL((k_proj_valu<BF16, MTV>), grid, dim3(kProjThreads), lds, stream, (const uint4*)rows, mode, \
-                     row_ids, n_dev, n_max, V, dvec, (const uint4*)h, M, SP, part, bs)
+                     row_ids, n_dev, n_max, V, dvec, (const uint4*)h, M, part, bs)
   switch (mt) {
     case 1: NS_LAUNCH_VALU(1); break;
     case 2: NS_LAUNCH_VALU(2); break;
@@ -1012,14 +999,14 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 template <int NMT, int RT, bool F16>
 void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
-                   int SP, float* part, const BatchStrides& bs) {
+                   float* part, const BatchStrides& bs) {
   hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows, mode,
-                     row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, SP, part, bs, B);
+                     row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, part, bs, B);
 }
 
 template <bool F16>
 int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
-                const void* h, int M, int S, int adapt, int SP, float* part, int B, const BatchStrides& bs,
+                const void* h, int M, int S, int adapt, float* part, int B, const BatchStrides& bs,
                 hipStream_t stream) {
   const int dv = d / 8;
   const int rt = pick_rt(M, n_max, B);
@@ -1039,10 +1026,10 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   }
   const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA(NMTV, RTV) \
-  launch_mfma_t<NMTV, RTV, F16>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, SP, part, bs)
+  launch_mfma_t<NMTV, RTV, F16>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, part, bs)
   if (rt == kMsplitRT) {
     hipLaunchKernelGGL((k_proj_msplit<kMsplitRT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows,
-                       mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, SP, part, bs, B);
+                       mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, part, bs, B);
     return ns_launch_status();
   }
   switch ((M + 15) / 16) {
@@ -1057,13 +1044,15 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
 
 int merge_chunks(int n_max) { return (n_max + kMergeChunk - 1) / kMergeChunk; }
 
-// Floats per column of the partial sums for S slices (monotonic in S, so a
-// workspace sized for the largest S fits every smaller one).
+// Slices the workspace holds, and the merge requests per column, for S
+// slices (monotonic in S, so a workspace sized for the largest S fits every
+// smaller one; the merge instances exist for these counts).
 int slice_pitch(int S) { return S <= 2 ? S : (S + 3) & ~3; }
 
-// Workspace layout: [0, 256) reserved; partial sums float[B][M][n_max][SP]
-// at 256; for n_max > kMergeChunk, chunk keys uint64[B][M][C][k] after them.
-size_t partial_floats(int n_max, int M, int SP) { return (size_t)SP * M * n_max; }
+// Workspace layout: [0, 256) reserved; partial sums float[B][SP][M][NP]
+// (NP = n_max rounded up to 4) at 256; for n_max > kMergeChunk, chunk keys
+// uint64[B][M][C][k] after them.
+size_t partial_floats(int n_max, int M, int SP) { return (size_t)SP * M * col_pitch(n_max); }
 size_t partial_bytes(int n_max, int M, int SP, int B) {
   return align256(partial_floats(n_max, M, SP) * B * sizeof(float));
 }
@@ -1141,9 +1130,9 @@ bool draft_dims_ok(int32_t n_max, int32_t M, int32_t k, int32_t d) {
 
 extern "C" {
 
-// Workspace: partial sums [B x M x n_max x SP] float32 (SP = S for S <= 2,
-// else S rounded up to 4) at offset 256, then, when n_max > 4096, the chunk
-// keys and the chunks' log-sum-exp pairs.
+// Workspace: partial sums [B x SP x M x NP] float32 (SP = S for S <= 2, else
+// S rounded up to 4; NP = n_max rounded up to 4) at offset 256, then, when
+// n_max > 4096, the chunk keys and the chunks' log-sum-exp pairs.
 size_t nanospec_batch_draft_workspace_bytes(int32_t B, int32_t n_max, int32_t M, int32_t k, int32_t d) {
   if (B < 1 || B > NS_MAX_BATCH || !draft_dims_ok(n_max, M, k, d)) return 0;
   const int SP = slice_pitch(max_splits(n_max, M, d, B));
@@ -1212,14 +1201,14 @@ int draft_project(const void* rows, int32_t mode, const int32_t* row_ids, const 
                   hipStream_t stream) {
   (void)hipGetLastError();
   if (dtype == NS_BF16)
-    return launch_mfma<false>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.SP, p.part, B, p.bs,
+    return launch_mfma<false>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.part, B, p.bs,
                               stream);
   if (dtype == NS_FP16)
-    return launch_mfma<true>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.SP, p.part, B, p.bs,
+    return launch_mfma<true>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.part, B, p.bs,
                              stream);
   const int mt = pick_mt(M, d, 4);
   if (mt == 0) return NS_EINVAL;
-  return launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.SP, p.part, B, p.bs, stream);
+  return launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.part, B, p.bs, stream);
 }
 
 int draft_select(const int32_t* row_ids, const int32_t* n_dev, int32_t n_max, int32_t B, int32_t V, int32_t M,
