@@ -371,8 +371,9 @@ def main():
         out["ablation"] = ablation_leg(torch, ns, WL, cfg, W, dcode, flush_fn)
         progress("batched-sequences leg")
         out["batched"] = batch_leg(torch, ns, WL, cfg, W, dcode, flush_fn, [int(x) for x in args.batches.split(",")])
-        progress("stress leg")
-        out["stress"] = stress_leg(torch, ns, WL, flush_fn)
+        for name in ("qwen25_7b", "stress"):
+            progress(f"{name} leg")
+            out[name] = config_leg(torch, ns, WL, flush_fn, name)
     if not args.no_dense:
         out["dense"] = dense_compare(torch, ns, cfg, W, hs[Wm], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
     if not args.no_cpu_baseline:
@@ -903,15 +904,16 @@ def ablation_leg(torch, ns, WL, cfg, W, dcode, flush, steps=48, warm=16):
                         f"cold, hipGraph replay of {steps} steps", "points": out}
 
 
-def stress_leg(torch, ns, WL, flush, steps=32, warm=16):
-    """The stress workload (V=151936, d=4096, W_max=16384, M=64, k=16; a
-    uniform id stream keeps about 15.5k ids active): cold per-step times of
-    the state update and the INDEXED draft head (graph replay, the
-    cache-streaming read and the state-only graph subtracted), and the
-    full-vocabulary head at the same M.  W and h are drawn on the GPU from a
-    seeded generator with the workload's distributions (N(0, 0.02^2) and
-    N(0, 1), bf16)."""
-    cfg = WL.get_config("stress")
+def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
+    """One decode workload besides the headline one, e.g. the stress workload
+    (V=151936, d=4096, W_max=16384, M=64, k=16; a uniform id stream keeps
+    about 15.5k ids active) or the Qwen-2.5-7B-shaped head (V=151936,
+    d=3584, W_max=3072, M=60, k=10): cold per-step times of the state update
+    and the INDEXED draft head (graph replay, the cache-streaming read and
+    the state-only graph subtracted), and the full-vocabulary head at the
+    same M.  W and h are drawn on the GPU from a seeded generator with the
+    workload's distributions (N(0, 0.02^2) and N(0, 1), bf16)."""
+    cfg = WL.get_config(name)
     T = warm + steps
     g = torch.Generator(device="cuda")
     g.manual_seed(cfg.seed)
@@ -996,7 +998,8 @@ def stress_leg(torch, ns, WL, flush, steps=32, warm=16):
     t_ours = _event_time(torch, ours, flush, 10)
     t_vendor = _event_time(torch, vendor, flush, 10)
     step_us = (t_a - t_f) / steps * 1e3
-    res = {"workload": f"stress: V={cfg.V} d={cfg.d} W_max={cfg.w_max} M={cfg.M} k={cfg.k}, uniform id stream, "
+    stream_kind = "uniform id stream" if cfg.prompt_kind == "uniform" else "Zipf/pool id stream"
+    res = {"workload": f"{name}: V={cfg.V} d={cfg.d} W_max={cfg.w_max} M={cfg.M} k={cfg.k}, {stream_kind}, "
                        f"cold, hipGraph replay of {steps} steps",
            "mean_active": n_mean, "step_us": step_us, "state_update_us": (t_s - t_f) / steps * 1e3,
            "draft_us": draft_us, "draft_GBps": draft_bytes / (draft_us * 1e-6) / 1e9,
