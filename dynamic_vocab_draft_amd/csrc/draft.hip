@@ -215,15 +215,20 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
 // load units then touch half as many cache lines).  The LDS image is
 // row-major; position p of row r holds window chunk p ^ (r mod CPR), so the
 // ds_read_b128 of an MFMA fragment (lane (i, g) wants chunk 4 kk + g of row
-// i) spreads 8 consecutive lanes over distinct banks.  Hidden rows (M <= 16)
-// take the same route, aliased to row M - 1 past M.
+// i) spreads 8 consecutive lanes over distinct banks.  Hidden rows take the
+// same route, aliased to row M - 1 past M, except with two hidden tiles
+// (17 <= M <= 32), which load them into registers.
 //
 // Buffers are per wave and double-buffered: the next batch is requested
 // before the current one is read, and the wait is an explicit vmcnt of one
 // batch's load count.  The LDS reads are inline-asm ds_read_b128 followed by
 // an explicit lgkmcnt(0): the compiler would otherwise wait for every load
 // still in flight (it cannot tell the two buffers' loads apart across the
-// loop).  No block barrier until the four waves' tiles are summed.
+// loop).  Hidden rows loaded into registers get such a full wait from the
+// compiler before their first use in every other batch; through LDS they
+// also arrive as whole 128-byte runs instead of half lines, which measured
+// faster from three hidden tiles up (M = 60: 13.2 -> 12.3 us per call) and
+// slower with two.  No block barrier until the four waves' tiles are summed.
 // ---------------------------------------------------------------------------
 constexpr int kDmaKC = 2;                          // k-steps per batch (128-byte row runs)
 
@@ -260,12 +265,19 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction
   constexpr int NI = kTile / RPI;                  // load instructions per 16 rows
   constexpr int TB = kTile * CPR;                  // uint4 of one tile's batch window
-  constexpr bool BDMA = NMT == 1;                  // hidden rows through LDS too (M <= 16)
+  // Hidden rows reach the matrix cores through LDS as well, except for two
+  // hidden tiles (17 <= M <= 32), where loads into registers measured faster
+  // (the LDS copy would cost a block per CU).
+  constexpr bool HDMA = NMT != 2;
   __shared__ uint4 abuf0[kPW][RT * TB];
   __shared__ uint4 abuf1[kPW][RT * TB];
-  __shared__ uint4 bbuf0[kPW][BDMA ? TB : 1];
-  __shared__ uint4 bbuf1[kPW][BDMA ? TB : 1];
-  __shared__ f32x4_t red[kPW][RT][NMT][NS_WAVE];
+  __shared__ uint4 bbuf0[kPW][HDMA ? NMT * TB : 1];
+  __shared__ uint4 bbuf1[kPW][HDMA ? NMT * TB : 1];
+  // The wave tiles of the final sum reuse a staging buffer (RT NMT 4 KiB:
+  // within abuf0 for NMT <= 2, within bbuf0 otherwise, as RT <= 2).
+  static_assert(sizeof(f32x4_t) * kPW * RT * NMT * NS_WAVE <= (NMT <= 2 ? sizeof(abuf0) : sizeof(bbuf0)),
+                "wave tiles fit the reused buffer");
+  auto red = reinterpret_cast<f32x4_t (*)[RT][NMT][NS_WAVE]>(NMT <= 2 ? &abuf0[0][0] : &bbuf0[0][0]);
   // The 1-D grid is read as (tile group, sequence, slice, XCD lane), tile
   // group slowest: L = ((tg B + b) S + s) 8 + x.  Row tile tg 8 + x of
   // sequence b and slice s.  Dispatch then runs over the low (live) tiles of
@@ -343,21 +355,25 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       asrc[r][q] = rows + (size_t)(oks ? (mode == NS_INDEXED ? gsh : r0 + r * kTile + tr) : 0) * dv;
     }
   }
-  const uint4* hsrc[BDMA ? NI : 1];
-  if constexpr (BDMA) {
-#pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int m = q * RPI + rsub;
-      hsrc[q] = h + (size_t)(m < M ? m : M - 1) * dv;
-    }
-  }
-  const uint4* hrow[NMT];
+  // Hidden-row sources: by load instruction for the LDS route (lanes laid out
+  // as for the rows, rows past M alias row M - 1), by MFMA lane otherwise
+  // (padded lanes alias a real row).  Padded rows are zeroed as operands.
+  const uint4* hsrc[HDMA ? NMT : 1][NI];
+  const uint4* hrow[HDMA ? 1 : NMT];
   bool m_ok[NMT];
 #pragma unroll
   for (int t = 0; t < NMT; ++t) {
-    const int m = t * 16 + i;
-    m_ok[t] = m < M;
-    hrow[t] = h + (size_t)(m_ok[t] ? m : m % M) * dv;   // padded lanes alias a real row
+    m_ok[t] = t * 16 + i < M;
+    if constexpr (HDMA) {
+#pragma unroll
+      for (int q = 0; q < NI; ++q) {
+        const int m = t * 16 + q * RPI + rsub;
+        hsrc[t][q] = h + (size_t)(m < M ? m : M - 1) * dv;
+      }
+    } else {
+      const int m = t * 16 + i;
+      hrow[t] = h + (size_t)(m < M ? m : m % M) * dv;
+    }
   }
   // This wave's 32-column steps: the split's range, divided among the waves.
   const int ksteps = (dv + 3) >> 2;
@@ -377,8 +393,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 
   // Requests batch s0 into one buffer pair.  Chunks past the wave's range
   // or past d load column 0 of the same row (their products are zeroed).
-  auto issue = [&](int s0, uint4 (&ab)[kPW][RT * TB], uint4 (&bb)[kPW][BDMA ? TB : 1],
-                   uint4 (&bq)[KC][NMT]) {
+  constexpr int HB = HDMA ? NMT * TB : 1;
+  auto issue = [&](int s0, uint4 (&ab)[kPW][RT * TB], uint4 (&bb)[kPW][HB], uint4 (&bq)[KC][HDMA ? 1 : NMT]) {
     __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): earlier reads of these buffers done
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
@@ -386,9 +402,12 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       const int cc = (c < s_end * 4 && c < dv) ? c : 0;
 #pragma unroll
       for (int r = 0; r < RT; ++r) dma16(asrc[r][q] + cc, &ab[w][r * TB + q * NS_WAVE]);
-      if constexpr (BDMA) dma16(hsrc[q] + cc, &bb[w][q * NS_WAVE]);
+      if constexpr (HDMA) {
+#pragma unroll
+        for (int t = 0; t < NMT; ++t) dma16(hsrc[t][q] + cc, &bb[w][t * TB + q * NS_WAVE]);
+      }
     }
-    if constexpr (!BDMA) {
+    if constexpr (!HDMA) {
 #pragma unroll
       for (int kk = 0; kk < KC; ++kk) {
         const int c8 = (s0 + kk) * 4 + g;
@@ -398,22 +417,28 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       }
     }
   };
-  auto compute = [&](int s0, const uint4 (&ab)[kPW][RT * TB], const uint4 (&bb)[kPW][BDMA ? TB : 1],
-                     const uint4 (&bq)[KC][NMT]) {
-    uint4 af[KC][RT], bf[KC];
+  auto compute = [&](int s0, const uint4 (&ab)[kPW][RT * TB], const uint4 (&bb)[kPW][HB],
+                     const uint4 (&bq)[KC][HDMA ? 1 : NMT]) {
+    uint4 af[KC][RT], bf[KC][HDMA ? NMT : 1];
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
       const int off = i * CPR + ((4 * kk + g) ^ swz_i);
 #pragma unroll
       for (int r = 0; r < RT; ++r) af[kk][r] = lds_read_b128(&ab[w][r * TB + off]);
-      if constexpr (BDMA) bf[kk] = lds_read_b128(&bb[w][off]);
+      if constexpr (HDMA) {
+#pragma unroll
+        for (int t = 0; t < NMT; ++t) bf[kk][t] = lds_read_b128(&bb[w][t * TB + off]);
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) lds_ready(af[kk][r]);
-      if constexpr (BDMA) lds_ready(bf[kk]);
+      if constexpr (HDMA) {
+#pragma unroll
+        for (int t = 0; t < NMT; ++t) lds_ready(bf[kk][t]);
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
@@ -421,7 +446,10 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       const bool kok = (s0 + kk) < s_end && c8 < dv;
 #pragma unroll
       for (int t = 0; t < NMT; ++t) {
-        const uint4 bv = (kok && m_ok[t]) ? (BDMA ? bf[kk] : bq[kk][t]) : z;
+        uint4 hv;
+        if constexpr (HDMA) hv = bf[kk][t];
+        else hv = bq[kk][t];
+        const uint4 bv = (kok && m_ok[t]) ? hv : z;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           const uint4 av = (kok && ok[r]) ? af[kk][r] : z;
@@ -437,11 +465,11 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   };
   // vmcnt immediate (gfx9 encoding, expcnt and lgkmcnt left at their maxima)
   // that waits until at most one batch's loads are outstanding.
-  constexpr int NLOADS = NI * RT + (BDMA ? NI : KC * NMT);
+  constexpr int NLOADS = NI * RT + (HDMA ? NI * NMT : KC * NMT);
   static_assert(NLOADS < 64, "vmcnt range");
   constexpr int kWaitOneBatch = (NLOADS & 0xF) | (0x7 << 4) | (0xF << 8) | ((NLOADS >> 4) << 14);
   constexpr int kWaitAll = 0x0F70;
-  uint4 b0[KC][NMT], b1[KC][NMT];
+  uint4 b0[KC][HDMA ? 1 : NMT], b1[KC][HDMA ? 1 : NMT];
   if (s_begin < s_end) {                                // wave-uniform
     issue(s_begin, abuf0, bbuf0, b0);
     NS_ISSUE_FENCE();
@@ -465,6 +493,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       compute(s0 + KC, abuf1, bbuf1, b1);
     }
   }
+  __syncthreads();                                      // every wave is done with the buffer red reuses
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll

@@ -325,7 +325,8 @@ def test_projection_shapes(ns):
     """The projection kernels' edges: d / 8 of 1, 5, 33, 65 and 131 sixteen-
     byte chunks (the two-k-step batch window runs past d, and a wave's range
     can be shorter than a batch or empty), M across the 16-row hidden tiles
-    (hidden rows staged in LDS for M <= 16, loaded directly above), ragged
+    (hidden rows staged in LDS, except for 17 <= M <= 32, which loads them
+    into registers), ragged
     row tiles, both row modes, bf16 and fp16, the M-split kernel for
     48 < M <= 64 over many rows, and a large n_max whose blocks re-map
     themselves to the live row count."""
@@ -337,7 +338,7 @@ def test_projection_shapes(ns):
             bits = WL.f32_to_bf16_bits if dtype == "bf16" else WL.f32_to_fp16_bits
             W = bits((rng.standard_normal((V, d)) * 0.1).astype(np.float32))
             W_dev = dev_elems(W, dtype)
-            for M, n in ((1, 1), (7, 15), (16, 33), (17, 300), (40, 47), (64, 129)):
+            for M, n in ((1, 1), (7, 15), (16, 33), (17, 300), (32, 64), (33, 190), (40, 47), (64, 129)):
                 h = bits(rng.standard_normal((M, d)).astype(np.float32))
                 I = np.sort(rng.choice(V, size=n, replace=False))
                 k = min(8, n)
