@@ -714,13 +714,13 @@ constexpr int kMergeColsWide = 8;
 // the per-chunk selection and the key merge.
 constexpr int kMergeColsWide16 = 16;
 
-// A column's partial sums of slices 0 .. SPT-1, `stride` floats apart (one
-// slice's M runs of NP floats).  Slices at or past the launch's S lie inside
-// the workspace but hold nothing the sum uses.
+// A column's partial sums of slices 0 .. S-1 (S <= SPT), `stride` floats
+// apart (one slice's M runs of NP floats).  Registers past S repeat slice 0
+// (the same lines, so no further memory traffic) and are not summed.
 template <int SPT>
-__device__ __forceinline__ void load_slices(const float* __restrict__ col, size_t stride, float (&p)[SPT]) {
+__device__ __forceinline__ void load_slices(const float* __restrict__ col, size_t stride, int S, float (&p)[SPT]) {
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) p[q] = col[q * stride];
+  for (int q = 0; q < SPT; ++q) p[q] = col[(q < S ? q : 0) * stride];
 }
 
 template <int SPT>
@@ -736,9 +736,11 @@ __device__ __forceinline__ float sum_slices(const float (&p)[SPT], int S) {
 // [c * 1024 U, (c + 1) * 1024 U) of hidden row m (at most U per thread),
 // optionally writes the logits, and selects that chunk's top k.  With one
 // chunk the winners go straight to the outputs; otherwise each chunk's k
-// keys go to cand_out[m][c][k] for k_merge_keys.  The first column of every
-// thread is requested in the same round as |I|, so the partial sums are in
-// flight before |I| is known.  With LOGP the emitted values are
+// keys go to cand_out[m][c][k] for k_merge_keys.  When S is fixed at launch,
+// the first column of every thread is requested in the same round as |I|, so
+// the partial sums are in flight before |I| is known; with `adapt` the slice
+// count follows |I|, which is read first, so that only live slices are
+// requested.  With LOGP the emitted values are
 // parent[m] + z - lse[m], lse[m] being the log-sum-exp of row m over all
 // active columns (a block max and a sum of exp(z - max) per chunk, combined
 // by k_merge_keys when there are several); the selection itself runs on z,
@@ -773,27 +775,32 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   const int n_raw = n_dev ? *n_dev : n_max;
   int gv[U];
   float pv[U][SPT];
+  const int j0 = col0 + tid;
+  const int jc0 = j0 < cend ? j0 : cend - 1;
   // LOGP: the parent score is requested in the first round too, as a vector
   // load (an opaque zero keeps it per lane): a scalar load would share the
   // LDS wait counter and stall the selection's first LDS wait on memory.
   // Without parents it reads a valid partial sum instead.
   const size_t row = (size_t)blockIdx.z * lp.M + m;
   float par_raw = 0.f;
-  {
-    const int j = col0 + tid;
-    const int jc = j < cend ? j : cend - 1;
-    gv[0] = row_ids ? row_ids[jc] : jc;
-    load_slices<SPT>(prow + jc, sstride, pv[0]);
-    if (LOGP) {
-      int zero;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-      par_raw = (lp.parent ? lp.parent + row : part)[zero];
-    }
+  if (!adapt) {                                      // launch-uniform; every slice of the pitch is live
+    gv[0] = row_ids ? row_ids[jc0] : jc0;
+    load_slices<SPT>(prow + jc0, sstride, SPT, pv[0]);
+  }
+  if (LOGP) {
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    par_raw = (lp.parent ? lp.parent + row : part)[zero];
   }
   NS_ISSUE_FENCE();
   const float par = (LOGP && lp.parent) ? par_raw : 0.f;
   const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
-  if (adapt) S = live_splits(n, (int)gridDim.x, gridDim.z, S);   // as the projection chose (grid: M x chunks x B)
+  if (adapt) {
+    S = live_splits(n, (int)gridDim.x, gridDim.z, S);   // as the projection chose (grid: M x chunks x B)
+    gv[0] = row_ids ? row_ids[jc0] : jc0;
+    load_slices<SPT>(prow + jc0, sstride, S, pv[0]);
+    NS_ISSUE_FENCE();
+  }
   const int lim = min(n, cend);                      // live columns of this chunk end here
   // With several chunks but every live column in chunk 0, chunk 0 writes the
   // final result and k_merge_keys does nothing; the other chunks are idle.
@@ -806,7 +813,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
       const int j = col0 + tid + u * NT;
       const int jc = j < lim ? j : lim - 1;
       gv[u] = row_ids ? row_ids[jc] : jc;
-      load_slices<SPT>(prow + jc, sstride, pv[u]);
+      load_slices<SPT>(prow + jc, sstride, adapt ? S : SPT, pv[u]);
     }
     NS_ISSUE_FENCE();
   }
@@ -970,9 +977,11 @@ int pick_rt(int M, int n_max, int B) { return use_msplit(n_max, M, B) ? kMsplitR
 // only known on the device (n_dev given) and M <= 16, S is sized as if at
 // most kLiveRowsHint rows of each sequence were live, so a few live rows out
 // of a large n_max still spread over the chip; the partial sums then cost at
-// most 4 M S / d of the row bytes (6% at d = 4096, M = 8, S = 8).  Larger M,
-// whose partial sums cost more, and calls with n known on the host use n_max.
-// Other dtypes use one slice.
+// most 4 M S / d of the row bytes (6% at d = 4096, M = 8, S = 8).  Larger M
+// and calls with n known on the host use n_max: re-mapping the M > 16
+// kernel's blocks to the live count measured slower (M = 64 at 3000 of 3072
+// rows 22.7 -> 26.7 us per call, M = 20 14.8 -> 20.1 us).  Other dtypes use
+// one slice.
 int launch_splits(bool n_known, int n_max, int M, int d, int dtype, int B) {
   if (!is_mfma_dtype(dtype)) return 1;
   const int ksteps = (d / 8 + 3) / 4;
@@ -1041,14 +1050,17 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   const int rt = pick_rt(M, n_max, B);
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and
   // exit), times S slices, per sequence; one 1-D grid for all B sequences.
-  // S > 1 only while tiles x B < kTargetBlocks, so the grid stays below 2^31.
+  // S > 1 only while tiles x B < kTargetBlocks, or with `adapt` (grid
+  // trimmed below), so the grid stays below 2^31.
   unsigned per_seq = (unsigned)(((n_max + kTile * rt - 1) / (kTile * rt) + 7) / 8) * 8u * (unsigned)S;
   if (adapt) {
-    // Blocks re-map to the live n with S_live = live_splits(n) slices, and
-    // tiles(n) x S_live < kTargetBlocks / B + tiles(n) (plus the rounding
-    // of tiles to 8), so the rest of a full tiles x S grid would only exit.
+    // Blocks re-map to the live n with S_live = live_splits(n) slices.  With
+    // t = tiles(n) and T = kTargetBlocks: S_live = 1 needs at most
+    // tiles_max + 7 blocks per sequence; otherwise t (S_live - 1) < T / B, so
+    // the round8(t) S_live blocks it needs stay below T / B + t + 7 S.  The
+    // rest of a full tiles x S grid would only exit.
     const unsigned tiles_max = (unsigned)((n_max + kTile * rt - 1) / (kTile * rt));
-    const unsigned bound = (unsigned)((kTargetBlocks + B - 1) / B) + tiles_max + 56u;
+    const unsigned bound = (unsigned)((kTargetBlocks + B - 1) / B) + tiles_max + 7u * (unsigned)S;
     const unsigned group = 8u * (unsigned)S;
     const unsigned trimmed = (bound + group - 1) / group * group;
     per_seq = trimmed < per_seq ? trimmed : per_seq;
