@@ -58,6 +58,9 @@ def parse():
                    help="only sweep the draft head over |I| x M (cold) and print one JSON line per point")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES (calibrates HBM byte counters) and exit")
+    p.add_argument("--head-probe", default="", metavar="M[,M...]",
+                   help="only run the full-vocabulary projection (V=151936, d=4096, bf16) three times for each "
+                        "M, for hardware counters, and exit")
     return p.parse_args()
 
 
@@ -76,6 +79,9 @@ def main():
     from dynamic_vocab_draft_amd import workloads as WL
 
     torch.cuda.set_device(0)
+    if args.head_probe:
+        head_probe(torch, ns, [int(x) for x in args.head_probe.split(",")])
+        return
     if args.sweep:
         sweep(torch, ns, WL, args)
         return
@@ -393,6 +399,24 @@ def copy_probe(torch, nbytes):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "copies": 3}), flush=True)
+
+
+def head_probe(torch, ns, Ms, V=151936, d=4096, k=16):
+    """The projection stage alone (nanospec_draft_project, PACKED over all V
+    rows of a seeded N(0, 0.02^2) bf16 head), three calls per M: the same
+    kernels as the full-vocabulary comparison, for per-kernel hardware
+    counters."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1005)
+    W = torch.randn((V, d), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+    for M in Ms:
+        h = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
+        ws = ns.alloc_workspace(V, M, k, d)
+        for _ in range(3):
+            ns.nanospec_draft_project(W, ns.NS_PACKED, None, None, V, V, d, ns.NS_BF16, h, M, k, ws)
+        torch.cuda.synchronize()
+        del ws
+    print(json.dumps({"head_probe_M": Ms, "V": V, "d": d, "calls_per_M": 3}), flush=True)
 
 
 DRAFT_SOURCES = ("dynamic_vocab_draft_amd/csrc/draft.hip", "dynamic_vocab_draft_amd/csrc/select.hpp",
