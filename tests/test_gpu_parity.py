@@ -379,6 +379,28 @@ def test_projection_shapes(ns):
         check_draft(out, h, W, I, 8, "bf16", f"adaptive slices M={M} n={n} n_max={n_max}")
 
 
+def test_slice_counts(ns):
+    """Slice counts the other tests do not reach (they use d <= 264, one
+    slice): n known only on the device with n_max above 3072 and M <= 16,
+    where the projection's blocks and the merge take the slice count from the
+    live n (re-mapping when it is below the launch's, the merge then
+    requesting only the live slices; one- and two-kernel merges), and d = 8192
+    with few rows, which launches 12 and 16 slices."""
+    say("slice counts")
+    rng = np.random.default_rng(47)
+    for d, V, cases in ((4096, 20000, ((8, 16384, 16384, 8), (8, 5000, 8192, 8), (16, 100, 4000, 16),
+                                       (1, 4000, 4100, 4))),
+                        (8192, 6000, ((8, 900, 1000, 8), (4, 2000, 2048, 8), (2, 50, 5000, 8)))):
+        W = WL.f32_to_bf16_bits((rng.standard_normal((V, d)) * 0.02).astype(np.float32))
+        W_dev = dev_elems(W, "bf16")
+        for M, n, n_max, k in cases:
+            h = WL.f32_to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+            I = np.sort(rng.choice(V, size=n, replace=False))
+            out = run_draft(ns, W_dev, dev_elems(h, "bf16"), I, n_max, V, d, "bf16", M, k, ns.NS_INDEXED)
+            check_draft(out, h, W, I, k, "bf16", f"slices d={d} M={M} n={n} n_max={n_max}")
+        del W_dev
+
+
 def test_merge_paths(ns):
     """Column counts around the merge kernel's limits (one column per thread,
     up to four per thread, the general kernel past 4096) and a logit pattern
