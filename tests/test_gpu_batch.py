@@ -115,7 +115,10 @@ def test_batch_llama3_8b(ns):
 
 
 def test_batch_qwen25_7b(ns):
+    # B = 3: 3 x 48 groups of 64 rows, the M-split projection; B = 2 (96
+    # groups) keeps the k-split kernel, hidden rows staged through LDS.
     run_batch(ns, "qwen25_7b", 3, 6, {5})
+    run_batch(ns, "qwen25_7b", 2, 4, {3})
 
 
 def test_batch_many_columns(ns):
