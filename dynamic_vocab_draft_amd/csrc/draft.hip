@@ -736,11 +736,11 @@ __device__ __forceinline__ float sum_slices(const float (&p)[SPT], int S) {
 // [c * 1024 U, (c + 1) * 1024 U) of hidden row m (at most U per thread),
 // optionally writes the logits, and selects that chunk's top k.  With one
 // chunk the winners go straight to the outputs; otherwise each chunk's k
-// keys go to cand_out[m][c][k] for k_merge_keys.  When S is fixed at launch,
-// the first column of every thread is requested in the same round as |I|, so
-// the partial sums are in flight before |I| is known; with `adapt` the slice
-// count follows |I|, which is read first, so that only live slices are
-// requested.  With LOGP the emitted values are
+// keys go to cand_out[m][c][k] for k_merge_keys.  The first column of every
+// thread is requested in the same round as |I|, so the partial sums are in
+// flight before |I| is known (every slice the workspace holds; with `adapt`
+// the live count may use fewer).  The further columns follow |I|, and with
+// `adapt` they request only the live slices.  With LOGP the emitted values are
 // parent[m] + z - lse[m], lse[m] being the log-sum-exp of row m over all
 // active columns (a block max and a sum of exp(z - max) per chunk, combined
 // by k_merge_keys when there are several); the selection itself runs on z,
@@ -783,10 +783,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   // Without parents it reads a valid partial sum instead.
   const size_t row = (size_t)blockIdx.z * lp.M + m;
   float par_raw = 0.f;
-  if (!adapt) {                                      // launch-uniform; every slice of the pitch is live
-    gv[0] = row_ids ? row_ids[jc0] : jc0;
-    load_slices<SPT>(prow + jc0, sstride, SPT, pv[0]);
-  }
+  gv[0] = row_ids ? row_ids[jc0] : jc0;
+  load_slices<SPT>(prow + jc0, sstride, SPT, pv[0]);
   if (LOGP) {
     int zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
@@ -795,12 +793,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   NS_ISSUE_FENCE();
   const float par = (LOGP && lp.parent) ? par_raw : 0.f;
   const int n = n_raw < 0 ? 0 : (n_raw > n_max ? n_max : n_raw);
-  if (adapt) {
-    S = live_splits(n, (int)gridDim.x, gridDim.z, S);   // as the projection chose (grid: M x chunks x B)
-    gv[0] = row_ids ? row_ids[jc0] : jc0;
-    load_slices<SPT>(prow + jc0, sstride, S, pv[0]);
-    NS_ISSUE_FENCE();
-  }
+  if (adapt) S = live_splits(n, (int)gridDim.x, gridDim.z, S);   // as the projection chose (grid: M x chunks x B)
   const int lim = min(n, cend);                      // live columns of this chunk end here
   // With several chunks but every live column in chunk 0, chunk 0 writes the
   // final result and k_merge_keys does nothing; the other chunks are idle.
