@@ -68,7 +68,7 @@ constexpr int kPW = 4;                            // waves per MFMA projection b
 constexpr int kPThreads = kPW * NS_WAVE;
 constexpr int kTile = 16;                         // rows per MFMA tile
 constexpr int kKC = 4;                            // 32-column steps per wave and slice, at least
-constexpr int kTargetBlocks = 1536;               // MFMA blocks aimed for when choosing S
+constexpr int kTargetBlocks = 768;                // MFMA blocks aimed for when choosing S
 constexpr int kMaxSplits = 16;
 constexpr int kLiveRowsHint = 3072;               // live rows assumed when sizing S without n
 
@@ -970,7 +970,7 @@ int pick_rt(int M, int n_max, int B) { return use_msplit(n_max, M, B) ? kMsplitR
 // only known on the device (n_dev given) and M <= 16, S is sized as if at
 // most kLiveRowsHint rows of each sequence were live, so a few live rows out
 // of a large n_max still spread over the chip; the partial sums then cost at
-// most 4 M S / d of the row bytes (6% at d = 4096, M = 8, S = 8).  Larger M
+// most 4 M S / d of the row bytes (3% at d = 4096, M = 8, S = 4).  Larger M
 // and calls with n known on the host use n_max: re-mapping the M > 16
 // kernel's blocks to the live count measured slower (M = 64 at 3000 of 3072
 // rows 22.7 -> 26.7 us per call, M = 20 14.8 -> 20.1 us).  Other dtypes use
