@@ -957,7 +957,7 @@ int pick_mt(int M, int d, int esz) {
 // ~900 live rows of 3072 it is 11 us against 13 us).
 constexpr int kMsplitRT = 4;
 constexpr int kMsplitMinTiles = 128;
-constexpr int kMsplitTargetBlocks = 384;
+constexpr int kMsplitTargetBlocks = 512;
 
 bool use_msplit(int n_max, int M, int B) {
   return M > 48 && (long)((n_max + kTile * kMsplitRT - 1) / (kTile * kMsplitRT)) * B >= kMsplitMinTiles;
