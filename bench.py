@@ -67,7 +67,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no multi-GPU "
               f"path.", file=sys.stderr)
         sys.exit(2)
 

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_pack_plan(const uint32_t* __re
   const int nv = (nw + 3) >> 2;                        // 16-byte vectors of bitmap words
   const uint4* __restrict__ act4 = (const uint4*)act;
   uint4* __restrict__ held4 = (uint4*)p.held;
-  // Round 1: bitmap vectors and slot ids (indices clamped, results masked).
+  // First load round: bitmap vectors and slot ids (indices clamped, results masked).
   uint4 a[G], h[G];
   int sid[SPT];
 #pragma unroll
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_pack_plan(const uint32_t* __re
     a[i] = make_uint4(a[i].x & m0, a[i].y & m1, a[i].z & m2, a[i].w & m3);
     h[i] = make_uint4(h[i].x & m0, h[i].y & m1, h[i].z & m2, h[i].w & m3);
   }
-  // Round 2: is each slot's id still active?
+  // Second load round: is each slot's id still active?
   uint32_t aw[SPT];
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
