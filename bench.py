@@ -87,7 +87,9 @@ def main():
         return
     cfg = WL.get_config(args.config)
     K, Wm = args.steps, args.warmup
-    T = Wm + K
+    # Generous id script: the lead-in (steps until |S| reaches W_max, each
+    # step appends at least k_ver ids) plus warm-up and timed steps.
+    T_script = Wm + K + -(-max(0, cfg.w_max - cfg.prompt_len) // max(1, cfg.k_ver)) + 1
     dcode = ns.NS_BF16 if cfg.dtype == "bf16" else ns.NS_FP32
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
@@ -99,16 +101,29 @@ def main():
     # ---- inputs, resident on the GPU before timing ------------------------
     W_host = WL.make_weights(cfg)
     W = dev(W_host)
-    script = WL.make_id_script(cfg, steps=T)
+    script = WL.make_id_script(cfg, steps=T_script)
     trees = [torch.as_tensor(t, dtype=torch.int32).cuda() for t in script.tree]
     vers = [torch.as_tensor(v, dtype=torch.int32).cuda() for v in script.ver]
-    hs = torch.stack([dev(WL.make_hidden(cfg, t)) for t in range(T)])
     prompt = torch.as_tensor(script.prompt, dtype=torch.int32).cuda()
-
-    progress(f"{cfg.name} inputs resident on the GPU")
     st = ns.NanoSpecState(cfg.V, cfg.w_max)
     ids = torch.empty(cfg.w_max, dtype=torch.int32, device="cuda")
     n_act = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    # Lead-in: the untimed steps until the window is full (|S| >= W_max, read
+    # from the state), so the warm-up and timed steps that follow run at the
+    # workload's steady-state |I| whatever --steps is.
+    s_len = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
+    lead = 0
+    ns.nanospec_state_window(st, None, s_len)
+    while int(s_len.item()) < cfg.w_max:
+        ns.nanospec_step_update(st, trees[lead], trees[lead].numel(), vers[lead], vers[lead].numel(), ids, n_act)
+        ns.nanospec_state_window(st, None, s_len)
+        lead += 1
+    t0 = lead + Wm                               # first timed step
+    T = t0 + K
+    hs = torch.stack([dev(WL.make_hidden(cfg, t)) for t in range(T)])
+    progress(f"{cfg.name} inputs resident on the GPU; lead-in {lead} steps, timed steps {t0}..{T - 1}")
     packed = torch.zeros((cfg.w_max, cfg.d), dtype=tdt, device="cuda")
     pk = ns.NanoSpecPacked(cfg.V, cfg.w_max)
     slot_rows = torch.zeros((cfg.w_max, cfg.d), dtype=tdt, device="cuda")
@@ -167,7 +182,7 @@ def main():
 
     def body(mode, cold, with_state=True, with_draft=True):
         def run():
-            for t in range(Wm, T):
+            for t in range(t0, T):
                 if cold:
                     sink.copy_(flush_lines[:, (t * 7) % 128])
                 if with_state:
@@ -181,7 +196,7 @@ def main():
         if mode == SLOTS:
             ns.nanospec_packed_reset(pk)
             pack_update()
-        for t in range(Wm):
+        for t in range(t0):
             state_part(t)
             if mode == SLOTS:
                 pack_update()
@@ -253,7 +268,7 @@ def main():
         g_warm = capture(body(m, False), m)
         g_state = capture(body(m, True, True, False), m)
         t_cold = time_graph(g_cold, mode=m)
-        ok = bool(torch.equal(tids[Wm:], ref_ids[Wm:]) and torch.equal(tvals[Wm:], ref_vals[Wm:]))
+        ok = bool(torch.equal(tids[t0:], ref_ids[t0:]) and torch.equal(tvals[t0:], ref_vals[t0:]))
         t_warm = time_graph(g_warm, mode=m)
         t_state = time_graph(g_state, mode=m)
         t_draft = time_diff(g_cold, g_state, mode=m)
@@ -272,7 +287,7 @@ def main():
     del g_proj, g_st
 
     ms = r["cold_ms"]
-    n_mean = float(np.mean(sizes[Wm:]))
+    n_mean = float(np.mean(sizes[t0:]))
     s = cfg.elem_bytes
     # Algorithmic bytes of one draft-head call: active rows, h, row ids, outputs.
     draft_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + n_mean * 4 + cfg.M * cfg.k * 8
@@ -299,25 +314,26 @@ def main():
         "config": {"workload": f"{cfg.name}: V={cfg.V} d={cfg.d} W_max={cfg.w_max} M={cfg.M} k={cfg.k}, "
                                f"{cfg.n_tree} draft-tree + {cfg.k_ver} verify ids per step",
                    "mode": mname[best], "cache": "cold (512 MiB streamed through the caches between steps)",
-                   "mean_active": n_mean, "timing": "hipGraph replay of the timed steps"},
+                   "mean_active": n_mean, "lead_in_steps": lead, "timed_steps": [t0, T - 1],
+                   "timing": "hipGraph replay of the timed steps"},
         "roofline": {"bound": "hbm", "achieved": proj_GBps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": proj_GBps / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg.name, "indexed", "traffic_bytes_per_projection"),
+                     "traffic": measured_traffic(cfg.name, "indexed", n_mean, "traffic_bytes_per_projection"),
                      "kernel": "k_proj_mfma (nanospec_draft_project, INDEXED)",
                      "bytes_per_launch": proj_bytes, "avg_launch_us": t_proj_ms * 1e3,
                      "draft_call": {"kernels": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols",
                                     "mode": mname[best], "bytes": draft_bytes, "avg_us": r["draft_ms"] * 1e3,
                                     "achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
-                                    "traffic": measured_traffic(cfg.name, mname[best])}},
+                                    "traffic": measured_traffic(cfg.name, mname[best], n_mean)}},
         "step": {"alg_bytes": step_bytes, "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
                  "state_update_us": r["state_ms"] * 1e3, "draft_us": r["draft_ms"] * 1e3,
                  "warm_ms": r["warm_ms"], "eager_warm_ms": r["eager_warm_ms"],
                  "per_mode": {mname[m]: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res[m].items()}
                               for m in modes},
                  "flush_ms": t_flush / K,
-                 "slots": {"mean_entering_rows": float(np.mean(enters[Wm:])),
-                           "mean_slots_in_use": float(np.mean(n_slots[Wm:])),
-                           "gather_bytes_per_step": float(np.mean(enters[Wm:])) * 2 * cfg.d * s,
+                 "slots": {"mean_entering_rows": float(np.mean(enters[t0:])),
+                           "mean_slots_in_use": float(np.mean(n_slots[t0:])),
+                           "gather_bytes_per_step": float(np.mean(enters[t0:])) * 2 * cfg.d * s,
                            "full_gather_bytes_per_step": n_mean * 2 * cfg.d * s}},
         "cpu_baseline": None,
     }
@@ -326,7 +342,7 @@ def main():
         progress("prefill top-K leg")
         out["prefill"] = prefill_leg(torch, ns, WL, flush_fn)
         progress("gather / backbone overlap leg")
-        out["overlap"] = overlap_leg(torch, ns, cfg, W, ids, n_act, packed, hs[Wm], ws, dcode, copy_stream,
+        out["overlap"] = overlap_leg(torch, ns, cfg, W, ids, n_act, packed, hs[t0], ws, dcode, copy_stream,
                                      flush_fn)
         progress("decode pipeline leg")
         backbone = make_backbone(torch, cfg)
@@ -369,7 +385,7 @@ def main():
                  "slots_serial": Head(SLOTS, head_slots(False)),
                  "slots_overlap": Head(SLOTS, head_slots(True)),
                  "full_gather_overlap": Head(ns.NS_PACKED, head_full_gather)}
-        out["pipeline"] = pipeline_leg(torch, cfg, backbone, warm_up_state, state_part, heads, flush_fn, Wm,
+        out["pipeline"] = pipeline_leg(torch, cfg, backbone, warm_up_state, state_part, heads, flush_fn, t0,
                                        min(K, 40), copy_stream)
         progress("tree drafting leg")
         out["tree"] = tree_leg(torch, ns, cfg, W, ids, n_act, dcode, flush_fn)
@@ -381,7 +397,7 @@ def main():
             progress(f"{name} leg")
             out[name] = config_leg(torch, ns, WL, flush_fn, name)
     if not args.no_dense:
-        out["dense"] = dense_compare(torch, ns, cfg, W, hs[Wm], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
+        out["dense"] = dense_compare(torch, ns, cfg, W, hs[t0], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
     if not args.no_cpu_baseline:
         progress("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg, W_host, args.cpu_seconds)
@@ -442,12 +458,13 @@ def kernel_source_hash(sources=DRAFT_SOURCES):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, mode, key="traffic_bytes_per_call"):
+def measured_traffic(workload, mode, mean_active, key="traffic_bytes_per_call"):
     """HBM bytes per draft-head call (or, with key
     traffic_bytes_per_projection, per k_proj_mfma launch) from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy
-    calibration), or None when there is none for this workload and mode or
-    the kernel sources changed since the counters were taken."""
+    calibration), or None when there is none for this workload and mode, the
+    kernel sources changed since the counters were taken, or the summary's
+    mean |I| is more than 5% away from this run's (the bytes scale with it)."""
     path = os.path.join(ROOT, "profiles", f"draft_head_{workload}_traffic.txt")
     try:
         with open(path) as f:
@@ -458,6 +475,8 @@ def measured_traffic(workload, mode, key="traffic_bytes_per_call"):
     if kv.get("source_sha256") != kernel_source_hash() or kv.get("mode") != mode:
         return None
     try:
+        if abs(float(kv["mean_active"]) - mean_active) > 0.05 * mean_active:
+            return None
         return float(kv[key])
     except (KeyError, ValueError):
         return None
