@@ -614,16 +614,18 @@ ns_state_view make_view(char* p, int32_t V, int32_t w_max) {
   return v;
 }
 
-// Raises the dynamic-LDS limits of the state kernels for this V / W_max.
-int prepare_kernels(int32_t V, int32_t w_max) {
-  int rc = set_lds_limit((const void*)k_active, lds_bitmap_bytes(V));
-  if (rc == NS_OK) rc = set_lds_limit((const void*)k_step, lds_bitmap_bytes(V));
-  const size_t fast_max = fast_lds_bytes(V, w_max, kFastMaxIds);
-  const size_t lim = fast_max < kFastLdsMax ? fast_max : kFastLdsMax;
+// Sets the dynamic-LDS limits of the state kernels that a state of this
+// W_max launches.  The limits are the largest any state may ask for (the
+// bitmap of NS_MAX_V ids, kFastLdsMax), not this state's own needs: the
+// attribute belongs to the kernel, so a state created later with a smaller V
+// must not lower it below what an earlier state still launches with.
+int prepare_kernels(int32_t /*V*/, int32_t w_max) {
+  int rc = set_lds_limit((const void*)k_active, lds_bitmap_bytes(NS_MAX_V));
+  if (rc == NS_OK) rc = set_lds_limit((const void*)k_step, lds_bitmap_bytes(NS_MAX_V));
   step_fast_fn fast_fn = pick_step_fast(w_max);
-  if (rc == NS_OK && fast_fn) rc = set_lds_limit((const void*)fast_fn, lim);
+  if (rc == NS_OK && fast_fn) rc = set_lds_limit((const void*)fast_fn, kFastLdsMax);
   step_fast_batch_fn batch_fn = pick_step_fast_batch(w_max);
-  if (rc == NS_OK && batch_fn) rc = set_lds_limit((const void*)batch_fn, lim);
+  if (rc == NS_OK && batch_fn) rc = set_lds_limit((const void*)batch_fn, kFastLdsMax);
   return rc;
 }
 

@@ -238,6 +238,31 @@ def test_state_edges(ns):
         check_state(g1, s1, V, "w_max=1")
 
 
+def test_state_lds_limit_kept_for_earlier_state(ns):
+    """A state whose step kernel needs more dynamic LDS (large V at W_max =
+    16384) still steps after a state with a smaller V and the same W_max is
+    created: creating a state must not lower a kernel's LDS limit below what
+    an earlier state launches with."""
+    say("LDS limit: large-V state stepped after a smaller-V state is created")
+    rng = np.random.default_rng(77)
+    big = GpuSeq(ns, 151936, 16384)
+    seq = O.Sequence_(16384)
+    prompt = rng.integers(0, 151936, size=16384)
+    big.append(prompt, 0)
+    seq.append_prompt(prompt)
+    small = GpuSeq(ns, 128256, 16384)              # created second, smaller V
+    for t in range(3):
+        tree = rng.integers(0, 151936, size=60)
+        ver = rng.choice(151936, size=8, replace=False)
+        big.step(tree, ver)
+        seq.step(tree, ver)
+        check_state(big, seq, 151936, f"large-V state step {t}")
+    small.step([1, 2, 3], [4])
+    s2 = O.Sequence_(16384)
+    s2.step([1, 2, 3], [4])
+    check_state(small, s2, 128256, "small-V state")
+
+
 def test_step_update_paths(ns):
     """nanospec_step_update on both kernels: tuples of up to 512 ids take the
     one-round-trip LDS path, longer ones the general path; w_max not a
