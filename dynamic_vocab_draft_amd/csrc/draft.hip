@@ -41,6 +41,8 @@
 //       k from the chunks' keys, unless every live column is in chunk 0,
 //       which then writes the result itself.  No k rounds of cross-lane
 //       reductions.
+#include <mutex>
+
 #include "common.hpp"
 #include "select.hpp"
 
@@ -1325,6 +1327,57 @@ int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* r
                                 float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream) {
   return draft_call(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
                     ws_bytes, stream, true, parent, lse);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free draft head: the workspace (partial sums, chunk keys) is a
+// fixed device array of the library instead of a caller buffer.  Each GPU the
+// library runs on holds its own copy until the process ends; its address on a
+// device is resolved once, on the first call with that device current, and
+// kept.  The kernels then receive that address exactly as they receive a
+// caller's workspace (the array's name is only a host-side stand-in).
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[NS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (NS_OK), or an error.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NS_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return NS_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NS_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nanospec_draft_logits_topk_noalloc(const void* rows, int32_t mode, const int32_t* row_ids, const int32_t* n_dev,
+                                       int32_t n_max, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
+                                       int32_t k, float* logits, int32_t* topk_ids, float* topk_vals,
+                                       hipStream_t stream) {
+  const size_t need = nanospec_draft_workspace_bytes(n_max, M, k, d);
+  if (need == 0) return NS_EINVAL;
+  if (need > (size_t)NS_NOALLOC_SCRATCH_BYTES) return NS_ESCRATCH;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != NS_OK) return rc;
+  return draft_call(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
+                    (size_t)NS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -579,6 +579,7 @@ const char* nanospec_strerror(int code) {
     case NS_EDTYPE: return "unknown dtype or mode";
     case NS_ECAPACITY: return "buffer too small";
     case NS_EHIP: return "HIP launch or runtime error";
+    case NS_ESCRATCH: return "request larger than the fixed scratch of the allocation-free draft head";
     default: return "unknown error code";
   }
 }

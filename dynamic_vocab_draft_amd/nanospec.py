@@ -21,7 +21,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnanospec.so")
 
-NS_OK, NS_EINVAL, NS_EDTYPE, NS_ECAPACITY, NS_EHIP = 0, 1, 2, 3, 4
+NS_OK, NS_EINVAL, NS_EDTYPE, NS_ECAPACITY, NS_EHIP, NS_ESCRATCH = 0, 1, 2, 3, 4, 5
+NS_NOALLOC_SCRATCH_BYTES = 8 << 20
 NS_BF16, NS_FP32, NS_FP16 = 0, 1, 2
 NS_PACKED, NS_INDEXED = 0, 1
 NS_STATUS_BAD_ID = 0x1
@@ -82,6 +83,8 @@ _SIGS = {
     "nanospec_draft_workspace_bytes": (c_size, [c_int32, c_int32, c_int32, c_int32]),
     "nanospec_draft_logits_topk": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32,
                                                   c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "nanospec_draft_logits_topk_noalloc": (ctypes.c_int, [c_vp, c_int32, c_vp, c_vp, c_int32, c_int32, c_int32,
+                                                          c_int32, c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_vp]),
     "nanospec_prefill_topk": (ctypes.c_int, [c_vp, c_int32, c_int32, c_int32, c_int32, c_vp, c_vp, c_vp]),
     "nanospec_batch_state_bytes": (c_size, [c_int32, c_int32, c_int32]),
     "nanospec_batch_create": (ctypes.c_int, [ctypes.POINTER(c_vp), c_int32, c_int32, c_int32, c_vp, c_size, c_vp]),
@@ -251,6 +254,15 @@ def nanospec_draft_logits_topk(rows: torch.Tensor, mode: int, row_ids: Optional[
                                            _ptr(h), M, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_vals),
                                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "nanospec_draft_logits_topk")
+
+
+def nanospec_draft_logits_topk_noalloc(rows: torch.Tensor, mode: int, row_ids: Optional[torch.Tensor],
+                                       n_dev: Optional[torch.Tensor], n_max: int, V: int, d: int, dtype: int,
+                                       h: torch.Tensor, M: int, k: int, logits: Optional[torch.Tensor],
+                                       topk_ids: torch.Tensor, topk_vals: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_draft_logits_topk_noalloc(_ptr(rows), mode, _ptr(row_ids), _ptr(n_dev), n_max, V, d, dtype,
+                                                   _ptr(h), M, k, _ptr(logits), _ptr(topk_ids), _ptr(topk_vals),
+                                                   _stream(stream)), "nanospec_draft_logits_topk_noalloc")
 
 
 def nanospec_draft_logprob_topk(rows: torch.Tensor, mode: int, row_ids: Optional[torch.Tensor],

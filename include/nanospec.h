@@ -54,6 +54,7 @@ extern "C" {
 #define NS_EDTYPE    2   /* unknown dtype or mode */
 #define NS_ECAPACITY 3   /* state or workspace buffer too small */
 #define NS_EHIP      4   /* a HIP launch or runtime call failed */
+#define NS_ESCRATCH  5   /* larger than the fixed scratch of nanospec_draft_logits_topk_noalloc */
 
 /* ---- element types of W_head, h and logits ---------------------------- */
 #define NS_BF16 0        /* bfloat16, stored as 16-bit patterns */
@@ -332,6 +333,29 @@ int nanospec_draft_select(const int32_t* row_ids, const int32_t* n_dev, int32_t 
                           int32_t V, int32_t d, int32_t dtype, int32_t M, int32_t k,
                           float* logits, int32_t* topk_ids, float* topk_vals, void* ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/* Allocation-free variant of nanospec_draft_logits_topk, for callers that
+ * cannot allocate device memory around the call (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, rules and results as nanospec_draft_logits_topk, without the
+ * workspace: the kernels use a fixed device array of the library of
+ * NS_NOALLOC_SCRATCH_BYTES (8 MiB), one copy per GPU, held until the process
+ * ends.  The first call on a device (which must be the current device, the
+ * device of `stream`) resolves that array's address with hipGetSymbolAddress
+ * and keeps it; no call allocates or frees memory.  Every call on one GPU
+ * shares the array, and it needs no initialisation; calls that may overlap
+ * on one GPU (different streams without ordering between them) race on it
+ * and must be ordered by the caller.
+ * Errors: as nanospec_draft_logits_topk (but never NS_ECAPACITY), plus
+ * NS_ESCRATCH when nanospec_draft_workspace_bytes(n_max, M, k, d) exceeds
+ * NS_NOALLOC_SCRATCH_BYTES (nothing is enqueued): e.g. n_max = 3072 fits
+ * every M <= 64 at d = 4096, n_max = 16384 fits M <= 16 only. */
+#define NS_NOALLOC_SCRATCH_BYTES (8u << 20)
+int nanospec_draft_logits_topk_noalloc(const void* rows, int32_t mode, const int32_t* row_ids,
+                                       const int32_t* n_dev, int32_t n_max, int32_t V,
+                                       int32_t d, int32_t dtype, const void* h, int32_t M,
+                                       int32_t k, float* logits, int32_t* topk_ids,
+                                       float* topk_vals, hipStream_t stream);
 
 /* ======================================================================
  * The draft head for a batch of B independent sequences sharing W_head, in

@@ -155,3 +155,20 @@ def test_host_validation_rejects_before_launch(ns):
     assert L.nanospec_prefill_topk(fake, 4, 10, 9, 2, fake, fake, None) == ns.NS_EDTYPE
     assert L.nanospec_prefill_topk(None, 4, 10, 0, 2, fake, fake, None) == ns.NS_EINVAL
     assert L.nanospec_prefill_topk(None, 0, 10, 0, 2, fake, fake, None) == ns.NS_OK   # L = 0: nothing to do
+
+
+def test_noalloc_rejects_oversize_before_launch(ns):
+    """The allocation-free draft head refuses a workspace need above its fixed
+    scratch (NS_ESCRATCH) and bad dimensions (NS_EINVAL) before any HIP call."""
+    L = ns._lib
+    fake = ctypes.c_void_p(0x1000)
+    need = L.nanospec_draft_workspace_bytes(16384, 64, 16, 4096)
+    assert need > ns.NS_NOALLOC_SCRATCH_BYTES
+    assert L.nanospec_draft_logits_topk_noalloc(fake, ns.NS_INDEXED, fake, fake, 16384, 151936, 4096, ns.NS_BF16,
+                                                fake, 64, 16, None, fake, fake, None) == ns.NS_ESCRATCH
+    assert L.nanospec_draft_logits_topk_noalloc(fake, ns.NS_INDEXED, fake, fake, 3072, 128256, 4096, ns.NS_BF16,
+                                                fake, 65, 8, None, fake, fake, None) == ns.NS_EINVAL
+    # the workloads the header names as fitting do fit
+    for n_max, M, k in ((3072, 64, 16), (3072, 8, 8), (16384, 16, 16)):
+        assert L.nanospec_draft_workspace_bytes(n_max, M, k, 4096) <= ns.NS_NOALLOC_SCRATCH_BYTES
+    assert L.nanospec_strerror(ns.NS_ESCRATCH) != b"unknown error code"
