@@ -221,16 +221,21 @@ __global__ __launch_bounds__(kProjThreads) void k_proj_valu(const uint4* __restr
 // same route, aliased to row M - 1 past M, except with two hidden tiles
 // (17 <= M <= 32), which load them into registers.
 //
-// Buffers are per wave and double-buffered: the next batch is requested
-// before the current one is read, and the wait is an explicit vmcnt of one
-// batch's load count.  The LDS reads are inline-asm ds_read_b128 followed by
-// an explicit lgkmcnt(0): the compiler would otherwise wait for every load
-// still in flight (it cannot tell the two buffers' loads apart across the
-// loop).  Hidden rows loaded into registers get such a full wait from the
-// compiler before their first use in every other batch; through LDS they
-// also arrive as whole 128-byte runs instead of half lines, which measured
-// faster from three hidden tiles up (M = 60: 13.2 -> 12.3 us per call) and
-// slower with two.  No block barrier until the four waves' tiles are summed.
+// Buffers are per wave, NB of them: the wave's first NB batches are
+// requested at once and batch b + NB refills batch b's buffers once b is
+// multiplied; the waits are explicit vmcnts counting the batches still in
+// flight.  With one hidden tile NB = 4, which puts a wave's whole range in
+// flight for d = 4096 over four slices (8 KiB of rows instead of two 2 KiB
+// batches at a time: 5.12 -> 4.84 us per projection at 1000 live rows of the
+// Llama-shaped head, same box, bit-identical results), and the hidden rows
+// past M are not fetched at all.  The LDS reads are inline-asm ds_read_b128
+// followed by an explicit lgkmcnt(0): the compiler would otherwise wait for
+// every load still in flight (it cannot tell the buffers' loads apart across
+// the loop).  Hidden rows loaded into registers get such a full wait from the
+// compiler before their first use; through LDS they also arrive as whole
+// 128-byte runs instead of half lines, which measured faster from three
+// hidden tiles up (M = 60: 13.2 -> 12.3 us per call) and slower with two.
+// No block barrier until the four waves' tiles are summed.
 // ---------------------------------------------------------------------------
 constexpr int kDmaKC = 2;                          // k-steps per batch (128-byte row runs)
 
@@ -255,7 +260,21 @@ __device__ __forceinline__ void dma16(const uint4* src, uint4* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-template <int NMT, int RT, bool F16>
+// vmcnt immediate (gfx9 encoding, expcnt and lgkmcnt left at their maxima).
+__host__ __device__ constexpr int vm_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+// Waits until at most `left` (< NB) batches of L vector loads each are still
+// outstanding: loads complete in issue order, so the oldest batch has landed.
+template <int L, int NB>
+__device__ __forceinline__ void wait_batches(int left) {
+  static_assert(NB >= 1 && NB <= 4 && (NB - 1) * L < 64, "vmcnt range");
+  if (NB > 3 && left >= 3) __builtin_amdgcn_s_waitcnt(vm_imm(NB > 3 ? 3 * L : 0));
+  else if (NB > 2 && left == 2) __builtin_amdgcn_s_waitcnt(vm_imm(NB > 2 ? 2 * L : 0));
+  else if (NB > 1 && left == 1) __builtin_amdgcn_s_waitcnt(vm_imm(L));
+  else __builtin_amdgcn_s_waitcnt(vm_imm(0));
+}
+
+template <int NMT, int RT, bool F16, int HI, int NB>
 __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict__ rows, int mode,
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
@@ -271,15 +290,17 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // hidden tiles (17 <= M <= 32), where loads into registers measured faster
   // (the LDS copy would cost a block per CU).
   constexpr bool HDMA = NMT != 2;
-  __shared__ uint4 abuf0[kPW][RT * TB];
-  __shared__ uint4 abuf1[kPW][RT * TB];
-  __shared__ uint4 bbuf0[kPW][HDMA ? NMT * TB : 1];
-  __shared__ uint4 bbuf1[kPW][HDMA ? NMT * TB : 1];
-  // The wave tiles of the final sum reuse a staging buffer (RT NMT 4 KiB:
-  // within abuf0 for NMT <= 2, within bbuf0 otherwise, as RT <= 2).
-  static_assert(sizeof(f32x4_t) * kPW * RT * NMT * NS_WAVE <= (NMT <= 2 ? sizeof(abuf0) : sizeof(bbuf0)),
+  // Through LDS, HI load instructions per batch fetch the hidden rows: rows
+  // past M are not fetched when HI < NMT NI (their operand lanes are zeroed).
+  static_assert(!HDMA || (HI >= 1 && HI <= NMT * NI), "hidden-row loads per batch");
+  // NB batch buffers per wave: up to NB batches of one wave are in flight.
+  __shared__ uint4 abuf[NB][kPW][RT * TB];
+  __shared__ uint4 bbuf[NB][kPW][HDMA ? NMT * TB : 1];
+  // The wave tiles of the final sum reuse the staging buffers (RT NMT 4 KiB:
+  // within abuf for NMT <= 2, within bbuf otherwise, as RT <= 2).
+  static_assert(sizeof(f32x4_t) * kPW * RT * NMT * NS_WAVE <= (NMT <= 2 ? sizeof(abuf) : sizeof(bbuf)),
                 "wave tiles fit the reused buffer");
-  auto red = reinterpret_cast<f32x4_t (*)[RT][NMT][NS_WAVE]>(NMT <= 2 ? &abuf0[0][0] : &bbuf0[0][0]);
+  auto red = reinterpret_cast<f32x4_t (*)[RT][NMT][NS_WAVE]>(NMT <= 2 ? &abuf[0][0][0] : &bbuf[0][0][0]);
   // The 1-D grid is read as (tile group, sequence, slice, XCD lane), tile
   // group slowest: L = ((tg B + b) S + s) 8 + x.  Row tile tg 8 + x of
   // sequence b and slice s.  Dispatch then runs over the low (live) tiles of
@@ -360,21 +381,22 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // Hidden-row sources: by load instruction for the LDS route (lanes laid out
   // as for the rows, rows past M alias row M - 1), by MFMA lane otherwise
   // (padded lanes alias a real row).  Padded rows are zeroed as operands.
-  const uint4* hsrc[HDMA ? NMT : 1][NI];
+  const uint4* hsrc[HDMA ? HI : 1];
   const uint4* hrow[HDMA ? 1 : NMT];
   bool m_ok[NMT];
 #pragma unroll
   for (int t = 0; t < NMT; ++t) {
     m_ok[t] = t * 16 + i < M;
-    if constexpr (HDMA) {
-#pragma unroll
-      for (int q = 0; q < NI; ++q) {
-        const int m = t * 16 + q * RPI + rsub;
-        hsrc[t][q] = h + (size_t)(m < M ? m : M - 1) * dv;
-      }
-    } else {
+    if constexpr (!HDMA) {
       const int m = t * 16 + i;
       hrow[t] = h + (size_t)(m < M ? m : m % M) * dv;
+    }
+  }
+  if constexpr (HDMA) {
+#pragma unroll
+    for (int hq = 0; hq < HI; ++hq) {                   // instruction hq: tile hq / NI, rows (hq % NI) RPI ..
+      const int m = (hq / NI) * 16 + (hq % NI) * RPI + rsub;
+      hsrc[hq] = h + (size_t)(m < M ? m : M - 1) * dv;
     }
   }
   // This wave's 32-column steps: the split's range, divided among the waves.
@@ -393,7 +415,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   const uint4 z = make_uint4(0, 0, 0, 0);
   const int swz_i = i & (CPR - 1);
 
-  // Requests batch s0 into one buffer pair.  Chunks past the wave's range
+  // Requests batch s0 into one set of buffers.  Chunks past the wave's range
   // or past d load column 0 of the same row (their products are zeroed).
   constexpr int HB = HDMA ? NMT * TB : 1;
   auto issue = [&](int s0, uint4 (&ab)[kPW][RT * TB], uint4 (&bb)[kPW][HB], uint4 (&bq)[KC][HDMA ? 1 : NMT]) {
@@ -404,9 +426,13 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       const int cc = (c < s_end * 4 && c < dv) ? c : 0;
 #pragma unroll
       for (int r = 0; r < RT; ++r) dma16(asrc[r][q] + cc, &ab[w][r * TB + q * NS_WAVE]);
-      if constexpr (HDMA) {
+    }
+    if constexpr (HDMA) {
 #pragma unroll
-        for (int t = 0; t < NMT; ++t) dma16(hsrc[t][q] + cc, &bb[w][t * TB + q * NS_WAVE]);
+      for (int hq = 0; hq < HI; ++hq) {
+        const int c = s0 * 4 + apos[hq % NI];
+        const int cc = (c < s_end * 4 && c < dv) ? c : 0;
+        dma16(hsrc[hq] + cc, &bb[w][(hq / NI) * TB + (hq % NI) * NS_WAVE]);
       }
     }
     if constexpr (!HDMA) {
@@ -465,34 +491,32 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       }
     }
   };
-  // vmcnt immediate (gfx9 encoding, expcnt and lgkmcnt left at their maxima)
-  // that waits until at most one batch's loads are outstanding.
-  constexpr int NLOADS = NI * RT + (HDMA ? NI * NMT : KC * NMT);
-  static_assert(NLOADS < 64, "vmcnt range");
-  constexpr int kWaitOneBatch = (NLOADS & 0xF) | (0x7 << 4) | (0xF << 8) | ((NLOADS >> 4) << 14);
-  constexpr int kWaitAll = 0x0F70;
-  uint4 b0[KC][HDMA ? 1 : NMT], b1[KC][HDMA ? 1 : NMT];
-  if (s_begin < s_end) {                                // wave-uniform
-    issue(s_begin, abuf0, bbuf0, b0);
+  // Loads per batch (vmcnt units), and the wave's batches.  The first NB
+  // batches are requested at once (for d = 4096 over four slices that is the
+  // wave's whole range, 8 KiB of rows); batch b + NB reuses batch b's buffers
+  // as soon as b is multiplied.  The loop over buffers is unrolled, so every
+  // buffer (and every register copy of hidden rows) has a fixed index.
+  constexpr int NLOADS = NI * RT + (HDMA ? HI : KC * NMT);
+  uint4 bq[NB][KC][HDMA ? 1 : NMT];
+  const int nb = s_begin < s_end ? (s_end - s_begin + KC - 1) / KC : 0;   // wave-uniform
+  if (nb > 0) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (u < nb) issue(s_begin + u * KC, abuf[u], bbuf[u], bq[u]);
     NS_ISSUE_FENCE();
-    for (int s0 = s_begin; s0 < s_end; s0 += 2 * KC) {
-      if (s0 + KC < s_end) {
-        issue(s0 + KC, abuf1, bbuf1, b1);
-        NS_ISSUE_FENCE();
-        __builtin_amdgcn_s_waitcnt(kWaitOneBatch);
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitAll);
+    for (int b0 = 0; b0 < nb; b0 += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int b = b0 + u;
+        if (b < nb) {
+          wait_batches<NLOADS, NB>(min(nb - b - 1, NB - 1));
+          compute(s_begin + b * KC, abuf[u], bbuf[u], bq[u]);
+          if (b + NB < nb) {
+            issue(s_begin + (b + NB) * KC, abuf[u], bbuf[u], bq[u]);
+            NS_ISSUE_FENCE();
+          }
+        }
       }
-      compute(s0, abuf0, bbuf0, b0);
-      if (s0 + KC >= s_end) break;
-      if (s0 + 2 * KC < s_end) {
-        issue(s0 + 2 * KC, abuf0, bbuf0, b0);
-        NS_ISSUE_FENCE();
-        __builtin_amdgcn_s_waitcnt(kWaitOneBatch);
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitAll);
-      }
-      compute(s0 + KC, abuf1, bbuf1, b1);
     }
   }
   __syncthreads();                                      // every wave is done with the buffer red reuses
@@ -1029,12 +1053,13 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   return ns_launch_status();
 }
 
-template <int NMT, int RT, bool F16>
+template <int NMT, int RT, bool F16, int HI, int NB>
 void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
                    float* part, const BatchStrides& bs) {
-  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows, mode,
-                     row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, part, bs, B);
+  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB>), dim3(blocks), dim3(kPThreads), 0, stream,
+                     (const uint4*)rows, mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, part, bs,
+                     B);
 }
 
 template <bool F16>
@@ -1061,18 +1086,25 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
     per_seq = trimmed < per_seq ? trimmed : per_seq;
   }
   const unsigned blocks = per_seq * (unsigned)B;
-#define NS_LAUNCH_MFMA(NMTV, RTV) \
-  launch_mfma_t<NMTV, RTV, F16>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, part, bs)
+#define NS_LAUNCH_MFMA(NMTV, RTV, HIV, NBV)                                                                     \
+  launch_mfma_t<NMTV, RTV, F16, HIV, NBV>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, \
+                                          part, bs)
   if (rt == kMsplitRT) {
     hipLaunchKernelGGL((k_proj_msplit<kMsplitRT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows,
                        mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, part, bs, B);
     return ns_launch_status();
   }
+  // One hidden tile: four batch buffers per wave (64 KiB of LDS per block),
+  // and only the hidden rows that exist are fetched (one load instruction per
+  // batch covers eight rows).  More tiles keep two buffers (LDS).
   switch ((M + 15) / 16) {
-    case 1: NS_LAUNCH_MFMA(1, 1); break;
-    case 2: NS_LAUNCH_MFMA(2, 2); break;
-    case 3: NS_LAUNCH_MFMA(3, 2); break;
-    default: NS_LAUNCH_MFMA(4, 2); break;
+    case 1:
+      if (M <= 8) NS_LAUNCH_MFMA(1, 1, 1, 4);
+      else NS_LAUNCH_MFMA(1, 1, 2, 4);
+      break;
+    case 2: NS_LAUNCH_MFMA(2, 2, 1, 2); break;
+    case 3: NS_LAUNCH_MFMA(3, 2, 6, 2); break;
+    default: NS_LAUNCH_MFMA(4, 2, 8, 2); break;
   }
 #undef NS_LAUNCH_MFMA
   return ns_launch_status();
