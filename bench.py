@@ -396,6 +396,9 @@ def main():
         for name in ("qwen25_7b", "stress"):
             progress(f"{name} leg")
             out[name] = config_leg(torch, ns, WL, flush_fn, name)
+    # The launch floor of the step's chain: the same cold protocol with three
+    # dependent launches that do nothing but touch one element each.
+    out["dispatch_floor"] = dispatch_floor(torch, lambda i: sink.copy_(flush_lines[:, i % 128]), K, args.reps)
     if not args.no_dense:
         out["dense"] = dense_compare(torch, ns, cfg, W, hs[t0], dcode, lambda i: sink.copy_(flush_lines[:, i % 128]), ms)
     if not args.no_cpu_baseline:
@@ -1112,6 +1115,46 @@ def sweep(torch, ns, WL, args):
                               "GBps": nbytes / (us * 1e-6) / 1e9,
                               "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}), flush=True)
             del g_all, g_fl
+
+
+def dispatch_floor(torch, flush, K, reps):
+    """Graph-replayed chains of three dependent launches that each add 1 to a
+    one-element tensor, after the same cache-streaming read as the timed
+    steps: the time a three-launch step costs when its kernels do no work.
+    Returns microseconds per chain and per launch (the read's graph is
+    subtracted)."""
+    x = torch.zeros(1, device="cuda")
+
+    def chain(with_launches):
+        def run():
+            for t in range(K):
+                flush(t * 7)
+                if with_launches:
+                    for _ in range(3):
+                        x.add_(1.0)
+        return run
+
+    def graph_time(fn):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        ts = []
+        for _ in range(max(reps, 5)):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_chain = graph_time(chain(True))
+    t_read = graph_time(chain(False))
+    per_chain = (t_chain - t_read) / K * 1e3
+    return {"what": "three dependent one-element launches after the cache-streaming read, graph replay",
+            "us_per_chain": per_chain, "us_per_launch": per_chain / 3}
 
 
 def dense_compare(torch, ns, cfg, W, h, dcode, flush, step_ms):
