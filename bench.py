@@ -1203,55 +1203,49 @@ def _cpu_model():
     return "unknown"
 
 
-def _oracle_steps(cfg, W, seconds, script, hs):
-    """Decode steps of the oracle as written in about `seconds`."""
-    import oracle.nanospec_oracle as O
+def _oracle_steps(C, cfg, W, seconds, script, hs, threads):
+    """Decode steps of the C++ oracle in about `seconds`: stream update,
+    window, sorted unique, float64 projection of W[I, :] (the gather is the
+    row reads) and top-k.  Returns (steps, passes, seconds, threads that ran)."""
     done = passes = 0
+    used = 1
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        seq = O.Sequence_(cfg.w_max)
+        seq = C.Sequence(cfg.w_max)
         seq.append_prompt(script.prompt)
         for t in range(cfg.steps):
             seq.step(script.tree[t], script.ver[t])
             I = seq.active()
-            O.draft_head(hs[t], W, I, cfg.k, cfg.dtype)
+            logits, used = C.project(hs[t], W, I, cfg.dtype, threads=threads)
+            C.topk(logits, I, cfg.k)
             done += 1
             if time.perf_counter() - t0 >= seconds:
                 break
         passes += 1
-    return done, passes, time.perf_counter() - t0
+    return done, passes, time.perf_counter() - t0, used
 
 
 def cpu_baseline(cfg, W, seconds):
-    """The CPU oracle as written (numpy, float64) on a bounded sample of the
-    same workload: as many decode steps as fit in about `seconds` with the
-    BLAS pool on every host core, then a shorter sample on one thread, and
-    the full-vocabulary float64 head once (context for the dense
-    comparison)."""
-    import oracle.nanospec_oracle as O
+    """The C++ oracle (oracle/nanospec_oracle.cpp, float64, OpenMP over the
+    projection's (m, j) pairs) on a bounded sample of the same workload: as
+    many decode steps as fit in about `seconds` on every host core the
+    OpenMP runtime is given, then a shorter sample on one thread, and the
+    full-vocabulary float64 head once (context for the dense comparison)."""
+    import oracle.nanospec_oracle_cpp as C
     from dynamic_vocab_draft_amd import workloads as WL
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        used = max((int(i.get("num_threads", 1)) for i in threadpool_info()), default=1)
-    except ImportError:  # pragma: no cover
-        threadpool_limits, used = None, 1
     script = WL.make_id_script(cfg)
     hs = [WL.make_hidden(cfg, t) for t in range(cfg.steps)]
-    done, passes, el = _oracle_steps(cfg, W, seconds, script, hs)
-    one = None
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=1):
-            d1, _, e1 = _oracle_steps(cfg, W, seconds / 3, script, hs)
-        one = d1 / e1
+    done, passes, el, used = _oracle_steps(C, cfg, W, seconds, script, hs, threads=0)
+    d1, _, e1, _ = _oracle_steps(C, cfg, W, seconds / 3, script, hs, threads=1)
     t0 = time.perf_counter()
-    O.dense_logits(hs[0], W, cfg.dtype)
+    C.project(hs[0], W, np.arange(cfg.V), cfg.dtype, threads=0)
     dense_s = time.perf_counter() - t0
     return {"value": done / el, "unit": "steps/s", "cores": int(used), "kind": "oracle",
             "sample": f"{done} decode steps of {cfg.name} ({passes} pass(es) over its {cfg.steps} steps: stream "
-                      f"update, window, unique, gather, fp64 projection, top-k) in {el:.1f} s; BLAS threads {used}, "
-                      f"host has {os.cpu_count()} logical CPUs",
-            "single_thread_steps_per_s": one, "cpu_model": _cpu_model(),
-            "dense_f64_head_s": dense_s}
+                      f"update, window, sorted unique, fp64 projection of W[I, :], top-k) in {el:.1f} s by the C++ "
+                      f"oracle on {used} OpenMP threads; host has {os.cpu_count()} logical CPUs",
+            "single_thread_steps_per_s": d1 / e1, "cpu_model": _cpu_model(),
+            "dense_f64_head_s": dense_s, "dense_f64_head_threads": int(used)}
 
 
 if __name__ == "__main__":
