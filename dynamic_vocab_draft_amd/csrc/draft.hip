@@ -73,6 +73,8 @@ constexpr int kKC = 4;                            // 32-column steps per wave an
 constexpr int kTargetBlocks = 768;                // MFMA blocks aimed for when choosing S
 constexpr int kMaxSplits = 16;
 constexpr int kLiveRowsHint = 3072;               // live rows assumed when sizing S without n
+constexpr int kBatchLiveRowsHint = 1024;          // rows per sequence a batched launch covers per pass, at most
+constexpr int kBatchTargetBlocks = 1024;          // blocks a batched launch aims for
 
 
 // Per-sequence element strides of a batched call (sequence b = blockIdx.z in
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
                                                          int S, int adapt, float* __restrict__ part,
-                                                         BatchStrides bs, int B) {
+                                                         BatchStrides bs, int B, int tile_step) {
   constexpr int KC = kDmaKC;
   constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
   constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction
@@ -353,6 +355,10 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       }
     }
   }
+  // With tile_step > 0 (batches launched for fewer tiles per sequence than
+  // n_max holds) the block then takes the tiles tile_step rows further on
+  // for as long as they hold live rows.
+  for (;;) {
   if (r0 >= n) return;                                  // block-uniform: nothing live here
   bool ok[RT];
 #pragma unroll
@@ -499,6 +505,17 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   constexpr int NLOADS = NI * RT + (HDMA ? HI : KC * NMT);
   uint4 bq[NB][KC][HDMA ? 1 : NMT];
   const int nb = s_begin < s_end ? (s_end - s_begin + KC - 1) / KC : 0;   // wave-uniform
+  // The row ids of this block's next tile (tile_step > 0) are requested
+  // before this tile's rows, so they land while the rows stream (loads
+  // complete in issue order, so the batch waits below cover them).
+  int gid_next[RT];
+  if (tile_step > 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = r0 + tile_step + r * kTile + i;
+      gid_next[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+    }
+  }
   if (nb > 0) {
 #pragma unroll
     for (int u = 0; u < NB; ++u)
@@ -540,6 +557,13 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
     const int m = t * 16 + (l2 & 15);
     const int q0 = r0 + r * kTile + (l2 >> 4) * 4;
     if (m < M && q0 < n_max) *(f32x4_t*)(part + ((size_t)split * M + m) * NP + q0) = sum;
+  }
+  if (tile_step == 0) return;                           // launch-uniform
+  r0 += tile_step;
+  if (r0 >= n) return;                                  // block-uniform
+  __syncthreads();                                      // red is read before the buffers it aliases refill
+#pragma unroll
+  for (int r = 0; r < RT; ++r) gid[r] = gid_next[r];
   }
 }
 
@@ -1056,10 +1080,10 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 template <int NMT, int RT, bool F16, int HI, int NB>
 void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
-                   float* part, const BatchStrides& bs) {
+                   float* part, const BatchStrides& bs, int tile_step) {
   hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB>), dim3(blocks), dim3(kPThreads), 0, stream,
                      (const uint4*)rows, mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, part, bs,
-                     B);
+                     B, tile_step);
 }
 
 template <bool F16>
@@ -1067,7 +1091,22 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
                 const void* h, int M, int S, int adapt, float* part, int B, const BatchStrides& bs,
                 hipStream_t stream) {
   const int dv = d / 8;
-  const int rt = pick_rt(M, n_max, B);
+  const bool msplit = use_msplit(n_max, M, B);
+  // Batches of one slice per tile (below) with one hidden tile of at most 8
+  // rows take taller tiles as B grows (16 rt rows, rt the largest of 1, 2, 4
+  // that still gives about kBatchTargetBlocks blocks for kBatchLiveRowsHint
+  // rows per sequence) and a single batch buffer per wave: more blocks per
+  // CU (40 KiB of LDS at rt = 4, four blocks) and one hidden-row load per
+  // 4 rt row loads.  Measured on the Llama-shaped batch (mean |I| about
+  // 780): B = 64 0.56 -> 0.66 of HBM peak, B = 32 0.53 -> 0.59.
+  const bool batched = B > 1 && S == 1 && !adapt && !msplit;
+  int rt = pick_rt(M, n_max, B);
+  int nb_bufs = 4;
+  if (batched && M <= 8) {
+    const long per_rt1 = (long)B * (kBatchLiveRowsHint / kTile);
+    rt = per_rt1 >= 4L * kBatchTargetBlocks ? 4 : (per_rt1 >= 2L * kBatchTargetBlocks ? 2 : 1);
+    nb_bufs = rt > 1 ? 1 : 4;
+  }
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and
   // exit), times S slices, per sequence; one 1-D grid for all B sequences.
   // S > 1 only while tiles x B < kTargetBlocks, or with `adapt` (grid
@@ -1085,11 +1124,30 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
     const unsigned trimmed = (bound + group - 1) / group * group;
     per_seq = trimmed < per_seq ? trimmed : per_seq;
   }
+  // Batches of one slice per tile: launch the tiles of kBatchLiveRowsHint
+  // rows per sequence and let each block step on by that many rows while
+  // its sequence has live rows there.  Launching all of n_max's tiles left
+  // most blocks dead (about 850 live rows of 3072 per sequence in the
+  // Llama-shaped batch), and each dead block still took a slot for one
+  // round trip.
+  int tile_step = 0;
+  if (batched) {
+    // About kBatchTargetBlocks blocks in all, each taking every
+    // hint_tiles-th tile of its sequence: at large B a block streams several
+    // tiles, the next tile's row ids requested while the current rows stream.
+    unsigned hint_tiles = (unsigned)((kBatchLiveRowsHint + kTile * rt - 1) / (kTile * rt) + 7) / 8 * 8;
+    const unsigned fill = ((unsigned)kBatchTargetBlocks / (unsigned)B + 7) / 8 * 8;
+    hint_tiles = fill > 8 ? (fill < hint_tiles ? fill : hint_tiles) : 8;
+    if (hint_tiles < per_seq) {
+      per_seq = hint_tiles;
+      tile_step = (int)hint_tiles * kTile * rt;
+    }
+  }
   const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA(NMTV, RTV, HIV, NBV)                                                                     \
   launch_mfma_t<NMTV, RTV, F16, HIV, NBV>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, \
-                                          part, bs)
-  if (rt == kMsplitRT) {
+                                          part, bs, tile_step)
+  if (msplit) {
     hipLaunchKernelGGL((k_proj_msplit<kMsplitRT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows,
                        mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, part, bs, B);
     return ns_launch_status();
@@ -1099,8 +1157,14 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   // batch covers eight rows).  More tiles keep two buffers (LDS).
   switch ((M + 15) / 16) {
     case 1:
-      if (M <= 8) NS_LAUNCH_MFMA(1, 1, 1, 4);
-      else NS_LAUNCH_MFMA(1, 1, 2, 4);
+      if (M <= 8 && nb_bufs == 1) {
+        if (rt == 4) NS_LAUNCH_MFMA(1, 4, 1, 1);
+        else NS_LAUNCH_MFMA(1, 2, 1, 1);
+      } else if (M <= 8) {
+        NS_LAUNCH_MFMA(1, 1, 1, 4);
+      } else {
+        NS_LAUNCH_MFMA(1, 1, 2, 4);
+      }
       break;
     case 2: NS_LAUNCH_MFMA(2, 2, 1, 2); break;
     case 3: NS_LAUNCH_MFMA(3, 2, 6, 2); break;

@@ -219,3 +219,42 @@ def test_many_active_ids_staged(ns):
                 I = seqs[0].active()
                 assert len(I) > 4096, f"few active ids: {len(I)}"
                 assert int(n1.item()) == len(I) and np.array_equal(ids1[:len(I)].cpu().numpy(), I), "single-state ids"
+
+
+@pytest.mark.parametrize("M,dtype,B", [(8, "bf16", 6), (20, "bf16", 6), (16, "fp16", 6), (8, "bf16", 32),
+                                       (8, "fp16", 64), (8, "bf16", 64)])
+def test_batch_rows_beyond_one_pass(ns, M, dtype, B):
+    """A batched head launches the tiles of 1024 rows per sequence and steps
+    on by that much while rows are live (tiles of 16, 32 or 64 rows as B
+    grows, with M <= 8): sequences with 3072, 2500, 1025, 1024, 17, 0, 777,
+    64, 65 and 1 live rows of n_max = 3072, repeated up to B, each checked
+    against the oracle (logits to tolerance, top-k by the set rule)."""
+    say(f"batched head past one pass: M={M} {dtype} B={B}")
+    rng = np.random.default_rng(61 + M + B)
+    V, d, k, n_max = 50000, 512, 8, 3072
+    pattern = [3072, 2500, 1025, 1024, 17, 0, 777, 64, 65, 1]
+    counts = [pattern[b % len(pattern)] for b in range(B)]
+    W = WL.to_bits((rng.standard_normal((V, d)) * 0.02).astype(np.float32), dtype)
+    W_dev = dev_elems(W, dtype)
+    ids = np.full((B, n_max), -1, np.int32)
+    Is = []
+    for b, c in enumerate(counts):
+        I = np.sort(rng.choice(V, size=c, replace=False)).astype(np.int64)
+        ids[b, :c] = I
+        Is.append(I)
+    hs = [WL.to_bits(rng.standard_normal((M, d)).astype(np.float32), dtype) for _ in range(B)]
+    ws = ns.alloc_batch_workspace(B, n_max, M, k, d)
+    logits = torch.full((B, M, n_max), float("nan"), device="cuda")
+    tids = torch.empty((B, M, k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((B, M, k), device="cuda")
+    ns.nanospec_batch_draft_logits_topk(W_dev, dev_i32(ids.reshape(-1)), dev_i32(np.array(counts, np.int32)), n_max,
+                                        B, V, d, dcode_of(ns, dtype), dev_elems(np.stack(hs), dtype), M, k, logits,
+                                        tids, tvals, ws)
+    torch.cuda.synchronize()
+    lg, ti, tv = logits.cpu().numpy(), tids.cpu().numpy(), tvals.cpu().numpy()
+    for b in range(B):
+        ref, o_ids, o_vals = O.draft_head(hs[b], W, Is[b], k, dtype)
+        c = counts[b]
+        check_logits(lg[b][:, :c], ref, f"sequence {b} ({c} live)")
+        assert np.isnan(lg[b][:, c:]).all(), f"sequence {b}: columns past n written"
+        check_topk(ti[b], tv[b], ref, Is[b], o_ids, o_vals, k, f"sequence {b} ({c} live)")
