@@ -58,6 +58,19 @@ def parse():
                    help="only sweep the draft head over |I| x M (cold) and print one JSON line per point")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES (calibrates HBM byte counters) and exit")
+    p.add_argument("--overlap-study", action="store_true",
+                   help="only run the gather/backbone overlap variants (graph and eager, 13 and 1000 gathered "
+                        "rows), separated by host pauses so a kernel trace splits them, and exit")
+    p.add_argument("--trace-summary", default="", metavar="CSV",
+                   help="only summarize a rocprofv3 kernel-trace CSV of an --overlap-study run (no GPU) and exit")
+    p.add_argument("--step-trace-summary", default="", metavar="CSV",
+                   help="only summarize a rocprofv3 kernel-trace CSV of a bench run per decode-step kernel (no GPU) "
+                        "and exit")
+    p.add_argument("--counter-summary", nargs=5, default=None,
+                   metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "BENCH_OUT"),
+                   help="only write the draft-head traffic summary (no GPU) from FETCH_SIZE and WRITE_SIZE counter "
+                        "CSVs of an indexed bench run, the two counters of a --copy-probe run, and that bench run's "
+                        "output (its JSON line gives mean |I| and the algorithmic bytes), and exit")
     p.add_argument("--head-probe", default="", metavar="M[,M...]",
                    help="only run the full-vocabulary projection (V=151936, d=4096, bf16) three times for each "
                         "M, for hardware counters, and exit")
@@ -71,6 +84,15 @@ def main():
               f"path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.trace_summary:
+        print(overlap_trace_summary(args.trace_summary))
+        return
+    if args.step_trace_summary:
+        print(step_trace_summary(args.step_trace_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary, workload=args.config))
+        return
     import torch
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
@@ -84,6 +106,9 @@ def main():
         return
     if args.sweep:
         sweep(torch, ns, WL, args)
+        return
+    if args.overlap_study:
+        overlap_study(torch, ns, WL)
         return
     cfg = WL.get_config(args.config)
     K, Wm = args.steps, args.warmup
@@ -485,6 +510,152 @@ def measured_traffic(workload, mode, mean_active, key="traffic_bytes_per_call"):
         return None
 
 
+def _counter_rows(path):
+    """Per dispatch (in dispatch order): (kernel name, summed counter value)
+    of a rocprofv3 --pmc CSV holding one counter."""
+    import csv
+    by = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            if key in by:
+                by[key][1] += val
+            else:
+                by[key] = [name, val]
+    return [tuple(by[k]) for k in sorted(by)]
+
+
+def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_out, workload="llama3_8b"):
+    """The draft head's HBM traffic per call from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch) over the cold indexed steps of a bench run: dispatch
+    runs of cache-streaming read, k_step_fast, k_proj_mfma, k_merge_cols.
+    Each counter is scaled by what it reads for a plain device copy of known
+    size (the --copy-probe run).  Mean |I| and the algorithmic bytes come
+    from the bench run's JSON line.  Returns the summary text that
+    measured_traffic() reads."""
+    with open(bench_out) as f:
+        line = [l for l in f if l.startswith("{") and '"metric"' in l][-1]
+    b = json.loads(line)
+    mean_active = float(b["config"]["mean_active"])
+    alg_proj = float(b["roofline"]["bytes_per_launch"])
+    alg_call = float(b["roofline"]["draft_call"]["bytes"])
+    step_kernels = ("elementwise_kernel_manual_unroll", "k_step_fast", "k_proj_mfma", "k_merge_cols")
+    per = {}
+    steps = {}
+    for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        acc = {k: [] for k in step_kernels[1:]}
+        for i in range(len(rows) - 3):
+            if all(kernel_base_name(rows[i + j][0]) == step_kernels[j] for j in range(4)):
+                for j in range(1, 4):
+                    acc[step_kernels[j]].append(rows[i + j][1])
+        steps[tag] = len(acc["k_proj_mfma"])
+        if steps[tag] == 0:
+            raise SystemExit(f"{path}: no cold indexed step (read, k_step_fast, k_proj_mfma, k_merge_cols) found")
+        per[tag] = {k: float(np.mean(v)) for k, v in acc.items()}
+    cal = {}
+    for tag, path in (("FETCH_SIZE", copy_fetch_csv), ("WRITE_SIZE", copy_write_csv)):
+        rows = [v for n, v in _counter_rows(path) if "copyBuffer" in kernel_base_name(n)]
+        cal[tag] = rows
+    # The copy probe moves COPY_BYTES each way; the calibration is true KiB / counted KiB.
+    true_kib = COPY_PROBE_BYTES / 1024.0
+    f_cal = true_kib / float(np.median(cal["FETCH_SIZE"]))
+    w_cal = true_kib / float(np.median(cal["WRITE_SIZE"]))
+    kib = 1024.0
+    proj = (per["FETCH_SIZE"]["k_proj_mfma"] * f_cal + per["WRITE_SIZE"]["k_proj_mfma"] * w_cal) * kib
+    merge = (per["FETCH_SIZE"]["k_merge_cols"] * f_cal + per["WRITE_SIZE"]["k_merge_cols"] * w_cal) * kib
+    call = proj + merge
+    out = [
+        f"# HBM traffic of one draft-head call (k_proj_mfma + k_merge_cols), cold indexed steps of the",
+        f"# {workload} workload ({b['config']['workload']}; mean |I| = {mean_active:.2f} over the timed steps).",
+        f"# bench.py reads traffic_bytes_per_call from this file while source_sha256 matches its kernel sources",
+        f"# and its mean |I| is within 5% of this value.",
+        f"source_sha256: {kernel_source_hash()}",
+        f"mode: indexed",
+        f"mean_active: {mean_active:.2f}",
+        f"traffic_bytes_per_call: {call:.0f}",
+        f"algorithmic_bytes_per_call: {alg_call:.0f}",
+        f"traffic_bytes_per_projection: {proj:.0f}",
+        f"algorithmic_bytes_per_projection: {alg_proj:.0f}",
+        f"fetch_calibration: {f_cal:.4f}",
+        f"write_calibration: {w_cal:.4f}",
+        "",
+        "Per-dispatch means over the cold steps (dispatch run: cache-streaming read, k_step_fast, k_proj_mfma,",
+        "k_merge_cols), KiB as the counters read them:",
+    ]
+    for tag in ("FETCH_SIZE", "WRITE_SIZE"):
+        out.append(f"  {tag} ({steps[tag]} steps): " + ", ".join(f"{k} {v:.1f}" for k, v in per[tag].items()))
+    out += [
+        f"  copy calibration: a {COPY_PROBE_BYTES}-byte device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE "
+        f"{np.median(cal['FETCH_SIZE']):.1f} KiB and WRITE_SIZE {np.median(cal['WRITE_SIZE']):.1f} KiB",
+        f"  (true {true_kib:.0f} KiB each), so FETCH_SIZE is scaled by {f_cal:.4f} and WRITE_SIZE by {w_cal:.4f}.",
+        f"  draft call: {call / 1e6:.3f} MB per call, {call / alg_call:.3f}x the algorithmic bytes.",
+        f"  k_proj_mfma alone: {proj / 1e6:.3f} MB per launch, {proj / alg_proj:.3f}x its algorithmic bytes "
+        f"(active rows, h, row ids; the partial sums it writes are implementation bytes).",
+    ]
+    return "\n".join(out)
+
+
+COPY_PROBE_BYTES = 268435456
+
+STEP_PATTERNS = {
+    "indexed": ("k_step_fast", "k_proj_mfma", "k_merge_cols"),
+    "packed": ("k_step_fast", "k_gather", "k_proj_mfma", "k_merge_cols"),
+    "slots": ("k_step_fast", "k_pack_plan", "k_gather", "k_proj_mfma", "k_merge_cols"),
+}
+
+
+def kernel_base_name(name):
+    """A trace's kernel name without return type, namespaces, template
+    arguments and parameters (full or -T truncated names alike)."""
+    import re
+    name = re.sub(r"\(.*", "", name.replace("void ", "")).split("<")[0]
+    return name.split("::")[-1].strip()
+
+
+def step_trace_summary(path):
+    """Per-kernel spans (End - Start, us) of the cold decode steps in a
+    kernel trace of a bench run: dispatch runs of the cache-streaming read
+    followed by one mode's step kernels, consecutive on one queue.  Also the
+    per-step sum of the indexed step's kernels."""
+    import csv
+    ks = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kernel_base_name(r["Kernel_Name"]),
+                       r["Queue_Id"]))
+    ks.sort()
+    read = "elementwise_kernel_manual_unroll"
+    lines = ["| mode | steps | kernel | mean | median | min | max |", "|---|---|---|---|---|---|---|"]
+    step_sums = []
+    for mode, pat in STEP_PATTERNS.items():
+        spans = {k: [] for k in pat}
+        n = 0
+        for i in range(len(ks) - len(pat)):
+            if ks[i][2] != read:
+                continue
+            seq = ks[i + 1:i + 1 + len(pat)]
+            if all(p == q[2] for p, q in zip(pat, seq)) and len({q[3] for q in seq}) == 1:
+                n += 1
+                for p, q in zip(pat, seq):
+                    spans[p].append((q[1] - q[0]) / 1e3)
+                if mode == "indexed":
+                    step_sums.append(sum((q[1] - q[0]) / 1e3 for q in seq))
+        for p in pat:
+            v = np.array(spans[p]) if spans[p] else None
+            if v is not None:
+                lines.append(f"| {mode} | {n} | {p} | {v.mean():.3f} | {np.median(v):.3f} | {v.min():.3f} | "
+                             f"{v.max():.3f} |")
+    if step_sums:
+        v = np.array(step_sums)
+        lines.append("")
+        lines.append(f"Per-step kernel time (indexed, cold; the sum of its kernels' spans over {len(v)} steps): "
+                     f"p10 {np.percentile(v, 10):.2f} us, median {np.median(v):.2f} us, "
+                     f"p90 {np.percentile(v, 90):.2f} us.")
+    return "\n".join(lines)
+
+
 def measured_prefill_traffic():
     """HBM bytes per k_prefill launch on the prefill workload (FETCH_SIZE +
     WRITE_SIZE, scaled by the copy calibration) from the committed counter
@@ -695,6 +866,160 @@ def overlap_leg(torch, ns, cfg, W, ids, n_act, packed, h, ws, dcode, copy_stream
             "T_serial_ms": r["serial"], "T_overlap_ms": r["overlap"], "T_forkjoin_no_gather_ms": r["forkjoin"],
             "hidden_fraction": (r["serial"] - r["overlap"]) / r["gather"] if r["gather"] > 0 else None,
             "note": "cold, hipGraph replay of 20 repetitions per variant, cache-streaming read subtracted"}
+
+
+OVERLAP_VARIANTS = [("flush", 13), ("backbone", 13), ("serial", 13), ("overlap", 13), ("forkjoin", 13),
+                    ("serial", 1000), ("overlap", 1000)]
+
+
+def overlap_study(torch, ns, WL, R=20, reps=3):
+    """The overlap leg's variants, for a kernel trace: per repetition the
+    cache-streaming read, then the backbone stand-in alone, or with a gather
+    of n rows and the PACKED head serially on one stream ("serial"), or the
+    gather forked to a second stream beside the backbone and joined before
+    the head ("overlap"), or the same fork and join with nothing on the
+    second stream ("forkjoin").  n = 13 is the slot-stable buffer's typical
+    per-step delta, n = 1000 a whole active set.  Each variant runs R
+    repetitions as a graph replay (reps times) and then eagerly (reps times),
+    with host pauses between runs so the trace splits into one cluster per
+    run.  Prints the per-repetition times (us, the read subtracted)."""
+    torch.cuda.set_device(0)
+    cfg = WL.get_config("llama3_8b")
+    W = torch.from_numpy(WL.make_weights(cfg).view(np.int16)).cuda().view(torch.bfloat16)
+    flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    lines = flush_buf.view(-1, 128)
+    sink = torch.empty(lines.shape[0], dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(cfg.seed + 11)
+    ids = torch.as_tensor(np.sort(rng.choice(cfg.V, size=cfg.w_max, replace=False)).astype(np.int32)).cuda()
+    counts = {n: torch.tensor([n], dtype=torch.int32, device="cuda") for n in (13, 1000)}
+    packed = torch.empty((cfg.w_max, cfg.d), dtype=torch.bfloat16, device="cuda")
+    h = torch.randn((cfg.M, cfg.d), device="cuda").to(torch.bfloat16)
+    ws = ns.alloc_workspace(cfg.w_max, cfg.M, cfg.k, cfg.d)
+    tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
+    tvals = torch.empty((cfg.M, cfg.k), device="cuda")
+    backbone = make_backbone(torch, cfg)
+    copy = torch.cuda.Stream()
+
+    def gather(stream, n):
+        ns.nanospec_gather_rows(W, cfg.V, cfg.d, ns.NS_BF16, ids, counts[n], cfg.w_max, packed, stream=stream)
+
+    def head():
+        ns.nanospec_draft_logits_topk(packed, ns.NS_PACKED, ids, counts[1000], cfg.w_max, cfg.V, cfg.d, ns.NS_BF16,
+                                      h, cfg.M, cfg.k, None, tids, tvals, ws)
+
+    def variant(kind, n):
+        def run():
+            comp = torch.cuda.current_stream()
+            for i in range(R):
+                sink.copy_(lines[:, i % 128])
+                if kind == "backbone":
+                    backbone()
+                elif kind == "serial":
+                    backbone()
+                    gather(comp, n)
+                    head()
+                elif kind == "overlap":
+                    copy.wait_stream(comp)
+                    gather(copy, n)
+                    backbone()
+                    comp.wait_stream(copy)
+                    head()
+                elif kind == "forkjoin":
+                    copy.wait_stream(comp)
+                    backbone()
+                    comp.wait_stream(copy)
+                    head()
+        return run
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            time.sleep(0.05)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) / R * 1e3
+
+    for kd, n in OVERLAP_VARIANTS:
+        variant(kd, n)()
+    torch.cuda.synchronize()
+    res = {}
+    for kd, n in OVERLAP_VARIANTS:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            variant(kd, n)()
+        torch.cuda.synchronize()
+        res[f"graph_{kd}_{n}"] = timed(g.replay)
+        del g
+    for kd, n in OVERLAP_VARIANTS:
+        res[f"eager_{kd}_{n}"] = timed(variant(kd, n))
+    out = {k: round(v - res[k.split("_")[0] + "_flush_13"], 2) for k, v in res.items()}
+    print(json.dumps({"overlap_study_us_per_repetition": out, "R": R, "reps": reps}), flush=True)
+
+
+def overlap_trace_summary(path, R=20):
+    """Markdown table of a kernel trace of an --overlap-study run: the runs
+    are the trace's clusters of R cache-streaming reads (split at pauses of
+    more than 20 ms), in the study's order (graph replays, then eager runs,
+    reps of each variant).  Per repetition, from the end of its read: when
+    the first GEMM and the gather start, the GEMMs' summed durations, how
+    long after the last GEMM the head starts, the head's span (projection
+    start to merge end) and the whole repetition; medians over a run's
+    repetitions, then over its reps."""
+    import csv
+    ks = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            nm = r["Kernel_Name"]
+            kind = ("gemm" if "Cijk" in nm else "gather" if "k_gather" in nm else
+                    "head" if ("k_proj" in nm or "k_merge" in nm) else
+                    "read" if ("copy" in nm.lower() and "elementwise" in nm) else "other")
+            ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind, r["Queue_Id"]))
+    ks.sort()
+    clusters = [[ks[0]]]
+    for k in ks[1:]:
+        if k[0] - max(x[1] for x in clusters[-1][-8:]) > 20_000_000:
+            clusters.append([k])
+        else:
+            clusters[-1].append(k)
+    runs = [c for c in clusters if sum(1 for k in c if k[2] == "read") == R]
+    reps = len(runs) // (2 * len(OVERLAP_VARIANTS))
+    cols = ["first_gemm_us", "gather_start_us", "gather_us", "gemm_sum_us", "head_after_gemm_us", "head_span_us",
+            "repetition_us"]
+    lines = ["| run | variant | gathered rows | " + " | ".join(cols) + " |", "|---" * (3 + len(cols)) + "|"]
+    for vi, (kd, n) in enumerate(OVERLAP_VARIANTS * 2):
+        mode = "graph" if vi < len(OVERLAP_VARIANTS) else "eager"
+        meds = []
+        for c in runs[vi * reps:(vi + 1) * reps]:
+            reads = [k for k in c if k[2] == "read"]
+            per = {col: [] for col in cols}
+            for i in range(R):
+                t0 = reads[i][1]
+                t1 = reads[i + 1][0] if i + 1 < R else max(k[1] for k in c)
+                inrep = [k for k in c if t0 <= k[0] <= t1]
+                g = [k for k in inrep if k[2] == "gemm"]
+                ga = [k for k in inrep if k[2] == "gather"]
+                hd = [k for k in inrep if k[2] == "head"]
+                per["repetition_us"].append((t1 - t0) / 1e3)
+                if g:
+                    per["first_gemm_us"].append((g[0][0] - t0) / 1e3)
+                    per["gemm_sum_us"].append(sum(k[1] - k[0] for k in g) / 1e3)
+                if ga:
+                    per["gather_start_us"].append((ga[0][0] - t0) / 1e3)
+                    per["gather_us"].append((ga[0][1] - ga[0][0]) / 1e3)
+                if hd and g:
+                    per["head_after_gemm_us"].append((hd[0][0] - g[-1][1]) / 1e3)
+                    per["head_span_us"].append((hd[-1][1] - hd[0][0]) / 1e3)
+            meds.append({col: (float(np.median(v)) if v else None) for col, v in per.items()})
+        cells = []
+        for col in cols:
+            v = [m[col] for m in meds if m[col] is not None]
+            cells.append(f"{np.median(v):.1f}" if v else "-")
+        lines.append(f"| {mode} | {kd} | {n} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
 
 
 def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
@@ -1058,8 +1383,13 @@ def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
 
 
 def sweep(torch, ns, WL, args):
-    """Draft head alone (INDEXED, cold, graph replay) over |I| x M on the
-    Llama-3-8B-shaped head; one JSON line per point."""
+    """Draft head alone (INDEXED, graph replay) over |I| x M on the
+    Llama-3-8B-shaped head; one JSON line per point.  Cold: 512 MiB streamed
+    through the caches before every call, the read alone subtracted.  Warm
+    (us_warm): the same calls back to back, so the rows a call reads were
+    read by the call before (up to 16384 rows x 8 KiB = 128 MiB, within the
+    256 MB Infinity Cache): the distance between the two shows whether the
+    cold protocol really reads the rows from HBM."""
     cfg = WL.get_config("llama3_8b")
     W_host = WL.make_weights(cfg)
     W = torch.from_numpy(W_host.view(np.int16)).cuda().view(torch.bfloat16)
@@ -1080,10 +1410,11 @@ def sweep(torch, ns, WL, args):
             tids = torch.empty((M, k), dtype=torch.int32, device="cuda")
             tvals = torch.empty((M, k), dtype=torch.float32, device="cuda")
 
-            def body(with_head):
+            def body(with_head, cold=True):
                 def run():
                     for i in range(R):
-                        sink.copy_(lines[:, (i * 7) % 128])
+                        if cold:
+                            sink.copy_(lines[:, (i * 7) % 128])
                         if with_head:
                             ns.nanospec_draft_logits_topk(W, ns.NS_INDEXED, ids, n_dev, n, cfg.V, cfg.d, ns.NS_BF16,
                                                           h, M, k, None, tids, tvals, ws)
@@ -1108,13 +1439,15 @@ def sweep(torch, ns, WL, args):
                     ts.append(a.elapsed_time(b))
                 return float(np.median(ts))
 
-            g_all, g_fl = capture(body(True)), capture(body(False))
+            g_all, g_fl, g_warm = capture(body(True)), capture(body(False)), capture(body(True, cold=False))
             us = (timed(g_all) - timed(g_fl)) / R * 1e3
+            us_warm = timed(g_warm) / R * 1e3
             nbytes = n * cfg.d * 2 + M * cfg.d * 2 + n * 4 + M * k * 8
             print(json.dumps({"n": n, "M": M, "k": k, "d": cfg.d, "us": us, "bytes": nbytes,
                               "GBps": nbytes / (us * 1e-6) / 1e9,
-                              "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}), flush=True)
-            del g_all, g_fl
+                              "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                              "us_warm": us_warm}), flush=True)
+            del g_all, g_fl, g_warm
 
 
 def dispatch_floor(torch, flush, K, reps):
