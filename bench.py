@@ -490,14 +490,15 @@ def kernel_source_hash(sources=DRAFT_SOURCES):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, mode, mean_active, key="traffic_bytes_per_call"):
+def measured_traffic(workload, mode, mean_active, key="traffic_bytes_per_call", path=None):
     """HBM bytes per draft-head call (or, with key
     traffic_bytes_per_projection, per k_proj_mfma launch) from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy
     calibration), or None when there is none for this workload and mode, the
     kernel sources changed since the counters were taken, or the summary's
     mean |I| is more than 5% away from this run's (the bytes scale with it)."""
-    path = os.path.join(ROOT, "profiles", f"draft_head_{workload}_traffic.txt")
+    if path is None:
+        path = os.path.join(ROOT, "profiles", f"draft_head_{workload}_traffic.txt")
     try:
         with open(path) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
@@ -614,7 +615,8 @@ def kernel_base_name(name):
     """A trace's kernel name without return type, namespaces, template
     arguments and parameters (full or -T truncated names alike)."""
     import re
-    name = re.sub(r"\(.*", "", name.replace("void ", "")).split("<")[0]
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    name = re.sub(r"\(.*", "", name).split("<")[0]
     return name.split("::")[-1].strip()
 
 
