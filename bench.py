@@ -348,7 +348,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": proj_GBps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": proj_GBps / HBM_PEAK_GBS,
                      "traffic": measured_traffic(cfg.name, "indexed", n_mean, "traffic_bytes_per_projection"),
-                     "kernel": "k_proj_mfma (nanospec_draft_project, INDEXED)",
+                     "kernel": "projection stage: nanospec_draft_project (INDEXED; k_proj_mfma, or k_proj_msplit "
+                               "for 48 < M <= 64 over many rows)",
                      "bytes_per_launch": proj_bytes, "avg_launch_us": t_proj_ms * 1e3,
                      "draft_call": {"kernels": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols",
                                     "mode": mname[best], "bytes": draft_bytes, "avg_us": r["draft_ms"] * 1e3,
@@ -545,19 +546,22 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
     mean_active = float(b["config"]["mean_active"])
     alg_proj = float(b["roofline"]["bytes_per_launch"])
     alg_call = float(b["roofline"]["draft_call"]["bytes"])
-    step_kernels = ("elementwise_kernel_manual_unroll", "k_step_fast", "k_proj_mfma", "k_merge_cols")
+    step_kernels = (("elementwise_kernel_manual_unroll",), ("k_step_fast",), PROJ_KERNELS, ("k_merge_cols",))
     per = {}
     steps = {}
+    pname = None
     for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path)
-        acc = {k: [] for k in step_kernels[1:]}
+        acc = {"k_step_fast": [], "proj": [], "k_merge_cols": []}
         for i in range(len(rows) - 3):
-            if all(kernel_base_name(rows[i + j][0]) == step_kernels[j] for j in range(4)):
-                for j in range(1, 4):
-                    acc[step_kernels[j]].append(rows[i + j][1])
-        steps[tag] = len(acc["k_proj_mfma"])
+            names = [kernel_base_name(rows[i + j][0]) for j in range(4)]
+            if all(names[j] in step_kernels[j] for j in range(4)):
+                pname = names[2]
+                for j, key in ((1, "k_step_fast"), (2, "proj"), (3, "k_merge_cols")):
+                    acc[key].append(rows[i + j][1])
+        steps[tag] = len(acc["proj"])
         if steps[tag] == 0:
-            raise SystemExit(f"{path}: no cold indexed step (read, k_step_fast, k_proj_mfma, k_merge_cols) found")
+            raise SystemExit(f"{path}: no cold indexed step (read, k_step_fast, projection, k_merge_cols) found")
         per[tag] = {k: float(np.mean(v)) for k, v in acc.items()}
     cal = {}
     for tag, path in (("FETCH_SIZE", copy_fetch_csv), ("WRITE_SIZE", copy_write_csv)):
@@ -568,11 +572,11 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
     f_cal = true_kib / float(np.median(cal["FETCH_SIZE"]))
     w_cal = true_kib / float(np.median(cal["WRITE_SIZE"]))
     kib = 1024.0
-    proj = (per["FETCH_SIZE"]["k_proj_mfma"] * f_cal + per["WRITE_SIZE"]["k_proj_mfma"] * w_cal) * kib
+    proj = (per["FETCH_SIZE"]["proj"] * f_cal + per["WRITE_SIZE"]["proj"] * w_cal) * kib
     merge = (per["FETCH_SIZE"]["k_merge_cols"] * f_cal + per["WRITE_SIZE"]["k_merge_cols"] * w_cal) * kib
     call = proj + merge
     out = [
-        f"# HBM traffic of one draft-head call (k_proj_mfma + k_merge_cols), cold indexed steps of the",
+        f"# HBM traffic of one draft-head call ({pname} + k_merge_cols), cold indexed steps of the",
         f"# {workload} workload ({b['config']['workload']}; mean |I| = {mean_active:.2f} over the timed steps).",
         f"# bench.py reads traffic_bytes_per_call from this file while source_sha256 matches its kernel sources",
         f"# and its mean |I| is within 5% of this value.",
@@ -586,17 +590,18 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
         f"fetch_calibration: {f_cal:.4f}",
         f"write_calibration: {w_cal:.4f}",
         "",
-        "Per-dispatch means over the cold steps (dispatch run: cache-streaming read, k_step_fast, k_proj_mfma,",
+        f"Per-dispatch means over the cold steps (dispatch run: cache-streaming read, k_step_fast, {pname},",
         "k_merge_cols), KiB as the counters read them:",
     ]
     for tag in ("FETCH_SIZE", "WRITE_SIZE"):
-        out.append(f"  {tag} ({steps[tag]} steps): " + ", ".join(f"{k} {v:.1f}" for k, v in per[tag].items()))
+        out.append(f"  {tag} ({steps[tag]} steps): " + ", ".join(f"{pname if k == 'proj' else k} {v:.1f}"
+                                                                 for k, v in per[tag].items()))
     out += [
         f"  copy calibration: a {COPY_PROBE_BYTES}-byte device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE "
         f"{np.median(cal['FETCH_SIZE']):.1f} KiB and WRITE_SIZE {np.median(cal['WRITE_SIZE']):.1f} KiB",
         f"  (true {true_kib:.0f} KiB each), so FETCH_SIZE is scaled by {f_cal:.4f} and WRITE_SIZE by {w_cal:.4f}.",
         f"  draft call: {call / 1e6:.3f} MB per call, {call / alg_call:.3f}x the algorithmic bytes.",
-        f"  k_proj_mfma alone: {proj / 1e6:.3f} MB per launch, {proj / alg_proj:.3f}x its algorithmic bytes "
+        f"  {pname} alone: {proj / 1e6:.3f} MB per launch, {proj / alg_proj:.3f}x its algorithmic bytes "
         f"(active rows, h, row ids; the partial sums it writes are implementation bytes).",
     ]
     return "\n".join(out)
@@ -604,10 +609,14 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
 
 COPY_PROBE_BYTES = 268435456
 
+# The projection stage's kernel: MFMA k-split, MFMA M-split (48 < M <= 64
+# over many rows) or the fp32 VALU kernel.
+PROJ_KERNELS = ("k_proj_mfma", "k_proj_msplit", "k_proj_valu")
+
 STEP_PATTERNS = {
-    "indexed": ("k_step_fast", "k_proj_mfma", "k_merge_cols"),
-    "packed": ("k_step_fast", "k_gather", "k_proj_mfma", "k_merge_cols"),
-    "slots": ("k_step_fast", "k_pack_plan", "k_gather", "k_proj_mfma", "k_merge_cols"),
+    "indexed": (("k_step_fast",), PROJ_KERNELS, ("k_merge_cols",)),
+    "packed": (("k_step_fast",), ("k_gather",), PROJ_KERNELS, ("k_merge_cols",)),
+    "slots": (("k_step_fast",), ("k_pack_plan",), ("k_gather",), PROJ_KERNELS, ("k_merge_cols",)),
 }
 
 
@@ -636,23 +645,22 @@ def step_trace_summary(path):
     lines = ["| mode | steps | kernel | mean | median | min | max |", "|---|---|---|---|---|---|---|"]
     step_sums = []
     for mode, pat in STEP_PATTERNS.items():
-        spans = {k: [] for k in pat}
+        spans = {}                                        # kernel name -> spans, in step order
         n = 0
         for i in range(len(ks) - len(pat)):
             if ks[i][2] != read:
                 continue
             seq = ks[i + 1:i + 1 + len(pat)]
-            if all(p == q[2] for p, q in zip(pat, seq)) and len({q[3] for q in seq}) == 1:
+            if all(q[2] in p for p, q in zip(pat, seq)) and len({q[3] for q in seq}) == 1:
                 n += 1
-                for p, q in zip(pat, seq):
-                    spans[p].append((q[1] - q[0]) / 1e3)
+                for q in seq:
+                    spans.setdefault(q[2], []).append((q[1] - q[0]) / 1e3)
                 if mode == "indexed":
                     step_sums.append(sum((q[1] - q[0]) / 1e3 for q in seq))
-        for p in pat:
-            v = np.array(spans[p]) if spans[p] else None
-            if v is not None:
-                lines.append(f"| {mode} | {n} | {p} | {v.mean():.3f} | {np.median(v):.3f} | {v.min():.3f} | "
-                             f"{v.max():.3f} |")
+        for name, sp in spans.items():
+            v = np.array(sp)
+            lines.append(f"| {mode} | {n} | {name} | {v.mean():.3f} | {np.median(v):.3f} | {v.min():.3f} | "
+                         f"{v.max():.3f} |")
     if step_sums:
         v = np.array(step_sums)
         lines.append("")
