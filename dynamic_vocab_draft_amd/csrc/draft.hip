@@ -299,7 +299,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   __shared__ uint4 abuf[NB][kPW][RT * TB];
   __shared__ uint4 bbuf[NB][kPW][HDMA ? NMT * TB : 1];
   // The wave tiles of the final sum reuse the staging buffers (RT NMT 4 KiB:
-  // within abuf for NMT <= 2, within bbuf otherwise, as RT <= 2).
+  // within abuf for NMT <= 2, within bbuf otherwise; checked below for every
+  // instance).
   static_assert(sizeof(f32x4_t) * kPW * RT * NMT * NS_WAVE <= (NMT <= 2 ? sizeof(abuf) : sizeof(bbuf)),
                 "wave tiles fit the reused buffer");
   auto red = reinterpret_cast<f32x4_t (*)[RT][NMT][NS_WAVE]>(NMT <= 2 ? &abuf[0][0][0] : &bbuf[0][0][0]);
