@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--step-trace-summary", default="", metavar="CSV",
                    help="only summarize a rocprofv3 kernel-trace CSV of a bench run per decode-step kernel (no GPU) "
                         "and exit")
+    p.add_argument("--sq-summary", nargs="+", default=None, metavar="CSV",
+                   help="only tabulate the per-dispatch counters of rocprofv3 --pmc CSVs of a --head-probe run "
+                        "(median over each projection kernel's dispatches; no GPU) and exit")
     p.add_argument("--counter-summary", nargs=5, default=None,
                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "BENCH_OUT"),
                    help="only write the draft-head traffic summary (no GPU) from FETCH_SIZE and WRITE_SIZE counter "
@@ -89,6 +92,9 @@ def main():
         return
     if args.step_trace_summary:
         print(step_trace_summary(args.step_trace_summary))
+        return
+    if args.sq_summary:
+        print(sq_summary(args.sq_summary))
         return
     if args.counter_summary:
         print(counter_summary(*args.counter_summary, workload=args.config))
@@ -608,6 +614,31 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
 
 
 COPY_PROBE_BYTES = 268435456
+
+
+def sq_summary(paths, kernels=("k_proj_msplit", "k_proj_mfma")):
+    """Markdown table of hardware counters from rocprofv3 --pmc CSVs: per
+    dispatch, each counter summed over the rows rocprofv3 reports for it;
+    per kernel, the median over its dispatches."""
+    import csv
+    per = {}                                            # (kernel, counter) -> [values]
+    for path in paths:
+        acc = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = kernel_base_name(r["Kernel_Name"])
+                if name not in kernels:
+                    continue
+                key = (int(r["Dispatch_Id"]), name, r["Counter_Name"])
+                acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name, counter), v in acc.items():
+            per.setdefault((name, counter), []).append(v)
+    counters = sorted({c for _, c in per})
+    lines = ["| counter | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]
+    for c in counters:
+        cells = [f"{np.median(per[(k, c)]):.0f}" if (k, c) in per else "-" for k in kernels]
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
 
 # The projection stage's kernel: MFMA k-split, MFMA M-split (48 < M <= 64
 # over many rows) or the fp32 VALU kernel.
