@@ -74,6 +74,13 @@ def parse():
                    help="only write the draft-head traffic summary (no GPU) from FETCH_SIZE and WRITE_SIZE counter "
                         "CSVs of an indexed bench run, the two counters of a --copy-probe run, and that bench run's "
                         "output (its JSON line gives mean |I| and the algorithmic bytes), and exit")
+    p.add_argument("--prefill-probe", action="store_true",
+                   help="only run the prefill top-K_pre leg (cold, 12 calls), print its JSON and exit")
+    p.add_argument("--prefill-counter-summary", nargs=5, default=None,
+                   metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV", "TRACE_CSV"),
+                   help="only write the prefill traffic summary (no GPU) from FETCH_SIZE and WRITE_SIZE counter "
+                        "CSVs and a kernel-trace CSV of --prefill-probe runs and the two counters of a --copy-probe "
+                        "run, and exit")
     p.add_argument("--head-probe", default="", metavar="M[,M...]",
                    help="only run the full-vocabulary projection (V=151936, d=4096, bf16) three times for each "
                         "M, for hardware counters, and exit")
@@ -99,6 +106,9 @@ def main():
     if args.counter_summary:
         print(counter_summary(*args.counter_summary, workload=args.config))
         return
+    if args.prefill_counter_summary:
+        print(prefill_counter_summary(*args.prefill_counter_summary))
+        return
     import torch
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
@@ -107,6 +117,12 @@ def main():
     from dynamic_vocab_draft_amd import workloads as WL
 
     torch.cuda.set_device(0)
+    if args.prefill_probe:
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        lines = flush.view(-1, 128)
+        sink = torch.empty(lines.shape[0], dtype=torch.uint8, device="cuda")
+        print(json.dumps(prefill_leg(torch, ns, WL, lambda i: sink.copy_(lines[:, i % 128]))))
+        return
     if args.head_probe:
         head_probe(torch, ns, [int(x) for x in args.head_probe.split(",")])
         return
@@ -699,6 +715,70 @@ def step_trace_summary(path):
                      f"p10 {np.percentile(v, 10):.2f} us, median {np.median(v):.2f} us, "
                      f"p90 {np.percentile(v, 90):.2f} us.")
     return "\n".join(lines)
+
+
+def prefill_counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, trace_csv):
+    """The prefill top-K_pre pass's HBM traffic per k_prefill launch from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch, scaled by the --copy-probe
+    calibration) and its duration from a kernel trace, all of --prefill-probe
+    runs.  Returns the summary text that measured_prefill_traffic() reads."""
+    import csv
+    from dynamic_vocab_draft_amd import workloads as WL
+    cfg = WL.get_config("prefill")
+    alg = cfg.L * cfg.V * 2 + cfg.L * cfg.k_pre * 8
+    per = {}
+    for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        v = [val for n, val in _counter_rows(path) if kernel_base_name(n) == "k_prefill"]
+        if not v:
+            raise SystemExit(f"{path}: no k_prefill dispatch")
+        per[tag] = v
+    cal = {}
+    for tag, path in (("FETCH_SIZE", copy_fetch_csv), ("WRITE_SIZE", copy_write_csv)):
+        cal[tag] = float(np.median([v for n, v in _counter_rows(path) if "copyBuffer" in kernel_base_name(n)]))
+    true_kib = COPY_PROBE_BYTES / 1024.0
+    f_cal, w_cal = true_kib / cal["FETCH_SIZE"], true_kib / cal["WRITE_SIZE"]
+    fetch = float(np.mean(per["FETCH_SIZE"])) * f_cal * 1024.0
+    write = float(np.mean(per["WRITE_SIZE"])) * w_cal * 1024.0
+    with open(trace_csv) as f:
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(f)
+              if kernel_base_name(r["Kernel_Name"]) == "k_prefill"]
+    if not us:
+        raise SystemExit(f"{trace_csv}: no k_prefill dispatch")
+    t = float(np.mean(us))
+    return "\n".join([
+        "# HBM traffic and duration of k_prefill (nanospec_prefill_topk) on the prefill workload:",
+        f"# L={cfg.L} positions x V={cfg.V} bf16 logits (N(0, {cfg.sigma:g}^2) plus {cfg.n_peaks} peaks of "
+        f"+{cfg.peak:g} per row), K_pre={cfg.k_pre}, cold.",
+        "# bench.py reports traffic_bytes_per_call from this file while source_sha256 matches prefill.hip + common.hpp.",
+        f"source_sha256: {kernel_source_hash(PREFILL_SOURCES)}",
+        f"traffic_bytes_per_call: {fetch + write:.0f}",
+        f"algorithmic_bytes_per_call: {alg}",
+        f"fetch_calibration: {f_cal:.4f}",
+        f"write_calibration: {w_cal:.4f}",
+        "",
+        f"Per-dispatch counters ({len(per['FETCH_SIZE'])} dispatches each, KiB as read): FETCH_SIZE mean "
+        f"{np.mean(per['FETCH_SIZE']):.1f} (min {min(per['FETCH_SIZE']):.1f}, max {max(per['FETCH_SIZE']):.1f}),",
+        f"WRITE_SIZE mean {np.mean(per['WRITE_SIZE']):.1f}. Scaled by the copy calibration (a {COPY_PROBE_BYTES}-byte "
+        f"device copy reads FETCH_SIZE {cal['FETCH_SIZE']:.1f} KiB and WRITE_SIZE {cal['WRITE_SIZE']:.1f} KiB):",
+        f"fetch {fetch / 1e9:.4f} GB + write {write / 1e6:.3f} MB = {(fetch + write) / 1e9:.4f} GB per launch, "
+        f"{(fetch + write) / alg:.4f}x the algorithmic bytes (the logits once plus the L x K_pre outputs).",
+        "",
+        f"Kernel trace ({len(us)} dispatches, cold): mean {t:.1f} us, min {min(us):.1f}, max {max(us):.1f}",
+        f"= {alg / (t * 1e-6) / 1e9:.0f} GB/s ({alg / (t * 1e-6) / 1e9 / HBM_PEAK_GBS:.3f} of 8 TB/s).",
+        "",
+        "Commands (run from /tmp with TMPDIR=/tmp; REPO is the repository root, OUT an output directory):",
+        "  rocprofv3 --kernel-trace --stats -T --output-format csv -d $OUT/pkt -o p -- python3 $REPO/bench.py "
+        "--prefill-probe",
+        "  rocprofv3 --pmc FETCH_SIZE -T --output-format csv -d $OUT/ppf -o p -- python3 $REPO/bench.py --prefill-probe",
+        "  rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d $OUT/ppw -o p -- python3 $REPO/bench.py --prefill-probe",
+        "  rocprofv3 --pmc FETCH_SIZE -T --output-format csv -d $OUT/cf -o copy -- python3 $REPO/bench.py "
+        "--copy-probe 268435456",
+        "  rocprofv3 --pmc WRITE_SIZE -T --output-format csv -d $OUT/cw -o copy -- python3 $REPO/bench.py "
+        "--copy-probe 268435456",
+        "  python3 $REPO/bench.py --prefill-counter-summary $OUT/ppf/p_counter_collection.csv "
+        "$OUT/ppw/p_counter_collection.csv $OUT/cf/copy_counter_collection.csv $OUT/cw/copy_counter_collection.csv "
+        "$OUT/pkt/p_kernel_trace.csv",
+    ])
 
 
 def measured_prefill_traffic():

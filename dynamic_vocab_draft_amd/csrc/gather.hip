@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(const uint4* __restri
 
 int ns::launch_row_copy(const void* w, int V, int dvec, const int32_t* ids, const int32_t* dst,
                         const int32_t* n_dev, int n_max, void* out, hipStream_t stream, int max_blocks) {
-  int grid = (n_max + kRowsPerBlock - 1) / kRowsPerBlock;
+  int grid = (int)(((int64_t)n_max + kRowsPerBlock - 1) / kRowsPerBlock);
   if (max_blocks > 0 && grid > max_blocks) grid = max_blocks;
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kGatherThreads), 0, stream, (const uint4*)w, V, dvec, ids, dst,

@@ -304,7 +304,8 @@ int nanospec_packed_update(nanospec_packed* pk, const nanospec_state* st,
  * results (the slice count depends on n_max, M, d and the live count).
  * row_ids must be distinct apart from holes.
  * Errors: NS_EINVAL (nulls, M not in [1,64], k not in [1,64], d % 8 != 0,
- * n_max < 1), NS_EDTYPE, NS_ECAPACITY (ws too small), NS_EHIP. */
+ * n_max not in [1, NS_MAX_V]), NS_EDTYPE, NS_ECAPACITY (ws too small),
+ * NS_EHIP.  nanospec_draft_workspace_bytes returns 0 for such dims. */
 size_t nanospec_draft_workspace_bytes(int32_t n_max, int32_t M, int32_t k, int32_t d);
 int nanospec_draft_logits_topk(const void* rows, int32_t mode, const int32_t* row_ids,
                                const int32_t* n_dev, int32_t n_max, int32_t V,

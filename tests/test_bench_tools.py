@@ -15,7 +15,7 @@ import bench  # noqa: E402
 
 READ = "void at::native::elementwise_kernel_manual_unroll<128, 8, Foo>(int, Foo)"
 STEP = "void (anonymous namespace)::k_step_fast<HIP_vector_type<int, 4u>, 2>(ns_state_view, int const*)"
-PROJ = "void (anonymous namespace)::k_proj_mfma<1, 1, false, 1, 4>(uint4 const*, int)"
+PROJ = "void (anonymous namespace)::k_proj_mfma<1, 1, false, 1, 4, true>(uint4 const*, int)"
 MERGE = "void (anonymous namespace)::k_merge_cols<4, true, 4, false>(float const*, int)"
 
 
@@ -110,3 +110,22 @@ def test_committed_traffic_summary_matches_the_sources():
     path = os.path.join(ROOT, "profiles", "draft_head_llama3_8b_traffic.txt")
     kv = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith((" ", "#")))
     assert kv["source_sha256"].strip() == bench.kernel_source_hash()
+
+
+def test_prefill_counter_summary(tmp_path):
+    """k_prefill dispatches among others: counters are averaged over the
+    k_prefill dispatches only and scaled by the copy calibration; the trace
+    gives the mean duration."""
+    PRE = "void (anonymous namespace)::k_prefill<0, true, 4>(void const*, int)"
+    _counters(tmp_path / "f.csv", [(READ, 7.0), (PRE, 500000.0), (READ, 7.0), (PRE, 500010.0)])
+    _counters(tmp_path / "w.csv", [(READ, 7.0), (PRE, 190.0), (READ, 7.0), (PRE, 200.0)])
+    kib = bench.COPY_PROBE_BYTES / 1024
+    _counters(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", kib / 2)] * 3)
+    _counters(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", kib)] * 3)
+    _trace(tmp_path / "t.csv", [(READ, 0, 90_000, 1), (PRE, 100_000, 280_000, 1), (PRE, 300_000, 500_000, 1)])
+    out = bench.prefill_counter_summary(*(str(tmp_path / n) for n in ("f.csv", "w.csv", "cf.csv", "cw.csv", "t.csv")))
+    kv = dict(l.split(":", 1) for l in out.splitlines() if ":" in l and not l.startswith((" ", "#")))
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    assert float(kv["traffic_bytes_per_call"]) == pytest.approx((500005.0 * 2 + 195.0) * 1024, abs=1)
+    assert kv["source_sha256"] == bench.kernel_source_hash(bench.PREFILL_SOURCES)
+    assert "mean 190.0 us, min 180.0, max 200.0" in out
