@@ -209,7 +209,10 @@ __global__ __launch_bounds__(kStateThreads) void k_step(ns_state_view v, const i
 // C = |C_draft| + |C_ver|, the new entries take slots (len + p) mod w_max, so
 // an old slot s survives iff C < w_max and (s - len) mod w_max >= C.  Slots
 // never written hold -1.  The ascending compaction gives each thread a
-// contiguous run of WPT words (a multiple of 8, read as 16-byte LDS vectors).
+// contiguous run of WPT words (at least 8, a multiple of 4, read as 16-byte
+// LDS vectors): the fewest that cover the bitmap, so that every wave has
+// words to scan (a multiple of 8 left the last waves idle for V just above
+// 2^17, and the others with twice the words).
 constexpr int kFastThreads = 512;
 constexpr int kFastMaxIds = kFastThreads;      // one tuple entry per thread
 constexpr int kFastMaxRing = 32 * kFastThreads; // ring entries held in registers
@@ -218,7 +221,8 @@ constexpr int kFastStageMinIds = 4096;          // ids from which the compaction
 
 __host__ __device__ __forceinline__ int fast_wpt(int V) {
   const int words = (V + 31) >> 5;
-  return ((words + kFastThreads * 8 - 1) / (kFastThreads * 8)) * 8;
+  const int w4 = ((words + kFastThreads * 4 - 1) / (kFastThreads * 4)) * 4;
+  return w4 < 8 ? 8 : w4;
 }
 
 // Ints of LDS that stage the ascending active ids before one coalesced copy
@@ -233,6 +237,17 @@ __host__ __device__ __forceinline__ int fast_stage_ints(int V, int w_max) {
 }
 
 __device__ __forceinline__ void bm_set(uint32_t* bm, int id) { atomicOr(&bm[id >> 5], 1u << (id & 31)); }
+
+__device__ __forceinline__ void bm_store4(uint32_t* __restrict__ dst, int w, int words, uint4 a, bool vec) {
+  if (vec && w + 4 <= words) {
+    *(uint4*)(dst + w) = a;
+    return;
+  }
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (w + e < words) dst[w + e] = x[e];
+}
 
 __device__ __forceinline__ void bm_store8(uint32_t* __restrict__ dst, int w, int words, uint4 a, uint4 b, bool vec) {
   if (vec && w + 8 <= words) {
@@ -386,12 +401,19 @@ __device__ __forceinline__ void step_fast_body(const ns_state_view& v, const int
   pc += __popc(c0b.x) + __popc(c0b.y) + __popc(c0b.z) + __popc(c0b.w);
   bm_store8(v.bitmap, wbase, words, c0a, c0b, true);
   if (bitmap_out) bm_store8(bitmap_out, wbase, words, c0a, c0b, out_vec);
-  for (int c = 2; c < wpt / 4; c += 2) {
+  int c = 2;
+  for (; c + 1 < wpt / 4; c += 2) {
     const uint4 x = bm4[c], y = bm4[c + 1];
     pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
     pc += __popc(y.x) + __popc(y.y) + __popc(y.z) + __popc(y.w);
     bm_store8(v.bitmap, wbase + 4 * c, words, x, y, true);
     if (bitmap_out) bm_store8(bitmap_out, wbase + 4 * c, words, x, y, out_vec);
+  }
+  if (c < wpt / 4) {                                  // an odd run of four words
+    const uint4 x = bm4[c];
+    pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+    bm_store4(v.bitmap, wbase + 4 * c, words, x, true);
+    if (bitmap_out) bm_store4(bitmap_out, wbase + 4 * c, words, x, out_vec);
   }
   int n_tot = 0;
   int off = ns::block_excl_scan<kFastThreads>(pc, sh_scan, &n_tot);
