@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--config", default="llama3_8b")
-    p.add_argument("--mode", choices=["auto", "packed", "indexed", "slots"], default="auto")
+    p.add_argument("--mode", default="auto",
+                   help="auto (every mode) or a comma-separated list of packed, indexed, slots, decode")
     p.add_argument("--reps", type=int, default=5, help="graph replays per measurement (median)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
@@ -175,7 +176,9 @@ def main():
     pk = ns.NanoSpecPacked(cfg.V, cfg.w_max)
     slot_rows = torch.zeros((cfg.w_max, cfg.d), dtype=tdt, device="cuda")
     SLOTS = "slots"
+    DECODE = "decode"                            # nanospec_decode_step: state update and draft head in one call
     ws = ns.alloc_workspace(cfg.w_max, cfg.M, cfg.k, cfg.d)
+    ws_dec = ns.alloc_decode_workspace(cfg.w_max, cfg.n_tree + cfg.k_ver, cfg.M, cfg.k, cfg.d)
     tids = torch.empty((T, cfg.M, cfg.k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((T, cfg.M, cfg.k), dtype=torch.float32, device="cuda")
     flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
@@ -207,6 +210,14 @@ def main():
         n_slots.append(int(pk.n_slots.item()))
     sizes = np.array(sizes)
 
+    def decode_part(t):
+        ns.nanospec_decode_step(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n_act, W, cfg.V,
+                                cfg.d, dcode, hs[t], cfg.M, cfg.k, tids[t], tvals[t], ws_dec)
+
+    def decode_project(t):                       # the step's first launch alone (timing)
+        ns.nanospec_decode_step_project(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n_act, W,
+                                        cfg.V, cfg.d, dcode, hs[t], cfg.M, cfg.k, ws_dec)
+
     def draft_part(t, mode):
         comp = torch.cuda.current_stream()
         rows = W
@@ -228,10 +239,18 @@ def main():
                                       None, tids[t], tvals[t], ws)
 
     def body(mode, cold, with_state=True, with_draft=True):
+        # In the decode mode, with_state alone is the step's first launch
+        # (the state update beside the projection).
         def run():
             for t in range(t0, T):
                 if cold:
                     sink.copy_(flush_lines[:, (t * 7) % 128])
+                if mode == DECODE:
+                    if with_state and with_draft:
+                        decode_part(t)
+                    elif with_state:
+                        decode_project(t)
+                    continue
                 if with_state:
                     state_part(t)
                 if with_draft:
@@ -244,6 +263,9 @@ def main():
             ns.nanospec_packed_reset(pk)
             pack_update()
         for t in range(t0):
+            if mode == DECODE and t == t0 - 1:
+                decode_part(t)                   # the state keeps I_t: the timed steps take the fused form
+                continue
             state_part(t)
             if mode == SLOTS:
                 pack_update()
@@ -299,9 +321,12 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3
 
-    modes = {"packed": [ns.NS_PACKED], "indexed": [ns.NS_INDEXED], "slots": [SLOTS],
-             "auto": [ns.NS_PACKED, ns.NS_INDEXED, SLOTS]}[args.mode]
-    mname = {ns.NS_PACKED: "packed", ns.NS_INDEXED: "indexed", SLOTS: "slots"}
+    by_name = {"packed": ns.NS_PACKED, "indexed": ns.NS_INDEXED, "slots": SLOTS, "decode": DECODE}
+    names = list(by_name) if args.mode == "auto" else args.mode.split(",")
+    if not names or any(n not in by_name for n in names):
+        raise SystemExit(f"--mode: auto or a comma-separated list of {', '.join(by_name)}")
+    modes = [by_name[n] for n in names]
+    mname = {ns.NS_PACKED: "packed", ns.NS_INDEXED: "indexed", SLOTS: "slots", DECODE: "decode"}
     g_flush = capture(body(None, True, False, False))
     t_flush = time_graph(g_flush, needs_state=False)
 
@@ -326,12 +351,19 @@ def main():
         res[m] = dict(cold_ms=t_step / K, warm_ms=t_warm / K,
                       draft_ms=t_draft / K, state_ms=t_st / K,
                       eager_warm_ms=time_eager(body(m, False), m) / K, replay_matches_eager=ok)
+        if m == DECODE:                                # first launch, and the merge launch after it
+            res[m]["project_ms"] = res[m].pop("state_ms")
+            res[m]["select_ms"] = res[m].pop("draft_ms")
         del g_cold, g_warm, g_state
         progress(f"mode {mname[m]}: {res[m]['cold_ms'] * 1e3:.2f} us/step cold")
     best = min(modes, key=lambda m: res[m]["cold_ms"])
     r = res[best]
-    # The dominant kernel, k_proj_mfma, timed on its own: the INDEXED
-    # projection stage after the state update, minus the state update alone.
+    # The separate calls' figures (draft call, state update) come from the
+    # fastest separate mode, when one ran.
+    sep = [m for m in modes if m != DECODE]
+    rs = res[min(sep, key=lambda m: res[m]["cold_ms"])] if sep else None
+    # The projection stage on its own: the INDEXED projection after the
+    # state update, minus the state update alone.
     g_proj = capture(body("project", True))
     g_st = capture(body("project", True, True, False))
     t_proj_ms = time_diff(g_proj, g_st) / K
@@ -340,14 +372,47 @@ def main():
     ms = r["cold_ms"]
     n_mean = float(np.mean(sizes[t0:]))
     s = cfg.elem_bytes
+    words = (cfg.V + 31) // 32
     # Algorithmic bytes of one draft-head call: active rows, h, row ids, outputs.
     draft_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + n_mean * 4 + cfg.M * cfg.k * 8
-    achieved = draft_bytes / (r["draft_ms"] * 1e-3) / 1e9
     # The projection's own algorithmic bytes: active rows, h and row ids.
     proj_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + n_mean * 4
     proj_GBps = proj_bytes / (t_proj_ms * 1e-3) / 1e9
-    # ... plus the state update: ring read, tuple ids, bitmap + id list writes.
-    step_bytes = draft_bytes + cfg.w_max * 4 + (cfg.n_tree + cfg.k_ver) * 4 + ((cfg.V + 31) // 32) * 4 + n_mean * 4
+    # The state update's: ring read, tuple ids, bitmap write (and the id list).
+    state_bytes = cfg.w_max * 4 + (cfg.n_tree + cfg.k_ver) * 4 + words * 4
+    step_bytes = draft_bytes + state_bytes + n_mean * 4
+    projection_stage = {"kernel": "nanospec_draft_project (INDEXED; k_proj_mfma, or k_proj_msplit for 48 < M <= 64 "
+                                  "over many rows)",
+                        "bytes_per_launch": proj_bytes, "avg_launch_us": t_proj_ms * 1e3, "achieved": proj_GBps,
+                        "frac": proj_GBps / HBM_PEAK_GBS,
+                        "traffic": measured_traffic(cfg.name, "indexed", n_mean, "traffic_bytes_per_projection")}
+    draft_call = None
+    if rs is not None:
+        achieved = draft_bytes / (rs["draft_ms"] * 1e-3) / 1e9
+        sname = mname[min(sep, key=lambda m: res[m]["cold_ms"])]
+        draft_call = {"kernels": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols", "mode": sname,
+                      "bytes": draft_bytes, "avg_us": rs["draft_ms"] * 1e3, "achieved": achieved,
+                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name, sname, n_mean)}
+    if best == DECODE:
+        # The step's dominant kernel is its first launch: the projection of
+        # the tuple and I_t columns with the state update in block 0.  Its
+        # algorithmic bytes: the projection's (I_{t+1} rows, h, ids) and the
+        # state update's.
+        a_bytes = proj_bytes + state_bytes
+        a_us = r["project_ms"] * 1e3
+        a_GBps = a_bytes / (a_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": a_GBps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": a_GBps / HBM_PEAK_GBS,
+                    "traffic": measured_traffic(cfg.name, "decode", n_mean, "traffic_bytes_per_decode_project"),
+                    "kernel": "first launch of nanospec_decode_step (nanospec_decode_step_project): k_proj_mfma "
+                              "with the window-state update in block 0",
+                    "bytes_per_launch": a_bytes, "avg_launch_us": a_us,
+                    "projection_stage": projection_stage, "draft_call": draft_call}
+    else:
+        roofline = {"bound": "hbm", "achieved": proj_GBps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": proj_GBps / HBM_PEAK_GBS, "traffic": projection_stage["traffic"],
+                    "kernel": projection_stage["kernel"], "bytes_per_launch": proj_bytes,
+                    "avg_launch_us": t_proj_ms * 1e3, "draft_call": draft_call}
 
     out = {
         "metric": "draft LM-head steps/s (V=128k,d=4096,W_max=3072) + achieved HBM GB/s vs peak",
@@ -367,18 +432,12 @@ def main():
                    "mode": mname[best], "cache": "cold (512 MiB streamed through the caches between steps)",
                    "mean_active": n_mean, "lead_in_steps": lead, "timed_steps": [t0, T - 1],
                    "timing": "hipGraph replay of the timed steps"},
-        "roofline": {"bound": "hbm", "achieved": proj_GBps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": proj_GBps / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg.name, "indexed", n_mean, "traffic_bytes_per_projection"),
-                     "kernel": "projection stage: nanospec_draft_project (INDEXED; k_proj_mfma, or k_proj_msplit "
-                               "for 48 < M <= 64 over many rows)",
-                     "bytes_per_launch": proj_bytes, "avg_launch_us": t_proj_ms * 1e3,
-                     "draft_call": {"kernels": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols",
-                                    "mode": mname[best], "bytes": draft_bytes, "avg_us": r["draft_ms"] * 1e3,
-                                    "achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
-                                    "traffic": measured_traffic(cfg.name, mname[best], n_mean)}},
+        "roofline": roofline,
         "step": {"alg_bytes": step_bytes, "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
-                 "state_update_us": r["state_ms"] * 1e3, "draft_us": r["draft_ms"] * 1e3,
+                 "state_update_us": rs["state_ms"] * 1e3 if rs else None,
+                 "draft_us": rs["draft_ms"] * 1e3 if rs else None,
+                 "decode_first_launch_us": res[DECODE]["project_ms"] * 1e3 if DECODE in res else None,
+                 "decode_merge_us": res[DECODE]["select_ms"] * 1e3 if DECODE in res else None,
                  "warm_ms": r["warm_ms"], "eager_warm_ms": r["eager_warm_ms"],
                  "per_mode": {mname[m]: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res[m].items()}
                               for m in modes},
@@ -491,7 +550,8 @@ def head_probe(torch, ns, Ms, V=151936, d=4096, k=16):
 
 
 DRAFT_SOURCES = ("dynamic_vocab_draft_amd/csrc/draft.hip", "dynamic_vocab_draft_amd/csrc/select.hpp",
-                 "dynamic_vocab_draft_amd/csrc/common.hpp")
+                 "dynamic_vocab_draft_amd/csrc/common.hpp", "dynamic_vocab_draft_amd/csrc/state_fast.hpp",
+                 "dynamic_vocab_draft_amd/csrc/state_internal.hpp")
 
 
 PREFILL_SOURCES = ("dynamic_vocab_draft_amd/csrc/prefill.hip", "dynamic_vocab_draft_amd/csrc/common.hpp")
@@ -515,11 +575,13 @@ def kernel_source_hash(sources=DRAFT_SOURCES):
 
 def measured_traffic(workload, mode, mean_active, key="traffic_bytes_per_call", path=None):
     """HBM bytes per draft-head call (or, with key
-    traffic_bytes_per_projection, per k_proj_mfma launch) from the committed
-    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy
-    calibration), or None when there is none for this workload and mode, the
-    kernel sources changed since the counters were taken, or the summary's
-    mean |I| is more than 5% away from this run's (the bytes scale with it)."""
+    traffic_bytes_per_projection, per k_proj_mfma launch; with
+    traffic_bytes_per_decode_project, per first launch of the decode step)
+    from the committed counter summary (FETCH_SIZE + WRITE_SIZE, scaled by
+    the copy calibration), or None when there is none for this workload and
+    mode, the kernel sources changed since the counters were taken, or the
+    summary's mean |I| is more than 5% away from this run's (the bytes scale
+    with it)."""
     if path is None:
         path = os.path.join(ROOT, "profiles", f"draft_head_{workload}_traffic.txt")
     try:
@@ -528,7 +590,7 @@ def measured_traffic(workload, mode, mean_active, key="traffic_bytes_per_call", 
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_sha256") != kernel_source_hash() or kv.get("mode") != mode:
+    if kv.get("source_sha256") != kernel_source_hash() or mode not in kv.get("modes", "").split():
         return None
     try:
         if abs(float(kv["mean_active"]) - mean_active) > 0.05 * mean_active:
@@ -555,56 +617,74 @@ def _counter_rows(path):
 
 
 def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_out, workload="llama3_8b"):
-    """The draft head's HBM traffic per call from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch) over the cold indexed steps of a bench run: dispatch
-    runs of cache-streaming read, k_step_fast, k_proj_mfma, k_merge_cols.
-    Each counter is scaled by what it reads for a plain device copy of known
-    size (the --copy-probe run).  Mean |I| and the algorithmic bytes come
-    from the bench run's JSON line.  Returns the summary text that
-    measured_traffic() reads."""
+    """HBM traffic per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+    over the cold steps of an indexed (+ decode) bench run: dispatch runs of
+    cache-streaming read, k_step_fast, k_proj_mfma, k_merge_cols (indexed)
+    and of read, k_proj_mfma, k_merge_fused (the decode step's two launches,
+    when the run's fastest mode was decode).  Each counter is scaled by what
+    it reads for a plain device copy of known size (the --copy-probe run).
+    Mean |I| and the algorithmic bytes come from the bench run's JSON line.
+    Returns the summary text that measured_traffic() reads."""
     with open(bench_out) as f:
         line = [l for l in f if l.startswith("{") and '"metric"' in l][-1]
     b = json.loads(line)
     mean_active = float(b["config"]["mean_active"])
-    alg_proj = float(b["roofline"]["bytes_per_launch"])
-    alg_call = float(b["roofline"]["draft_call"]["bytes"])
-    step_kernels = (("elementwise_kernel_manual_unroll",), ("k_step_fast",), PROJ_KERNELS, ("k_merge_cols",))
-    per = {}
-    steps = {}
-    pname = None
+    rf = b["roofline"]
+    if rf.get("draft_call") is None:
+        raise SystemExit(f"{bench_out}: needs a run of the indexed mode")
+    with_decode = b["config"]["mode"] == "decode"
+    alg_dec = float(rf["bytes_per_launch"]) if with_decode else None
+    alg_proj = float(rf.get("projection_stage", rf)["bytes_per_launch"])
+    alg_call = float(rf["draft_call"]["bytes"])
+    patterns = {"indexed": (("elementwise_kernel_manual_unroll",), ("k_step_fast",), PROJ_KERNELS, ("k_merge_cols",))}
+    if with_decode:
+        patterns["decode"] = (("elementwise_kernel_manual_unroll",), PROJ_KERNELS, ("k_merge_fused",))
+    per, steps, pname = {}, {}, None
     for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path)
-        acc = {"k_step_fast": [], "proj": [], "k_merge_cols": []}
-        for i in range(len(rows) - 3):
-            names = [kernel_base_name(rows[i + j][0]) for j in range(4)]
-            if all(names[j] in step_kernels[j] for j in range(4)):
-                pname = names[2]
-                for j, key in ((1, "k_step_fast"), (2, "proj"), (3, "k_merge_cols")):
-                    acc[key].append(rows[i + j][1])
-        steps[tag] = len(acc["proj"])
-        if steps[tag] == 0:
-            raise SystemExit(f"{path}: no cold indexed step (read, k_step_fast, projection, k_merge_cols) found")
-        per[tag] = {k: float(np.mean(v)) for k, v in acc.items()}
+        acc = {(mode, j): [] for mode, pat in patterns.items() for j in range(1, len(pat))}
+        for mode, pat in patterns.items():
+            for i in range(len(rows) - len(pat) + 1):
+                names = [kernel_base_name(rows[i + j][0]) for j in range(len(pat))]
+                if all(names[j] in pat[j] for j in range(len(pat))):
+                    if mode == "indexed":
+                        pname = names[2]
+                    for j in range(1, len(pat)):
+                        acc[(mode, j)].append(rows[i + j][1])
+        for mode in patterns:
+            steps[(tag, mode)] = len(acc[(mode, 1)])
+            if steps[(tag, mode)] == 0:
+                raise SystemExit(f"{path}: no cold {mode} step found")
+        per[tag] = {key: float(np.mean(v)) for key, v in acc.items()}
     cal = {}
     for tag, path in (("FETCH_SIZE", copy_fetch_csv), ("WRITE_SIZE", copy_write_csv)):
-        rows = [v for n, v in _counter_rows(path) if "copyBuffer" in kernel_base_name(n)]
-        cal[tag] = rows
+        cal[tag] = [v for n, v in _counter_rows(path) if "copyBuffer" in kernel_base_name(n)]
     # The copy probe moves COPY_BYTES each way; the calibration is true KiB / counted KiB.
     true_kib = COPY_PROBE_BYTES / 1024.0
     f_cal = true_kib / float(np.median(cal["FETCH_SIZE"]))
     w_cal = true_kib / float(np.median(cal["WRITE_SIZE"]))
     kib = 1024.0
-    proj = (per["FETCH_SIZE"]["proj"] * f_cal + per["WRITE_SIZE"]["proj"] * w_cal) * kib
-    merge = (per["FETCH_SIZE"]["k_merge_cols"] * f_cal + per["WRITE_SIZE"]["k_merge_cols"] * w_cal) * kib
+    by = lambda key: (per["FETCH_SIZE"][key] * f_cal + per["WRITE_SIZE"][key] * w_cal) * kib
+    proj, merge = by(("indexed", 2)), by(("indexed", 3))
     call = proj + merge
-    out = [
-        f"# HBM traffic of one draft-head call ({pname} + k_merge_cols), cold indexed steps of the",
-        f"# {workload} workload ({b['config']['workload']}; mean |I| = {mean_active:.2f} over the timed steps).",
-        f"# bench.py reads traffic_bytes_per_call from this file while source_sha256 matches its kernel sources",
-        f"# and its mean |I| is within 5% of this value.",
+    head = [
+        f"# HBM traffic per launch, cold steps of the {workload} workload ({b['config']['workload']};",
+        f"# mean |I| = {mean_active:.2f} over the timed steps): "
+        + (f"the decode step (nanospec_decode_step: {pname} with the state update in block 0, then "
+           f"k_merge_fused) and " if with_decode else "")
+        + f"the separate draft-head call ({pname} + k_merge_cols, indexed).",
+        f"# bench.py reads the traffic_bytes_* values from this file while source_sha256 matches its kernel",
+        f"# sources and its mean |I| is within 5% of this value.",
         f"source_sha256: {kernel_source_hash()}",
-        f"mode: indexed",
+        f"modes: indexed" + (" decode" if with_decode else ""),
         f"mean_active: {mean_active:.2f}",
+    ]
+    if with_decode:
+        dproj, dmerge = by(("decode", 1)), by(("decode", 2))
+        head += [f"traffic_bytes_per_decode_project: {dproj:.0f}",
+                 f"algorithmic_bytes_per_decode_project: {alg_dec:.0f}",
+                 f"traffic_bytes_per_decode_step: {dproj + dmerge:.0f}"]
+    out = head + [
         f"traffic_bytes_per_call: {call:.0f}",
         f"algorithmic_bytes_per_call: {alg_call:.0f}",
         f"traffic_bytes_per_projection: {proj:.0f}",
@@ -612,16 +692,25 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
         f"fetch_calibration: {f_cal:.4f}",
         f"write_calibration: {w_cal:.4f}",
         "",
-        f"Per-dispatch means over the cold steps (dispatch run: cache-streaming read, k_step_fast, {pname},",
-        "k_merge_cols), KiB as the counters read them:",
+        "Per-dispatch means over the cold steps, KiB as the counters read them:",
     ]
     for tag in ("FETCH_SIZE", "WRITE_SIZE"):
-        out.append(f"  {tag} ({steps[tag]} steps): " + ", ".join(f"{pname if k == 'proj' else k} {v:.1f}"
-                                                                 for k, v in per[tag].items()))
+        dec = (f"decode ({steps[(tag, 'decode')]} steps) {pname} (with the state update) "
+               f"{per[tag][('decode', 1)]:.1f}, k_merge_fused {per[tag][('decode', 2)]:.1f}; " if with_decode else "")
+        out.append(f"  {tag}: {dec}indexed ({steps[(tag, 'indexed')]} steps) k_step_fast "
+                   f"{per[tag][('indexed', 1)]:.1f}, {pname} {per[tag][('indexed', 2)]:.1f}, k_merge_cols "
+                   f"{per[tag][('indexed', 3)]:.1f}")
     out += [
         f"  copy calibration: a {COPY_PROBE_BYTES}-byte device copy (__amd_rocclr_copyBuffer) reads FETCH_SIZE "
         f"{np.median(cal['FETCH_SIZE']):.1f} KiB and WRITE_SIZE {np.median(cal['WRITE_SIZE']):.1f} KiB",
         f"  (true {true_kib:.0f} KiB each), so FETCH_SIZE is scaled by {f_cal:.4f} and WRITE_SIZE by {w_cal:.4f}.",
+    ]
+    if with_decode:
+        out.append(f"  decode step, first launch: {dproj / 1e6:.3f} MB, {dproj / alg_dec:.3f}x its algorithmic bytes "
+                   f"(I_(t+1) rows, h, ids, the state update's ring, tuples and bitmap; it also reads the rows of "
+                   f"the tuple and I_t ids that are not in I_(t+1), and writes partial sums); whole step "
+                   f"{(dproj + dmerge) / 1e6:.3f} MB.")
+    out += [
         f"  draft call: {call / 1e6:.3f} MB per call, {call / alg_call:.3f}x the algorithmic bytes.",
         f"  {pname} alone: {proj / 1e6:.3f} MB per launch, {proj / alg_proj:.3f}x its algorithmic bytes "
         f"(active rows, h, row ids; the partial sums it writes are implementation bytes).",
@@ -661,6 +750,7 @@ def sq_summary(paths, kernels=("k_proj_msplit", "k_proj_mfma")):
 PROJ_KERNELS = ("k_proj_mfma", "k_proj_msplit", "k_proj_valu")
 
 STEP_PATTERNS = {
+    "decode": (PROJ_KERNELS, ("k_merge_fused",)),
     "indexed": (("k_step_fast",), PROJ_KERNELS, ("k_merge_cols",)),
     "packed": (("k_step_fast",), ("k_gather",), PROJ_KERNELS, ("k_merge_cols",)),
     "slots": (("k_step_fast",), ("k_pack_plan",), ("k_gather",), PROJ_KERNELS, ("k_merge_cols",)),
@@ -680,7 +770,7 @@ def step_trace_summary(path):
     """Per-kernel spans (End - Start, us) of the cold decode steps in a
     kernel trace of a bench run: dispatch runs of the cache-streaming read
     followed by one mode's step kernels, consecutive on one queue.  Also the
-    per-step sum of the indexed step's kernels."""
+    per-step sums of the decode and indexed steps' kernels."""
     import csv
     ks = []
     with open(path) as f:
@@ -690,7 +780,7 @@ def step_trace_summary(path):
     ks.sort()
     read = "elementwise_kernel_manual_unroll"
     lines = ["| mode | steps | kernel | mean | median | min | max |", "|---|---|---|---|---|---|---|"]
-    step_sums = []
+    step_sums = {"decode": [], "indexed": []}
     for mode, pat in STEP_PATTERNS.items():
         spans = {}                                        # kernel name -> spans, in step order
         n = 0
@@ -702,16 +792,18 @@ def step_trace_summary(path):
                 n += 1
                 for q in seq:
                     spans.setdefault(q[2], []).append((q[1] - q[0]) / 1e3)
-                if mode == "indexed":
-                    step_sums.append(sum((q[1] - q[0]) / 1e3 for q in seq))
+                if mode in step_sums:
+                    step_sums[mode].append(sum((q[1] - q[0]) / 1e3 for q in seq))
         for name, sp in spans.items():
             v = np.array(sp)
             lines.append(f"| {mode} | {n} | {name} | {v.mean():.3f} | {np.median(v):.3f} | {v.min():.3f} | "
                          f"{v.max():.3f} |")
-    if step_sums:
-        v = np.array(step_sums)
+    for mode, sums in step_sums.items():
+        if not sums:
+            continue
+        v = np.array(sums)
         lines.append("")
-        lines.append(f"Per-step kernel time (indexed, cold; the sum of its kernels' spans over {len(v)} steps): "
+        lines.append(f"Per-step kernel time ({mode}, cold; the sum of its kernels' spans over {len(v)} steps): "
                      f"p10 {np.percentile(v, 10):.2f} us, median {np.median(v):.2f} us, "
                      f"p90 {np.percentile(v, 90):.2f} us.")
     return "\n".join(lines)
@@ -1406,8 +1498,9 @@ def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
     about 15.5k ids active) or the Qwen-2.5-7B-shaped head (V=151936,
     d=3584, W_max=3072, M=60, k=10): cold per-step times of the state update
     and the INDEXED draft head (graph replay, the cache-streaming read and
-    the state-only graph subtracted), and the full-vocabulary head at the
-    same M.  W and h are drawn on the GPU from a seeded generator with the
+    the state-only graph subtracted), of the same step as one
+    nanospec_decode_step call (two launches at W_max <= 3072, three above),
+    and the full-vocabulary head at the same M.  W and h are drawn on the GPU from a seeded generator with the
     workload's distributions (N(0, 0.02^2) and N(0, 1), bf16)."""
     cfg = WL.get_config(name)
     T = warm + steps
@@ -1425,13 +1518,21 @@ def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
     ws = ns.alloc_workspace(cfg.w_max, cfg.M, cfg.k, cfg.d)
     tids = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
     tvals = torch.empty((cfg.M, cfg.k), device="cuda")
+    wsdec = ns.alloc_decode_workspace(cfg.w_max, cfg.n_tree + cfg.k_ver, cfg.M, cfg.k, cfg.d)
 
-    def init():
+    def decode(t):
+        ns.nanospec_decode_step(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n, W, cfg.V, cfg.d,
+                                ns.NS_BF16, hs[t], cfg.M, cfg.k, tids, tvals, wsdec)
+
+    def init(with_decode=False):
         ns.nanospec_state_reset(st)
         ns.nanospec_stream_append(st, prompt, prompt.numel(), 0)
         ns.nanospec_active_vocab(st, ids, n)
         for t in range(warm):
-            ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n)
+            if with_decode and t == warm - 1:
+                decode(t)                          # the state keeps I_t for the timed decode steps
+            else:
+                ns.nanospec_step_update(st, trees[t], trees[t].numel(), vers[t], vers[t].numel(), ids, n)
 
     sizes = []
 
@@ -1453,15 +1554,20 @@ def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
     torch.cuda.synchronize()
     n_mean = float(torch.stack(sizes).float().mean().item())
 
-    def timed(fn):
-        init()
+    def decode_body():
+        for t in range(warm, T):
+            flush(t)
+            decode(t)
+
+    def timed(fn, with_decode=False):
+        init(with_decode)
         torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
             fn()
         ts = []
         for _ in range(5):
-            init()
+            init(with_decode)
             torch.cuda.synchronize()
             a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -1475,6 +1581,7 @@ def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
     t_f = timed(body(False, False))
     t_s = timed(body(True, False))
     t_a = timed(body(True, True))
+    t_d = timed(decode_body, with_decode=True)
     draft_us = (t_a - t_s) / steps * 1e3
     s = cfg.elem_bytes
     draft_bytes = n_mean * cfg.d * s + cfg.M * cfg.d * s + 4 * n_mean + 8 * cfg.M * cfg.k
@@ -1498,12 +1605,13 @@ def config_leg(torch, ns, WL, flush, name, steps=32, warm=16):
     res = {"workload": f"{name}: V={cfg.V} d={cfg.d} W_max={cfg.w_max} M={cfg.M} k={cfg.k}, {stream_kind}, "
                        f"cold, hipGraph replay of {steps} steps",
            "mean_active": n_mean, "step_us": step_us, "state_update_us": (t_s - t_f) / steps * 1e3,
+           "decode_step_us": (t_d - t_f) / steps * 1e3,
            "draft_us": draft_us, "draft_GBps": draft_bytes / (draft_us * 1e-6) / 1e9,
            "draft_frac_of_peak": draft_bytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
            "dense_ours_ms": t_ours, "dense_torch_ms": t_vendor,
            "dense_ours_GBps": cfg.V * cfg.d * s / (t_ours * 1e-3) / 1e9,
-           "speedup_vs_dense": min(t_ours, t_vendor) * 1e3 / step_us}
-    del st, ws, wsd, W, hs
+           "speedup_vs_dense": min(t_ours, t_vendor) * 1e3 / min(step_us, (t_d - t_f) / steps * 1e3)}
+    del st, ws, wsd, wsdec, W, hs
     return res
 
 

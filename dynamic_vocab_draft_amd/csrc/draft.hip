@@ -41,10 +41,12 @@
 //       k from the chunks' keys, unless every live column is in chunk 0,
 //       which then writes the result itself.  No k rounds of cross-lane
 //       reductions.
+#include <atomic>
 #include <mutex>
 
 #include "common.hpp"
 #include "select.hpp"
+#include "state_fast.hpp"
 
 namespace {
 
@@ -283,13 +285,39 @@ __device__ __forceinline__ void wait_batches(int left) {
   else __builtin_amdgcn_s_waitcnt(vm_imm(0));
 }
 
-template <int NMT, int RT, bool F16, int HI, int NB, bool NT>
+// The first launch of the fused decode step (nanospec_decode_step): the
+// projection with FUSE runs the window-state update in block 0, beside the
+// projection in the other blocks, which cannot depend on it.  They project a
+// superset of I_{t+1}: columns [0, nd + nv) are the step's tuple entries and
+// [cbase, cbase + n_cur) are I_t (the state's cur; cbase is nd + nv rounded
+// up to a tile); every id of I_{t+1} is in one of them.  Slice-0 blocks write
+// each live column's id to colid and, for a tuple column, whether its id is
+// in I_t (the state's bitmap still holds I_t) to told; the update writes
+// which columns hold ids of I_{t+1} (FuseCtl).  W_max is at most kPThreads
+// kFuseCU and a multiple of 4.
+constexpr int kFuseCU = 12;                       // I_t entries per state-update thread
+constexpr int kFuseRU = 3;                        // 16-byte ring loads per state-update thread
+constexpr int kFuseMaxWmax = kPThreads * kFuseCU;
+static_assert(kFuseMaxWmax <= kPThreads * kFuseRU * 4, "ring loads cover W_max");
+
+struct FuseArgs {
+  ns_state_view v;
+  const int32_t* dids;
+  int nd;
+  const int32_t* vids;
+  int nv;
+  FuseCtl fc;
+  int32_t* colid;
+  uint8_t* told;
+};
+
+template <int NMT, int RT, bool F16, int HI, int NB, bool NT, bool FUSE>
 __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict__ rows, int mode,
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
                                                          int S, int adapt, float* __restrict__ part,
-                                                         BatchStrides bs, int B, int tile_step) {
+                                                         BatchStrides bs, int B, int tile_step, FuseArgs fa) {
   constexpr int KC = kDmaKC;
   constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
   constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction
@@ -311,13 +339,20 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   static_assert(sizeof(f32x4_t) * kPW * RT * NMT * NS_WAVE <= (NMT <= 2 ? sizeof(abuf) : sizeof(bbuf)),
                 "wave tiles fit the reused buffer");
   auto red = reinterpret_cast<f32x4_t (*)[RT][NMT][NS_WAVE]>(NMT <= 2 ? &abuf[0][0][0] : &bbuf[0][0][0]);
+  if constexpr (FUSE) {
+    if (blockIdx.x == 0) {                              // the window-state update, in abuf's LDS
+      step_fast_body<int4, kFuseRU, kPThreads, kFuseCU>((int4*)&abuf[0][0][0], 0, fa.v, fa.dids, fa.nd, fa.vids, fa.nv,
+                                                        nullptr, nullptr, nullptr, fa.fc);
+      return;
+    }
+  }
   // The 1-D grid is read as (tile group, sequence, slice, XCD lane), tile
   // group slowest: L = ((tg B + b) S + s) 8 + x.  Row tile tg 8 + x of
   // sequence b and slice s.  Dispatch then runs over the low (live) tiles of
   // every sequence before any sequence's high tiles, and every slice of a
   // tile goes to the same XCD (L mod 8).  kblk = (tg S + s) 8 + x is the
   // block's index among its sequence's blocks; for B = 1 it is L.
-  const unsigned L = blockIdx.x;
+  const unsigned L = blockIdx.x - (FUSE ? 1u : 0u);
   const int seq = (int)((L / (8u * (unsigned)S)) % (unsigned)B);
   const unsigned kblk = (L / (8u * (unsigned)S * (unsigned)B)) * (8u * (unsigned)S) + L % (8u * (unsigned)S);
   {
@@ -340,12 +375,26 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   int r0 = (int)((kblk / (8 * S)) * 8 + (kblk & 7)) * (kTile * RT);
   int split = (int)((kblk >> 3) % S);
   // Independent loads first: the active count and this lane's row ids.
-  const int n = clamp_n(n_dev, n_max);
+  // Fused: |I_t| and the ids of the tuple and I_t columns; a column is live
+  // iff it holds an entry of either.
+  const int cb = fa.fc.cbase, nt = fa.nd + fa.nv;
+  int n_old = 0;
+  if constexpr (FUSE) {
+    n_old = *fa.fc.n_cur;
+    n_old = n_old < 0 ? 0 : (n_old > fa.v.w_max ? fa.v.w_max : n_old);
+  }
+  auto col_id = [&](int row) -> int {
+    if (row < nt) return row < fa.nd ? fa.dids[row] : fa.vids[row - fa.nd];
+    return (row >= cb && row - cb < fa.v.w_max) ? fa.fc.cur[row - cb] : -1;
+  };
+  auto col_live = [&](int row) { return row < nt || (row >= cb && row < cb + n_old); };
+  const int n = FUSE ? n_max : clamp_n(n_dev, n_max);
   int gid[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const int row = r0 + r * kTile + i;
-    gid[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+    if constexpr (FUSE) gid[r] = row < n_max ? col_id(row) : -1;
+    else gid[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
   }
   // With `adapt`, S was launched for a few live rows: if n calls for fewer
   // slices, the block maps itself again and reloads its row ids (one more
@@ -368,11 +417,24 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // for as long as they hold live rows.
   for (;;) {
   if (r0 >= n) return;                                  // block-uniform: nothing live here
+  if (FUSE && r0 >= nt && (r0 >= cb + n_old || r0 + kTile * RT <= cb)) return;   // block-uniform
   bool ok[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const int row = r0 + r * kTile + i;
-    ok[r] = row < n && gid[r] >= 0 && gid[r] < V;
+    ok[r] = (FUSE ? col_live(row) : row < n) && gid[r] >= 0 && gid[r] < V;
+  }
+  // The merge reads each column's id from colid and, for a tuple column,
+  // whether its id is in I_t from told (its word of the I_t bitmap is
+  // requested here and written out after the rows).
+  uint32_t obits[RT];
+  if (FUSE && split == 0 && lane < kTile) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = r0 + r * kTile + i;
+      if (row < n_max) fa.colid[row] = ok[r] ? gid[r] : -1;
+      obits[r] = (row < nt && ok[r]) ? fa.v.bitmap[gid[r] >> 5] : 0u;
+    }
   }
   // Load sources.  Row tr of a tile is requested by the lanes of instruction
   // tr / RPI with L / CPR == tr % RPI; lanes 0..15 hold the tile's row ids.
@@ -524,7 +586,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int row = r0 + tile_step + r * kTile + i;
-      gid_next[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
+      if constexpr (FUSE) gid_next[r] = row < n_max ? col_id(row) : -1;
+      else gid_next[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
     }
   }
   if (nb > 0) {
@@ -568,6 +631,13 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
     const int m = t * 16 + (l2 & 15);
     const int q0 = r0 + r * kTile + (l2 >> 4) * 4;
     if (m < M && q0 < n_max) *(f32x4_t*)(part + ((size_t)split * M + m) * NP + q0) = sum;
+  }
+  if (FUSE && split == 0 && lane < kTile) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = r0 + r * kTile + i;
+      if (row < nt) fa.told[row] = (uint8_t)((obits[r] >> (gid[r] & 31)) & 1u);
+    }
   }
   if (tile_step == 0) return;                           // launch-uniform
   r0 += tile_step;
@@ -943,6 +1013,141 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_cols(const float* __res
   }
 }
 
+// k_merge_fused: the merge of the fused decode step (one chunk of at most
+// 4096 columns, logits only).  Block m < M sums the S partials of every live
+// column of hidden row m (the tuple columns and the I_t columns), keeps
+// those the state update flagged as members of I_{t+1}, with the ids the
+// projection wrote, and selects their top k exactly as k_merge_cols does.
+// The first 2048 columns are requested with |I_t|, the rest only when
+// |I_t| reaches them.  Block M turns the update's bitmap of I_{t+1}
+// (next_bm) into the state's bitmap and the ascending ids, written to
+// active_ids and to the state's cur (with their count to n_active and
+// n_cur), and adds the step's appended entries (hdr[1]) to |S|; no other
+// block of this launch reads any of them.
+constexpr int kFuseCompactWords = 8;                 // bitmap words per thread of block M, at most
+
+// Bitmap words per thread of block M: 4 or 8, as few as cover ceil(V/32).
+__host__ __device__ __forceinline__ int fused_compact_wq(int V) {
+  return ((V + 31) >> 5) <= 4 * kMergeThreads ? 4 : 8;
+}
+
+__device__ __forceinline__ void fused_compact(const uint32_t* __restrict__ next_bm, uint32_t* __restrict__ bitmap,
+                                              int V, int w_max, int32_t* __restrict__ ids,
+                                              int32_t* __restrict__ n_ids, int32_t* __restrict__ cur,
+                                              int32_t* __restrict__ n_cur, int64_t* __restrict__ len, int appended) {
+  __shared__ int sh_scan[kMergeThreads / NS_WAVE + 1];
+  const int tid = threadIdx.x;
+  const int words = (V + 31) >> 5;
+  const int wq = fused_compact_wq(V);
+  const int w0 = tid * wq;
+  uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+  if (w0 < words) {                                   // next_bm has next_words(V) words, zero past ceil(V/32)
+    a = *(const uint4*)(next_bm + w0);
+    if (wq > 4) b = *(const uint4*)(next_bm + w0 + 4);
+  }
+  const int pc = __popc(a.x) + __popc(a.y) + __popc(a.z) + __popc(a.w) + __popc(b.x) + __popc(b.y) +
+                 __popc(b.z) + __popc(b.w);
+  if (w0 < words) {
+    if (wq > 4) bm_store8(bitmap, w0, words, a, b, true);
+    else bm_store4(bitmap, w0, words, a, true);
+  }
+  int tot = 0;
+  int off = ns::block_excl_scan<kMergeThreads>(pc, sh_scan, &tot);
+  // A thread holds a few ids at most, so the stores of one wave fall on
+  // nearly consecutive positions.
+  auto emit = [&](uint32_t x, int w) {
+    while (x) {
+      const int id = (w << 5) + (__ffs(x) - 1);
+      if (off < w_max) {
+        ids[off] = id;
+        cur[off] = id;
+      }
+      ++off;
+      x &= x - 1u;
+    }
+  };
+  emit(a.x, w0); emit(a.y, w0 + 1); emit(a.z, w0 + 2); emit(a.w, w0 + 3);
+  emit(b.x, w0 + 4); emit(b.y, w0 + 5); emit(b.z, w0 + 6); emit(b.w, w0 + 7);
+  if (tid == 0) {
+    const int n = tot < w_max ? tot : w_max;
+    *n_ids = n;
+    *n_cur = n;
+    *len += appended;
+  }
+}
+
+template <int SPT>
+__global__ __launch_bounds__(kMergeThreads) void k_merge_fused(const float* __restrict__ part, int S, int n_max,
+                                                               int M, int cbase, int nt,
+                                                               const int32_t* __restrict__ colid,
+                                                               const uint8_t* __restrict__ flags,
+                                                               const uint8_t* __restrict__ told,
+                                                               const int32_t* __restrict__ hdr, int V, int k,
+                                                               int32_t* __restrict__ out_ids,
+                                                               float* __restrict__ out_vals,
+                                                               const uint32_t* __restrict__ next_bm,
+                                                               uint32_t* __restrict__ bitmap,
+                                                               int32_t* __restrict__ act_ids,
+                                                               int32_t* __restrict__ n_act,
+                                                               int32_t* __restrict__ cur, int32_t* __restrict__ n_cur,
+                                                               int64_t* __restrict__ len, int w_max) {
+  constexpr int U = kMergeCols;
+  __shared__ SelectSmem sm;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  if (m == M) {                                       // block-uniform
+    fused_compact(next_bm, bitmap, V, w_max, act_ids, n_act, cur, n_cur, len, hdr[1]);
+    return;
+  }
+  const float* prow = part + (size_t)m * col_pitch(n_max);
+  const size_t sstride = (size_t)M * col_pitch(n_max);
+  // One round of loads: |I_t| and every column's partials, id and flag
+  // (indices clamped, so all in bounds).
+  constexpr int U1 = 2;                              // columns per thread requested with |I_t|
+  const int n_old_raw = hdr[0];
+  float pv[U][SPT];
+  int gv[U], fv[U];
+  auto request = [&](int u) {
+    const int j = tid + u * kMergeThreads;
+    const int jc = j < n_max ? j : n_max - 1;
+    gv[u] = colid[jc];
+    fv[u] = flags[jc];
+    load_slices<SPT>(prow + jc, sstride, S, pv[u]);
+  };
+#pragma unroll
+  for (int u = 0; u < U1; ++u) request(u);
+  const int in_old = tid < nt ? told[tid] : 0;       // tuple columns are all below kMergeThreads
+  NS_ISSUE_FENCE();
+  const int n_old = n_old_raw < 0 ? 0 : (n_old_raw > w_max ? w_max : n_old_raw);
+  const bool more = cbase + n_old > U1 * kMergeThreads;           // block-uniform
+  if (more) {
+#pragma unroll
+    for (int u = U1; u < U; ++u) request(u);
+    NS_ISSUE_FENCE();
+  }
+  float val[U];
+  int gid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = tid + u * kMergeThreads;
+    const bool live = (u < U1 || more) && j < n_max && (j < nt ? in_old == 0 : (j >= cbase && j < cbase + n_old)) &&
+                      fv[u] != 0 && gv[u] >= 0 && gv[u] < V;
+    val[u] = live ? sum_slices<SPT>(pv[u], S) : 0.f;
+    gid[u] = live ? gv[u] : -1;
+  }
+  block_select_topk<U>(val, gid, k, n_max, sm, [&](int r, uint64_t x) {
+    out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
+    out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
+  });
+}
+
+// Fallback of the decode step: the state's cur / n_cur from I_{t+1}.
+__global__ void k_copy_cur(int32_t* __restrict__ cur, int32_t* __restrict__ n_cur, const int32_t* __restrict__ ids,
+                           const int32_t* __restrict__ n, int w_max) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g == 0) *n_cur = *n;
+  for (int j = g; j < w_max; j += gridDim.x * blockDim.x) cur[j] = ids[j];
+}
+
 // k_merge_keys: the final top k of hidden row m over the C chunks' keys
 // (nk = C * k of them, at most PER per thread).  With LOGP the chunks'
 // (max, sum) pairs give the row's log-sum-exp, combined in chunk order.
@@ -1068,6 +1273,38 @@ int max_splits(int n_max, int M, int d, int B) {
   return a > b ? a : b;
 }
 
+// Blocks of the single-sequence MFMA projection for M hidden rows that the
+// current device holds at once, less one (the state-update block of the
+// fused decode step), or 0 when the runtime cannot tell.  Cached per device
+// and instance.
+int resident_cap(int M) {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs][5];
+  const int inst = M <= 8 ? 0 : (M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 48 ? 3 : 4)));
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int c = cache[dev][inst].load(std::memory_order_relaxed);
+  if (c != 0) return c > 0 ? c : 0;
+  const void* fn = inst == 0   ? (const void*)k_proj_mfma<1, 1, false, 1, 4, true, false>
+                   : inst == 1 ? (const void*)k_proj_mfma<1, 1, false, 2, 4, true, false>
+                   : inst == 2 ? (const void*)k_proj_mfma<2, 2, false, 1, 2, true, false>
+                   : inst == 3 ? (const void*)k_proj_mfma<3, 2, false, 6, 2, true, false>
+                               : (const void*)k_proj_mfma<4, 2, false, 8, 2, true, false>;
+  int cus = 0, bpc = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kPThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    c = -1;
+  } else {
+    c = cus * bpc - 1 > 0 ? cus * bpc - 1 : -1;
+  }
+  cache[dev][inst].store(c, std::memory_order_relaxed);
+  return c > 0 ? c : 0;
+}
+
 template <bool BF16>
 int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V,
                 int d, const void* h, int M, float* part, int B, const BatchStrides& bs, hipStream_t stream) {
@@ -1090,19 +1327,19 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   return ns_launch_status();
 }
 
-template <int NMT, int RT, bool F16, int HI, int NB, bool NT>
+template <int NMT, int RT, bool F16, int HI, int NB, bool NT, bool FUSE>
 void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
-                   float* part, const BatchStrides& bs, int tile_step) {
-  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB, NT>), dim3(blocks), dim3(kPThreads), 0, stream,
-                     (const uint4*)rows, mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt, part, bs,
-                     B, tile_step);
+                   float* part, const BatchStrides& bs, int tile_step, const FuseArgs& fa) {
+  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB, NT, FUSE>), dim3(blocks + (FUSE ? 1u : 0u)), dim3(kPThreads),
+                     0, stream, (const uint4*)rows, mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt,
+                     part, bs, B, tile_step, fa);
 }
 
 template <bool F16>
 int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_t* n_dev, int n_max, int V, int d,
                 const void* h, int M, int S, int adapt, float* part, int B, const BatchStrides& bs,
-                hipStream_t stream) {
+                hipStream_t stream, const FuseArgs* fa = nullptr, int max_blocks = 0) {
   const int dv = d / 8;
   const bool msplit = use_msplit(n_max, M, B);
   // Batches of one slice per tile (below) with one hidden tile of at most 8
@@ -1112,7 +1349,7 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   // CU (40 KiB of LDS at rt = 4, four blocks) and one hidden-row load per
   // 4 rt row loads.  Measured on the Llama-shaped batch (mean |I| about
   // 780): B = 64 0.56 -> 0.66 of HBM peak, B = 32 0.53 -> 0.59.
-  const bool batched = B > 1 && S == 1 && !adapt && !msplit;
+  const bool batched = !fa && B > 1 && S == 1 && !adapt && !msplit;
   int rt = pick_rt(M, n_max, B);
   int nb_bufs = 4;
   if (batched && M <= 8) {
@@ -1156,10 +1393,36 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
       tile_step = (int)hint_tiles * kTile * rt;
     }
   }
+  // With max_blocks (a single sequence whose live row count only the device
+  // knows), the grid is cut to whole groups of 8 tiles x S slices within
+  // max_blocks, all resident at once, and each block steps on by the tiles
+  // the grid covers while its rows are live.  Past the live rows a full grid
+  // is mostly blocks that only read the count and exit, and with one block
+  // per CU they queue behind the live ones.  Qwen-shaped head (M = 60, one
+  // block per CU, S = 7): fused decode-step projection over about 1080 live
+  // of 3152 columns 9.0 -> 7.2 us, separate draft head over about 1000 live
+  // of 3072 rows 6.2 us either way; fewer slices so that 1280 rows fit one
+  // pass (S = 6) measured slower (7.7 us separate).
+  if (max_blocks > 0 && !batched && !adapt && B == 1) {
+    const unsigned group = 8u * (unsigned)S;
+    const unsigned lim = (unsigned)max_blocks / group * group;
+    if (lim > 0 && lim < per_seq) {
+      per_seq = lim;
+      tile_step = (int)(lim / (unsigned)S) * kTile * rt;
+    }
+  }
   const unsigned blocks = per_seq * (unsigned)B;
+#define NS_LAUNCH_MFMA_ONLY(NMTV, RTV, HIV, NBV, NTV)                                                         \
+  launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, false>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, \
+                                                      S, adapt, part, bs, tile_step, FuseArgs{})
 #define NS_LAUNCH_MFMA(NMTV, RTV, HIV, NBV, NTV)                                                                \
-  launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, S, adapt, \
-                                          part, bs, tile_step)
+  do {                                                                                                          \
+    if (fa)                                                                                                     \
+      launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, true>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, \
+                                                         h, M, S, adapt, part, bs, tile_step, *fa);              \
+    else                                                                                                        \
+      NS_LAUNCH_MFMA_ONLY(NMTV, RTV, HIV, NBV, NTV);                                                            \
+  } while (0)
   if (msplit) {
     hipLaunchKernelGGL((k_proj_msplit<kMsplitRT, F16>), dim3(blocks), dim3(kPThreads), 0, stream, (const uint4*)rows,
                        mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, part, bs, B);
@@ -1173,8 +1436,8 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   switch ((M + 15) / 16) {
     case 1:
       if (M <= 8 && nb_bufs == 1) {
-        if (rt == 4) NS_LAUNCH_MFMA(1, 4, 1, 1, false);
-        else NS_LAUNCH_MFMA(1, 2, 1, 1, false);
+        if (rt == 4) NS_LAUNCH_MFMA_ONLY(1, 4, 1, 1, false);
+        else NS_LAUNCH_MFMA_ONLY(1, 2, 1, 1, false);
       } else if (M <= 8) {
         NS_LAUNCH_MFMA(1, 1, 1, 4, true);
       } else {
@@ -1186,6 +1449,7 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
     default: NS_LAUNCH_MFMA(4, 2, 8, 2, true); break;
   }
 #undef NS_LAUNCH_MFMA
+#undef NS_LAUNCH_MFMA_ONLY
   return ns_launch_status();
 }
 
@@ -1304,7 +1568,7 @@ namespace {
 // partial-sum layout and workspace regions follow from the arguments alone,
 // so nanospec_draft_project and nanospec_draft_select agree.
 struct DraftPlan {
-  int S, SP, adapt, C;
+  int S, SP, adapt, C, max_blocks;
   BatchStrides bs;
   float* part;
   uint64_t* cand;
@@ -1331,6 +1595,11 @@ DraftPlan draft_plan(const int32_t* n_dev, int32_t n_max, int32_t B, int32_t d, 
   // Only a launch sized by kLiveRowsHint can over-split; the kernels then
   // size S from the live n.
   p.adapt = (is_mfma_dtype(dtype) && n_dev != nullptr && M <= 16 && n_max > kLiveRowsHint) ? 1 : 0;
+  // One sequence whose count only the device knows: a grid of resident
+  // blocks (launch_mfma's max_blocks).
+  p.max_blocks = 0;
+  if (is_mfma_dtype(dtype) && n_dev != nullptr && B == 1 && !p.adapt && !use_msplit(n_max, M, B))
+    p.max_blocks = resident_cap(M);
   p.C = merge_chunks(n_max);
   const int esz = dtype == NS_FP32 ? 4 : 2;
   p.bs.rows = 0;                                 // W_head (or one packed buffer) shared
@@ -1352,10 +1621,10 @@ int draft_project(const void* rows, int32_t mode, const int32_t* row_ids, const 
   (void)hipGetLastError();
   if (dtype == NS_BF16)
     return launch_mfma<false>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.part, B, p.bs,
-                              stream);
+                              stream, nullptr, p.max_blocks);
   if (dtype == NS_FP16)
     return launch_mfma<true>(rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.S, p.adapt, p.part, B, p.bs,
-                             stream);
+                             stream, nullptr, p.max_blocks);
   const int mt = pick_mt(M, d, 4);
   if (mt == 0) return NS_EINVAL;
   return launch_valu<false>(mt, rows, mode, row_ids, n_dev, n_max, V, d, h, M, p.part, B, p.bs, stream);
@@ -1441,6 +1710,190 @@ int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* r
                                 float* topk_vals, void* ws, size_t ws_bytes, hipStream_t stream) {
   return draft_call(rows, mode, row_ids, n_dev, n_max, 1, V, d, dtype, h, M, k, logits, topk_ids, topk_vals, ws,
                     ws_bytes, stream, true, parent, lse);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The decode step in one call: nanospec_step_update then the INDEXED draft
+// head on the new active set, with the same results.  When the state's cur
+// holds I_t (the previous call was a decode step on this state) and the
+// shapes allow it, the step takes two launches instead of three: the
+// projection with the state update in its block 0 (k_proj_mfma with FUSE),
+// then k_merge_fused.  Otherwise the three separate launches run and a copy
+// refreshes cur.  nanospec_decode_step_project enqueues the first launch
+// (the first two of three) and records the form in the state's handle;
+// nanospec_decode_step_select enqueues the rest.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kFuseLds = 32768;                  // abuf of every single-sequence MFMA projection instance
+
+struct DecodeLayout {
+  int cbase, n_cols, S, SP;
+  size_t part, colid, flags, told, total;
+};
+
+// Columns: the n_tuple tuple entries, then I_t from the next tile boundary.
+DecodeLayout decode_layout(int32_t w_max, int32_t n_tuple, int32_t M, int32_t d) {
+  DecodeLayout L;
+  L.cbase = ((n_tuple > 0 ? n_tuple : 0) + kTile - 1) / kTile * kTile;
+  L.n_cols = L.cbase + w_max;
+  L.S = launch_splits(false, w_max, M, d, NS_BF16, 1);   // the slices of the separate draft head
+  L.SP = slice_pitch(L.S);
+  L.part = 256;
+  L.colid = L.part + partial_bytes(L.n_cols, M, L.SP, 1);
+  L.flags = L.colid + align256((size_t)L.n_cols * 4);
+  L.told = L.flags + align256((size_t)L.n_cols);
+  L.total = L.told + align256((size_t)(n_tuple > 0 ? n_tuple : 1));
+  return L;
+}
+
+// LDS of the state-update block of the fused step: the bitmap and the
+// tuple ids and first positions.
+size_t fused_state_lds(int V, int n_tuple) {
+  const int nd64 = (n_tuple + NS_WAVE - 1) & ~(NS_WAVE - 1);
+  return ((size_t)kPThreads * fused_wpt<kPThreads>(V) + 2 * (size_t)nd64) * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nanospec_decode_step_workspace_bytes(int32_t w_max, int32_t n_tuple, int32_t M, int32_t k, int32_t d) {
+  if (w_max < 1 || w_max > NS_MAX_WMAX || n_tuple < 0 || n_tuple > 2 * kFastMaxIds) return 0;
+  const size_t sep = nanospec_draft_workspace_bytes(w_max, M, k, d);
+  if (sep == 0) return 0;
+  const size_t fused = decode_layout(w_max, n_tuple, M, d).total;
+  return sep > fused ? sep : fused;
+}
+
+int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, int32_t n_draft,
+                                 const int32_t* ver_ids, int32_t n_ver, int32_t* active_ids, int32_t* n_active,
+                                 const void* w, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
+                                 int32_t k, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!st || !active_ids || !n_active || n_draft < 0 || n_ver < 0) return NS_EINVAL;
+  if ((n_draft > 0 && !draft_ids) || (n_ver > 0 && !ver_ids)) return NS_EINVAL;
+  if (n_draft > kFastMaxIds || n_ver > kFastMaxIds) return NS_EINVAL;
+  const ns_state_view& v = st->view;
+  if (V != v.V) return NS_EINVAL;
+  const int w_max = v.w_max;
+  int rc = draft_check(w, NS_INDEXED, active_ids, w_max, 1, V, d, dtype, h, M, k, ws, ws_bytes);
+  if (rc != NS_OK) return rc;
+  if (ws_bytes < nanospec_decode_step_workspace_bytes(w_max, n_draft + n_ver, M, k, d)) return NS_ECAPACITY;
+  const int nd = st->mode == NS_STREAM_CTX_ONLY ? 0 : n_draft;
+  const int nv = st->mode == NS_STREAM_CTX_ONLY ? 0 : n_ver;
+  const DecodeLayout L = decode_layout(w_max, nd + nv, M, d);
+  const bool fuse = st->cur_valid && is_mfma_dtype(dtype) && (w_max & 3) == 0 && w_max <= kFuseMaxWmax &&
+                    nd + nv <= kPThreads && fused_state_lds(V, nd + nv) <= kFuseLds &&
+                    ((V + 31) >> 5) <= kFuseCompactWords * kMergeThreads && !use_msplit(L.n_cols, M, 1) &&
+                    L.n_cols <= kMergeChunk && L.SP <= 16;
+  nanospec_state::Pending pd;
+  pd.nt = nd + nv;
+  pd.d = d;
+  pd.dtype = dtype;
+  pd.M = M;
+  pd.k = k;
+  pd.ws = ws;
+  pd.ids = active_ids;
+  pd.n = n_active;
+  if (!fuse) {
+    rc = nanospec_step_update(st, draft_ids, n_draft, ver_ids, n_ver, active_ids, n_active, nullptr, stream);
+    if (rc != NS_OK) return rc;
+    const DraftPlan p = draft_plan(n_active, w_max, 1, d, dtype, M, k, ws);
+    rc = draft_project(w, NS_INDEXED, active_ids, n_active, w_max, 1, V, d, dtype, h, M, p, stream);
+    if (rc != NS_OK) return rc;
+    pd.form = 1;
+    st->pending = pd;
+    return NS_OK;
+  }
+  char* base = (char*)ws;
+  FuseArgs fa;
+  fa.v = v;
+  fa.dids = nd > 0 ? draft_ids : v.ring;             // read unconditionally by the update
+  fa.nd = nd;
+  fa.vids = nv > 0 ? ver_ids : v.ring;
+  fa.nv = nv;
+  fa.fc = FuseCtl{v.cur, v.n_cur, (uint8_t*)(base + L.flags), (int32_t*)base, v.next_bm, L.cbase};
+  fa.told = (uint8_t*)(base + L.told);
+  fa.colid = (int32_t*)(base + L.colid);
+  BatchStrides bs{};
+  bs.part = partial_floats(L.n_cols, M, L.SP);
+  // The slices of the separate draft head on I_{t+1} (draft_plan: L.S), so
+  // that both forms sum the same partials, and a grid of resident blocks.
+  const int cap = resident_cap(M);
+  float* part = (float*)(base + L.part);
+  (void)hipGetLastError();
+  rc = dtype == NS_BF16
+           ? launch_mfma<false>(w, NS_INDEXED, nullptr, nullptr, L.n_cols, V, d, h, M, L.S, 0, part, 1, bs, stream,
+                                &fa, cap)
+           : launch_mfma<true>(w, NS_INDEXED, nullptr, nullptr, L.n_cols, V, d, h, M, L.S, 0, part, 1, bs, stream,
+                               &fa, cap);
+  if (rc != NS_OK) return rc;
+  pd.form = 2;
+  st->pending = pd;
+  return NS_OK;
+}
+
+int nanospec_decode_step_select(nanospec_state* st, int32_t* active_ids, int32_t* n_active, int32_t V, int32_t d,
+                                int32_t dtype, int32_t M, int32_t k, int32_t* topk_ids, float* topk_vals, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (!st || !topk_ids || !topk_vals) return NS_EINVAL;
+  const nanospec_state::Pending pd = st->pending;
+  if (pd.form == 0 || pd.ws != ws || pd.ids != active_ids || pd.n != n_active || pd.d != d || pd.dtype != dtype ||
+      pd.M != M || pd.k != k)
+    return NS_EINVAL;
+  const ns_state_view& v = st->view;
+  if (V != v.V) return NS_EINVAL;
+  const int w_max = v.w_max;
+  if (ws_bytes < nanospec_decode_step_workspace_bytes(w_max, pd.nt, M, k, d)) return NS_ECAPACITY;
+  st->pending.form = 0;
+  int rc;
+  if (pd.form == 1) {
+    const DraftPlan p = draft_plan(n_active, w_max, 1, d, dtype, M, k, ws);
+    rc = draft_select(active_ids, n_active, w_max, 1, V, M, k, nullptr, topk_ids, topk_vals, p, false, nullptr,
+                      nullptr, stream);
+    if (rc != NS_OK) return rc;
+    (void)hipGetLastError();
+    const int g = (w_max + 255) / 256;
+    hipLaunchKernelGGL(k_copy_cur, dim3(g > 64 ? 64 : g), dim3(256), 0, stream, v.cur, v.n_cur, active_ids, n_active,
+                       w_max);
+    rc = ns_launch_status();
+    if (rc == NS_OK) st->cur_valid = true;
+    return rc;
+  }
+  const DecodeLayout L = decode_layout(w_max, pd.nt, M, d);
+  char* base = (char*)ws;
+  (void)hipGetLastError();
+#define NS_LAUNCH_FMERGE(SPV)                                                                                    \
+  hipLaunchKernelGGL((k_merge_fused<SPV>), dim3(M + 1), dim3(kMergeThreads), 0, stream, (const float*)(base + L.part), \
+                     L.S, L.n_cols, M, L.cbase, pd.nt, (const int32_t*)(base + L.colid),                          \
+                     (const uint8_t*)(base + L.flags), (const uint8_t*)(base + L.told), (const int32_t*)base, V, k,  \
+                     topk_ids, topk_vals, v.next_bm, v.bitmap, active_ids, n_active, v.cur, v.n_cur, v.len, w_max)
+  switch (L.SP) {
+    case 1: NS_LAUNCH_FMERGE(1); break;
+    case 2: NS_LAUNCH_FMERGE(2); break;
+    case 4: NS_LAUNCH_FMERGE(4); break;
+    case 8: NS_LAUNCH_FMERGE(8); break;
+    case 12: NS_LAUNCH_FMERGE(12); break;
+    default: NS_LAUNCH_FMERGE(16); break;
+  }
+#undef NS_LAUNCH_FMERGE
+  rc = ns_launch_status();
+  if (rc == NS_OK) st->cur_valid = true;
+  return rc;
+}
+
+int nanospec_decode_step(nanospec_state* st, const int32_t* draft_ids, int32_t n_draft, const int32_t* ver_ids,
+                         int32_t n_ver, int32_t* active_ids, int32_t* n_active, const void* w, int32_t V, int32_t d,
+                         int32_t dtype, const void* h, int32_t M, int32_t k, int32_t* topk_ids, float* topk_vals,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!topk_ids || !topk_vals) return NS_EINVAL;
+  const int rc = nanospec_decode_step_project(st, draft_ids, n_draft, ver_ids, n_ver, active_ids, n_active, w, V, d,
+                                              dtype, h, M, k, ws, ws_bytes, stream);
+  if (rc != NS_OK) return rc;
+  return nanospec_decode_step_select(st, active_ids, n_active, V, d, dtype, M, k, topk_ids, topk_vals, ws, ws_bytes,
+                                     stream);
 }
 
 }  // extern "C"

@@ -8,11 +8,16 @@
 // stays on the GPU as a bitmap and is updated by device kernels only.
 //
 // Device layout of a state (caller-owned, 256-byte aligned):
-//   [0, 256)            control: int64 len (|S|), uint32 status
+//   [0, 256)            control: int64 len (|S|), uint32 status, int32 n_cur
 //   ring   int32[w_max] S entry p lives at ring[p % w_max] while p >= |S|-w_max
 //   first  int32[V]     per-id first position inside the current append
 //                       (INT32_MAX between calls)
 //   bitmap uint32[ceil(V/32)]  the active set of the latest rebuild
+//   cur    int32[w_max] the active set in ascending order (n_cur of them),
+//                       as left by the latest nanospec_decode_step
+//   next   uint32[ceil(V/32) rounded up to 8]  the bitmap of I_{t+1}, passed
+//                       between the two launches of a decode step (words
+//                       past ceil(V/32) stay zero)
 //
 // All state kernels run as ONE workgroup of 1024 threads: the per-step work
 // is a few thousand ids and words, so a single CU finishes it in a few
@@ -23,6 +28,7 @@
 
 #include "common.hpp"
 #include "state_internal.hpp"
+#include "state_fast.hpp"
 
 namespace {
 
@@ -199,268 +205,15 @@ __global__ __launch_bounds__(kStateThreads) void k_step(ns_state_view v, const i
   finish(s, len, sh_flag);
 }
 
-// Per-step update with one round of global loads and no LDS copy of the
-// ring.  Every global read the step needs (|S|, the whole ring, both tuples)
-// is issued at once; each thread keeps its ring slots in registers.  C_draft
-// is deduplicated against an LDS copy of the tuple (fine for a draft tree of
-// up to kFastMaxIds ids).  After the tuple positions are scanned, the active
-// bitmap is built in LDS from (a) the new entries that land in the window and
-// (b) the old slots that they do not overwrite: with |S| = len and
-// C = |C_draft| + |C_ver|, the new entries take slots (len + p) mod w_max, so
-// an old slot s survives iff C < w_max and (s - len) mod w_max >= C.  Slots
-// never written hold -1.  The ascending compaction gives each thread a
-// contiguous run of WPT words (at least 8, a multiple of 4, read as 16-byte
-// LDS vectors): the fewest that cover the bitmap, so that every wave has
-// words to scan (a multiple of 8 left the last waves idle for V just above
-// 2^17, and the others with twice the words).
-constexpr int kFastThreads = 512;
-constexpr int kFastMaxIds = kFastThreads;      // one tuple entry per thread
-constexpr int kFastMaxRing = 32 * kFastThreads; // ring entries held in registers
-constexpr size_t kFastLdsMax = 144 * 1024;
-constexpr int kFastStageMinIds = 4096;          // ids from which the compaction is staged in LDS
-
-__host__ __device__ __forceinline__ int fast_wpt(int V) {
-  const int words = (V + 31) >> 5;
-  const int w4 = ((words + kFastThreads * 4 - 1) / (kFastThreads * 4)) * 4;
-  return w4 < 8 ? 8 : w4;
-}
-
-// Ints of LDS that stage the ascending active ids before one coalesced copy
-// to active_ids (at most min(W_max, V) ids), or 0 when the bitmap, the
-// staging area and the largest tuples would not fit kFastLdsMax; then the
-// ids are written to global memory directly from the compaction.
-__host__ __device__ __forceinline__ int fast_stage_ints(int V, int w_max) {
-  const int n = w_max < V ? w_max : V;
-  const int ints = (n + 3) & ~3;
-  const size_t need = ((size_t)kFastThreads * fast_wpt(V) + (size_t)ints + 2 * (size_t)kFastMaxIds) * 4;
-  return need <= kFastLdsMax ? ints : 0;
-}
-
-__device__ __forceinline__ void bm_set(uint32_t* bm, int id) { atomicOr(&bm[id >> 5], 1u << (id & 31)); }
-
-__device__ __forceinline__ void bm_store4(uint32_t* __restrict__ dst, int w, int words, uint4 a, bool vec) {
-  if (vec && w + 4 <= words) {
-    *(uint4*)(dst + w) = a;
-    return;
-  }
-  const uint32_t x[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (w + e < words) dst[w + e] = x[e];
-}
-
-__device__ __forceinline__ void bm_store8(uint32_t* __restrict__ dst, int w, int words, uint4 a, uint4 b, bool vec) {
-  if (vec && w + 8 <= words) {
-    ((uint4*)(dst + w))[0] = a;
-    ((uint4*)(dst + w))[1] = b;
-    return;
-  }
-  const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (w + e < words) dst[w + e] = x[e];
-}
-
-template <typename T, int RU>
-__device__ __forceinline__ void step_fast_body(const ns_state_view& v, const int32_t* draft_ids, int n_draft,
-                                               const int32_t* ver_ids, int n_ver, int32_t* __restrict__ active_ids,
-                                               int32_t* __restrict__ n_active, uint32_t* __restrict__ bitmap_out) {
-  constexpr int EPT = (int)(sizeof(T) / 4);     // ring entries per load
-  constexpr int NW = kFastThreads / NS_WAVE;
-  extern __shared__ int4 lds4[];
-  __shared__ int sh_scan[NW + 1];
-  __shared__ int sh_flag;
-  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), wv = tid / NS_WAVE;
-  const int w_max = v.w_max, V = v.V;
-  const int words = (V + 31) >> 5;
-  const int wpt = fast_wpt(V);
-  const int nd64 = (n_draft + NS_WAVE - 1) & ~(NS_WAVE - 1);
-  const int stage = fast_stage_ints(V, w_max);
-  uint32_t* bm = (uint32_t*)lds4;                                 // kFastThreads * wpt words
-  int32_t* sids = (int32_t*)(bm + (size_t)kFastThreads * wpt);    // stage ids (16-byte aligned)
-  int32_t* dids = sids + stage;                                   // nd64 ids (-1 padding)
-  int32_t* sfp = dids + nd64;                                     // nd64 first positions
-  // ---- one round of global loads --------------------------------------
-  // An index the compiler cannot prove uniform keeps |S| in a vector
-  // register, so no early wait is placed on it ahead of the other loads.
-  int zero;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  const int nl = w_max / EPT;                                     // loads covering the ring
-  const T* src = (const T*)v.ring;
-  T r[RU];
-#pragma unroll
-  for (int u = 0; u < RU; ++u) {
-    const int q = tid + u * kFastThreads;
-    r[u] = src[q < nl ? q : 0];
-  }
-  const int64_t len_in = v.len[zero];
-  const int d_in = draft_ids[tid < n_draft ? tid : 0];
-  const int v_in = ver_ids[tid < n_ver ? tid : 0];
-  NS_ISSUE_FENCE();
-  for (int w = tid; w < kFastThreads * wpt; w += kFastThreads) bm[w] = 0u;
-  for (int q = tid; q < nd64; q += kFastThreads) {
-    dids[q] = q < n_draft ? d_in : -1;
-    sfp[q] = q;
-  }
-  if (tid == 0) sh_flag = 0;
-  __syncthreads();
-  // ---- C_draft first occurrences ---------------------------------------
-  // Position i keeps its id iff no earlier position holds it.  The j range
-  // is split over the waves (wave w compares against ids
-  // [w * nd64 / 8, (w + 1) * nd64 / 8), read as broadcast 4-id LDS words) and
-  // each lane takes positions lane, lane + 64, ...; a smaller equal position
-  // is folded into sfp[i] with an LDS atomicMin.
-  {
-    const int cj = nd64 / NW;                                   // a multiple of 8
-    const int4* d4 = (const int4*)(dids + wv * cj);
-    for (int i = lane; i < n_draft; i += NS_WAVE) {
-      const int x = dids[i];
-      int fp = INT32_MAX;
-      for (int c4 = 0; c4 < cj / 4; c4 += 2) {
-        const int4 qa = d4[c4], qb = d4[c4 + 1];
-        const int j = wv * cj + 4 * c4;
-        fp = min(fp, qa.x == x ? j : INT32_MAX);
-        fp = min(fp, qa.y == x ? j + 1 : INT32_MAX);
-        fp = min(fp, qa.z == x ? j + 2 : INT32_MAX);
-        fp = min(fp, qa.w == x ? j + 3 : INT32_MAX);
-        fp = min(fp, qb.x == x ? j + 4 : INT32_MAX);
-        fp = min(fp, qb.y == x ? j + 5 : INT32_MAX);
-        fp = min(fp, qb.z == x ? j + 6 : INT32_MAX);
-        fp = min(fp, qb.w == x ? j + 7 : INT32_MAX);
-      }
-      if (fp < i) atomicMin(&sfp[i], fp);
-    }
-  }
-  __syncthreads();
-  // ---- tuple positions (C_draft deduplicated, then C_ver as given) ----
-  bool keep_d = false, keep_v = false, bad = false;
-  if (tid < n_draft) {
-    keep_d = d_in >= 0 && d_in < V;
-    bad |= !keep_d;
-    keep_d &= sfp[tid] == tid;
-  }
-  if (tid < n_ver) {
-    keep_v = v_in >= 0 && v_in < V;
-    bad |= !keep_v;
-  }
-  if (bad) sh_flag = 1;
-  int total = 0;
-  const int pre = ns::block_excl_scan<kFastThreads>((keep_d ? 1 : 0) | (keep_v ? 0x10000 : 0), sh_scan, &total);
-  const int Cd = total & 0xFFFF, Cv = total >> 16, C = Cd + Cv;
-  const int64_t len = len_in;
-  int lm;                                               // slot of position |S|
-  if (len < ((int64_t)1 << 31)) lm = (int)((uint32_t)len % (uint32_t)w_max);
-  else lm = (int)(len % (int64_t)w_max);
-  auto slot_of = [&](int p) {                           // (lm + p) mod w_max, p < 2^16
-    int x = lm + p;
-    if (x >= w_max) x -= w_max;
-    if (x >= w_max) x %= w_max;
-    return x;
-  };
-  // New entries: only the last w_max of this step can be inside the window.
-  if (keep_d) {
-    const int p = pre & 0xFFFF;
-    if (p >= C - w_max) {
-      v.ring[slot_of(p)] = d_in;
-      bm_set(bm, d_in);
-    }
-  }
-  if (keep_v) {
-    const int p = Cd + (pre >> 16);
-    if (p >= C - w_max) {
-      v.ring[slot_of(p)] = v_in;
-      bm_set(bm, v_in);
-    }
-  }
-  // Old entries that stay in the window.
-  if (C < w_max) {
-#pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int q = tid + u * kFastThreads;
-      if (q < nl) {
-        const int32_t* e = (const int32_t*)&r[u];
-#pragma unroll
-        for (int x = 0; x < EPT; ++x) {
-          const int slot = q * EPT + x;
-          const int id = e[x];
-          int rel = slot - lm;
-          rel += rel < 0 ? w_max : 0;
-          if (rel >= C && id >= 0 && id < V) bm_set(bm, id);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // ---- ascending compaction; the bitmap goes out from registers ---------
-  const bool out_vec = bitmap_out && ((((uintptr_t)bitmap_out) & 15u) == 0);
-  const uint4* bm4 = (const uint4*)(bm + (size_t)tid * wpt);
-  const int wbase = tid * wpt;
-  int pc = 0;
-  uint4 c0a = bm4[0], c0b = bm4[1];                   // first 8 words stay in registers
-  pc += __popc(c0a.x) + __popc(c0a.y) + __popc(c0a.z) + __popc(c0a.w);
-  pc += __popc(c0b.x) + __popc(c0b.y) + __popc(c0b.z) + __popc(c0b.w);
-  bm_store8(v.bitmap, wbase, words, c0a, c0b, true);
-  if (bitmap_out) bm_store8(bitmap_out, wbase, words, c0a, c0b, out_vec);
-  int c = 2;
-  for (; c + 1 < wpt / 4; c += 2) {
-    const uint4 x = bm4[c], y = bm4[c + 1];
-    pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
-    pc += __popc(y.x) + __popc(y.y) + __popc(y.z) + __popc(y.w);
-    bm_store8(v.bitmap, wbase + 4 * c, words, x, y, true);
-    if (bitmap_out) bm_store8(bitmap_out, wbase + 4 * c, words, x, y, out_vec);
-  }
-  if (c < wpt / 4) {                                  // an odd run of four words
-    const uint4 x = bm4[c];
-    pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
-    bm_store4(v.bitmap, wbase + 4 * c, words, x, true);
-    if (bitmap_out) bm_store4(bitmap_out, wbase + 4 * c, words, x, out_vec);
-  }
-  int n_tot = 0;
-  int off = ns::block_excl_scan<kFastThreads>(pc, sh_scan, &n_tot);
-  // Each thread writes its ids at its prefix offset, straight to active_ids
-  // (every lane of a store then hits its own cache line) or, for many ids,
-  // into the LDS staging area followed by one coalesced copy.  Measured on
-  // the same GPU: 967 ids, 4.90 us direct vs 5.21 staged; 15.5k ids, 14.7 us
-  // direct vs 12.2 staged.  n_tot is block-uniform after the scan.
-  const bool staged = stage && n_tot >= kFastStageMinIds;
-  int32_t* const dst = staged ? sids : active_ids;
-  auto emit = [&](uint32_t b, int w) {
-    while (b) {
-      dst[off++] = (w << 5) + (__ffs(b) - 1);
-      b &= b - 1u;
-    }
-  };
-  emit(c0a.x, wbase); emit(c0a.y, wbase + 1); emit(c0a.z, wbase + 2); emit(c0a.w, wbase + 3);
-  emit(c0b.x, wbase + 4); emit(c0b.y, wbase + 5); emit(c0b.z, wbase + 6); emit(c0b.w, wbase + 7);
-  for (int c = 2; c < wpt / 4; ++c) {
-    const uint4 x = bm4[c];
-    const int w = wbase + 4 * c;
-    emit(x.x, w); emit(x.y, w + 1); emit(x.z, w + 2); emit(x.w, w + 3);
-  }
-  if (staged) {                                         // block-uniform
-    __syncthreads();
-    if ((((uintptr_t)active_ids) & 15u) == 0) {
-      const int n4 = n_tot >> 2;
-      for (int i = tid; i < n4; i += kFastThreads) ((int4*)active_ids)[i] = ((const int4*)sids)[i];
-      for (int i = (n4 << 2) + tid; i < n_tot; i += kFastThreads) active_ids[i] = sids[i];
-    } else {
-      for (int i = tid; i < n_tot; i += kFastThreads) active_ids[i] = sids[i];
-    }
-  }
-  if (tid == 0) {
-    *n_active = n_tot;
-    *v.len = len + C;
-    if (sh_flag) atomicOr(v.status, NS_STATUS_BAD_ID);
-  }
-}
-
 template <typename T, int RU>
 __global__ __launch_bounds__(kFastThreads) void k_step_fast(ns_state_view v, const int32_t* draft_ids,
                                                             int n_draft, const int32_t* ver_ids, int n_ver,
                                                             int32_t* __restrict__ active_ids,
                                                             int32_t* __restrict__ n_active,
                                                             uint32_t* __restrict__ bitmap_out) {
-  step_fast_body<T, RU>(v, draft_ids, n_draft, ver_ids, n_ver, active_ids, n_active, bitmap_out);
+  extern __shared__ int4 lds4[];
+  step_fast_body<T, RU, kFastThreads, 0>(lds4, fast_stage_ints(v.V, v.w_max), v, draft_ids, n_draft, ver_ids, n_ver,
+                                         active_ids, n_active, bitmap_out, FuseCtl{});
 }
 
 // B sequences, one workgroup each: sequence b's state is sequence 0's moved
@@ -484,12 +237,17 @@ __global__ __launch_bounds__(kFastThreads) void k_step_fast_batch(ns_state_view 
   v.ring = (int32_t*)((char*)v0.ring + off);
   v.first = (int32_t*)((char*)v0.first + off);
   v.bitmap = (uint32_t*)((char*)v0.bitmap + off);
+  v.cur = (int32_t*)((char*)v0.cur + off);
+  v.n_cur = (int32_t*)((char*)v0.n_cur + off);
+  v.next_bm = (uint32_t*)((char*)v0.next_bm + off);
   const int nd = min(max(n_draft[b], 0), nd_max);
   const int nv = min(max(n_ver[b], 0), nv_max);
   const int words = (v0.V + 31) >> 5;
-  step_fast_body<T, RU>(v, draft_ids + (size_t)b * draft_stride, nd, ver_ids + (size_t)b * ver_stride, nv,
-                        active_ids + (size_t)b * v0.w_max, n_active + b,
-                        bitmap_out ? bitmap_out + (size_t)b * words : nullptr);
+  extern __shared__ int4 lds4[];
+  step_fast_body<T, RU, kFastThreads, 0>(lds4, fast_stage_ints(v0.V, v0.w_max), v, draft_ids + (size_t)b * draft_stride,
+                                         nd, ver_ids + (size_t)b * ver_stride, nv, active_ids + (size_t)b * v0.w_max,
+                                         n_active + b, bitmap_out ? bitmap_out + (size_t)b * words : nullptr,
+                                         FuseCtl{});
 }
 
 size_t fast_lds_bytes(int V, int w_max, int n_draft) {
@@ -545,11 +303,12 @@ step_fast_fn pick_step_fast(int w_max) {
 __global__ void k_init(ns_state_view v) {
   const int gt = blockIdx.x * blockDim.x + threadIdx.x;
   const int gs = gridDim.x * blockDim.x;
-  if (gt == 0) { *v.len = 0; *v.status = 0u; }
+  if (gt == 0) { *v.len = 0; *v.status = 0u; *v.n_cur = 0; }
   for (int i = gt; i < v.w_max; i += gs) v.ring[i] = -1;
   for (int i = gt; i < v.V; i += gs) v.first[i] = INT32_MAX;
   const int words = (v.V + 31) >> 5;
   for (int i = gt; i < words; i += gs) v.bitmap[i] = 0u;
+  for (int i = gt; i < next_words(v.V); i += gs) v.next_bm[i] = 0u;
 }
 
 __global__ void k_window(ns_state_view v, int32_t* __restrict__ window, int64_t* __restrict__ len_out) {
@@ -614,6 +373,8 @@ size_t nanospec_state_bytes(int32_t V, int32_t w_max) {
   b += align256((size_t)w_max * 4);
   b += align256((size_t)V * 4);
   b += align256((size_t)((V + 31) >> 5) * 4);
+  b += align256((size_t)w_max * 4);
+  b += align256((size_t)next_words(V) * 4);
   return b;
 }
 
@@ -632,6 +393,11 @@ ns_state_view make_view(char* p, int32_t V, int32_t w_max) {
   v.first = (int32_t*)(p + off);
   off += align256((size_t)V * 4);
   v.bitmap = (uint32_t*)(p + off);
+  off += align256((size_t)((V + 31) >> 5) * 4);
+  v.cur = (int32_t*)(p + off);
+  off += align256((size_t)w_max * 4);
+  v.next_bm = (uint32_t*)(p + off);
+  v.n_cur = (int32_t*)(p + 16);
   v.V = V;
   v.w_max = w_max;
   return v;
@@ -729,6 +495,7 @@ int nanospec_batch_step_update(nanospec_batch* bt, const int32_t* draft_ids, int
   if (draft_stride < nd_max || ver_stride < nv_max) return NS_EINVAL;
   for (int b = 0; b < bt->B; ++b)                     // the batched kernel appends for every member
     if (bt->members[b].mode == NS_STREAM_CTX_ONLY) return NS_EINVAL;
+  for (int b = 0; b < bt->B; ++b) bt->members[b].drop_cur();
   const ns_state_view& v0 = bt->members[0].view;
   step_fast_batch_fn fn = pick_step_fast_batch(v0.w_max);
   const size_t lds = fast_lds_bytes(v0.V, v0.w_max, nd_max);
@@ -741,6 +508,7 @@ int nanospec_batch_step_update(nanospec_batch* bt, const int32_t* draft_ids, int
 
 int nanospec_state_reset(nanospec_state* st, hipStream_t stream) {
   if (!st) return NS_EINVAL;
+  st->drop_cur();
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_init, dim3(fill_grid(st->view)), dim3(256), 0, stream, st->view);
   return ns_launch_status();
@@ -785,6 +553,7 @@ int nanospec_stream_append(nanospec_state* st, const int32_t* ids, int32_t n, in
   if (!st || n < 0 || (n > 0 && !ids)) return NS_EINVAL;
   if (dedup_first != 0 && dedup_first != 1) return NS_EINVAL;
   if (n == 0 || st->mode == NS_STREAM_EXT_ONLY) return NS_OK;   // ext-only: no prompt context
+  st->drop_cur();
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_append, dim3(1), dim3(kStateThreads), 0, stream, st->view, ids, n, dedup_first);
   return ns_launch_status();
@@ -793,6 +562,7 @@ int nanospec_stream_append(nanospec_state* st, const int32_t* ids, int32_t n, in
 int nanospec_active_vocab(nanospec_state* st, int32_t* active_ids, int32_t* n_active, uint32_t* bitmap,
                           hipStream_t stream) {
   if (!st || !active_ids || !n_active) return NS_EINVAL;
+  st->drop_cur();
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_active, dim3(1), dim3(kStateThreads), lds_bitmap_bytes(st->view.V), stream, st->view,
                      active_ids, n_active, bitmap);
@@ -805,6 +575,7 @@ int nanospec_step_update(nanospec_state* st, const int32_t* draft_ids, int32_t n
   if (!st || !active_ids || !n_active || n_draft < 0 || n_ver < 0) return NS_EINVAL;
   if ((n_draft > 0 && !draft_ids) || (n_ver > 0 && !ver_ids)) return NS_EINVAL;
   if (st->mode == NS_STREAM_CTX_ONLY) n_draft = n_ver = 0;     // ctx-only: nothing added while decoding
+  st->drop_cur();
   (void)hipGetLastError();
   const size_t fast = fast_lds_bytes(st->view.V, st->view.w_max, n_draft);
   step_fast_fn fast_fn = pick_step_fast(st->view.w_max);

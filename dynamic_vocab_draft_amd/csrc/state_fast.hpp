@@ -1,0 +1,341 @@
+// The one-workgroup decode-step update of a window state (C_draft dedup,
+// ring append, bitmap rebuild and ascending compaction), shared by the state
+// kernels and by the first launch of the fused decode step.
+//
+// MicroSpec/NanoSpec (arXiv 2605.26444) Sec. 3.2, "Dynamic Stream Update
+// (Decoding Phase)" and "Vocabulary Construction via Sliding Window".
+#pragma once
+#include "common.hpp"
+#include "state_internal.hpp"
+
+namespace {
+
+// Per-step update with one round of global loads and no LDS copy of the
+// ring.  Every global read the step needs (|S|, the whole ring, both tuples)
+// is issued at once; each thread keeps its ring slots in registers.  C_draft
+// is deduplicated against an LDS copy of the tuple (fine for a draft tree of
+// up to kFastMaxIds ids).  After the tuple positions are scanned, the active
+// bitmap is built in LDS from (a) the new entries that land in the window and
+// (b) the old slots that they do not overwrite: with |S| = len and
+// C = |C_draft| + |C_ver|, the new entries take slots (len + p) mod w_max, so
+// an old slot s survives iff C < w_max and (s - len) mod w_max >= C.  Slots
+// never written hold -1.  The ascending compaction gives each thread a
+// contiguous run of WPT words (at least 8, a multiple of 4, read as 16-byte
+// LDS vectors): the fewest that cover the bitmap, so that every wave has
+// words to scan (a multiple of 8 left the last waves idle for V just above
+// 2^17, and the others with twice the words).
+constexpr int kFastThreads = 512;
+constexpr int kFastMaxIds = kFastThreads;      // one tuple entry per thread
+constexpr int kFastMaxRing = 32 * kFastThreads; // ring entries held in registers
+constexpr size_t kFastLdsMax = 144 * 1024;
+constexpr int kFastStageMinIds = 4096;          // ids from which the compaction is staged in LDS
+
+template <int TH = kFastThreads>
+__host__ __device__ __forceinline__ int fast_wpt(int V) {
+  const int words = (V + 31) >> 5;
+  const int w4 = ((words + TH * 4 - 1) / (TH * 4)) * 4;
+  return w4 < 8 ? 8 : w4;
+}
+
+// Fused form: bitmap words per thread (a multiple of 4, at least 4: that
+// form compacts nothing).
+template <int TH>
+__host__ __device__ __forceinline__ int fused_wpt(int V) {
+  const int words = (V + 31) >> 5;
+  const int w4 = ((words + TH * 4 - 1) / (TH * 4)) * 4;
+  return w4 < 4 ? 4 : w4;
+}
+
+// Ints of LDS that stage the ascending active ids before one coalesced copy
+// to active_ids (at most min(W_max, V) ids), or 0 when the bitmap, the
+// staging area and the largest tuples would not fit kFastLdsMax; then the
+// ids are written to global memory directly from the compaction.
+__host__ __device__ __forceinline__ int fast_stage_ints(int V, int w_max) {
+  const int n = w_max < V ? w_max : V;
+  const int ints = (n + 3) & ~3;
+  const size_t need = ((size_t)kFastThreads * fast_wpt(V) + (size_t)ints + 2 * (size_t)kFastMaxIds) * 4;
+  return need <= kFastLdsMax ? ints : 0;
+}
+
+__device__ __forceinline__ void bm_set(uint32_t* bm, int id) { atomicOr(&bm[id >> 5], 1u << (id & 31)); }
+
+__device__ __forceinline__ void bm_store4(uint32_t* __restrict__ dst, int w, int words, uint4 a, bool vec) {
+  if (vec && w + 4 <= words) {
+    *(uint4*)(dst + w) = a;
+    return;
+  }
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (w + e < words) dst[w + e] = x[e];
+}
+
+__device__ __forceinline__ void bm_store8(uint32_t* __restrict__ dst, int w, int words, uint4 a, uint4 b, bool vec) {
+  if (vec && w + 8 <= words) {
+    ((uint4*)(dst + w))[0] = a;
+    ((uint4*)(dst + w))[1] = b;
+    return;
+  }
+  const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (w + e < words) dst[w + e] = x[e];
+}
+
+// Outputs of the state update when it runs beside the projection of a
+// fused decode step (nanospec_decode_step).  That projection reads the
+// columns [0, nd + nv) as the step's tuple entries (C_draft as given, then
+// C_ver) and [cbase, cbase + n_cur) as I_t (cur); the update flags each
+// column whose id is in I_{t+1}: an I_t column iff its id stays active, a
+// tuple column iff its id is active and this is its first occurrence in the
+// tuples.  (An id of both I_t and the tuples is then flagged twice; the
+// projection marks the tuple columns whose id is in I_t, and the merge keeps
+// only the I_t column.)  The bitmap of I_{t+1} goes to next_bm; the
+// ascending ids and the new |S| are left to the next launch (hdr[1]
+// carries the entries this step appends).
+struct FuseCtl {
+  const int32_t* cur;     // [w_max] I_t, ascending
+  const int32_t* n_cur;   // |I_t|
+  uint8_t* flags;         // [cbase + w_max] column membership flags
+  int32_t* hdr;           // hdr[0] <- |I_t|, hdr[1] <- entries appended (C)
+  uint32_t* next_bm;      // [ceil(V/32)] <- the bitmap of I_{t+1}
+  int cbase;              // column of I_t's first entry
+};
+
+// TH threads per workgroup.  CU > 0 selects the fused form (fc is used; at
+// most CU I_t entries per thread, TH CU >= w_max): the two tuples, together
+// at most TH entries, are compared as one sequence, |S| is not written, and
+// neither ids nor the state's bitmap are (active_ids, n_active, bitmap_out
+// and stage are unused).
+template <typename T, int RU, int TH, int CU>
+__device__ __forceinline__ void step_fast_body(int4* lds4, int stage, const ns_state_view& v, const int32_t* draft_ids,
+                                               int n_draft, const int32_t* ver_ids, int n_ver,
+                                               int32_t* __restrict__ active_ids, int32_t* __restrict__ n_active,
+                                               uint32_t* __restrict__ bitmap_out, const FuseCtl& fc) {
+  constexpr bool FUSE = CU > 0;
+  constexpr int EPT = (int)(sizeof(T) / 4);     // ring entries per load
+  constexpr int NW = TH / NS_WAVE;
+  __shared__ int sh_scan[NW + 1];
+  __shared__ int sh_flag;
+  const int tid = threadIdx.x, lane = tid & (NS_WAVE - 1), wv = tid / NS_WAVE;
+  const int w_max = v.w_max, V = v.V;
+  const int words = (V + 31) >> 5;
+  const int wpt = FUSE ? fused_wpt<TH>(V) : fast_wpt<TH>(V);
+  const int ntup = FUSE ? n_draft + n_ver : n_draft;              // entries compared for first occurrences
+  const int nd64 = (ntup + NS_WAVE - 1) & ~(NS_WAVE - 1);
+  uint32_t* bm = (uint32_t*)lds4;                                 // TH * wpt words
+  int32_t* sids = (int32_t*)(bm + (size_t)TH * wpt);              // stage ids (16-byte aligned)
+  int32_t* dids = sids + stage;                                   // nd64 ids (-1 padding)
+  int32_t* sfp = dids + nd64;                                     // nd64 first positions
+  // ---- one round of global loads --------------------------------------
+  // An index the compiler cannot prove uniform keeps |S| in a vector
+  // register, so no early wait is placed on it ahead of the other loads.
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  const int nl = w_max / EPT;                                     // loads covering the ring
+  const T* src = (const T*)v.ring;
+  T r[RU];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int q = tid + u * TH;
+    r[u] = src[q < nl ? q : 0];
+  }
+  const int64_t len_in = v.len[zero];
+  const int d_in = draft_ids[tid < n_draft ? tid : 0];
+  const int v_in = ver_ids[tid < n_ver ? tid : 0];
+  // Fused form: |I_t| and this thread's entries of I_t, in the same round.
+  int n_old = 0;
+  int32_t curv[FUSE ? CU : 1];
+  if constexpr (FUSE) {
+    n_old = fc.n_cur[zero];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int j = tid + u * TH;
+      curv[u] = fc.cur[j < w_max ? j : 0];
+    }
+  }
+  NS_ISSUE_FENCE();
+  for (int w = tid; w < TH * wpt; w += TH) bm[w] = 0u;
+  if constexpr (FUSE) {                           // dids = C_draft, then C_ver, then -1
+    if (tid < n_draft) dids[tid] = d_in;
+    if (tid < n_ver) dids[n_draft + tid] = v_in;
+    if (tid >= ntup && tid < nd64) dids[tid] = -1;
+    if (tid < nd64) sfp[tid] = tid;
+  } else {
+    for (int q = tid; q < nd64; q += TH) {
+      dids[q] = q < n_draft ? d_in : -1;
+      sfp[q] = q;
+    }
+  }
+  if (tid == 0) sh_flag = 0;
+  __syncthreads();
+  // ---- C_draft first occurrences ---------------------------------------
+  // Position i keeps its id iff no earlier position holds it.  The j range
+  // is split over the waves (wave w compares against ids
+  // [w * nd64 / 8, (w + 1) * nd64 / 8), read as broadcast 4-id LDS words) and
+  // each lane takes positions lane, lane + 64, ...; a smaller equal position
+  // is folded into sfp[i] with an LDS atomicMin.
+  {
+    const int cj = nd64 / NW;                                   // a multiple of 8
+    const int4* d4 = (const int4*)(dids + wv * cj);
+    for (int i = lane; i < ntup; i += NS_WAVE) {
+      const int x = dids[i];
+      int fp = INT32_MAX;
+      for (int c4 = 0; c4 < cj / 4; c4 += 2) {
+        const int4 qa = d4[c4], qb = d4[c4 + 1];
+        const int j = wv * cj + 4 * c4;
+        fp = min(fp, qa.x == x ? j : INT32_MAX);
+        fp = min(fp, qa.y == x ? j + 1 : INT32_MAX);
+        fp = min(fp, qa.z == x ? j + 2 : INT32_MAX);
+        fp = min(fp, qa.w == x ? j + 3 : INT32_MAX);
+        fp = min(fp, qb.x == x ? j + 4 : INT32_MAX);
+        fp = min(fp, qb.y == x ? j + 5 : INT32_MAX);
+        fp = min(fp, qb.z == x ? j + 6 : INT32_MAX);
+        fp = min(fp, qb.w == x ? j + 7 : INT32_MAX);
+      }
+      if (fp < i) atomicMin(&sfp[i], fp);
+    }
+  }
+  __syncthreads();
+  // ---- tuple positions (C_draft deduplicated, then C_ver as given) ----
+  bool keep_d = false, keep_v = false, bad = false;
+  if (tid < n_draft) {
+    keep_d = d_in >= 0 && d_in < V;
+    bad |= !keep_d;
+    keep_d &= sfp[tid] == tid;
+  }
+  if (tid < n_ver) {
+    keep_v = v_in >= 0 && v_in < V;
+    bad |= !keep_v;
+  }
+  if (bad) sh_flag = 1;
+  int total = 0;
+  const int pre = ns::block_excl_scan<TH>((keep_d ? 1 : 0) | (keep_v ? 0x10000 : 0), sh_scan, &total);
+  const int Cd = total & 0xFFFF, Cv = total >> 16, C = Cd + Cv;
+  const int64_t len = len_in;
+  int lm;                                               // slot of position |S|
+  if (len < ((int64_t)1 << 31)) lm = (int)((uint32_t)len % (uint32_t)w_max);
+  else lm = (int)(len % (int64_t)w_max);
+  auto slot_of = [&](int p) {                           // (lm + p) mod w_max, p < 2^16
+    int x = lm + p;
+    if (x >= w_max) x -= w_max;
+    if (x >= w_max) x %= w_max;
+    return x;
+  };
+  // New entries: only the last w_max of this step can be inside the window.
+  if (keep_d) {
+    const int p = pre & 0xFFFF;
+    if (p >= C - w_max) {
+      v.ring[slot_of(p)] = d_in;
+      bm_set(bm, d_in);
+    }
+  }
+  if (keep_v) {
+    const int p = Cd + (pre >> 16);
+    if (p >= C - w_max) {
+      v.ring[slot_of(p)] = v_in;
+      bm_set(bm, v_in);
+    }
+  }
+  // Old entries that stay in the window.
+  if (C < w_max) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int q = tid + u * TH;
+      if (q < nl) {
+        const int32_t* e = (const int32_t*)&r[u];
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) {
+          const int slot = q * EPT + x;
+          const int id = e[x];
+          int rel = slot - lm;
+          rel += rel < 0 ? w_max : 0;
+          if (rel >= C && id >= 0 && id < V) bm_set(bm, id);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // Fused form: the new bitmap to next_bm, then the column flags.
+  if constexpr (FUSE) {
+    const uint4* b4 = (const uint4*)(bm + (size_t)tid * wpt);
+    for (int c = 0; c < wpt / 4; ++c) bm_store4(fc.next_bm, tid * wpt + 4 * c, words, b4[c], true);
+    auto member = [&](int id) { return id >= 0 && id < V && ((bm[id >> 5] >> (id & 31)) & 1u) != 0; };
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int j = tid + u * TH;
+      if (j < n_old && j < w_max) fc.flags[fc.cbase + j] = member(curv[u]) ? 1 : 0;
+    }
+    if (tid < n_draft) fc.flags[tid] = (sfp[tid] == tid && member(d_in)) ? 1 : 0;
+    if (tid < n_ver) fc.flags[n_draft + tid] = (sfp[n_draft + tid] == n_draft + tid && member(v_in)) ? 1 : 0;
+    if (tid == 0) {
+      fc.hdr[0] = n_old;
+      fc.hdr[1] = C;
+      if (sh_flag) atomicOr(v.status, NS_STATUS_BAD_ID);
+    }
+    return;
+  }
+  // ---- ascending compaction; the bitmap goes out from registers ---------
+  const bool out_vec = bitmap_out && ((((uintptr_t)bitmap_out) & 15u) == 0);
+  const uint4* bm4 = (const uint4*)(bm + (size_t)tid * wpt);
+  const int wbase = tid * wpt;
+  int pc = 0;
+  uint4 c0a = bm4[0], c0b = bm4[1];                   // first 8 words stay in registers
+  pc += __popc(c0a.x) + __popc(c0a.y) + __popc(c0a.z) + __popc(c0a.w);
+  pc += __popc(c0b.x) + __popc(c0b.y) + __popc(c0b.z) + __popc(c0b.w);
+  bm_store8(v.bitmap, wbase, words, c0a, c0b, true);
+  if (bitmap_out) bm_store8(bitmap_out, wbase, words, c0a, c0b, out_vec);
+  int c = 2;
+  for (; c + 1 < wpt / 4; c += 2) {
+    const uint4 x = bm4[c], y = bm4[c + 1];
+    pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+    pc += __popc(y.x) + __popc(y.y) + __popc(y.z) + __popc(y.w);
+    bm_store8(v.bitmap, wbase + 4 * c, words, x, y, true);
+    if (bitmap_out) bm_store8(bitmap_out, wbase + 4 * c, words, x, y, out_vec);
+  }
+  if (c < wpt / 4) {                                  // an odd run of four words
+    const uint4 x = bm4[c];
+    pc += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+    bm_store4(v.bitmap, wbase + 4 * c, words, x, true);
+    if (bitmap_out) bm_store4(bitmap_out, wbase + 4 * c, words, x, out_vec);
+  }
+  int n_tot = 0;
+  int off = ns::block_excl_scan<TH>(pc, sh_scan, &n_tot);
+  // Each thread writes its ids at its prefix offset, straight to active_ids
+  // (every lane of a store then hits its own cache line) or, for many ids,
+  // into the LDS staging area followed by one coalesced copy.  Measured on
+  // the same GPU: 967 ids, 4.90 us direct vs 5.21 staged; 15.5k ids, 14.7 us
+  // direct vs 12.2 staged.  n_tot is block-uniform after the scan.
+  const bool staged = stage && n_tot >= kFastStageMinIds;
+  int32_t* const dst = staged ? sids : active_ids;
+  auto emit = [&](uint32_t b, int w) {
+    while (b) {
+      dst[off++] = (w << 5) + (__ffs(b) - 1);
+      b &= b - 1u;
+    }
+  };
+  emit(c0a.x, wbase); emit(c0a.y, wbase + 1); emit(c0a.z, wbase + 2); emit(c0a.w, wbase + 3);
+  emit(c0b.x, wbase + 4); emit(c0b.y, wbase + 5); emit(c0b.z, wbase + 6); emit(c0b.w, wbase + 7);
+  for (int c = 2; c < wpt / 4; ++c) {
+    const uint4 x = bm4[c];
+    const int w = wbase + 4 * c;
+    emit(x.x, w); emit(x.y, w + 1); emit(x.z, w + 2); emit(x.w, w + 3);
+  }
+  if (staged) {                                         // block-uniform
+    __syncthreads();
+    if ((((uintptr_t)active_ids) & 15u) == 0) {
+      const int n4 = n_tot >> 2;
+      for (int i = tid; i < n4; i += TH) ((int4*)active_ids)[i] = ((const int4*)sids)[i];
+      for (int i = (n4 << 2) + tid; i < n_tot; i += TH) active_ids[i] = sids[i];
+    } else {
+      for (int i = tid; i < n_tot; i += TH) active_ids[i] = sids[i];
+    }
+  }
+  if (tid == 0) {
+    *n_active = n_tot;
+    *v.len = len + C;
+    if (sh_flag) atomicOr(v.status, NS_STATUS_BAD_ID);
+  }
+}
+
+}  // namespace

@@ -113,6 +113,13 @@ _SIGS = {
     "nanospec_packed_destroy": (ctypes.c_int, [c_vp]),
     "nanospec_packed_slots": (ctypes.c_int, [c_vp] + [ctypes.POINTER(c_vp)] * 5),
     "nanospec_packed_update": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_vp, c_vp]),
+    "nanospec_decode_step_workspace_bytes": (c_size, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "nanospec_decode_step": (ctypes.c_int, [c_vp, c_vp, c_int32, c_vp, c_int32, c_vp, c_vp, c_vp, c_int32, c_int32,
+                                            c_int32, c_vp, c_int32, c_int32, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "nanospec_decode_step_project": (ctypes.c_int, [c_vp, c_vp, c_int32, c_vp, c_int32, c_vp, c_vp, c_vp, c_int32,
+                                                    c_int32, c_int32, c_vp, c_int32, c_int32, c_vp, c_size, c_vp]),
+    "nanospec_decode_step_select": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32, c_int32, c_vp,
+                                                   c_vp, c_vp, c_size, c_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -228,6 +235,49 @@ def nanospec_step_update(st: NanoSpecState, draft_ids: Optional[torch.Tensor], n
     _check(_lib.nanospec_step_update(st.handle, _ptr(draft_ids), n_draft, _ptr(ver_ids), n_ver,
                                      _ptr(active_ids), _ptr(n_active), _ptr(bitmap), _stream(stream)),
            "nanospec_step_update")
+
+
+def nanospec_decode_step_workspace_bytes(w_max: int, n_tuple: int, M: int, k: int, d: int) -> int:
+    return _lib.nanospec_decode_step_workspace_bytes(w_max, n_tuple, M, k, d)
+
+
+def nanospec_decode_step(st: NanoSpecState, draft_ids: Optional[torch.Tensor], n_draft: int,
+                         ver_ids: Optional[torch.Tensor], n_ver: int, active_ids: torch.Tensor,
+                         n_active: torch.Tensor, w: torch.Tensor, V: int, d: int, dtype: int, h: torch.Tensor,
+                         M: int, k: int, topk_ids: torch.Tensor, topk_vals: torch.Tensor, ws: torch.Tensor,
+                         stream=None) -> None:
+    _check(_lib.nanospec_decode_step(st.handle, _ptr(draft_ids), n_draft, _ptr(ver_ids), n_ver, _ptr(active_ids),
+                                     _ptr(n_active), _ptr(w), V, d, dtype, _ptr(h), M, k, _ptr(topk_ids),
+                                     _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nanospec_decode_step")
+
+
+def nanospec_decode_step_project(st: NanoSpecState, draft_ids: Optional[torch.Tensor], n_draft: int,
+                                 ver_ids: Optional[torch.Tensor], n_ver: int, active_ids: torch.Tensor,
+                                 n_active: torch.Tensor, w: torch.Tensor, V: int, d: int, dtype: int, h: torch.Tensor,
+                                 M: int, k: int, ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_decode_step_project(st.handle, _ptr(draft_ids), n_draft, _ptr(ver_ids), n_ver,
+                                             _ptr(active_ids), _ptr(n_active), _ptr(w), V, d, dtype, _ptr(h), M, k,
+                                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nanospec_decode_step_project")
+
+
+def nanospec_decode_step_select(st: NanoSpecState, active_ids: torch.Tensor, n_active: torch.Tensor, V: int, d: int,
+                                dtype: int, M: int, k: int, topk_ids: torch.Tensor, topk_vals: torch.Tensor,
+                                ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_decode_step_select(st.handle, _ptr(active_ids), _ptr(n_active), V, d, dtype, M, k,
+                                            _ptr(topk_ids), _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)), "nanospec_decode_step_select")
+
+
+def alloc_decode_workspace(w_max: int, n_tuple: int, M: int, k: int, d: int, device="cuda") -> torch.Tensor:
+    """A 256-byte-aligned uint8 workspace of nanospec_decode_step_workspace_bytes."""
+    nbytes = nanospec_decode_step_workspace_bytes(w_max, n_tuple, M, k, d)
+    if nbytes == 0:
+        raise NanoSpecError(NS_EINVAL, "nanospec_decode_step_workspace_bytes")
+    mem = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-mem.data_ptr()) % 256
+    return mem[off:off + nbytes]
 
 
 # ---------------------------------------------------------------------------

@@ -412,6 +412,67 @@ int nanospec_batch_draft_logprob_topk(const void* w, const int32_t* row_ids, con
                                       float* lse, float* logits, int32_t* topk_ids, float* topk_vals,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ======================================================================
+ * The decode step in one call (Sec. 3.2 decoding phase and sliding-window
+ * rebuild, then Sec. 3.1 Eq. 1 on W_head[I_{t+1}, :] with T_k): the same
+ * results as
+ *   nanospec_step_update(st, draft_ids, n_draft, ver_ids, n_ver, active_ids,
+ *                        n_active, NULL, stream);
+ *   nanospec_draft_logits_topk(w, NS_INDEXED, active_ids, n_active, w_max,
+ *                              V, d, dtype, h, M, k, NULL, topk_ids,
+ *                              topk_vals, ws, ws_bytes, stream);
+ * bit for bit (the logits output is not offered).  The state keeps I_t in
+ * ascending order (cur) between decode steps.  When it holds I_t, dtype is
+ * NS_BF16 or NS_FP16, W_max <= 3072 and a multiple of 4, n_draft + n_ver <=
+ * 256 and V <= about 200k, the step takes two launches instead of three: the
+ * state update runs beside the projection, which covers I_t and the tuple
+ * entries (a superset of I_{t+1}), and the merge keeps only members of
+ * I_{t+1}.  Otherwise the three launches run, followed by a copy of I_{t+1}
+ * into cur.  Any other call that changes the window or rebuilds I
+ * (stream_append, active_vocab, step_update, batch_step_update, reset) drops
+ * cur until the next decode step.
+ *   w, V, d, dtype, h, M, k, topk_ids, topk_vals : as nanospec_draft_logits_topk
+ *              in NS_INDEXED mode; V must be the state's V.
+ *   ws       : >= nanospec_decode_step_workspace_bytes(w_max, n_draft + n_ver,
+ *              M, k, d) bytes, 256-byte aligned.
+ * Errors: NS_EINVAL (nulls, counts, limits, V mismatch), NS_EDTYPE,
+ * NS_ECAPACITY, NS_EHIP (see the conventions on kernels already enqueued). */
+size_t nanospec_decode_step_workspace_bytes(int32_t w_max, int32_t n_tuple, int32_t M, int32_t k, int32_t d);
+int nanospec_decode_step(nanospec_state* st, const int32_t* draft_ids, int32_t n_draft,
+                         const int32_t* ver_ids, int32_t n_ver, int32_t* active_ids,
+                         int32_t* n_active, const void* w, int32_t V, int32_t d, int32_t dtype,
+                         const void* h, int32_t M, int32_t k, int32_t* topk_ids, float* topk_vals,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The two stages of nanospec_decode_step, for callers that place them
+ * separately (and to time the first launch on its own):
+ *   nanospec_decode_step_project : the state update and the projection
+ *       (the fused first launch, or the state update and the projection
+ *       stage of the three-launch form); same arguments as the whole call
+ *       minus the outputs (k only sizes the workspace).  Records the form
+ *       in the state's handle.
+ *   nanospec_decode_step_select  : the merge, top-k and map to global ids,
+ *       and the state's cur (and, in the fused form, I_{t+1} in active_ids /
+ *       n_active, the state's bitmap and |S|); writes topk_ids / topk_vals
+ *       exactly as the whole call.
+ * select must follow project on the same state, workspace, active_ids and
+ * n_active, with the same V, d, dtype, M and k (else NS_EINVAL, nothing
+ * enqueued); the pair then gives bit-identical results to
+ * nanospec_decode_step.  Between the two the state is mid-update: any other
+ * call that changes it drops the pending step (select then returns
+ * NS_EINVAL), and a fused project that is not followed by its select leaves
+ * the window undefined until nanospec_state_reset.  Errors as for the whole
+ * call. */
+int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, int32_t n_draft,
+                                 const int32_t* ver_ids, int32_t n_ver, int32_t* active_ids,
+                                 int32_t* n_active, const void* w, int32_t V, int32_t d,
+                                 int32_t dtype, const void* h, int32_t M, int32_t k, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+int nanospec_decode_step_select(nanospec_state* st, int32_t* active_ids, int32_t* n_active,
+                                int32_t V, int32_t d, int32_t dtype, int32_t M, int32_t k,
+                                int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* Best-k selection over draft-tree candidates, B independent selections:
  *   vals, ids : [B x C] candidate scores and token ids (device); id -1 marks
  *               an empty candidate, which is never selected;

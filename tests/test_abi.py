@@ -50,8 +50,9 @@ def test_codes_and_sizes(ns):
     assert L.nanospec_state_bytes(10, 0) == 0
     assert L.nanospec_state_bytes(ns.NS_MAX_V + 1, 10) == 0
     b = L.nanospec_state_bytes(128256, 3072)
-    # control + ring + first[V] + bitmap, each 256-byte aligned
-    assert b == 256 + 12288 + 513024 + 16128
+    # control + ring + first[V] + bitmap + the kept active set + the decode step's next bitmap
+    # (ceil(V/32) rounded up to 8 words), each 256-byte aligned
+    assert b == 256 + 12288 + 513024 + 16128 + 12288 + 16128
     assert L.nanospec_draft_workspace_bytes(3072, 8, 8, 4096) >= 3072 * 8 * 4
     assert L.nanospec_draft_workspace_bytes(3072, 65, 8, 4096) == 0
     assert L.nanospec_draft_workspace_bytes(3072, 8, 65, 4096) == 0
@@ -64,6 +65,11 @@ def test_codes_and_sizes(ns):
     assert w1 == L.nanospec_draft_workspace_bytes(3072, 8, 8, 4096)
     assert L.nanospec_batch_draft_workspace_bytes(8, 3072, 8, 8, 4096) >= 8 * 3072 * 8 * 4
     assert L.nanospec_batch_draft_workspace_bytes(0, 3072, 8, 8, 4096) == 0
+    # the decode step: at least the separate draft head's workspace; the tuple bound is checked
+    dw = L.nanospec_decode_step_workspace_bytes(3072, 68, 8, 8, 4096)
+    assert dw >= L.nanospec_draft_workspace_bytes(3072, 8, 8, 4096) and dw % 256 == 0
+    assert L.nanospec_decode_step_workspace_bytes(3072, -1, 8, 8, 4096) == 0
+    assert L.nanospec_decode_step_workspace_bytes(3072, 68, 65, 8, 4096) == 0
 
 
 def test_host_validation_rejects_before_launch(ns):
@@ -78,6 +84,12 @@ def test_host_validation_rejects_before_launch(ns):
     assert L.nanospec_active_vocab(None, fake, fake, None, None) == ns.NS_EINVAL
     assert L.nanospec_state_status(None, None, None) == ns.NS_EINVAL
     assert L.nanospec_state_destroy(None) == ns.NS_EINVAL
+    assert L.nanospec_decode_step(None, fake, 3, fake, 1, fake, fake, fake, 100, 64, ns.NS_BF16, fake, 8, 8, fake,
+                                  fake, fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_decode_step_project(None, fake, 3, fake, 1, fake, fake, fake, 100, 64, ns.NS_BF16, fake, 8, 8,
+                                          fake, 1 << 20, None) == ns.NS_EINVAL
+    assert L.nanospec_decode_step_select(None, fake, fake, 100, 64, ns.NS_BF16, 8, 8, fake, fake, fake, 1 << 20,
+                                         None) == ns.NS_EINVAL
     # gather: null, bad d, bad dtype, misaligned
     assert L.nanospec_gather_rows(None, 10, 8, 0, fake, None, 4, fake, None) == ns.NS_EINVAL
     assert L.nanospec_gather_rows(fake, 10, 12, 0, fake, None, 4, fake, None) == ns.NS_EINVAL

@@ -17,6 +17,8 @@ READ = "void at::native::elementwise_kernel_manual_unroll<128, 8, Foo>(int, Foo)
 STEP = "void (anonymous namespace)::k_step_fast<HIP_vector_type<int, 4u>, 2>(ns_state_view, int const*)"
 PROJ = "void (anonymous namespace)::k_proj_mfma<1, 1, false, 1, 4, true>(uint4 const*, int)"
 MERGE = "void (anonymous namespace)::k_merge_cols<4, true, 4, false>(float const*, int)"
+FPROJ = "void (anonymous namespace)::k_proj_mfma<1, 1, false, 1, 4, true, true>(uint4 const*, int)"
+FMERGE = "void (anonymous namespace)::k_merge_fused<4>(float const*, int)"
 
 
 def test_more_than_one_gpu_exits_with_a_message():
@@ -36,8 +38,17 @@ def _trace(path, rows):
 def test_step_trace_summary(tmp_path):
     """Two cold indexed steps with spans of 5/5 and 4/6 us per kernel, one
     step broken by a kernel of another name, and a step on two queues: only
-    the two intact steps are counted."""
+    the two intact steps are counted; two decode steps of 6 + 4 and 5 + 5
+    us, and a decode step's first launch alone (not a step)."""
     rows, t = [], 1_000_000
+    for durs in ((6000, 4000), (5000, 5000)):
+        rows.append((READ, t, t + 90_000, 1))
+        t += 90_000
+        for name, d in zip((FPROJ, FMERGE), durs):
+            rows.append((name, t, t + d, 1))
+            t += d
+    rows += [(READ, t, t + 90_000, 1), (FPROJ, t + 90_000, t + 96_000, 1)]
+    t += 100_000
     for durs in ((5000, 5000, 4000), (4000, 6000, 5000)):
         rows.append((READ, t, t + 90_000, 1))
         t += 90_000
@@ -59,7 +70,12 @@ def test_step_trace_summary(tmp_path):
     assert "| indexed | 2 | k_step_fast | 4.500 | 4.500 | 4.000 | 5.000 |" in out
     assert "| indexed | 2 | k_proj_mfma | 5.500 |" in out
     assert "| indexed | 2 | k_merge_cols | 4.500 |" in out
-    assert "median 14.50 us" in out
+    assert "Per-step kernel time (indexed, cold; the sum of its kernels' spans over 2 steps): " \
+           "p10 14.10 us, median 14.50 us" in out
+    assert "| decode | 2 | k_proj_mfma | 5.500 |" in out
+    assert "| decode | 2 | k_merge_fused | 4.500 |" in out
+    assert "Per-step kernel time (decode, cold; the sum of its kernels' spans over 2 steps): " \
+           "p10 10.00 us, median 10.00 us" in out
     assert "| packed |" not in out
 
 
@@ -75,16 +91,20 @@ def _counters(path, rows):
 
 def test_counter_summary_and_traffic_lookup(tmp_path):
     """FETCH_SIZE reads half the copy's bytes (calibration 2), WRITE_SIZE all
-    of them (1): the summary scales each counter, and measured_traffic reads
-    the result back only for a mean |I| within 5% of the recorded one."""
+    of them (1): the summary scales each counter, for the indexed and the
+    decode steps, and measured_traffic reads the result back only for a mean
+    |I| within 5% of the recorded one."""
     step = [(READ, 1.0), (STEP, 10.0), (PROJ, 4000.0), (MERGE, 100.0)]
-    _counters(tmp_path / "f.csv", step * 3)
-    _counters(tmp_path / "w.csv", [(READ, 1.0), (STEP, 20.0), (PROJ, 100.0), (MERGE, 1.0)] * 3)
+    dstep = [(READ, 1.0), (FPROJ, 4500.0), (FMERGE, 150.0)]
+    _counters(tmp_path / "f.csv", step * 3 + [(READ, 1.0), (FPROJ, 1.0)] + dstep * 2)
+    _counters(tmp_path / "w.csv", [(READ, 1.0), (STEP, 20.0), (PROJ, 100.0), (MERGE, 1.0)] * 3 +
+              [(READ, 1.0), (FPROJ, 1.0)] + [(READ, 1.0), (FPROJ, 120.0), (FMERGE, 30.0)] * 2)
     kib = bench.COPY_PROBE_BYTES / 1024
     _counters(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", kib / 2)] * 3)
     _counters(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", kib)] * 3)
-    line = {"metric": "m", "config": {"workload": "w", "mean_active": 1000.0},
-            "roofline": {"bytes_per_launch": 8.0e6, "draft_call": {"bytes": 8.1e6}}}
+    line = {"metric": "m", "config": {"workload": "w", "mean_active": 1000.0, "mode": "decode"},
+            "roofline": {"bytes_per_launch": 8.05e6, "projection_stage": {"bytes_per_launch": 8.0e6},
+                         "draft_call": {"bytes": 8.1e6}}}
     (tmp_path / "bench.out").write_text("progress\n" + json.dumps(line) + "\n")
     out = bench.counter_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
                                 str(tmp_path / "cw.csv"), str(tmp_path / "bench.out"))
@@ -96,10 +116,16 @@ def test_counter_summary_and_traffic_lookup(tmp_path):
     call = proj + (100.0 * 2 + 1.0) * 1024
     assert float(kv["traffic_bytes_per_projection"]) == pytest.approx(proj, abs=1)
     assert float(kv["traffic_bytes_per_call"]) == pytest.approx(call, abs=1)
-    assert kv["source_sha256"] == bench.kernel_source_hash() and kv["mode"] == "indexed"
+    dproj = (4500.0 * 2 + 120.0) * 1024
+    assert float(kv["traffic_bytes_per_decode_project"]) == pytest.approx(dproj, abs=1)
+    assert float(kv["traffic_bytes_per_decode_step"]) == pytest.approx(dproj + (150.0 * 2 + 30.0) * 1024, abs=1)
+    assert float(kv["algorithmic_bytes_per_decode_project"]) == pytest.approx(8.05e6)
+    assert kv["source_sha256"] == bench.kernel_source_hash() and kv["modes"].split() == ["indexed", "decode"]
     p = tmp_path / "traffic.txt"
     p.write_text(out)
     assert bench.measured_traffic("w", "indexed", 1040.0, path=str(p)) == pytest.approx(call, abs=1)
+    assert bench.measured_traffic("w", "decode", 1000.0, "traffic_bytes_per_decode_project",
+                                  path=str(p)) == pytest.approx(dproj, abs=1)
     assert bench.measured_traffic("w", "indexed", 1060.0, path=str(p)) is None
     assert bench.measured_traffic("w", "packed", 1000.0, path=str(p)) is None
 

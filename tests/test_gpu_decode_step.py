@@ -1,0 +1,277 @@
+"""nanospec_decode_step, the decode step in one call (NanoSpec Sec. 3.2,
+decoding phase and sliding-window rebuild, then Sec. 3.1 Eq. 1 on
+W_head[I_{t+1}, :] with T_k).
+
+Two states run the same id script: one through nanospec_decode_step, the
+other through nanospec_step_update and then nanospec_draft_logits_topk
+(INDEXED).  At every step the active set, |I| and the top-k ids and values
+must be identical bit for bit; on sampled steps both are also checked against
+the oracle.  The step takes the two-launch form (state update beside the
+projection) once the state holds its active set from a previous decode step;
+its first launch then writes |I_t| into the first word of the workspace, which
+the tests set to a sentinel before each call to see which form ran.  The
+first step, and the step after an append or after a separate rebuild, take
+the three-launch form.  Shapes: the Llama- and Qwen-shaped heads (one and four
+hidden tiles), two hidden tiles, fp16, a tiny fp32 head (always three
+launches), both stream-source modes, and a HIP graph of fused steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.nanospec_oracle as O
+from dynamic_vocab_draft_amd import workloads as WL
+from tests.gpu_common import check_topk, dcode_of, dev_elems, dev_i32, say
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -12345
+
+
+@pytest.fixture(scope="module")
+def ns():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from dynamic_vocab_draft_amd import nanospec
+    return nanospec
+
+
+class Pair:
+    """The same sequence driven through the one-call step (a) and the
+    separate calls (b)."""
+
+    def __init__(self, ns, cfg, W_dev, dcode, M, k, mode=None):
+        self.ns, self.cfg, self.W, self.dcode, self.M, self.k = ns, cfg, W_dev, dcode, M, k
+        self.st_a = ns.NanoSpecState(cfg.V, cfg.w_max)
+        self.st_b = ns.NanoSpecState(cfg.V, cfg.w_max)
+        if mode is not None:
+            ns.nanospec_state_set_mode(self.st_a, mode)
+            ns.nanospec_state_set_mode(self.st_b, mode)
+        mk = lambda: (torch.empty(cfg.w_max, dtype=torch.int32, device="cuda"),
+                      torch.zeros(1, dtype=torch.int32, device="cuda"),
+                      torch.empty((M, k), dtype=torch.int32, device="cuda"),
+                      torch.empty((M, k), dtype=torch.float32, device="cuda"))
+        self.a, self.b = mk(), mk()
+        self.ws_a = ns.alloc_decode_workspace(cfg.w_max, 2 * 256, M, k, cfg.d)
+        self.ws_b = ns.alloc_workspace(cfg.w_max, M, k, cfg.d)
+        self.ws_b_decode = ns.alloc_decode_workspace(cfg.w_max, 2 * 256, M, k, cfg.d)
+
+    def append(self, ids):
+        d = dev_i32(ids)
+        for st in (self.st_a, self.st_b):
+            self.ns.nanospec_stream_append(st, d, len(ids), 0)
+
+    def rebuild(self):
+        for st, (ids, n, _, _) in ((self.st_a, self.a), (self.st_b, self.b)):
+            self.ns.nanospec_active_vocab(st, ids, n)
+
+    def step(self, tree, ver, h_dev):
+        ns, cfg = self.ns, self.cfg
+        td, vd = dev_i32(tree), dev_i32(ver)
+        ids, n, ti, tv = self.a
+        self.ws_a.view(torch.int32)[0] = SENTINEL
+        ns.nanospec_decode_step(self.st_a, td, len(tree), vd, len(ver), ids, n, self.W, cfg.V, cfg.d, self.dcode,
+                                h_dev, self.M, self.k, ti, tv, self.ws_a)
+        ids, n, ti, tv = self.b
+        ns.nanospec_step_update(self.st_b, td, len(tree), vd, len(ver), ids, n)
+        ns.nanospec_draft_logits_topk(self.W, ns.NS_INDEXED, ids, n, cfg.w_max, cfg.V, cfg.d, self.dcode, h_dev,
+                                      self.M, self.k, None, ti, tv, self.ws_b)
+
+    def fused_ran(self):
+        return int(self.ws_a.view(torch.int32)[0].item()) != SENTINEL
+
+    def compare(self, what):
+        torch.cuda.synchronize()
+        na, nb = int(self.a[1].item()), int(self.b[1].item())
+        assert na == nb, f"{what}: |I| {na} != {nb}"
+        assert torch.equal(self.a[0][:na], self.b[0][:nb]), f"{what}: active sets differ"
+        assert torch.equal(self.a[2], self.b[2]), f"{what}: top-k ids differ"
+        assert torch.equal(self.a[3], self.b[3]), f"{what}: top-k values differ"
+        return na
+
+
+def _run(ns, name, steps, check_every, M=None, k=None, dtype=None, mode=None, expect_fused=True):
+    cfg = WL.get_config(name)
+    M = M or cfg.M
+    k = k or cfg.k
+    dtype = dtype or cfg.dtype
+    say(f"decode step {name} M={M} k={k} {dtype} mode={mode}: generating inputs")
+    W = WL.make_weights(cfg)
+    if dtype != cfg.dtype:                                 # fp16 copies of the bf16 weights
+        W = WL.f32_to_fp16_bits(WL.bf16_bits_to_f32(W))
+    W_dev = dev_elems(W, dtype)
+    dcode = dcode_of(ns, dtype)
+    script = WL.make_id_script(cfg, steps)
+    seq = O.Sequence_(cfg.w_max, mode or "full")
+    code = {None: None, "ctx_only": ns.NS_STREAM_CTX_ONLY, "ext_only": ns.NS_STREAM_EXT_ONLY}[mode]
+    pair = Pair(ns, cfg, W_dev, dcode, M, k, code)
+    seq.append_prompt(script.prompt)
+    pair.append(script.prompt)
+    pair.rebuild()
+    fused_steps = 0
+    for t, tree, ver in WL.iter_steps(cfg, script):
+        h = WL.make_hidden(cfg, t, M=M)
+        if dtype != cfg.dtype:
+            h = WL.f32_to_fp16_bits(WL.bf16_bits_to_f32(h))
+        h_dev = dev_elems(h, dtype)
+        seq.step(tree, ver)
+        pair.step(tree, ver, h_dev)
+        what = f"{name} step {t}"
+        nn = pair.compare(what)
+        fused = pair.fused_ran()
+        fused_steps += fused
+        if t == 0:
+            assert not fused, f"{what}: the first step has no kept active set"
+        elif expect_fused:
+            assert fused, f"{what}: expected the two-launch form"
+        if t % check_every and t != steps - 1:
+            continue
+        I = seq.active()
+        assert nn == len(I) and np.array_equal(pair.a[0][:nn].cpu().numpy(), I), f"{what}: active set vs oracle"
+        ref, o_ids, o_vals = O.draft_head(h, W, I, k, dtype)
+        check_topk(pair.a[2].cpu().numpy(), pair.a[3].cpu().numpy(), ref, I, o_ids, o_vals, k, what)
+        say(f"{what}: |I| = {nn}, {'two' if fused else 'three'} launches, ok")
+    assert ns.nanospec_state_status(pair.st_a) == 0
+    return pair, fused_steps
+
+
+def test_decode_step_llama3_8b(ns):
+    _run(ns, "llama3_8b", steps=48, check_every=8)
+
+
+def test_decode_step_qwen25_7b(ns):
+    _run(ns, "qwen25_7b", steps=24, check_every=8)
+
+
+def test_decode_step_two_hidden_tiles_fp16(ns):
+    _run(ns, "llama3_8b", steps=20, check_every=10, M=20, k=16, dtype="fp16")
+
+
+def test_decode_step_tiny_fp32_three_launches(ns):
+    _run(ns, "tiny", steps=8, check_every=2, expect_fused=False)
+
+
+@pytest.mark.parametrize("mode", ["ctx_only", "ext_only"])
+def test_decode_step_stream_sources(ns, mode):
+    _run(ns, "llama3_8b", steps=12, check_every=4, M=4, k=8, mode=mode)
+
+
+def test_decode_step_after_append_and_rebuild(ns):
+    """An append, or a separate rebuild, drops the kept active set: the next
+    decode step takes three launches, and the one after it two again."""
+    cfg = WL.get_config("llama3_8b")
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    script = WL.make_id_script(cfg, 12)
+    pair = Pair(ns, cfg, W_dev, ns.NS_BF16, 8, 8)
+    seq = O.Sequence_(cfg.w_max)
+    seq.append_prompt(script.prompt)
+    pair.append(script.prompt)
+    pair.rebuild()
+    rng = np.random.default_rng(3)
+    for t, tree, ver in WL.iter_steps(cfg, script):
+        if t == 4:                                   # an append between steps
+            extra = rng.integers(0, cfg.V, size=100).astype(np.int32)
+            seq.append_prompt(extra)
+            pair.append(extra)
+        if t == 8:                                   # a separate rebuild
+            pair.rebuild()
+        h_dev = dev_elems(WL.make_hidden(cfg, t), cfg.dtype)
+        seq.step(tree, ver)
+        pair.step(tree, ver, h_dev)
+        pair.compare(f"step {t}")
+        assert pair.fused_ran() == (t not in (0, 4, 8)), f"step {t}: launch form"
+        I = seq.active()
+        nn = int(pair.a[1].item())
+        assert np.array_equal(pair.a[0][:nn].cpu().numpy(), I), f"step {t}: active set vs oracle"
+
+
+def test_decode_step_graph_replay(ns):
+    """Fused steps captured in a HIP graph and replayed give the results of
+    the same steps run eagerly on a twin state."""
+    cfg = WL.get_config("llama3_8b")
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    script = WL.make_id_script(cfg, 16)
+    steps = list(WL.iter_steps(cfg, script))
+    hs = [dev_elems(WL.make_hidden(cfg, t), cfg.dtype) for t, _, _ in steps]
+    trees = [dev_i32(tr) for _, tr, _ in steps]
+    vers = [dev_i32(v) for _, _, v in steps]
+
+    def fresh():
+        st = ns.NanoSpecState(cfg.V, cfg.w_max)
+        ids = torch.empty(cfg.w_max, dtype=torch.int32, device="cuda")
+        n = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ti = torch.empty((cfg.M, cfg.k), dtype=torch.int32, device="cuda")
+        tv = torch.empty((cfg.M, cfg.k), dtype=torch.float32, device="cuda")
+        ws = ns.alloc_decode_workspace(cfg.w_max, 512, cfg.M, cfg.k, cfg.d)
+        ns.nanospec_stream_append(st, dev_i32(script.prompt), len(script.prompt), 0)
+        ns.nanospec_active_vocab(st, ids, n)
+        return st, ids, n, ti, tv, ws
+
+    def run(obj, lo, hi):
+        st, ids, n, ti, tv, ws = obj
+        for i in range(lo, hi):
+            ns.nanospec_decode_step(st, trees[i], trees[i].numel(), vers[i], vers[i].numel(), ids, n, W_dev, cfg.V,
+                                    cfg.d, ns.NS_BF16, hs[i], cfg.M, cfg.k, ti, tv, ws)
+
+    eager, graphed = fresh(), fresh()
+    run(eager, 0, 2)
+    run(graphed, 0, 2)                               # both now keep their active sets
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(graphed, 2, 8)
+    for rep in range(3):                             # each replay repeats steps 2..7 on the advanced state
+        run(eager, 2, 8)
+        g.replay()
+        torch.cuda.synchronize()
+        n = int(eager[2].item())
+        assert int(graphed[2].item()) == n, f"replay {rep}: |I| differs"
+        for a, b, what in ((eager[1][:n], graphed[1][:n], "active ids"), (eager[3], graphed[3], "top-k ids"),
+                           (eager[4], graphed[4], "top-k values")):
+            assert torch.equal(a, b), f"replay {rep}: {what} differ"
+
+
+def test_decode_step_split_calls(ns):
+    """nanospec_decode_step_project then _select on one state, the one-call
+    step on a twin: identical outputs at every step, in both forms (the
+    first step takes three launches).  select is refused without a pending
+    project, with other buffers than project's, and after another call on
+    the state in between."""
+    cfg = WL.get_config("llama3_8b")
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    script = WL.make_id_script(cfg, 10)
+    M, k = 8, 8
+    pair = Pair(ns, cfg, W_dev, ns.NS_BF16, M, k)
+    pair.append(script.prompt)
+    pair.rebuild()
+    st, (ids, n, ti, tv), ws = pair.st_a, pair.a, pair.ws_a
+    sel = lambda i=ids, nn=n: ns.nanospec_decode_step_select(st, i, nn, cfg.V, cfg.d, ns.NS_BF16, M, k, ti, tv, ws)
+    with pytest.raises(ns.NanoSpecError):                # nothing pending
+        sel()
+    for t, tree, ver in WL.iter_steps(cfg, script):
+        h_dev = dev_elems(WL.make_hidden(cfg, t), cfg.dtype)
+        td, vd = dev_i32(tree), dev_i32(ver)
+        ws.view(torch.int32)[0] = SENTINEL
+        ns.nanospec_decode_step_project(st, td, len(tree), vd, len(ver), ids, n, W_dev, cfg.V, cfg.d, ns.NS_BF16,
+                                        h_dev, M, k, ws)
+        if t == 3:                                       # select with another active-set buffer
+            with pytest.raises(ns.NanoSpecError):
+                sel(i=pair.b[0])
+        sel()
+        b_ids, b_n, b_ti, b_tv = pair.b
+        ns.nanospec_decode_step(pair.st_b, td, len(tree), vd, len(ver), b_ids, b_n, W_dev, cfg.V, cfg.d,
+                                ns.NS_BF16, h_dev, M, k, b_ti, b_tv, pair.ws_b_decode)
+        torch.cuda.synchronize()
+        assert pair.fused_ran() == (t > 0), f"step {t}: launch form"
+        na = int(n.item())
+        assert na == int(b_n.item()) and torch.equal(ids[:na], b_ids[:na]), f"step {t}: active sets differ"
+        assert torch.equal(ti, b_ti) and torch.equal(tv, b_tv), f"step {t}: top-k differs"
+    # Another call on the state between project and select drops the pending step.
+    tree, ver = script.tree[0], script.ver[0]
+    ns.nanospec_decode_step_project(st, dev_i32(tree), len(tree), dev_i32(ver), len(ver), ids, n, W_dev, cfg.V,
+                                    cfg.d, ns.NS_BF16, dev_elems(WL.make_hidden(cfg, 0), cfg.dtype), M, k, ws)
+    ns.nanospec_stream_append(st, dev_i32(tree), len(tree), 0)
+    with pytest.raises(ns.NanoSpecError):
+        sel()
+    torch.cuda.synchronize()
