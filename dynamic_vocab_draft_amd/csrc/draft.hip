@@ -317,7 +317,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
                                                          int dv, const uint4* __restrict__ h, int M,
                                                          int S, int adapt, float* __restrict__ part,
-                                                         BatchStrides bs, int B, int tile_step, FuseArgs fa) {
+                                                         BatchStrides bs, int B, int tile_step, int dense,
+                                                         FuseArgs fa) {
   constexpr int KC = kDmaKC;
   constexpr int CPR = 4 * KC;                      // 16-byte chunks of one row per batch
   constexpr int RPI = NS_WAVE / CPR;               // rows per load instruction
@@ -374,6 +375,16 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // its CUs, whatever n_max is.
   int r0 = (int)((kblk / (8 * S)) * 8 + (kblk & 7)) * (kTile * RT);
   int split = (int)((kblk >> 3) % S);
+  // With dense > 0 (one sequence, a grid of `dense` resident blocks) the
+  // blocks take the (tile, slice) items in tile order instead: item q is
+  // tile q / S, slice q % S, and block L takes items L, L + dense, ... for as
+  // long as they hold live rows, so the live items fill the grid's first
+  // blocks whatever the live tile count.
+  unsigned q = kblk;
+  if (dense > 0) {
+    r0 = (int)(q / (unsigned)S) * (kTile * RT);
+    split = (int)(q % (unsigned)S);
+  }
   // Independent loads first: the active count and this lane's row ids.
   // Fused: |I_t| and the ids of the tuple and I_t columns; a column is live
   // iff it holds an entry of either.
@@ -578,14 +589,21 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   constexpr int NLOADS = NI * RT + (HDMA ? HI : KC * NMT);
   uint4 bq[NB][KC][HDMA ? 1 : NMT];
   const int nb = s_begin < s_end ? (s_end - s_begin + KC - 1) / KC : 0;   // wave-uniform
-  // The row ids of this block's next tile (tile_step > 0) are requested
-  // before this tile's rows, so they land while the rows stream (loads
-  // complete in issue order, so the batch waits below cover them).
+  // The row ids of this block's next tile (tile_step > 0 or dense > 0) are
+  // requested before this tile's rows, so they land while the rows stream
+  // (loads complete in issue order, so the batch waits below cover them).
   int gid_next[RT];
-  if (tile_step > 0) {
+  int r0_next = -1, split_next = split;
+  if (dense > 0) {
+    r0_next = (int)((q + (unsigned)dense) / (unsigned)S) * (kTile * RT);
+    split_next = (int)((q + (unsigned)dense) % (unsigned)S);
+  } else if (tile_step > 0) {
+    r0_next = r0 + tile_step;
+  }
+  if (r0_next >= 0) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int row = r0 + tile_step + r * kTile + i;
+      const int row = r0_next + r * kTile + i;
       if constexpr (FUSE) gid_next[r] = row < n_max ? col_id(row) : -1;
       else gid_next[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
     }
@@ -639,8 +657,10 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
       if (row < nt) fa.told[row] = (uint8_t)((obits[r] >> (gid[r] & 31)) & 1u);
     }
   }
-  if (tile_step == 0) return;                           // launch-uniform
-  r0 += tile_step;
+  if (r0_next < 0) return;                              // launch-uniform
+  r0 = r0_next;
+  split = split_next;
+  q += (unsigned)dense;
   if (r0 >= n) return;                                  // block-uniform
   __syncthreads();                                      // red is read before the buffers it aliases refill
 #pragma unroll
@@ -1274,9 +1294,8 @@ int max_splits(int n_max, int M, int d, int B) {
 }
 
 // Blocks of the single-sequence MFMA projection for M hidden rows that the
-// current device holds at once, less one (the state-update block of the
-// fused decode step), or 0 when the runtime cannot tell.  Cached per device
-// and instance.
+// current device holds at once, or 0 when the runtime cannot tell.  Cached
+// per device and instance.
 int resident_cap(int M) {
   constexpr int kDevs = 64;
   static std::atomic<int> cache[kDevs][5];
@@ -1299,7 +1318,7 @@ int resident_cap(int M) {
     (void)hipGetLastError();
     c = -1;
   } else {
-    c = cus * bpc - 1 > 0 ? cus * bpc - 1 : -1;
+    c = cus * bpc > 0 ? cus * bpc : -1;
   }
   cache[dev][inst].store(c, std::memory_order_relaxed);
   return c > 0 ? c : 0;
@@ -1330,10 +1349,10 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
 template <int NMT, int RT, bool F16, int HI, int NB, bool NT, bool FUSE>
 void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
-                   float* part, const BatchStrides& bs, int tile_step, const FuseArgs& fa) {
+                   float* part, const BatchStrides& bs, int tile_step, int dense, const FuseArgs& fa) {
   hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB, NT, FUSE>), dim3(blocks + (FUSE ? 1u : 0u)), dim3(kPThreads),
                      0, stream, (const uint4*)rows, mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt,
-                     part, bs, B, tile_step, fa);
+                     part, bs, B, tile_step, dense, fa);
 }
 
 template <bool F16>
@@ -1394,32 +1413,34 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
     }
   }
   // With max_blocks (a single sequence whose live row count only the device
-  // knows), the grid is cut to whole groups of 8 tiles x S slices within
-  // max_blocks, all resident at once, and each block steps on by the tiles
-  // the grid covers while its rows are live.  Past the live rows a full grid
-  // is mostly blocks that only read the count and exit, and with one block
-  // per CU they queue behind the live ones.  Qwen-shaped head (M = 60, one
-  // block per CU, S = 7): fused decode-step projection over about 1080 live
-  // of 3152 columns 9.0 -> 7.2 us, separate draft head over about 1000 live
-  // of 3072 rows 6.2 us either way; fewer slices so that 1280 rows fit one
-  // pass (S = 6) measured slower (7.7 us separate).
+  // knows), the grid is cut to a multiple of 8 blocks within max_blocks, all
+  // resident at once, and the blocks take the (tile, slice) items in tile
+  // order (dense > 0), so the live items, whatever their count, fill the
+  // first blocks.  Past the live rows a full grid is mostly blocks that only
+  // read the count and exit, and with one block per CU they queue behind the
+  // live ones.  Qwen-shaped head (M = 60, one block per CU, S = 7, about
+  // 1080 live of 3152 columns): fused decode-step projection 9.0 -> 7.2 us
+  // with the grid cut to whole groups of 8 tiles x S slices (the live tiles
+  // past 32 then took a second pass), decode step 15.8 -> 12.8 us with the
+  // dense order; fewer slices so that 1280 rows fit whole groups (S = 6)
+  // measured slower (separate draft head 6.2 -> 7.7 us).
+  int dense = 0;
   if (max_blocks > 0 && !batched && !adapt && B == 1) {
-    const unsigned group = 8u * (unsigned)S;
-    const unsigned lim = (unsigned)max_blocks / group * group;
+    const unsigned lim = (unsigned)max_blocks / 8u * 8u;
     if (lim > 0 && lim < per_seq) {
       per_seq = lim;
-      tile_step = (int)(lim / (unsigned)S) * kTile * rt;
+      dense = (int)lim;
     }
   }
   const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA_ONLY(NMTV, RTV, HIV, NBV, NTV)                                                         \
   launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, false>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, \
-                                                      S, adapt, part, bs, tile_step, FuseArgs{})
+                                                      S, adapt, part, bs, tile_step, dense, FuseArgs{})
 #define NS_LAUNCH_MFMA(NMTV, RTV, HIV, NBV, NTV)                                                                \
   do {                                                                                                          \
     if (fa)                                                                                                     \
       launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, true>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, \
-                                                         h, M, S, adapt, part, bs, tile_step, *fa);              \
+                                                         h, M, S, adapt, part, bs, tile_step, dense, *fa);       \
     else                                                                                                        \
       NS_LAUNCH_MFMA_ONLY(NMTV, RTV, HIV, NBV, NTV);                                                            \
   } while (0)
@@ -1820,8 +1841,9 @@ int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, i
   BatchStrides bs{};
   bs.part = partial_floats(L.n_cols, M, L.SP);
   // The slices of the separate draft head on I_{t+1} (draft_plan: L.S), so
-  // that both forms sum the same partials, and a grid of resident blocks.
-  const int cap = resident_cap(M);
+  // that both forms sum the same partials, and a grid of resident blocks
+  // beside the state-update block.
+  const int cap = resident_cap(M) - 1;
   float* part = (float*)(base + L.part);
   (void)hipGetLastError();
   rc = dtype == NS_BF16
