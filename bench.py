@@ -459,8 +459,8 @@ def main():
         backbone = make_backbone(torch, cfg)
 
         class Head:
-            def __init__(self, mode, fn):
-                self.mode, self.fn = mode, fn
+            def __init__(self, mode, fn, owns_state=False):
+                self.mode, self.fn, self.owns_state = mode, fn, owns_state
 
             def __call__(self, t, comp, copy):
                 self.fn(t, comp, copy)
@@ -492,7 +492,12 @@ def main():
             ns.nanospec_draft_logits_topk(packed, ns.NS_PACKED, ids, n_act, cfg.w_max, cfg.V, cfg.d, dcode, hs[t],
                                           cfg.M, cfg.k, None, tids[t], tvals[t], ws)
 
-        heads = {"indexed": Head(ns.NS_INDEXED, head_indexed),
+        def head_decode(t, comp, copy):
+            backbone()
+            decode_part(t)
+
+        heads = {"decode": Head(DECODE, head_decode, owns_state=True),
+                 "indexed": Head(ns.NS_INDEXED, head_indexed),
                  "slots_serial": Head(SLOTS, head_slots(False)),
                  "slots_overlap": Head(SLOTS, head_slots(True)),
                  "full_gather_overlap": Head(ns.NS_PACKED, head_full_gather)}
@@ -957,23 +962,26 @@ def pipeline_leg(torch, cfg, backbone, warm_up, state_part, heads, flush, Wm, R,
     draft backbone stand-in, and the draft head in one of several variants
     (``heads[name](t, comp, copy)`` enqueues the head's part after the state
     update: it may fork work to the copy stream and must join it before the
-    head).  ``base`` runs the state update and the backbone only.  Graph
-    replay of R steps, cold, the cache-streaming read subtracted; per-step ms."""
+    head; a head with ``owns_state`` runs the state update itself and follows
+    no separate one).  ``base`` runs the state update and the backbone only,
+    ``backbone`` the backbone alone.  Graph replay of R steps, cold, the
+    cache-streaming read subtracted; per-step ms."""
     def run_fn(name):
         def run():
             comp = torch.cuda.current_stream()
             for t in range(Wm, Wm + R):
                 flush(t)
-                state_part(t)
+                if name not in ("flush", "backbone") and not (name in heads and heads[name].owns_state):
+                    state_part(t)
                 if name == "flush":
                     continue
-                if name == "base":
+                if name in ("base", "backbone"):
                     backbone()
                 else:
                     heads[name](t, comp, copy_stream)
         return run
 
-    names = ["flush", "base"] + list(heads)
+    names = ["flush", "base", "backbone"] + list(heads)
     out = {}
     for name in names:
         mode = heads[name].mode if name in heads else None
@@ -998,10 +1006,14 @@ def pipeline_leg(torch, cfg, backbone, warm_up, state_part, heads, flush, Wm, R,
         del g
     flush_ms = out.pop("flush")
     res = {name: v - flush_ms for name, v in out.items()}
+    # A head's cost over the backbone: over base when it follows the separate
+    # state update, over the backbone alone when it runs the update itself.
     return {"backbone": "bf16 GEMM chain, Llama-3-8B decoder-layer weight shapes, M rows",
             "steps": R, "step_ms": res,
-            "head_cost_ms": {name: res[name] - res["base"] for name in heads},
-            "note": "per step: state update, backbone, draft head variant; cold; hipGraph replay"}
+            "head_cost_ms": {name: res[name] - res["backbone" if heads[name].owns_state else "base"]
+                             for name in heads},
+            "note": "per step: state update, backbone, draft head variant (decode: backbone, then the decode "
+                    "step with its own state update); cold; hipGraph replay"}
 
 
 def overlap_leg(torch, ns, cfg, W, ids, n_act, packed, h, ws, dcode, copy_stream, flush):

@@ -130,6 +130,14 @@ def _run(ns, name, steps, check_every, M=None, k=None, dtype=None, mode=None, ex
         check_topk(pair.a[2].cpu().numpy(), pair.a[3].cpu().numpy(), ref, I, o_ids, o_vals, k, what)
         say(f"{what}: |I| = {nn}, {'two' if fused else 'three'} launches, ok")
     assert ns.nanospec_state_status(pair.st_a) == 0
+    # The state's bitmap after the last step holds I exactly: the slot-stable
+    # buffer, planned from it, maps exactly I.
+    pk = ns.NanoSpecPacked(cfg.V, cfg.w_max)
+    ns.nanospec_packed_update(pk, pair.st_a, W_dev, cfg.d, dcode, torch.zeros((cfg.w_max, cfg.d),
+                              dtype=torch.bfloat16 if dtype != "fp32" else torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    slots = pk.slot_ids.cpu().numpy()
+    assert np.array_equal(np.sort(slots[slots >= 0]), seq.active()), f"{name}: the state's bitmap is not I"
     return pair, fused_steps
 
 
