@@ -1742,7 +1742,7 @@ int nanospec_draft_logprob_topk(const void* rows, int32_t mode, const int32_t* r
 // shapes allow it, the step takes two launches instead of three: the
 // projection with the state update in its block 0 (k_proj_mfma with FUSE),
 // then k_merge_fused.  Otherwise the three separate launches run and a copy
-// refreshes cur.  nanospec_decode_step_project enqueues the first launch
+// refreshes cur (only for shapes that allow the two-launch form).  nanospec_decode_step_project enqueues the first launch
 // (the first two of three) and records the form in the state's handle;
 // nanospec_decode_step_select enqueues the rest.
 // ---------------------------------------------------------------------------
@@ -1805,11 +1805,15 @@ int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, i
   const int nd = st->mode == NS_STREAM_CTX_ONLY ? 0 : n_draft;
   const int nv = st->mode == NS_STREAM_CTX_ONLY ? 0 : n_ver;
   const DecodeLayout L = decode_layout(w_max, nd + nv, M, d);
-  const bool fuse = st->cur_valid && is_mfma_dtype(dtype) && (w_max & 3) == 0 && w_max <= kFuseMaxWmax &&
-                    nd + nv <= kPThreads && fused_state_lds(V, nd + nv) <= kFuseLds &&
-                    ((V + 31) >> 5) <= kFuseCompactWords * kMergeThreads && !use_msplit(L.n_cols, M, 1) &&
-                    L.n_cols <= kMergeChunk && L.SP <= 16;
+  // Shapes for which the two-launch form exists; it then needs only the kept
+  // I_t (cur_valid).
+  const bool fusable = is_mfma_dtype(dtype) && (w_max & 3) == 0 && w_max <= kFuseMaxWmax && nd + nv <= kPThreads &&
+                       fused_state_lds(V, nd + nv) <= kFuseLds &&
+                       ((V + 31) >> 5) <= kFuseCompactWords * kMergeThreads && !use_msplit(L.n_cols, M, 1) &&
+                       L.n_cols <= kMergeChunk && L.SP <= 16;
+  const bool fuse = fusable && st->cur_valid;
   nanospec_state::Pending pd;
+  pd.keep = fusable;
   pd.nt = nd + nv;
   pd.d = d;
   pd.dtype = dtype;
@@ -1875,7 +1879,7 @@ int nanospec_decode_step_select(nanospec_state* st, int32_t* active_ids, int32_t
     const DraftPlan p = draft_plan(n_active, w_max, 1, d, dtype, M, k, ws);
     rc = draft_select(active_ids, n_active, w_max, 1, V, M, k, nullptr, topk_ids, topk_vals, p, false, nullptr,
                       nullptr, stream);
-    if (rc != NS_OK) return rc;
+    if (rc != NS_OK || !pd.keep) return rc;   // shapes without the two-launch form keep no I_t
     (void)hipGetLastError();
     const int g = (w_max + 255) / 256;
     hipLaunchKernelGGL(k_copy_cur, dim3(g > 64 ? 64 : g), dim3(256), 0, stream, v.cur, v.n_cur, active_ids, n_active,

@@ -33,6 +33,7 @@ struct nanospec_state {
   // form (0 none, 1 three launches, 2 fused) and what select must match.
   struct Pending {
     int form = 0;
+    bool keep = false;   // the shapes allow the two-launch form: keep I_{t+1} in cur
     int nt = 0, d = 0, dtype = 0, M = 0, k = 0;
     const void* ws = nullptr;
     const int32_t* ids = nullptr;

@@ -428,7 +428,8 @@ int nanospec_batch_draft_logprob_topk(const void* w, const int32_t* row_ids, con
  * state update runs beside the projection, which covers I_t and the tuple
  * entries (a superset of I_{t+1}), and the merge keeps only members of
  * I_{t+1}.  Otherwise the three launches run, followed by a copy of I_{t+1}
- * into cur.  Any other call that changes the window or rebuilds I
+ * into cur when the shapes allow the two-launch form (and by nothing when
+ * they do not: no I_t is kept then).  Any other call that changes the window or rebuilds I
  * (stream_append, active_vocab, step_update, batch_step_update, reset) drops
  * cur until the next decode step.
  *   w, V, d, dtype, h, M, k, topk_ids, topk_vals : as nanospec_draft_logits_topk
