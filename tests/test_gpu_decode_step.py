@@ -283,3 +283,83 @@ def test_decode_step_split_calls(ns):
     with pytest.raises(ns.NanoSpecError):
         sel()
     torch.cuda.synchronize()
+
+
+def _edge_run(ns, cfg, steps, expect):
+    """Drives a Pair through (tree, ver) steps and checks, at every step,
+    identical outputs in both forms, the launch form against `expect`, the
+    active set against the oracle, and the state's status bits."""
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    script = WL.make_id_script(cfg, 4)
+    pair = Pair(ns, cfg, W_dev, ns.NS_BF16, 8, 8)
+    seq = O.Sequence_(cfg.w_max)
+    seq.append_prompt(script.prompt)
+    pair.append(script.prompt)
+    pair.rebuild()
+    for t, (tree, ver) in enumerate(steps):
+        h_dev = dev_elems(WL.make_hidden(cfg, t), cfg.dtype)
+        seq.step(tree, ver)
+        pair.step(tree, ver, h_dev)
+        nn = pair.compare(f"step {t}")
+        assert pair.fused_ran() == expect[t], f"step {t}: launch form"
+        I = seq.active()
+        assert nn == len(I) and np.array_equal(pair.a[0][:nn].cpu().numpy(), I), f"step {t}: active set vs oracle"
+    return pair
+
+
+def test_decode_step_forms_across_tuple_sizes(ns):
+    """A step with more than 256 tuple entries has no two-launch form: it
+    drops the kept I_t, so the step after it takes three launches and the one
+    after that two again.  A step with no tuple entries keeps I_t as it is."""
+    cfg = WL.get_config("llama3_8b")
+    rng = np.random.default_rng(11)
+    small = lambda: (rng.integers(0, cfg.V, 60).astype(np.int32), rng.integers(0, cfg.V, 8).astype(np.int32))
+    big = (rng.integers(0, cfg.V, 290).astype(np.int32), rng.integers(0, cfg.V, 8).astype(np.int32))
+    empty = (np.zeros(0, np.int32), np.zeros(0, np.int32))
+    steps = [small(), small(), big, small(), small(), empty, small()]
+    _edge_run(ns, cfg, steps, [False, True, False, False, True, True, True])
+
+
+def test_decode_step_w_max_not_multiple_of_4(ns):
+    """W_max = 3070: never the two-launch form, same results as the separate
+    calls."""
+    cfg = WL.get_config("llama3_8b", w_max=3070)
+    rng = np.random.default_rng(12)
+    steps = [(rng.integers(0, cfg.V, 60).astype(np.int32), rng.integers(0, cfg.V, 8).astype(np.int32))
+             for _ in range(4)]
+    _edge_run(ns, cfg, steps, [False] * 4)
+
+
+def test_decode_step_bad_ids(ns):
+    """Ids outside [0, V) in the tuples are skipped by both forms and set the
+    sticky status bit of both states."""
+    cfg = WL.get_config("llama3_8b")
+    rng = np.random.default_rng(13)
+    steps = []
+    for t in range(4):
+        tree = rng.integers(0, cfg.V, 60).astype(np.int32)
+        ver = rng.integers(0, cfg.V, 8).astype(np.int32)
+        if t == 2:
+            tree[[3, 17]] = [cfg.V, -5]
+            ver[1] = cfg.V + 100
+        steps.append((tree, ver))
+    # The oracle skips the same ids: drop them from its copy of the script.
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    script = WL.make_id_script(cfg, 4)
+    pair = Pair(ns, cfg, W_dev, ns.NS_BF16, 8, 8)
+    seq = O.Sequence_(cfg.w_max)
+    seq.append_prompt(script.prompt)
+    pair.append(script.prompt)
+    pair.rebuild()
+    for t, (tree, ver) in enumerate(steps):
+        h_dev = dev_elems(WL.make_hidden(cfg, t), cfg.dtype)
+        ok = lambda a: a[(a >= 0) & (a < cfg.V)]
+        seq.step(ok(tree), ok(ver))
+        pair.step(tree, ver, h_dev)
+        nn = pair.compare(f"step {t}")
+        assert pair.fused_ran() == (t > 0), f"step {t}: launch form"
+        I = seq.active()
+        assert nn == len(I) and np.array_equal(pair.a[0][:nn].cpu().numpy(), I), f"step {t}: active set vs oracle"
+    assert ns.nanospec_state_status(pair.st_a) == ns.nanospec_state_status(pair.st_b) != 0
