@@ -13,7 +13,10 @@ the tests set to a sentinel before each call to see which form ran.  The
 first step, and the step after an append or after a separate rebuild, take
 the three-launch form.  Shapes: the Llama- and Qwen-shaped heads (one and four
 hidden tiles), two hidden tiles, fp16, a tiny fp32 head (always three
-launches), both stream-source modes, and a HIP graph of fused steps."""
+launches), both stream-source modes, a HIP graph of fused steps, the step
+split into nanospec_decode_step_project and _select, the state's bitmap after
+the steps, and the edge cases of the form: tuples past 256 entries, empty
+tuples, W_max not a multiple of 4, and ids outside [0, V)."""
 import numpy as np
 import pytest
 import torch
