@@ -331,9 +331,14 @@ def main():
     t_flush = time_graph(g_flush, needs_state=False)
 
     res = {}
+    decode_fused = False
     for m in modes:
         # eager reference outputs for the replay check
+        if m == DECODE:
+            ws_dec.view(torch.int32)[0] = -1           # the fused first launch writes |I_t| here
         time_eager(body(m, False), m)
+        if m == DECODE:
+            decode_fused = int(ws_dec.view(torch.int32)[0].item()) >= 0
         ref_ids, ref_vals = tids.clone(), tvals.clone()
         tids.fill_(-7)
         g_cold = capture(body(m, True), m)
@@ -393,7 +398,7 @@ def main():
         draft_call = {"kernels": "nanospec_draft_logits_topk = k_proj_mfma + k_merge_cols", "mode": sname,
                       "bytes": draft_bytes, "avg_us": rs["draft_ms"] * 1e3, "achieved": achieved,
                       "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name, sname, n_mean)}
-    if best == DECODE:
+    if best == DECODE and decode_fused:
         # The step's dominant kernel is its first launch: the projection of
         # the tuple and I_t columns with the state update in block 0.  Its
         # algorithmic bytes: the projection's (I_{t+1} rows, h, ids) and the
@@ -430,14 +435,15 @@ def main():
         "config": {"workload": f"{cfg.name}: V={cfg.V} d={cfg.d} W_max={cfg.w_max} M={cfg.M} k={cfg.k}, "
                                f"{cfg.n_tree} draft-tree + {cfg.k_ver} verify ids per step",
                    "mode": mname[best], "cache": "cold (512 MiB streamed through the caches between steps)",
+                   "decode_two_launch_form": decode_fused if DECODE in modes else None,
                    "mean_active": n_mean, "lead_in_steps": lead, "timed_steps": [t0, T - 1],
                    "timing": "hipGraph replay of the timed steps"},
         "roofline": roofline,
         "step": {"alg_bytes": step_bytes, "step_GBps": step_bytes / (ms * 1e-3) / 1e9,
                  "state_update_us": rs["state_ms"] * 1e3 if rs else None,
                  "draft_us": rs["draft_ms"] * 1e3 if rs else None,
-                 "decode_first_launch_us": res[DECODE]["project_ms"] * 1e3 if DECODE in res else None,
-                 "decode_merge_us": res[DECODE]["select_ms"] * 1e3 if DECODE in res else None,
+                 "decode_first_launch_us": res[DECODE]["project_ms"] * 1e3 if DECODE in res and decode_fused else None,
+                 "decode_merge_us": res[DECODE]["select_ms"] * 1e3 if DECODE in res and decode_fused else None,
                  "warm_ms": r["warm_ms"], "eager_warm_ms": r["eager_warm_ms"],
                  "per_mode": {mname[m]: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res[m].items()}
                               for m in modes},
@@ -637,7 +643,7 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, bench_
     rf = b["roofline"]
     if rf.get("draft_call") is None:
         raise SystemExit(f"{bench_out}: needs a run of the indexed mode")
-    with_decode = b["config"]["mode"] == "decode"
+    with_decode = b["config"]["mode"] == "decode" and bool(b["config"].get("decode_two_launch_form"))
     alg_dec = float(rf["bytes_per_launch"]) if with_decode else None
     alg_proj = float(rf.get("projection_stage", rf)["bytes_per_launch"])
     alg_call = float(rf["draft_call"]["bytes"])

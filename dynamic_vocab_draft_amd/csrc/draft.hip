@@ -1802,6 +1802,7 @@ int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, i
   int rc = draft_check(w, NS_INDEXED, active_ids, w_max, 1, V, d, dtype, h, M, k, ws, ws_bytes);
   if (rc != NS_OK) return rc;
   if (ws_bytes < nanospec_decode_step_workspace_bytes(w_max, n_draft + n_ver, M, k, d)) return NS_ECAPACITY;
+  st->pending.form = 0;                              // a step this call replaces is not selected any more
   const int nd = st->mode == NS_STREAM_CTX_ONLY ? 0 : n_draft;
   const int nv = st->mode == NS_STREAM_CTX_ONLY ? 0 : n_ver;
   const DecodeLayout L = decode_layout(w_max, nd + nv, M, d);
@@ -1855,7 +1856,10 @@ int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, i
                                 &fa, cap)
            : launch_mfma<true>(w, NS_INDEXED, nullptr, nullptr, L.n_cols, V, d, h, M, L.S, 0, part, 1, bs, stream,
                                &fa, cap);
-  if (rc != NS_OK) return rc;
+  if (rc != NS_OK) {
+    st->drop_cur();
+    return rc;
+  }
   pd.form = 2;
   st->pending = pd;
   return NS_OK;
@@ -1888,6 +1892,8 @@ int nanospec_decode_step_select(nanospec_state* st, int32_t* active_ids, int32_t
     if (rc == NS_OK) st->cur_valid = true;
     return rc;
   }
+  // Fused form: unless the merge launches, cur no longer matches the window.
+  st->drop_cur();
   const DecodeLayout L = decode_layout(w_max, pd.nt, M, d);
   char* base = (char*)ws;
   (void)hipGetLastError();

@@ -155,7 +155,7 @@ __device__ __forceinline__ void step_fast_body(int4* lds4, int stage, const ns_s
     }
   }
   NS_ISSUE_FENCE();
-  for (int w = tid; w < TH * wpt; w += TH) bm[w] = 0u;
+  for (int w4 = tid; w4 < TH * wpt / 4; w4 += TH) lds4[w4] = make_int4(0, 0, 0, 0);   // wpt is a multiple of 4
   if constexpr (FUSE) {                           // dids = C_draft, then C_ver, then -1
     if (tid < n_draft) dids[tid] = d_in;
     if (tid < n_ver) dids[n_draft + tid] = v_in;

@@ -102,7 +102,8 @@ def test_counter_summary_and_traffic_lookup(tmp_path):
     kib = bench.COPY_PROBE_BYTES / 1024
     _counters(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", kib / 2)] * 3)
     _counters(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", kib)] * 3)
-    line = {"metric": "m", "config": {"workload": "w", "mean_active": 1000.0, "mode": "decode"},
+    line = {"metric": "m", "config": {"workload": "w", "mean_active": 1000.0, "mode": "decode",
+                                "decode_two_launch_form": True},
             "roofline": {"bytes_per_launch": 8.05e6, "projection_stage": {"bytes_per_launch": 8.0e6},
                          "draft_call": {"bytes": 8.1e6}}}
     (tmp_path / "bench.out").write_text("progress\n" + json.dumps(line) + "\n")
