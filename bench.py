@@ -1262,7 +1262,9 @@ def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
     batched step update and one batched draft head (INDEXED) per step, cold,
     graph replay; the step-update-only graph is subtracted for the draft
     time.  Algorithmic bytes of a batched draft call: the sum over sequences
-    of n_b*d*s + M*d*s + 4*n_b + 8*M*k."""
+    of n_b*d*s + M*d*s + 4*n_b + 8*M*k.  The same steps through the batched
+    decode step (two launches per step once the states hold their active
+    sets) are timed the same way."""
     res = []
     s = cfg.elem_bytes
     for B in Bs:
@@ -1286,13 +1288,24 @@ def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
         tvals = torch.empty((B, cfg.M, cfg.k), device="cuda")
         prompts = [torch.as_tensor(sc.prompt, dtype=torch.int32).cuda() for sc in scripts]
 
-        def init():
+        wsd = ns.alloc_batch_decode_workspace(B, cfg.w_max, nd + nv, cfg.M, cfg.k, cfg.d)
+
+        def decode(t):
+            ns.nanospec_batch_decode_step(bt, trees[t], nd, n_d, nd, vers[t], nv, n_v, nv, ids, n, W, cfg.V, cfg.d,
+                                          dcode, hs[t], cfg.M, cfg.k, tids, tvals, wsd)
+
+        def init(dec=False):
+            # dec: the last warm-up step is a decode step, so that the state
+            # holds its active set and every timed decode step is fused.
             for b in range(B):
                 m = bt.member(b)
                 ns.nanospec_state_reset(m)
                 ns.nanospec_stream_append(m, prompts[b], prompts[b].numel(), 0)
             for t in range(warm):
-                ns.nanospec_batch_step_update(bt, trees[t], nd, n_d, nd, vers[t], nv, n_v, nv, ids, n)
+                if dec and t == warm - 1:
+                    decode(t)
+                else:
+                    ns.nanospec_batch_step_update(bt, trees[t], nd, n_d, nd, vers[t], nv, n_v, nv, ids, n)
 
         sizes = []
 
@@ -1313,15 +1326,20 @@ def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
         torch.cuda.synchronize()
         n_mean = float(torch.stack(sizes).float().mean().item())
 
-        def timed(fn):
-            init()
+        def decode_body():
+            for t in range(warm, T):
+                flush(t)
+                decode(t)
+
+        def timed(fn, dec=False):
+            init(dec)
             torch.cuda.synchronize()
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 fn()
             ts = []
             for _ in range(3):
-                init()
+                init(dec)
                 torch.cuda.synchronize()
                 a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
@@ -1339,17 +1357,21 @@ def batch_leg(torch, ns, WL, cfg, W, dcode, flush, Bs, steps=48, warm=8):
         t_f = timed(flush_only)
         t_s = timed(body(False))
         t_a = timed(body(True))
+        t_d = timed(decode_body, dec=True)
         step_us = (t_a - t_f) / steps * 1e3
+        dec_us = (t_d - t_f) / steps * 1e3
         draft_us = (t_a - t_s) / steps * 1e3
         draft_bytes = B * (n_mean * cfg.d * s + cfg.M * cfg.d * s + 4 * n_mean + 8 * cfg.M * cfg.k)
         res.append({"B": B, "step_us": step_us, "sequence_steps_per_s": B / (step_us * 1e-6),
                     "state_update_us": (t_s - t_f) / steps * 1e3, "draft_us": draft_us,
                     "draft_GBps": draft_bytes / (draft_us * 1e-6) / 1e9,
                     "draft_frac_of_peak": draft_bytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                    "mean_active": n_mean})
-        del bt, hs, wsb
+                    "mean_active": n_mean, "decode_step_us": dec_us,
+                    "decode_sequence_steps_per_s": B / (dec_us * 1e-6)})
+        del bt, hs, wsb, wsd
     return {"workload": f"{cfg.name} x B independent sequences (seeds differ), batched step update + batched "
-                        f"INDEXED draft head, cold, hipGraph replay of {steps} steps", "per_B": res}
+                        f"INDEXED draft head, and the batched decode step, cold, hipGraph replay of {steps} steps",
+            "per_B": res}
 
 
 def tree_leg(torch, ns, cfg, W, ids, n_act, dcode, flush, K=10, F=10, N=60, D=5, R=20):
@@ -1478,15 +1500,20 @@ def ablation_leg(torch, ns, WL, cfg, W, dcode, flush, steps=48, warm=16):
         torch.cuda.synchronize()
         n_mean = float(torch.stack(sizes).float().mean().item())
 
-        def timed(fn):
-            init()
+        def decode_body():
+            for t in range(warm, T):
+                flush(t)
+                decode(t)
+
+        def timed(fn, dec=False):
+            init(dec)
             torch.cuda.synchronize()
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 fn()
             ts = []
             for _ in range(3):
-                init()
+                init(dec)
                 torch.cuda.synchronize()
                 a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()

@@ -300,18 +300,66 @@ constexpr int kFuseRU = 3;                        // 16-byte ring loads per stat
 constexpr int kFuseMaxWmax = kPThreads * kFuseCU;
 static_assert(kFuseMaxWmax <= kPThreads * kFuseRU * 4, "ring loads cover W_max");
 
+// The first sequence's arguments; sequence b's state lies st_stride bytes
+// further per sequence, its tuples dstride / vstride ids further, and its
+// workspace region (flags, hdr, colid, told) ws_stride bytes further.  nd and
+// nv are the tuple column counts (the batch's bounds); nd_dev / nv_dev, when
+// given, hold each sequence's own counts.
 struct FuseArgs {
   ns_state_view v;
+  size_t st_stride;
   const int32_t* dids;
-  int nd;
+  int nd, dstride;
+  const int32_t* nd_dev;
   const int32_t* vids;
-  int nv;
+  int nv, vstride;
+  const int32_t* nv_dev;
   FuseCtl fc;
   int32_t* colid;
   uint8_t* told;
+  size_t ws_stride;
 };
 
-template <int NMT, int RT, bool F16, int HI, int NB, bool NT, bool FUSE>
+// Sequence b's pointers (the counts nd / nv stay the column bounds).
+__device__ __forceinline__ FuseArgs fuse_seq(const FuseArgs& fa, int b) {
+  FuseArgs f = fa;
+  if (b == 0) return f;
+  const size_t so = (size_t)b * fa.st_stride, wo = (size_t)b * fa.ws_stride;
+  auto at = [](auto* p, size_t off) { return (decltype(p))((char*)p + off); };
+  f.v.len = at(fa.v.len, so);
+  f.v.status = at(fa.v.status, so);
+  f.v.ring = at(fa.v.ring, so);
+  f.v.first = at(fa.v.first, so);
+  f.v.bitmap = at(fa.v.bitmap, so);
+  f.v.cur = at(fa.v.cur, so);
+  f.v.n_cur = at(fa.v.n_cur, so);
+  f.v.next_bm = at(fa.v.next_bm, so);
+  f.fc.cur = at(fa.fc.cur, so);
+  f.fc.n_cur = at(fa.fc.n_cur, so);
+  f.fc.next_bm = at(fa.fc.next_bm, so);
+  f.fc.flags = at(fa.fc.flags, wo);
+  f.fc.hdr = at(fa.fc.hdr, wo);
+  f.colid = at(fa.colid, wo);
+  f.told = at(fa.told, wo);
+  f.dids = fa.dids + (size_t)b * fa.dstride;
+  f.vids = fa.vids + (size_t)b * fa.vstride;
+  return f;
+}
+
+// A sequence's own tuple count: the device count clamped to the bound, or the
+// bound when there are no device counts.
+__device__ __forceinline__ int fuse_count(const int32_t* dev, int b, int bound) {
+  if (!dev) return bound;
+  const int c = dev[b];
+  return c < 0 ? 0 : (c > bound ? bound : c);
+}
+
+// FUSE: 0 the projection alone; 1 the decode step's first launch for one
+// sequence (block 0 updates its state); 2 the same for a batch (blocks
+// 0..B-1, tuple counts per sequence).  The batch form is an instance of its
+// own: its per-sequence offsets and counts in the single form cost the
+// decode step 0.3-0.5 us.
+template <int NMT, int RT, bool F16, int HI, int NB, bool NT, int FUSE>
 __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict__ rows, int mode,
                                                          const int32_t* __restrict__ row_ids,
                                                          const int32_t* __restrict__ n_dev, int n_max, int V,
@@ -340,10 +388,22 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   static_assert(sizeof(f32x4_t) * kPW * RT * NMT * NS_WAVE <= (NMT <= 2 ? sizeof(abuf) : sizeof(bbuf)),
                 "wave tiles fit the reused buffer");
   auto red = reinterpret_cast<f32x4_t (*)[RT][NMT][NS_WAVE]>(NMT <= 2 ? &abuf[0][0][0] : &bbuf[0][0][0]);
-  if constexpr (FUSE) {
+  constexpr bool FB = FUSE == 2;
+  if constexpr (FUSE == 1) {
     if (blockIdx.x == 0) {                              // the window-state update, in abuf's LDS
       step_fast_body<int4, kFuseRU, kPThreads, kFuseCU>((int4*)&abuf[0][0][0], 0, fa.v, fa.dids, fa.nd, fa.vids, fa.nv,
                                                         nullptr, nullptr, nullptr, fa.fc);
+      return;
+    }
+  }
+  if constexpr (FB) {
+    if (blockIdx.x < (unsigned)B) {                     // sequence b's window-state update, in abuf's LDS
+      const int b = (int)blockIdx.x;
+      const FuseArgs f = fuse_seq(fa, b);
+      step_fast_body<int4, kFuseRU, kPThreads, kFuseCU>((int4*)&abuf[0][0][0], 0, f.v, f.dids,
+                                                        fuse_count(fa.nd_dev, b, fa.nd), f.vids,
+                                                        fuse_count(fa.nv_dev, b, fa.nv), nullptr, nullptr, nullptr,
+                                                        f.fc);
       return;
     }
   }
@@ -353,7 +413,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
   // every sequence before any sequence's high tiles, and every slice of a
   // tile goes to the same XCD (L mod 8).  kblk = (tg S + s) 8 + x is the
   // block's index among its sequence's blocks; for B = 1 it is L.
-  const unsigned L = blockIdx.x - (FUSE ? 1u : 0u);
+  const unsigned L = blockIdx.x - (FB ? (unsigned)B : (FUSE ? 1u : 0u));
   const int seq = (int)((L / (8u * (unsigned)S)) % (unsigned)B);
   const unsigned kblk = (L / (8u * (unsigned)S * (unsigned)B)) * (8u * (unsigned)S) + L % (8u * (unsigned)S);
   {
@@ -386,25 +446,33 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
     split = (int)(q % (unsigned)S);
   }
   // Independent loads first: the active count and this lane's row ids.
-  // Fused: |I_t| and the ids of the tuple and I_t columns; a column is live
-  // iff it holds an entry of either.
+  // Fused: |I_t|, the sequence's tuple counts and the ids of the tuple and
+  // I_t columns; a column is live iff it holds an entry of either.
+  const FuseArgs fs = FB ? fuse_seq(fa, seq) : fa;
   const int cb = fa.fc.cbase, nt = fa.nd + fa.nv;
-  int n_old = 0;
-  if constexpr (FUSE) {
-    n_old = *fa.fc.n_cur;
+  int n_old = 0, nd_s = 0, nv_s = 0;
+  if constexpr (FUSE != 0) {
+    n_old = *fs.fc.n_cur;
     n_old = n_old < 0 ? 0 : (n_old > fa.v.w_max ? fa.v.w_max : n_old);
+    if constexpr (FB) {
+      nd_s = fuse_count(fa.nd_dev, seq, fa.nd);
+      nv_s = fuse_count(fa.nv_dev, seq, fa.nv);
+    }
   }
   auto col_id = [&](int row) -> int {
-    if (row < nt) return row < fa.nd ? fa.dids[row] : fa.vids[row - fa.nd];
-    return (row >= cb && row - cb < fa.v.w_max) ? fa.fc.cur[row - cb] : -1;
+    if (row < nt) return row < fa.nd ? fs.dids[row] : fs.vids[row - fa.nd];
+    return (row >= cb && row - cb < fa.v.w_max) ? fs.fc.cur[row - cb] : -1;
   };
-  auto col_live = [&](int row) { return row < nt || (row >= cb && row < cb + n_old); };
+  auto col_live = [&](int row) {
+    if constexpr (FB) return row < nd_s || (row >= fa.nd && row < fa.nd + nv_s) || (row >= cb && row < cb + n_old);
+    else return row < nt || (row >= cb && row < cb + n_old);
+  };
   const int n = FUSE ? n_max : clamp_n(n_dev, n_max);
   int gid[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const int row = r0 + r * kTile + i;
-    if constexpr (FUSE) gid[r] = row < n_max ? col_id(row) : -1;
+    if constexpr (FUSE != 0) gid[r] = row < n_max ? col_id(row) : -1;
     else gid[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
   }
   // With `adapt`, S was launched for a few live rows: if n calls for fewer
@@ -443,8 +511,8 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int row = r0 + r * kTile + i;
-      if (row < n_max) fa.colid[row] = ok[r] ? gid[r] : -1;
-      obits[r] = (row < nt && ok[r]) ? fa.v.bitmap[gid[r] >> 5] : 0u;
+      if (row < n_max) fs.colid[row] = ok[r] ? gid[r] : -1;
+      obits[r] = (row < nt && ok[r]) ? fs.v.bitmap[gid[r] >> 5] : 0u;
     }
   }
   // Load sources.  Row tr of a tile is requested by the lanes of instruction
@@ -604,7 +672,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int row = r0_next + r * kTile + i;
-      if constexpr (FUSE) gid_next[r] = row < n_max ? col_id(row) : -1;
+      if constexpr (FUSE != 0) gid_next[r] = row < n_max ? col_id(row) : -1;
       else gid_next[r] = row < n_max ? (row_ids ? row_ids[row] : row) : -1;
     }
   }
@@ -654,7 +722,7 @@ __global__ __launch_bounds__(kPThreads) void k_proj_mfma(const uint4* __restrict
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int row = r0 + r * kTile + i;
-      if (row < nt) fa.told[row] = (uint8_t)((obits[r] >> (gid[r] & 31)) & 1u);
+      if (row < nt) fs.told[row] = (uint8_t)((obits[r] >> (gid[r] & 31)) & 1u);
     }
   }
   if (r0_next < 0) return;                              // launch-uniform
@@ -1096,24 +1164,53 @@ __device__ __forceinline__ void fused_compact(const uint32_t* __restrict__ next_
   }
 }
 
+// The merge's buffers for the first sequence; sequence b (blockIdx.z) finds
+// its partial sums part_stride floats further per sequence, its workspace
+// region (colid, flags, told, hdr) ws_stride bytes further, its state
+// st_stride bytes further, its outputs M k (top-k), w_max (ids) and 1
+// (count) further.
+struct MergeFuseArgs {
+  const float* part;
+  size_t part_stride;
+  const int32_t* colid;
+  const uint8_t* flags;
+  const uint8_t* told;
+  const int32_t* hdr;
+  size_t ws_stride;
+  int32_t* out_ids;
+  float* out_vals;
+  const uint32_t* next_bm;
+  uint32_t* bitmap;
+  int32_t* cur;
+  int32_t* n_cur;
+  int64_t* len;
+  size_t st_stride;
+  int32_t* act_ids;
+  int32_t* n_act;
+};
+
 template <int SPT>
-__global__ __launch_bounds__(kMergeThreads) void k_merge_fused(const float* __restrict__ part, int S, int n_max,
-                                                               int M, int cbase, int nt,
-                                                               const int32_t* __restrict__ colid,
-                                                               const uint8_t* __restrict__ flags,
-                                                               const uint8_t* __restrict__ told,
-                                                               const int32_t* __restrict__ hdr, int V, int k,
-                                                               int32_t* __restrict__ out_ids,
-                                                               float* __restrict__ out_vals,
-                                                               const uint32_t* __restrict__ next_bm,
-                                                               uint32_t* __restrict__ bitmap,
-                                                               int32_t* __restrict__ act_ids,
-                                                               int32_t* __restrict__ n_act,
-                                                               int32_t* __restrict__ cur, int32_t* __restrict__ n_cur,
-                                                               int64_t* __restrict__ len, int w_max) {
+__global__ __launch_bounds__(kMergeThreads) void k_merge_fused(MergeFuseArgs a, int S, int n_max, int M, int cbase,
+                                                               int nt, int V, int k, int w_max) {
   constexpr int U = kMergeCols;
   __shared__ SelectSmem sm;
   const int m = blockIdx.x, tid = threadIdx.x;
+  const size_t b = blockIdx.z;
+  auto at = [](auto* p, size_t off) { return (decltype(p))((char*)p + off); };
+  const float* __restrict__ part = a.part + b * a.part_stride;
+  const int32_t* __restrict__ colid = at(a.colid, b * a.ws_stride);
+  const uint8_t* __restrict__ flags = at(a.flags, b * a.ws_stride);
+  const uint8_t* __restrict__ told = at(a.told, b * a.ws_stride);
+  const int32_t* __restrict__ hdr = at(a.hdr, b * a.ws_stride);
+  int32_t* __restrict__ out_ids = a.out_ids + b * M * k;
+  float* __restrict__ out_vals = a.out_vals + b * M * k;
+  const uint32_t* __restrict__ next_bm = at(a.next_bm, b * a.st_stride);
+  uint32_t* __restrict__ bitmap = at(a.bitmap, b * a.st_stride);
+  int32_t* __restrict__ cur = at(a.cur, b * a.st_stride);
+  int32_t* __restrict__ n_cur = at(a.n_cur, b * a.st_stride);
+  int64_t* __restrict__ len = at(a.len, b * a.st_stride);
+  int32_t* __restrict__ act_ids = a.act_ids + b * w_max;
+  int32_t* __restrict__ n_act = a.n_act + b;
   if (m == M) {                                       // block-uniform
     fused_compact(next_bm, bitmap, V, w_max, act_ids, n_act, cur, n_cur, len, hdr[1]);
     return;
@@ -1158,6 +1255,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_fused(const float* __re
     out_ids[(size_t)m * k + r] = x ? ns::key_id(x) : -1;
     out_vals[(size_t)m * k + r] = x ? ns::key_val(x) : -INFINITY;
   });
+}
+
+// Fallback of the batched decode step: sequence blockIdx.y's cur / n_cur
+// from its I_{t+1} (states stride bytes apart).
+__global__ void k_copy_cur_batch(ns_state_view v0, size_t stride, const int32_t* __restrict__ ids,
+                                 const int32_t* __restrict__ n, int w_max) {
+  const size_t b = blockIdx.y;
+  int32_t* cur = (int32_t*)((char*)v0.cur + b * stride);
+  int32_t* n_cur = (int32_t*)((char*)v0.n_cur + b * stride);
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g == 0) *n_cur = n[b];
+  for (int j = g; j < w_max; j += gridDim.x * blockDim.x) cur[j] = ids[b * w_max + j];
 }
 
 // Fallback of the decode step: the state's cur / n_cur from I_{t+1}.
@@ -1251,6 +1360,14 @@ bool use_msplit(int n_max, int M, int B) {
 
 int pick_rt(int M, int n_max, int B) { return use_msplit(n_max, M, B) ? kMsplitRT : (M <= 16 ? 1 : 2); }
 
+// Tile height (16 rt rows) of a batch of B sequences of one slice per tile
+// with one hidden tile of at most 8 rows: the largest of 1, 2, 4 that still
+// gives about kBatchTargetBlocks blocks for kBatchLiveRowsHint rows each.
+int batch_rt(int B) {
+  const long per_rt1 = (long)B * (kBatchLiveRowsHint / kTile);
+  return per_rt1 >= 4L * kBatchTargetBlocks ? 4 : (per_rt1 >= 2L * kBatchTargetBlocks ? 2 : 1);
+}
+
 // Number of d-slices S for the MFMA path: about kTargetBlocks blocks, each
 // wave keeping at least kKC k-steps.  When the live row count is
 // only known on the device (n_dev given) and M <= 16, S is sized as if at
@@ -1307,11 +1424,11 @@ int resident_cap(int M) {
   }
   int c = cache[dev][inst].load(std::memory_order_relaxed);
   if (c != 0) return c > 0 ? c : 0;
-  const void* fn = inst == 0   ? (const void*)k_proj_mfma<1, 1, false, 1, 4, true, false>
-                   : inst == 1 ? (const void*)k_proj_mfma<1, 1, false, 2, 4, true, false>
-                   : inst == 2 ? (const void*)k_proj_mfma<2, 2, false, 1, 2, true, false>
-                   : inst == 3 ? (const void*)k_proj_mfma<3, 2, false, 6, 2, true, false>
-                               : (const void*)k_proj_mfma<4, 2, false, 8, 2, true, false>;
+  const void* fn = inst == 0   ? (const void*)k_proj_mfma<1, 1, false, 1, 4, true, 0>
+                   : inst == 1 ? (const void*)k_proj_mfma<1, 1, false, 2, 4, true, 0>
+                   : inst == 2 ? (const void*)k_proj_mfma<2, 2, false, 1, 2, true, 0>
+                   : inst == 3 ? (const void*)k_proj_mfma<3, 2, false, 6, 2, true, 0>
+                               : (const void*)k_proj_mfma<4, 2, false, 8, 2, true, 0>;
   int cus = 0, bpc = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, kPThreads, 0) != hipSuccess) {
@@ -1346,11 +1463,11 @@ int launch_valu(int mt, const void* rows, int mode, const int32_t* row_ids, cons
   return ns_launch_status();
 }
 
-template <int NMT, int RT, bool F16, int HI, int NB, bool NT, bool FUSE>
+template <int NMT, int RT, bool F16, int HI, int NB, bool NT, int FUSE>
 void launch_mfma_t(unsigned blocks, int B, hipStream_t stream, const void* rows, int mode, const int32_t* row_ids,
                    const int32_t* n_dev, int n_max, int V, int dv, const void* h, int M, int S, int adapt,
                    float* part, const BatchStrides& bs, int tile_step, int dense, const FuseArgs& fa) {
-  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB, NT, FUSE>), dim3(blocks + (FUSE ? 1u : 0u)), dim3(kPThreads),
+  hipLaunchKernelGGL((k_proj_mfma<NMT, RT, F16, HI, NB, NT, FUSE>), dim3(blocks + (FUSE == 2 ? (unsigned)B : (FUSE ? 1u : 0u))), dim3(kPThreads),
                      0, stream, (const uint4*)rows, mode, row_ids, n_dev, n_max, V, dv, (const uint4*)h, M, S, adapt,
                      part, bs, B, tile_step, dense, fa);
 }
@@ -1372,8 +1489,7 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   int rt = pick_rt(M, n_max, B);
   int nb_bufs = 4;
   if (batched && M <= 8) {
-    const long per_rt1 = (long)B * (kBatchLiveRowsHint / kTile);
-    rt = per_rt1 >= 4L * kBatchTargetBlocks ? 4 : (per_rt1 >= 2L * kBatchTargetBlocks ? 2 : 1);
+    rt = batch_rt(B);
     nb_bufs = rt > 1 ? 1 : 4;
   }
   // Tiles rounded up to a multiple of 8 (padded tiles start past n_max and
@@ -1424,6 +1540,16 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   // past 32 then took a second pass), decode step 15.8 -> 12.8 us with the
   // dense order; fewer slices so that 1280 rows fit whole groups (S = 6)
   // measured slower (separate draft head 6.2 -> 7.7 us).
+  // Batched fused decode steps: each pass covers the tuple columns and
+  // kBatchLiveRowsHint I_t columns per sequence; blocks step on while live.
+  if (fa && B > 1 && !adapt) {
+    const unsigned hint =
+        (unsigned)((fa->fc.cbase + kBatchLiveRowsHint + kTile * rt - 1) / (kTile * rt) + 7) / 8 * 8u;
+    if (hint * (unsigned)S < per_seq) {
+      per_seq = hint * (unsigned)S;
+      tile_step = (int)hint * kTile * rt;
+    }
+  }
   int dense = 0;
   if (max_blocks > 0 && !batched && !adapt && B == 1) {
     const unsigned lim = (unsigned)max_blocks / 8u * 8u;
@@ -1434,13 +1560,16 @@ int launch_mfma(const void* rows, int mode, const int32_t* row_ids, const int32_
   }
   const unsigned blocks = per_seq * (unsigned)B;
 #define NS_LAUNCH_MFMA_ONLY(NMTV, RTV, HIV, NBV, NTV)                                                         \
-  launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, false>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, \
-                                                      S, adapt, part, bs, tile_step, dense, FuseArgs{})
+  launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, 0>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, h, M, \
+                                                  S, adapt, part, bs, tile_step, dense, FuseArgs{})
 #define NS_LAUNCH_MFMA(NMTV, RTV, HIV, NBV, NTV)                                                                \
   do {                                                                                                          \
-    if (fa)                                                                                                     \
-      launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, true>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, \
-                                                         h, M, S, adapt, part, bs, tile_step, dense, *fa);       \
+    if (fa && B > 1)                                                                                            \
+      launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, 2>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, \
+                                                      h, M, S, adapt, part, bs, tile_step, dense, *fa);          \
+    else if (fa)                                                                                                \
+      launch_mfma_t<NMTV, RTV, F16, HIV, NBV, NTV, 1>(blocks, B, stream, rows, mode, row_ids, n_dev, n_max, V, dv, \
+                                                      h, M, S, adapt, part, bs, tile_step, dense, *fa);          \
     else                                                                                                        \
       NS_LAUNCH_MFMA_ONLY(NMTV, RTV, HIV, NBV, NTV);                                                            \
   } while (0)
@@ -1756,11 +1885,13 @@ struct DecodeLayout {
 };
 
 // Columns: the n_tuple tuple entries, then I_t from the next tile boundary.
-DecodeLayout decode_layout(int32_t w_max, int32_t n_tuple, int32_t M, int32_t d) {
+// One sequence's region; a batch of B holds B of them back to back, with the
+// slices of the separate batched draft head.
+DecodeLayout decode_layout(int32_t w_max, int32_t n_tuple, int32_t M, int32_t d, int32_t B = 1) {
   DecodeLayout L;
   L.cbase = ((n_tuple > 0 ? n_tuple : 0) + kTile - 1) / kTile * kTile;
   L.n_cols = L.cbase + w_max;
-  L.S = launch_splits(false, w_max, M, d, NS_BF16, 1);   // the slices of the separate draft head
+  L.S = launch_splits(false, w_max, M, d, NS_BF16, B);   // the slices of the separate draft head
   L.SP = slice_pitch(L.S);
   L.part = 256;
   L.colid = L.part + partial_bytes(L.n_cols, M, L.SP, 1);
@@ -1775,6 +1906,27 @@ DecodeLayout decode_layout(int32_t w_max, int32_t n_tuple, int32_t M, int32_t d)
 size_t fused_state_lds(int V, int n_tuple) {
   const int nd64 = (n_tuple + NS_WAVE - 1) & ~(NS_WAVE - 1);
   return ((size_t)kPThreads * fused_wpt<kPThreads>(V) + 2 * (size_t)nd64) * 4;
+}
+
+// The merge launch of the fused decode step for B sequences (grid M + 1 by
+// B), with the instance of the layout's slice pitch.
+int launch_merge_fused(const MergeFuseArgs& ma, const DecodeLayout& L, int M, int B, int nt, int V, int k, int w_max,
+                       hipStream_t stream) {
+  (void)hipGetLastError();
+  const dim3 grid(M + 1, 1, B);
+#define NS_LAUNCH_FMERGE(SPV)                                                                                      \
+  hipLaunchKernelGGL((k_merge_fused<SPV>), grid, dim3(kMergeThreads), 0, stream, ma, L.S, L.n_cols, M, L.cbase, nt, V, \
+                     k, w_max)
+  switch (L.SP) {
+    case 1: NS_LAUNCH_FMERGE(1); break;
+    case 2: NS_LAUNCH_FMERGE(2); break;
+    case 4: NS_LAUNCH_FMERGE(4); break;
+    case 8: NS_LAUNCH_FMERGE(8); break;
+    case 12: NS_LAUNCH_FMERGE(12); break;
+    default: NS_LAUNCH_FMERGE(16); break;
+  }
+#undef NS_LAUNCH_FMERGE
+  return ns_launch_status();
 }
 
 }  // namespace
@@ -1834,13 +1986,13 @@ int nanospec_decode_step_project(nanospec_state* st, const int32_t* draft_ids, i
     return NS_OK;
   }
   char* base = (char*)ws;
-  FuseArgs fa;
+  FuseArgs fa{};
   fa.v = v;
   fa.dids = nd > 0 ? draft_ids : v.ring;             // read unconditionally by the update
   fa.nd = nd;
   fa.vids = nv > 0 ? ver_ids : v.ring;
   fa.nv = nv;
-  fa.fc = FuseCtl{v.cur, v.n_cur, (uint8_t*)(base + L.flags), (int32_t*)base, v.next_bm, L.cbase};
+  fa.fc = FuseCtl{v.cur, v.n_cur, (uint8_t*)(base + L.flags), (int32_t*)base, v.next_bm, L.cbase, nd, nv};
   fa.told = (uint8_t*)(base + L.told);
   fa.colid = (int32_t*)(base + L.colid);
   BatchStrides bs{};
@@ -1897,21 +2049,22 @@ int nanospec_decode_step_select(nanospec_state* st, int32_t* active_ids, int32_t
   const DecodeLayout L = decode_layout(w_max, pd.nt, M, d);
   char* base = (char*)ws;
   (void)hipGetLastError();
-#define NS_LAUNCH_FMERGE(SPV)                                                                                    \
-  hipLaunchKernelGGL((k_merge_fused<SPV>), dim3(M + 1), dim3(kMergeThreads), 0, stream, (const float*)(base + L.part), \
-                     L.S, L.n_cols, M, L.cbase, pd.nt, (const int32_t*)(base + L.colid),                          \
-                     (const uint8_t*)(base + L.flags), (const uint8_t*)(base + L.told), (const int32_t*)base, V, k,  \
-                     topk_ids, topk_vals, v.next_bm, v.bitmap, active_ids, n_active, v.cur, v.n_cur, v.len, w_max)
-  switch (L.SP) {
-    case 1: NS_LAUNCH_FMERGE(1); break;
-    case 2: NS_LAUNCH_FMERGE(2); break;
-    case 4: NS_LAUNCH_FMERGE(4); break;
-    case 8: NS_LAUNCH_FMERGE(8); break;
-    case 12: NS_LAUNCH_FMERGE(12); break;
-    default: NS_LAUNCH_FMERGE(16); break;
-  }
-#undef NS_LAUNCH_FMERGE
-  rc = ns_launch_status();
+  MergeFuseArgs ma{};
+  ma.part = (const float*)(base + L.part);
+  ma.colid = (const int32_t*)(base + L.colid);
+  ma.flags = (const uint8_t*)(base + L.flags);
+  ma.told = (const uint8_t*)(base + L.told);
+  ma.hdr = (const int32_t*)base;
+  ma.out_ids = topk_ids;
+  ma.out_vals = topk_vals;
+  ma.next_bm = v.next_bm;
+  ma.bitmap = v.bitmap;
+  ma.cur = v.cur;
+  ma.n_cur = v.n_cur;
+  ma.len = v.len;
+  ma.act_ids = active_ids;
+  ma.n_act = n_active;
+  rc = launch_merge_fused(ma, L, M, 1, pd.nt, V, k, w_max, stream);
   if (rc == NS_OK) st->cur_valid = true;
   return rc;
 }
@@ -1926,6 +2079,121 @@ int nanospec_decode_step(nanospec_state* st, const int32_t* draft_ids, int32_t n
   if (rc != NS_OK) return rc;
   return nanospec_decode_step_select(st, active_ids, n_active, V, d, dtype, M, k, topk_ids, topk_vals, ws, ws_bytes,
                                      stream);
+}
+
+
+size_t nanospec_batch_decode_step_workspace_bytes(int32_t B, int32_t w_max, int32_t n_tuple, int32_t M, int32_t k,
+                                                  int32_t d) {
+  if (B < 1 || B > NS_MAX_BATCH || w_max < 1 || w_max > NS_MAX_WMAX || n_tuple < 0 || n_tuple > 2 * kFastMaxIds)
+    return 0;
+  const size_t sep = nanospec_batch_draft_workspace_bytes(B, w_max, M, k, d);
+  if (sep == 0) return 0;
+  const size_t fused = (size_t)B * decode_layout(w_max, n_tuple, M, d, B).total;
+  return sep > fused ? sep : fused;
+}
+
+int nanospec_batch_decode_step(nanospec_batch* bt, const int32_t* draft_ids, int32_t draft_stride,
+                               const int32_t* n_draft, int32_t nd_max, const int32_t* ver_ids, int32_t ver_stride,
+                               const int32_t* n_ver, int32_t nv_max, int32_t* active_ids, int32_t* n_active,
+                               const void* w, int32_t V, int32_t d, int32_t dtype, const void* h, int32_t M,
+                               int32_t k, int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!bt || !draft_ids || !ver_ids || !n_draft || !n_ver || !active_ids || !n_active || !topk_ids || !topk_vals)
+    return NS_EINVAL;
+  if (nd_max < 0 || nv_max < 0 || nd_max > kFastMaxIds || nv_max > kFastMaxIds) return NS_EINVAL;
+  if (draft_stride < nd_max || ver_stride < nv_max) return NS_EINVAL;
+  const int B = bt->B;
+  const ns_state_view& v0 = bt->members[0].view;
+  if (V != v0.V) return NS_EINVAL;
+  for (int b = 0; b < B; ++b)                         // as nanospec_batch_step_update
+    if (bt->members[b].mode == NS_STREAM_CTX_ONLY) return NS_EINVAL;
+  const int w_max = v0.w_max;
+  int rc = draft_check(w, NS_INDEXED, active_ids, w_max, B, V, d, dtype, h, M, k, ws, ws_bytes);
+  if (rc != NS_OK) return rc;
+  if (ws_bytes < nanospec_batch_decode_step_workspace_bytes(B, w_max, nd_max + nv_max, M, k, d)) return NS_ECAPACITY;
+  const int nt = nd_max + nv_max;
+  const DecodeLayout L = decode_layout(w_max, nt, M, d, B);
+  const bool fusable_shape = is_mfma_dtype(dtype) && (w_max & 3) == 0 && w_max <= kFuseMaxWmax && nt <= kPThreads &&
+                             fused_state_lds(V, nt) <= kFuseLds &&
+                             ((V + 31) >> 5) <= kFuseCompactWords * kMergeThreads && !use_msplit(L.n_cols, M, B) &&
+                             L.n_cols <= kMergeChunk && L.SP <= 16;
+  // Where the separate batched draft head takes taller tiles (M <= 8, B of
+  // 32 and more) the fused projection, which keeps 16-row tiles, measured
+  // slower than the three launches (Llama-shaped batch, B = 64: 106.6 against
+  // 88.4 us per step, B = 32: 55.6 against 53.8; B = 8: 23.3 against 24.1).
+  const bool tall = M <= 8 && B > 1 && L.S == 1 && batch_rt(B) > 1;
+  const bool fusable = fusable_shape && !tall;
+  bool kept = true;
+  for (int b = 0; b < B; ++b) kept = kept && bt->members[b].cur_valid;
+  if (!fusable || !kept) {
+    rc = nanospec_batch_step_update(bt, draft_ids, draft_stride, n_draft, nd_max, ver_ids, ver_stride, n_ver, nv_max,
+                                    active_ids, n_active, nullptr, stream);
+    if (rc != NS_OK) return rc;
+    rc = nanospec_batch_draft_logits_topk(w, active_ids, n_active, w_max, B, V, d, dtype, h, M, k, nullptr, topk_ids,
+                                          topk_vals, ws, ws_bytes, stream);
+    if (rc != NS_OK || !fusable) return rc;            // shapes without the two-launch form keep no I_t
+    (void)hipGetLastError();
+    const int g = (w_max + 255) / 256;
+    hipLaunchKernelGGL(k_copy_cur_batch, dim3(g > 64 ? 64 : g, B), dim3(256), 0, stream, v0, bt->stride, active_ids,
+                       n_active, w_max);
+    rc = ns_launch_status();
+    if (rc == NS_OK)
+      for (int b = 0; b < B; ++b) bt->members[b].cur_valid = true;
+    return rc;
+  }
+  for (int b = 0; b < B; ++b) bt->members[b].drop_cur();   // until the merge has launched
+  char* base = (char*)ws;
+  FuseArgs fa{};
+  fa.v = v0;
+  fa.st_stride = bt->stride;
+  fa.dids = draft_ids;
+  fa.nd = nd_max;
+  fa.dstride = draft_stride;
+  fa.nd_dev = n_draft;
+  fa.vids = ver_ids;
+  fa.nv = nv_max;
+  fa.vstride = ver_stride;
+  fa.nv_dev = n_ver;
+  fa.fc = FuseCtl{v0.cur, v0.n_cur, (uint8_t*)(base + L.flags), (int32_t*)base, v0.next_bm, L.cbase, nd_max, nv_max};
+  fa.told = (uint8_t*)(base + L.told);
+  fa.colid = (int32_t*)(base + L.colid);
+  fa.ws_stride = L.total;
+  BatchStrides bs{};
+  bs.part = L.total / sizeof(float);                  // each sequence's region, partial sums at L.part
+  bs.h = (size_t)M * d * (dtype == NS_FP32 ? 4 : 2) / 16;
+  // One sequence: the resident grid in tile order beside the state-update
+  // block, as the single-sequence step.
+  const int cap = B == 1 ? resident_cap(M) - 1 : 0;
+  float* part = (float*)(base + L.part);
+  (void)hipGetLastError();
+  rc = dtype == NS_BF16
+           ? launch_mfma<false>(w, NS_INDEXED, nullptr, nullptr, L.n_cols, V, d, h, M, L.S, 0, part, B, bs, stream,
+                                &fa, cap)
+           : launch_mfma<true>(w, NS_INDEXED, nullptr, nullptr, L.n_cols, V, d, h, M, L.S, 0, part, B, bs, stream,
+                               &fa, cap);
+  if (rc != NS_OK) return rc;
+  MergeFuseArgs ma{};
+  ma.part = part;
+  ma.part_stride = L.total / sizeof(float);
+  ma.colid = (const int32_t*)(base + L.colid);
+  ma.flags = (const uint8_t*)(base + L.flags);
+  ma.told = (const uint8_t*)(base + L.told);
+  ma.hdr = (const int32_t*)base;
+  ma.ws_stride = L.total;
+  ma.out_ids = topk_ids;
+  ma.out_vals = topk_vals;
+  ma.next_bm = v0.next_bm;
+  ma.bitmap = v0.bitmap;
+  ma.cur = v0.cur;
+  ma.n_cur = v0.n_cur;
+  ma.len = v0.len;
+  ma.st_stride = bt->stride;
+  ma.act_ids = active_ids;
+  ma.n_act = n_active;
+  rc = launch_merge_fused(ma, L, M, B, nt, V, k, w_max, stream);
+  if (rc == NS_OK)
+    for (int b = 0; b < B; ++b) bt->members[b].cur_valid = true;
+  return rc;
 }
 
 }  // extern "C"

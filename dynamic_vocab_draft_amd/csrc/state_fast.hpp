@@ -83,9 +83,11 @@ __device__ __forceinline__ void bm_store8(uint32_t* __restrict__ dst, int w, int
 }
 
 // Outputs of the state update when it runs beside the projection of a
-// fused decode step (nanospec_decode_step).  That projection reads the
-// columns [0, nd + nv) as the step's tuple entries (C_draft as given, then
-// C_ver) and [cbase, cbase + n_cur) as I_t (cur); the update flags each
+// fused decode step (nanospec_decode_step, nanospec_batch_decode_step).
+// That projection reads the columns [0, nd_cols) as the step's C_draft as
+// given, [nd_cols, nd_cols + nv_cols) as its C_ver (each padded to the
+// batch's largest count) and [cbase, cbase + n_cur) as I_t (cur); the
+// update flags each
 // column whose id is in I_{t+1}: an I_t column iff its id stays active, a
 // tuple column iff its id is active and this is its first occurrence in the
 // tuples.  (An id of both I_t and the tuples is then flagged twice; the
@@ -100,6 +102,8 @@ struct FuseCtl {
   int32_t* hdr;           // hdr[0] <- |I_t|, hdr[1] <- entries appended (C)
   uint32_t* next_bm;      // [ceil(V/32)] <- the bitmap of I_{t+1}
   int cbase;              // column of I_t's first entry
+  int nd_cols, nv_cols;   // tuple columns: C_draft in [0, nd_cols), C_ver in [nd_cols, nd_cols + nv_cols);
+                          // columns past this step's counts are flagged 0
 };
 
 // TH threads per workgroup.  CU > 0 selects the fused form (fc is used; at
@@ -266,8 +270,9 @@ __device__ __forceinline__ void step_fast_body(int4* lds4, int stage, const ns_s
       const int j = tid + u * TH;
       if (j < n_old && j < w_max) fc.flags[fc.cbase + j] = member(curv[u]) ? 1 : 0;
     }
-    if (tid < n_draft) fc.flags[tid] = (sfp[tid] == tid && member(d_in)) ? 1 : 0;
-    if (tid < n_ver) fc.flags[n_draft + tid] = (sfp[n_draft + tid] == n_draft + tid && member(v_in)) ? 1 : 0;
+    if (tid < fc.nd_cols) fc.flags[tid] = (tid < n_draft && sfp[tid] == tid && member(d_in)) ? 1 : 0;
+    if (tid < fc.nv_cols)
+      fc.flags[fc.nd_cols + tid] = (tid < n_ver && sfp[n_draft + tid] == n_draft + tid && member(v_in)) ? 1 : 0;
     if (tid == 0) {
       fc.hdr[0] = n_old;
       fc.hdr[1] = C;

@@ -120,6 +120,10 @@ _SIGS = {
                                                     c_int32, c_int32, c_vp, c_int32, c_int32, c_vp, c_size, c_vp]),
     "nanospec_decode_step_select": (ctypes.c_int, [c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_int32, c_int32, c_vp,
                                                    c_vp, c_vp, c_size, c_vp]),
+    "nanospec_batch_decode_step_workspace_bytes": (c_size, [c_int32] * 6),
+    "nanospec_batch_decode_step": (ctypes.c_int, [c_vp, c_vp, c_int32, c_vp, c_int32, c_vp, c_int32, c_vp, c_int32,
+                                                  c_vp, c_vp, c_vp, c_int32, c_int32, c_int32, c_vp, c_int32, c_int32,
+                                                  c_vp, c_vp, c_vp, c_size, c_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -493,6 +497,33 @@ def nanospec_packed_update(pk: NanoSpecPacked, st, w: torch.Tensor, d: int, dtyp
                            stream=None) -> None:
     _check(_lib.nanospec_packed_update(pk.handle, st.handle, _ptr(w), d, dtype, _ptr(rows), _stream(stream)),
            "nanospec_packed_update")
+
+
+def nanospec_batch_decode_step_workspace_bytes(B: int, w_max: int, n_tuple: int, M: int, k: int, d: int) -> int:
+    return _lib.nanospec_batch_decode_step_workspace_bytes(B, w_max, n_tuple, M, k, d)
+
+
+def nanospec_batch_decode_step(bt: "NanoSpecBatch", draft_ids: torch.Tensor, draft_stride: int, n_draft: torch.Tensor,
+                               nd_max: int, ver_ids: torch.Tensor, ver_stride: int, n_ver: torch.Tensor, nv_max: int,
+                               active_ids: torch.Tensor, n_active: torch.Tensor, w: torch.Tensor, V: int, d: int,
+                               dtype: int, h: torch.Tensor, M: int, k: int, topk_ids: torch.Tensor,
+                               topk_vals: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    _check(_lib.nanospec_batch_decode_step(bt.handle, _ptr(draft_ids), draft_stride, _ptr(n_draft), nd_max,
+                                           _ptr(ver_ids), ver_stride, _ptr(n_ver), nv_max, _ptr(active_ids),
+                                           _ptr(n_active), _ptr(w), V, d, dtype, _ptr(h), M, k, _ptr(topk_ids),
+                                           _ptr(topk_vals), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream)), "nanospec_batch_decode_step")
+
+
+def alloc_batch_decode_workspace(B: int, w_max: int, n_tuple: int, M: int, k: int, d: int,
+                                 device="cuda") -> torch.Tensor:
+    """A 256-byte-aligned uint8 workspace of nanospec_batch_decode_step_workspace_bytes."""
+    nbytes = nanospec_batch_decode_step_workspace_bytes(B, w_max, n_tuple, M, k, d)
+    if nbytes == 0:
+        raise NanoSpecError(NS_EINVAL, "nanospec_batch_decode_step_workspace_bytes")
+    mem = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-mem.data_ptr()) % 256
+    return mem[off:off + nbytes]
 
 
 def alloc_batch_workspace(B: int, n_max: int, M: int, k: int, d: int, device="cuda") -> torch.Tensor:

@@ -474,6 +474,41 @@ int nanospec_decode_step_select(nanospec_state* st, int32_t* active_ids, int32_t
                                 int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* The decode step for B independent sequences in one call: the results of
+ *   nanospec_batch_step_update(bt, draft_ids, draft_stride, n_draft, nd_max,
+ *                              ver_ids, ver_stride, n_ver, nv_max,
+ *                              active_ids, n_active, NULL, stream);
+ *   nanospec_batch_draft_logits_topk(w, active_ids, n_active, w_max, B, V, d,
+ *                                    dtype, h, M, k, NULL, topk_ids,
+ *                                    topk_vals, ws, ws_bytes, stream);
+ * bit for bit, for every sequence (Sec. 3.2 decoding phase and window
+ * rebuild, then Sec. 3.1 Eq. 1 with T_k, per sequence).  Arguments and
+ * layouts as in those two calls: sequence b's tuples at draft_ids + b *
+ * draft_stride (n_draft[b] <= nd_max of them, device counts) and ver_ids + b *
+ * ver_stride, its I_{t+1} at active_ids + b * w_max, its hidden rows at h + b
+ * * M * d, its top-k at topk_ids / topk_vals + b * M * k.  When every member
+ * keeps I_t (its previous step was a batched or single decode step) and the
+ * shapes allow it (as for nanospec_decode_step, with nd_max + nv_max <= 256;
+ * not for M <= 8 with B >= 32, where the separate batched head's taller tiles
+ * are faster), the step takes two launches: one state-update block per sequence beside the
+ * projection of the sequences' tuple and I_t columns, then the merge.
+ * Otherwise the three separate launches run (and a copy of every I_{t+1}
+ * into its state when the shapes allow the two-launch form).  A member in the
+ * CTX_ONLY stream mode is refused, as by nanospec_batch_step_update.
+ *   ws : >= nanospec_batch_decode_step_workspace_bytes(B, w_max,
+ *        nd_max + nv_max, M, k, d) bytes, 256-byte aligned.
+ * Errors: NS_EINVAL, NS_EDTYPE, NS_ECAPACITY, NS_EHIP (see the conventions on
+ * kernels already enqueued). */
+size_t nanospec_batch_decode_step_workspace_bytes(int32_t B, int32_t w_max, int32_t n_tuple,
+                                                  int32_t M, int32_t k, int32_t d);
+int nanospec_batch_decode_step(nanospec_batch* bt, const int32_t* draft_ids, int32_t draft_stride,
+                               const int32_t* n_draft, int32_t nd_max, const int32_t* ver_ids,
+                               int32_t ver_stride, const int32_t* n_ver, int32_t nv_max,
+                               int32_t* active_ids, int32_t* n_active, const void* w, int32_t V,
+                               int32_t d, int32_t dtype, const void* h, int32_t M, int32_t k,
+                               int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* Best-k selection over draft-tree candidates, B independent selections:
  *   vals, ids : [B x C] candidate scores and token ids (device); id -1 marks
  *               an empty candidate, which is never selected;

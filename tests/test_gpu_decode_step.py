@@ -366,3 +366,84 @@ def test_decode_step_bad_ids(ns):
         I = seq.active()
         assert nn == len(I) and np.array_equal(pair.a[0][:nn].cpu().numpy(), I), f"step {t}: active set vs oracle"
     assert ns.nanospec_state_status(pair.st_a) == ns.nanospec_state_status(pair.st_b) != 0
+
+
+@pytest.mark.parametrize("B", [1, 4, 32])
+def test_batch_decode_step(ns, B):
+    """B Llama-shaped sequences (B = 1 takes the single sequence's resident
+    grid; B = 32 keeps the three launches, where the separate batched head
+    takes taller tiles): nanospec_batch_decode_step on one batch,
+    nanospec_batch_step_update and nanospec_batch_draft_logits_topk on a twin,
+    identical bit for bit at every step; per-sequence tuple counts differ (so
+    the tuple columns are padded), the first step takes three launches and
+    the others two, and the first, middle and last sequences' active sets and
+    top-k match their own oracle sequences on sampled steps."""
+    steps = 10
+    cfg = WL.get_config("llama3_8b")
+    V, w_max, d, M, k = cfg.V, cfg.w_max, cfg.d, cfg.M, cfg.k
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    cfgs = [WL.get_config("llama3_8b", seed=cfg.seed + 100 * b) for b in range(B)]
+    scripts = [WL.make_id_script(c, steps) for c in cfgs]
+    nd_max, nv_max = cfg.n_tree, cfg.k_ver
+    A, Bt = ns.NanoSpecBatch(B, V, w_max), ns.NanoSpecBatch(B, V, w_max)
+    seqs = []
+    for b in range(B):
+        seq = O.Sequence_(w_max)
+        seq.append_prompt(scripts[b].prompt)
+        seqs.append(seq)
+        for bt in (A, Bt):
+            ns.nanospec_stream_append(bt.member(b), dev_i32(scripts[b].prompt), len(scripts[b].prompt), 0)
+    mk = lambda: (torch.full((B, w_max), -7, dtype=torch.int32, device="cuda"),
+                  torch.zeros(B, dtype=torch.int32, device="cuda"),
+                  torch.empty((B, M, k), dtype=torch.int32, device="cuda"),
+                  torch.empty((B, M, k), dtype=torch.float32, device="cuda"))
+    oa, ob = mk(), mk()
+    ws_a = ns.alloc_batch_decode_workspace(B, w_max, nd_max + nv_max, M, k, d)
+    ws_b = ns.alloc_batch_workspace(B, w_max, M, k, d)
+    rng = np.random.default_rng(21)
+    for t in range(steps):
+        trees, vers = [], []
+        for b in range(B):
+            tree, ver = scripts[b].tree[t], scripts[b].ver[t]
+            keep_t = len(tree) - int(rng.integers(0, 20)) if b % 2 else len(tree)
+            keep_v = len(ver) - int(rng.integers(0, 4)) if b == 3 else len(ver)
+            trees.append(tree[:keep_t])
+            vers.append(ver[:keep_v])
+        dr = np.full((B, nd_max), -1, np.int32)
+        vr = np.full((B, nv_max), -1, np.int32)
+        for b in range(B):
+            dr[b, :len(trees[b])] = trees[b]
+            vr[b, :len(vers[b])] = vers[b]
+        d_dev, v_dev = dev_i32(dr.reshape(-1)), dev_i32(vr.reshape(-1))
+        nd_dev = dev_i32(np.array([len(x) for x in trees], np.int32))
+        nv_dev = dev_i32(np.array([len(x) for x in vers], np.int32))
+        hs = [WL.make_hidden(cfgs[b], t) for b in range(B)]
+        h_dev = dev_elems(np.stack(hs), cfg.dtype)
+        ws_a.view(torch.int32)[0] = SENTINEL
+        ns.nanospec_batch_decode_step(A, d_dev, nd_max, nd_dev, nd_max, v_dev, nv_max, nv_dev, nv_max, oa[0], oa[1],
+                                      W_dev, V, d, ns.NS_BF16, h_dev, M, k, oa[2], oa[3], ws_a)
+        ns.nanospec_batch_step_update(Bt, d_dev, nd_max, nd_dev, nd_max, v_dev, nv_max, nv_dev, nv_max, ob[0], ob[1])
+        ns.nanospec_batch_draft_logits_topk(W_dev, ob[0], ob[1], w_max, B, V, d, ns.NS_BF16, h_dev, M, k, None,
+                                            ob[2], ob[3], ws_b)
+        torch.cuda.synchronize()
+        fused = int(ws_a.view(torch.int32)[0].item()) != SENTINEL
+        assert fused == (t > 0 and B < 32), f"step {t}: launch form"
+        assert torch.equal(oa[1], ob[1]), f"step {t}: counts differ"
+        for b in range(B):
+            nb = int(oa[1][b].item())
+            assert torch.equal(oa[0][b, :nb], ob[0][b, :nb]), f"step {t} seq {b}: active sets differ"
+        assert torch.equal(oa[2], ob[2]) and torch.equal(oa[3], ob[3]), f"step {t}: top-k differs"
+        for b in range(B):
+            seqs[b].step(trees[b], vers[b])
+        if t % 3 and t != steps - 1:
+            continue
+        for b in sorted({0, B // 2, B - 1}):
+            I = seqs[b].active()
+            nb = int(oa[1][b].item())
+            assert nb == len(I) and np.array_equal(oa[0][b, :nb].cpu().numpy(), I), f"step {t} seq {b}: vs oracle"
+            ref, o_ids, o_vals = O.draft_head(hs[b], W, I, k, cfg.dtype)
+            check_topk(oa[2][b].cpu().numpy(), oa[3][b].cpu().numpy(), ref, I, o_ids, o_vals, k, f"step {t} seq {b}")
+        say(f"batch decode step B={B} t={t}: {'two' if fused else 'three'} launches, ok")
+    for b in range(B):
+        assert ns.nanospec_state_status(A.member(b)) == 0
