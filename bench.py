@@ -1500,20 +1500,15 @@ def ablation_leg(torch, ns, WL, cfg, W, dcode, flush, steps=48, warm=16):
         torch.cuda.synchronize()
         n_mean = float(torch.stack(sizes).float().mean().item())
 
-        def decode_body():
-            for t in range(warm, T):
-                flush(t)
-                decode(t)
-
-        def timed(fn, dec=False):
-            init(dec)
+        def timed(fn):
+            init()
             torch.cuda.synchronize()
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 fn()
             ts = []
             for _ in range(3):
-                init(dec)
+                init()
                 torch.cuda.synchronize()
                 a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
