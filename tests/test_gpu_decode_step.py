@@ -16,7 +16,10 @@ hidden tiles), two hidden tiles, fp16, a tiny fp32 head (always three
 launches), both stream-source modes, a HIP graph of fused steps, the step
 split into nanospec_decode_step_project and _select, the state's bitmap after
 the steps, and the edge cases of the form: tuples past 256 entries, empty
-tuples, W_max not a multiple of 4, and ids outside [0, V)."""
+tuples, W_max not a multiple of 4, and ids outside [0, V).  The batched
+decode step (nanospec_batch_decode_step) against the separate batched calls:
+Llama-shaped B = 1, 4, 32, two hidden tiles in fp16, Qwen-shaped B = 2 and 3,
+with per-sequence tuple counts."""
 import numpy as np
 import pytest
 import torch
@@ -368,22 +371,35 @@ def test_decode_step_bad_ids(ns):
     assert ns.nanospec_state_status(pair.st_a) == ns.nanospec_state_status(pair.st_b) != 0
 
 
-@pytest.mark.parametrize("B", [1, 4, 32])
-def test_batch_decode_step(ns, B):
-    """B Llama-shaped sequences (B = 1 takes the single sequence's resident
-    grid; B = 32 keeps the three launches, where the separate batched head
-    takes taller tiles): nanospec_batch_decode_step on one batch,
+@pytest.mark.parametrize("name,B,M,dtype,two", [
+    ("llama3_8b", 1, None, None, True),       # the single sequence's resident grid
+    ("llama3_8b", 4, None, None, True),
+    ("llama3_8b", 32, None, None, False),     # the separate batched head's taller tiles
+    ("llama3_8b", 5, 20, "fp16", True),       # two hidden tiles, fp16
+    ("qwen25_7b", 2, None, None, True),       # four hidden tiles
+    ("qwen25_7b", 3, None, None, False),      # the M-split projection
+])
+def test_batch_decode_step(ns, name, B, M, dtype, two):
+    """B sequences of one workload (`two`: whether the steps after the first
+    take two launches; the forms that keep three are the shapes whose
+    separate batched head takes taller tiles or the M-split projection):
+    nanospec_batch_decode_step on one batch,
     nanospec_batch_step_update and nanospec_batch_draft_logits_topk on a twin,
     identical bit for bit at every step; per-sequence tuple counts differ (so
     the tuple columns are padded), the first step takes three launches and
     the others two, and the first, middle and last sequences' active sets and
     top-k match their own oracle sequences on sampled steps."""
     steps = 10
-    cfg = WL.get_config("llama3_8b")
-    V, w_max, d, M, k = cfg.V, cfg.w_max, cfg.d, cfg.M, cfg.k
+    cfg = WL.get_config(name)
+    M, dtype = M or cfg.M, dtype or cfg.dtype
+    V, w_max, d, k = cfg.V, cfg.w_max, cfg.d, cfg.k
+    say(f"batch decode step {name} B={B} M={M} {dtype}: generating inputs")
     W = WL.make_weights(cfg)
-    W_dev = dev_elems(W, cfg.dtype)
-    cfgs = [WL.get_config("llama3_8b", seed=cfg.seed + 100 * b) for b in range(B)]
+    if dtype != cfg.dtype:                                 # fp16 copies of the bf16 weights
+        W = WL.f32_to_fp16_bits(WL.bf16_bits_to_f32(W))
+    W_dev = dev_elems(W, dtype)
+    dcode = dcode_of(ns, dtype)
+    cfgs = [WL.get_config(name, seed=cfg.seed + 100 * b) for b in range(B)]
     scripts = [WL.make_id_script(c, steps) for c in cfgs]
     nd_max, nv_max = cfg.n_tree, cfg.k_ver
     A, Bt = ns.NanoSpecBatch(B, V, w_max), ns.NanoSpecBatch(B, V, w_max)
@@ -418,17 +434,19 @@ def test_batch_decode_step(ns, B):
         d_dev, v_dev = dev_i32(dr.reshape(-1)), dev_i32(vr.reshape(-1))
         nd_dev = dev_i32(np.array([len(x) for x in trees], np.int32))
         nv_dev = dev_i32(np.array([len(x) for x in vers], np.int32))
-        hs = [WL.make_hidden(cfgs[b], t) for b in range(B)]
-        h_dev = dev_elems(np.stack(hs), cfg.dtype)
+        hs = [WL.make_hidden(cfgs[b], t, M=M) for b in range(B)]
+        if dtype != cfg.dtype:
+            hs = [WL.f32_to_fp16_bits(WL.bf16_bits_to_f32(x)) for x in hs]
+        h_dev = dev_elems(np.stack(hs), dtype)
         ws_a.view(torch.int32)[0] = SENTINEL
         ns.nanospec_batch_decode_step(A, d_dev, nd_max, nd_dev, nd_max, v_dev, nv_max, nv_dev, nv_max, oa[0], oa[1],
-                                      W_dev, V, d, ns.NS_BF16, h_dev, M, k, oa[2], oa[3], ws_a)
+                                      W_dev, V, d, dcode, h_dev, M, k, oa[2], oa[3], ws_a)
         ns.nanospec_batch_step_update(Bt, d_dev, nd_max, nd_dev, nd_max, v_dev, nv_max, nv_dev, nv_max, ob[0], ob[1])
-        ns.nanospec_batch_draft_logits_topk(W_dev, ob[0], ob[1], w_max, B, V, d, ns.NS_BF16, h_dev, M, k, None,
+        ns.nanospec_batch_draft_logits_topk(W_dev, ob[0], ob[1], w_max, B, V, d, dcode, h_dev, M, k, None,
                                             ob[2], ob[3], ws_b)
         torch.cuda.synchronize()
         fused = int(ws_a.view(torch.int32)[0].item()) != SENTINEL
-        assert fused == (t > 0 and B < 32), f"step {t}: launch form"
+        assert fused == (t > 0 and two), f"step {t}: launch form"
         assert torch.equal(oa[1], ob[1]), f"step {t}: counts differ"
         for b in range(B):
             nb = int(oa[1][b].item())
@@ -442,7 +460,7 @@ def test_batch_decode_step(ns, B):
             I = seqs[b].active()
             nb = int(oa[1][b].item())
             assert nb == len(I) and np.array_equal(oa[0][b, :nb].cpu().numpy(), I), f"step {t} seq {b}: vs oracle"
-            ref, o_ids, o_vals = O.draft_head(hs[b], W, I, k, cfg.dtype)
+            ref, o_ids, o_vals = O.draft_head(hs[b], W, I, k, dtype)
             check_topk(oa[2][b].cpu().numpy(), oa[3][b].cpu().numpy(), ref, I, o_ids, o_vals, k, f"step {t} seq {b}")
         say(f"batch decode step B={B} t={t}: {'two' if fused else 'three'} launches, ok")
     for b in range(B):
