@@ -18,7 +18,7 @@ split into nanospec_decode_step_project and _select, the state's bitmap after
 the steps, and the edge cases of the form: tuples past 256 entries, empty
 tuples, W_max not a multiple of 4, and ids outside [0, V).  The batched
 decode step (nanospec_batch_decode_step) against the separate batched calls:
-Llama-shaped B = 1, 4, 32, two hidden tiles in fp16, Qwen-shaped B = 2 and 3,
+Llama-shaped B = 1, 4, 32, M = 12, 40, and 20 in fp16, Qwen-shaped B = 2 and 3,
 with per-sequence tuple counts."""
 import numpy as np
 import pytest
@@ -375,7 +375,9 @@ def test_decode_step_bad_ids(ns):
     ("llama3_8b", 1, None, None, True),       # the single sequence's resident grid
     ("llama3_8b", 4, None, None, True),
     ("llama3_8b", 32, None, None, False),     # the separate batched head's taller tiles
+    ("llama3_8b", 3, 12, None, True),         # one hidden tile of 9-16 rows
     ("llama3_8b", 5, 20, "fp16", True),       # two hidden tiles, fp16
+    ("llama3_8b", 2, 40, None, True),         # three hidden tiles
     ("qwen25_7b", 2, None, None, True),       # four hidden tiles
     ("qwen25_7b", 3, None, None, False),      # the M-split projection
 ])
