@@ -19,7 +19,8 @@ the steps, and the edge cases of the form: tuples past 256 entries, empty
 tuples, W_max not a multiple of 4, and ids outside [0, V).  The batched
 decode step (nanospec_batch_decode_step) against the separate batched calls:
 Llama-shaped B = 1, 4, 32, M = 12, 40, and 20 in fp16, Qwen-shaped B = 2 and 3,
-with per-sequence tuple counts."""
+with per-sequence tuple counts; and batched steps between single-sequence
+calls on members (an append, a single decode step)."""
 import numpy as np
 import pytest
 import torch
@@ -467,3 +468,83 @@ def test_batch_decode_step(ns, name, B, M, dtype, two):
         say(f"batch decode step B={B} t={t}: {'two' if fused else 'three'} launches, ok")
     for b in range(B):
         assert ns.nanospec_state_status(A.member(b)) == 0
+
+
+def test_batch_decode_step_with_member_calls(ns):
+    """Three Llama-shaped sequences through nanospec_batch_decode_step while
+    single-sequence calls act on members between the batched steps: an append
+    to one member (the next batched step takes three launches, the one after
+    two), then a single decode step on member 0 alone (the next batched step
+    still takes two).  The twin batch takes the separate calls throughout;
+    results agree bit for bit, and every member's active set matches its
+    oracle sequence at the end."""
+    B, steps = 3, 7
+    cfg = WL.get_config("llama3_8b")
+    V, w_max, d, M, k = cfg.V, cfg.w_max, cfg.d, cfg.M, cfg.k
+    W = WL.make_weights(cfg)
+    W_dev = dev_elems(W, cfg.dtype)
+    cfgs = [WL.get_config("llama3_8b", seed=cfg.seed + 300 * b) for b in range(B)]
+    scripts = [WL.make_id_script(c, steps) for c in cfgs]
+    nd, nv = cfg.n_tree, cfg.k_ver
+    A, Bt = ns.NanoSpecBatch(B, V, w_max), ns.NanoSpecBatch(B, V, w_max)
+    seqs = [O.Sequence_(w_max) for _ in range(B)]
+    for b in range(B):
+        seqs[b].append_prompt(scripts[b].prompt)
+        for bt in (A, Bt):
+            ns.nanospec_stream_append(bt.member(b), dev_i32(scripts[b].prompt), len(scripts[b].prompt), 0)
+    mk = lambda: (torch.empty((B, w_max), dtype=torch.int32, device="cuda"),
+                  torch.zeros(B, dtype=torch.int32, device="cuda"),
+                  torch.empty((B, M, k), dtype=torch.int32, device="cuda"),
+                  torch.empty((B, M, k), dtype=torch.float32, device="cuda"))
+    oa, ob = mk(), mk()
+    ws_a = ns.alloc_batch_decode_workspace(B, w_max, nd + nv, M, k, d)
+    ws_b = ns.alloc_batch_workspace(B, w_max, M, k, d)
+    ws_1 = ns.alloc_decode_workspace(w_max, nd + nv, M, k, d)
+    ws_1b = ns.alloc_workspace(w_max, M, k, d)
+    counts = lambda x: dev_i32(np.full(B, x, np.int32))
+    expect = {0: False, 1: True, 2: False, 3: True, 5: True, 6: True}   # batched steps: two launches?
+    for t in range(steps):
+        h = [WL.make_hidden(cfgs[b], t) for b in range(B)]
+        if t == 2:                                         # an append to member 1 drops its I_t
+            extra = np.array([5, 77, 1234, 9], np.int32)
+            seqs[1].append_prompt(extra)
+            for bt in (A, Bt):
+                ns.nanospec_stream_append(bt.member(1), dev_i32(extra), len(extra), 0)
+        if t == 4:                                         # member 0 alone, single-sequence calls
+            tr, vr = scripts[0].tree[t], scripts[0].ver[t]
+            td, vd, hd = dev_i32(tr), dev_i32(vr), dev_elems(h[0], cfg.dtype)
+            ns.nanospec_decode_step(A.member(0), td, nd, vd, nv, oa[0][0], oa[1][0:1], W_dev, V, d, ns.NS_BF16, hd,
+                                    M, k, oa[2][0], oa[3][0], ws_1)
+            ns.nanospec_step_update(Bt.member(0), td, nd, vd, nv, ob[0][0], ob[1][0:1])
+            ns.nanospec_draft_logits_topk(W_dev, ns.NS_INDEXED, ob[0][0], ob[1][0:1], w_max, V, d, ns.NS_BF16, hd,
+                                          M, k, None, ob[2][0], ob[3][0], ws_1b)
+            seqs[0].step(tr, vr)
+            torch.cuda.synchronize()
+            n0 = int(oa[1][0].item())
+            assert n0 == int(ob[1][0].item()) and torch.equal(oa[0][0, :n0], ob[0][0, :n0])
+            assert torch.equal(oa[2][0], ob[2][0]) and torch.equal(oa[3][0], ob[3][0]), "member 0 single step"
+            continue
+        dr = dev_i32(np.stack([scripts[b].tree[t] for b in range(B)]).reshape(-1))
+        vr = dev_i32(np.stack([scripts[b].ver[t] for b in range(B)]).reshape(-1))
+        h_dev = dev_elems(np.stack(h), cfg.dtype)
+        ws_a.view(torch.int32)[0] = SENTINEL
+        ns.nanospec_batch_decode_step(A, dr, nd, counts(nd), nd, vr, nv, counts(nv), nv, oa[0], oa[1], W_dev, V, d,
+                                      ns.NS_BF16, h_dev, M, k, oa[2], oa[3], ws_a)
+        ns.nanospec_batch_step_update(Bt, dr, nd, counts(nd), nd, vr, nv, counts(nv), nv, ob[0], ob[1])
+        ns.nanospec_batch_draft_logits_topk(W_dev, ob[0], ob[1], w_max, B, V, d, ns.NS_BF16, h_dev, M, k, None,
+                                            ob[2], ob[3], ws_b)
+        for b in range(B):
+            seqs[b].step(scripts[b].tree[t], scripts[b].ver[t])
+        torch.cuda.synchronize()
+        fused = int(ws_a.view(torch.int32)[0].item()) != SENTINEL
+        assert fused == expect[t], f"step {t}: launch form"
+        assert torch.equal(oa[1], ob[1]), f"step {t}: counts differ"
+        for b in range(B):
+            nb = int(oa[1][b].item())
+            assert torch.equal(oa[0][b, :nb], ob[0][b, :nb]), f"step {t} seq {b}: active sets differ"
+        assert torch.equal(oa[2], ob[2]) and torch.equal(oa[3], ob[3]), f"step {t}: top-k differs"
+        say(f"batch decode with member calls, step {t}: {'two' if fused else 'three'} launches, ok")
+    for b in range(B):
+        I = seqs[b].active()
+        nb = int(oa[1][b].item())
+        assert nb == len(I) and np.array_equal(oa[0][b, :nb].cpu().numpy(), I), f"seq {b}: vs oracle"
