@@ -67,6 +67,13 @@ int check_sizes() {
             const size_t wb = nanospec_batch_draft_workspace_bytes(B, n, M, k, d);
             if (B < 1 || B > NS_MAX_BATCH || w == 0) CHECK(wb == 0);
             else if (B == 1) CHECK(wb == w);
+            // the batched decode step: zero exactly where the separate batched head's is (for a valid
+            // tuple bound and n <= NS_MAX_WMAX), else at least as large
+            if (n <= NS_MAX_WMAX) {
+              const size_t wd = nanospec_batch_decode_step_workspace_bytes(B, n, 68, M, k, d);
+              CHECK(wb == 0 ? wd == 0 : (wd >= wb && wd % 256 == 0));
+              CHECK(nanospec_batch_decode_step_workspace_bytes(B, n, -1, M, k, d) == 0);
+            }
           }
         }
   return 0;
@@ -100,6 +107,10 @@ int check_rejections() {
   CHECK(nanospec_batch_step_update(nullptr, (const int32_t*)fake(1), 4, (const int32_t*)fake(2), 4,
                                    (const int32_t*)fake(3), 4, (const int32_t*)fake(4), 4, (int32_t*)fake(5),
                                    (int32_t*)fake(6), nullptr, nullptr) == NS_EINVAL);
+  CHECK(nanospec_batch_decode_step(nullptr, (const int32_t*)fake(1), 4, (const int32_t*)fake(2), 4,
+                                   (const int32_t*)fake(3), 4, (const int32_t*)fake(4), 4, (int32_t*)fake(5),
+                                   (int32_t*)fake(6), fake(7), 100, 64, NS_BF16, fake(8), 8, 8, (int32_t*)fake(9),
+                                   (float*)fake(10), fake(11), 1 << 20, nullptr) == NS_EINVAL);
   nanospec_packed* pk = nullptr;
   CHECK(nanospec_packed_create(&pk, 10, 0, fake(0), 1 << 20, nullptr) == NS_EINVAL);
   CHECK(nanospec_packed_create(&pk, 10, 4, fake(0), 16, nullptr) == NS_ECAPACITY);

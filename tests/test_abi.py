@@ -70,6 +70,13 @@ def test_codes_and_sizes(ns):
     assert dw >= L.nanospec_draft_workspace_bytes(3072, 8, 8, 4096) and dw % 256 == 0
     assert L.nanospec_decode_step_workspace_bytes(3072, -1, 8, 8, 4096) == 0
     assert L.nanospec_decode_step_workspace_bytes(3072, 68, 65, 8, 4096) == 0
+    # the batched decode step: B regions of the decode step, at least the separate batched head's
+    bw = L.nanospec_batch_decode_step_workspace_bytes(8, 3072, 68, 8, 8, 4096)
+    assert bw >= L.nanospec_batch_draft_workspace_bytes(8, 3072, 8, 8, 4096) and bw % 256 == 0
+    assert bw >= 8 * 3072 * 8 * 4 and bw > L.nanospec_batch_decode_step_workspace_bytes(1, 3072, 68, 8, 8, 4096)
+    assert L.nanospec_batch_decode_step_workspace_bytes(0, 3072, 68, 8, 8, 4096) == 0
+    assert L.nanospec_batch_decode_step_workspace_bytes(ns.NS_MAX_BATCH + 1, 3072, 68, 8, 8, 4096) == 0
+    assert L.nanospec_batch_decode_step_workspace_bytes(8, 3072, -1, 8, 8, 4096) == 0
 
 
 def test_host_validation_rejects_before_launch(ns):
@@ -90,6 +97,8 @@ def test_host_validation_rejects_before_launch(ns):
                                           fake, 1 << 20, None) == ns.NS_EINVAL
     assert L.nanospec_decode_step_select(None, fake, fake, 100, 64, ns.NS_BF16, 8, 8, fake, fake, fake, 1 << 20,
                                          None) == ns.NS_EINVAL
+    assert L.nanospec_batch_decode_step(None, fake, 3, fake, 3, fake, 1, fake, 1, fake, fake, fake, 100, 64,
+                                        ns.NS_BF16, fake, 8, 8, fake, fake, fake, 1 << 20, None) == ns.NS_EINVAL
     # gather: null, bad d, bad dtype, misaligned
     assert L.nanospec_gather_rows(None, 10, 8, 0, fake, None, 4, fake, None) == ns.NS_EINVAL
     assert L.nanospec_gather_rows(fake, 10, 12, 0, fake, None, 4, fake, None) == ns.NS_EINVAL
